@@ -1,0 +1,138 @@
+"""CPU oracle for the weight-streaming skinny matmul (TEST INFRASTRUCTURE ONLY).
+
+A plain fp64 C implementation (oracle.c) behind ctypes.  Only the tests, the
+smoke check and the bench's CPU-baseline leg may import this package; the
+library's product path never does, and this code shares nothing with it.
+
+All 16-bit float arrays cross this boundary as raw bit patterns (numpy uint16).
+
+What each function follows (page titles and sections; no code is taken from
+the pages, which print none for these steps):
+  mm          -- nx_batchscale_kat: C[m,n] = A[m,k] . W[k,n]; W stored [n][k]
+  dequant     -- opus r35 track A, section 1 (`dq_f16` to f16 weights), with the
+                 Q8_0-style format: blocks of 32 along k, int8 q, f16 scale d,
+                 w = RNE_f16(d * q)
+  topk        -- Strata PR #109, "What" (router top-10 per token), ties to the
+                 lower index
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+F16, BF16, Q8_0 = 1, 2, 4
+_KINDS = {"f16": F16, "bf16": BF16, "q8_0": Q8_0}
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_build.LIB):
+        _build.build()
+    lib = ctypes.CDLL(_build.LIB)
+    i64, i32, vp = ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p
+    lib.oracle_f16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_f16_to_f64.restype = ctypes.c_double
+    lib.oracle_bf16_to_f64.argtypes = [ctypes.c_uint16]
+    lib.oracle_bf16_to_f64.restype = ctypes.c_double
+    lib.oracle_f64_to_f16_rne.argtypes = [ctypes.c_double]
+    lib.oracle_f64_to_f16_rne.restype = ctypes.c_uint16
+    lib.oracle_dequant_q8_0.argtypes = [i64, i64, vp, vp, vp]
+    lib.oracle_dequant_q8_0.restype = ctypes.c_int
+    lib.oracle_mm.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int, vp, vp, vp,
+                              i64, ctypes.c_int, ctypes.c_int]
+    lib.oracle_mm.restype = ctypes.c_int
+    lib.oracle_topk.argtypes = [i64, i64, vp, i64, i32, vp, vp]
+    lib.oracle_topk.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def default_threads() -> int:
+    try:
+        return max(1, len(os.sched_getaffinity(0)))
+    except AttributeError:  # pragma: no cover
+        return os.cpu_count() or 1
+
+
+def _ptr(a: np.ndarray):
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+def f16_to_f64(bits) -> float:
+    return _load().oracle_f16_to_f64(int(bits))
+
+
+def bf16_to_f64(bits) -> float:
+    return _load().oracle_bf16_to_f64(int(bits))
+
+
+def f64_to_f16_rne(x: float) -> int:
+    return int(_load().oracle_f64_to_f16_rne(float(x)))
+
+
+def decode(bits: np.ndarray, kind: str) -> np.ndarray:
+    """fp64 values of an array of f16 / bf16 bit patterns (elementwise)."""
+    lib = _load()
+    fn = lib.oracle_bf16_to_f64 if kind == "bf16" else lib.oracle_f16_to_f64
+    flat = np.ascontiguousarray(bits, dtype=np.uint16).ravel()
+    lut = np.array([fn(v) for v in range(65536)], dtype=np.float64)
+    return lut[flat].reshape(np.shape(bits))
+
+
+def dequant_q8_0(qs: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """f16 bits [n][k] of RNE_f16(d[j][kk/32] * qs[j][kk])."""
+    qs = np.ascontiguousarray(qs, dtype=np.int8)
+    d = np.ascontiguousarray(d, dtype=np.uint16)
+    n, k = qs.shape
+    assert d.shape == (n, k // 32), (d.shape, qs.shape)
+    out = np.empty((n, k), dtype=np.uint16)
+    rc = _load().oracle_dequant_q8_0(n, k, _ptr(qs), _ptr(d), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_dequant_q8_0 failed ({rc})")
+    return out
+
+
+def mm(A: np.ndarray, a_kind: str, W: np.ndarray, w_kind: str, w_scales=None,
+       threads=None, absolute=False) -> np.ndarray:
+    """fp64 C[m][n] = sum_kk A[i][kk] * W[j][kk] (W stored [n][k]).
+
+    A: uint16 bits [m][k]; W: uint16 bits [n][k], or int8 codes [n][k] for
+    q8_0 with w_scales uint16 bits [n][k/32].  absolute=True returns
+    sum |A| * |W| instead (the fp32 rounding-error yardstick).
+    """
+    A = np.ascontiguousarray(A, dtype=np.uint16)
+    m, k = A.shape
+    if w_kind == "q8_0":
+        W = np.ascontiguousarray(W, dtype=np.int8)
+        w_scales = np.ascontiguousarray(w_scales, dtype=np.uint16)
+        sp = _ptr(w_scales)
+    else:
+        W = np.ascontiguousarray(W, dtype=np.uint16)
+        sp = None
+    n, k2 = W.shape
+    assert k2 == k, (A.shape, W.shape)
+    C = np.zeros((m, n), dtype=np.float64)
+    t = default_threads() if threads is None else int(threads)
+    rc = _load().oracle_mm(m, n, k, _KINDS[a_kind], _ptr(A), k, _KINDS[w_kind], _ptr(W), sp,
+                           _ptr(C), n, t, 1 if absolute else 0)
+    if rc != 0:
+        raise ValueError(f"oracle_mm failed ({rc})")
+    return C
+
+
+def topk(logits: np.ndarray, k: int):
+    """Per-row top-k: (idx int32 [m][k], val fp64 [m][k]), value desc, index asc."""
+    L = np.ascontiguousarray(logits, dtype=np.float64)
+    m, n = L.shape
+    idx = np.empty((m, k), dtype=np.int32)
+    val = np.empty((m, k), dtype=np.float64)
+    rc = _load().oracle_topk(m, n, _ptr(L), n, k, _ptr(idx), _ptr(val))
+    if rc != 0:
+        raise ValueError(f"oracle_topk failed ({rc})")
+    return idx, val

@@ -1,0 +1,305 @@
+"""Pins of the CPU oracle to things other than itself (CPU only).
+
+Every check below compares the oracle with an independent source: the hand
+examples in tests/golden/ (each file cites the page passage it follows), exact
+integer / rational arithmetic, numpy's and Python's own routines (f16 casts,
+BLAS dgemm, math.fsum, sorted), or closed forms.  They are chosen so that a
+plausible slip in the oracle -- a dropped term, a swapped operand, a wrong
+sign, an off-by-one in the block index, round-toward-zero instead of
+round-to-nearest-even -- fails at least one of them.
+"""
+import math
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads as WL
+from conftest import golden_lines
+
+F16_ALL = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+
+
+def np_f16(bits):
+    return np.asarray(bits, dtype=np.uint16).view(np.float16).astype(np.float64)
+
+
+def np_bf16(bits):
+    b = np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16
+    with np.errstate(invalid="ignore"):
+        return b.view(np.float32).astype(np.float64)
+
+
+def rounding_bound(k, abs_sum):
+    """Rigorous bound on |fl_fp64(sum) - exact| for a sequential sum of k exact
+    products: gamma_k * sum|a*w| with unit roundoff u = 2^-53."""
+    u = 2.0 ** -53
+    return (k * u / (1 - k * u)) * abs_sum * 1.0000001 + 1e-300
+
+
+# ---------------------------------------------------------------------------
+# scalar formats
+# ---------------------------------------------------------------------------
+
+def test_f16_decode_matches_numpy_all_patterns():
+    got = oracle.decode(F16_ALL, "f16")
+    ref = np_f16(F16_ALL)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_bf16_decode_matches_float32_upper_half_all_patterns():
+    got = oracle.decode(F16_ALL, "bf16")
+    ref = np_bf16(F16_ALL)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], ref[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(ref[~nan]))
+
+
+def test_f64_to_f16_rne_matches_numpy_on_random_and_edge_values():
+    rng = np.random.default_rng(7)
+    mags = np.concatenate([
+        2.0 ** rng.uniform(-30, 17, 20000),        # subnormal .. overflow
+        np.array([65504.0, 65519.99, 65520.0, 65535.0, 2.0 ** -24, 2.0 ** -25,
+                  2.0 ** -25 * 1.0000001, 3 * 2.0 ** -26, 2.0 ** -14, 2.0 ** -14 * (1 - 2 ** -12),
+                  1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, 0.0]),
+    ])
+    vals = np.concatenate([mags, -mags])
+    got = np.array([oracle.f64_to_f16_rne(v) for v in vals], dtype=np.uint16)
+    with np.errstate(over="ignore"):
+        ref = vals.astype(np.float16).view(np.uint16)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, [(vals[i], hex(got[i]), hex(ref[i])) for i in bad[:5]]
+
+
+# ---------------------------------------------------------------------------
+# dequant
+# ---------------------------------------------------------------------------
+
+def test_dequant_golden_values():
+    rows = [line.split() for line in golden_lines("dequant_q8_0_rne.txt")]
+    for d_hex, q, exp_hex in rows:
+        qs = np.zeros((1, 32), np.int8)
+        qs[0, 5] = int(q)
+        d = np.array([[int(d_hex, 16)]], np.uint16)
+        out = oracle.dequant_q8_0(qs, d)
+        assert out[0, 5] == int(exp_hex, 16), (d_hex, q, hex(out[0, 5]), exp_hex)
+        assert out[0, 0] == 0  # q = 0 -> +0
+
+
+def test_dequant_exhaustive_every_finite_scale_every_code():
+    """All 63488 finite f16 scales x all 256 int8 codes against numpy's
+    correctly rounded float64 -> float16 cast of the exact product."""
+    d_all = F16_ALL[((F16_ALL >> 10) & 0x1F) != 0x1F]          # finite scales
+    codes = np.arange(-128, 128, dtype=np.int16).astype(np.int8)  # 256 codes = 8 blocks
+    n = d_all.size
+    qs = np.broadcast_to(codes, (n, 256)).copy()
+    d = np.repeat(d_all[:, None], 8, axis=1)
+    got = oracle.dequant_q8_0(qs, d)
+    exact = np_f16(d_all)[:, None] * codes.astype(np.float64)[None, :]
+    with np.errstate(over="ignore"):
+        ref = exact.astype(np.float16).view(np.uint16)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, bad[:5]
+
+
+def test_dequant_uses_the_scale_of_each_32_block():
+    # distinct scales per block: a wrong block index (kk/16, kk/64, kk%32) fails
+    k = 128
+    qs = np.ones((2, k), np.int8)
+    d = WL.to_f16_bits(np.array([[1.0, 2.0, 4.0, 8.0], [0.5, 0.25, 0.125, 16.0]]))
+    out = np_f16(oracle.dequant_q8_0(qs, d))
+    expect = np.repeat(np_f16(d), 32, axis=1)
+    assert np.array_equal(out, expect)
+
+
+# ---------------------------------------------------------------------------
+# matmul
+# ---------------------------------------------------------------------------
+
+def _parse_matrix(s):
+    return np.array([[float(x) for x in row.split()] for row in s.split(";")])
+
+
+def test_hand_example_2x3x4():
+    lines = dict(line.split(":", 1) for line in golden_lines("hand_2x3x4.txt"))
+    A = _parse_matrix(lines["A"])
+    Wl = _parse_matrix(lines["W_logical"])
+    C = _parse_matrix(lines["C"])
+    for kind in ("f16", "bf16"):
+        got = oracle.mm(WL.to_bits(A, kind), kind, WL.to_bits(Wl.T.copy(), kind), kind)
+        assert np.array_equal(got, C), (kind, got)
+    # padding k with zeros (the GPU path needs k % 8 == 0) leaves C unchanged
+    Ap = np.zeros((2, 8)); Ap[:, :3] = A
+    Wp = np.zeros((4, 8)); Wp[:, :3] = Wl.T
+    got = oracle.mm(WL.to_f16_bits(Ap), "f16", WL.to_f16_bits(Wp), "f16")
+    assert np.array_equal(got, C)
+
+
+@pytest.mark.parametrize("kind", ["f16", "bf16"])
+@pytest.mark.parametrize("shape", [(1, 1, 1), (2, 3, 5), (3, 7, 16), (5, 4, 33)])
+def test_brute_force_exact_rationals(kind, shape):
+    m, n, k = shape
+    A = WL.gen_matrix((m, k), kind, ("normal", 1.0), 11 + m)
+    W = WL.gen_matrix((n, k), kind, ("normal", 0.02), 13 + n)
+    got = oracle.mm(A, kind, W, kind, threads=2)
+    dec = np_bf16 if kind == "bf16" else np_f16
+    a, w = dec(A), dec(W)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(Fraction(a[i, t]) * Fraction(w[j, t]) for t in range(k))
+            abs_sum = float(sum(abs(Fraction(a[i, t]) * Fraction(w[j, t])) for t in range(k)))
+            err = abs(Fraction(got[i, j]) - exact)
+            assert float(err) <= rounding_bound(k, abs_sum), (i, j, float(err))
+
+
+def test_brute_force_exact_rationals_q8_0():
+    m, n, k = 3, 5, 64
+    A = WL.gen_matrix((m, k), "f16", ("normal", 1.0), 21)
+    qs, d = WL.gen_q8_0(n, k, 22, 23)
+    got = oracle.mm(A, "f16", qs, "q8_0", w_scales=d)
+    a = np_f16(A)
+    # dequant by numpy's correctly rounded cast (independent of the oracle's)
+    w = (np.repeat(np_f16(d), 32, axis=1) * qs.astype(np.float64)).astype(np.float16).astype(np.float64)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(Fraction(a[i, t]) * Fraction(w[j, t]) for t in range(k))
+            abs_sum = float(sum(abs(Fraction(a[i, t]) * Fraction(w[j, t])) for t in range(k)))
+            assert float(abs(Fraction(got[i, j]) - exact)) <= rounding_bound(k, abs_sum)
+
+
+def _exact_int64(a_f64, w_f64):
+    """Exact C for f16-valued inputs: every f16 value is an integer multiple of
+    2^-24, so scaled by 2^24 both operands are int64 and C*2^48 is an exact
+    int64 product (guarded against overflow)."""
+    ai = np.rint(a_f64 * 2.0 ** 24).astype(np.int64)
+    wi = np.rint(w_f64 * 2.0 ** 24).astype(np.int64)
+    assert np.array_equal(ai.astype(np.float64) * 2.0 ** -24, a_f64)
+    assert np.array_equal(wi.astype(np.float64) * 2.0 ** -24, w_f64)
+    k = ai.shape[1]
+    assert float(np.abs(ai).max()) * float(np.abs(wi).max()) * k < 2.0 ** 62
+    c = ai @ wi.T
+    ca = np.abs(ai) @ np.abs(wi).T
+    return c, ca  # both scaled by 2^48
+
+
+@pytest.mark.parametrize("name,rows,cols", [
+    ("gemv_k896", 16, None),          # the whole m=16 output
+    ("narrow_n96", 64, None),
+    ("wide_n7680", 6, None),
+    ("q8_0_n512", 16, None),
+])
+def test_exact_int64_at_workload_shapes(name, rows, cols):
+    wl = WL.WORKLOADS[name]
+    A = WL.gen_a(wl, rows)
+    W = WL.gen_w(wl)
+    if wl.w_kind == "q8_0":
+        qs, d = W
+        got = oracle.mm(A, "f16", qs, "q8_0", w_scales=d)
+        w = (np.repeat(np_f16(d), 32, axis=1) * qs.astype(np.float64)).astype(np.float16).astype(np.float64)
+    else:
+        got = oracle.mm(A, wl.a_kind, W, wl.w_kind)
+        w = np_f16(W)
+    c, ca = _exact_int64(np_f16(A), w)
+    exact = c.astype(np.float64) * 2.0 ** -48  # within one rounding of exact
+    abs_sum = ca.astype(np.float64) * 2.0 ** -48
+    bound = rounding_bound(wl.k, abs_sum) + np.abs(exact) * 2.0 ** -52
+    assert np.all(np.abs(got - exact) <= bound)
+    # and as a sanity check the error really is tiny relative to the output scale
+    assert np.max(np.abs(got - exact)) / np.max(np.abs(exact)) < 1e-13
+
+
+def test_bf16_router_against_fsum():
+    """bf16 products are exact in fp64 (8 + 8 significant bits), so math.fsum
+    of the products is the exactly rounded C; sampled rows of the router."""
+    wl = WL.WORKLOADS["router_topk"]
+    A = WL.gen_a(wl, 16)[[0, 7, 15]]
+    W = WL.gen_w(wl)
+    got = oracle.mm(A, "bf16", W, "bf16")
+    a, w = np_bf16(A), np_bf16(W)
+    for i in range(A.shape[0]):
+        prods = a[i][None, :] * w           # exact
+        for j in range(0, wl.n, 5):
+            exact = math.fsum(prods[j].tolist())
+            bound = rounding_bound(wl.k, math.fsum(np.abs(prods[j]).tolist())) + abs(exact) * 2.0 ** -52
+            assert abs(got[i, j] - exact) <= bound, (i, j)
+
+
+def test_matches_blas_dgemm():
+    wl = WL.WORKLOADS["wide_n7680"]
+    A = WL.gen_a(wl, 40)
+    W = WL.gen_w(wl, n=300)
+    got = oracle.mm(A, "f16", W, "f16")
+    a, w = np_f16(A), np_f16(W)
+    ref = a @ w.T
+    abs_sum = np.abs(a) @ np.abs(w).T
+    assert np.all(np.abs(got - ref) <= 2 * rounding_bound(wl.k, abs_sum))
+
+
+def test_absolute_mode_is_sum_of_magnitudes():
+    A = WL.gen_matrix((4, 96), "f16", ("normal", 1.0), 31)
+    W = WL.gen_matrix((9, 96), "f16", ("normal", 0.1), 32)
+    got = oracle.mm(A, "f16", W, "f16", absolute=True)
+    _, ca = _exact_int64(np_f16(A), np_f16(W))
+    exact = ca.astype(np.float64) * 2.0 ** -48
+    assert np.all(np.abs(got - exact) <= rounding_bound(96, exact) + exact * 2.0 ** -52)
+
+
+def test_one_hot_rows_pick_weight_columns_exactly():
+    wl = WL.WORKLOADS["gemv_k896"]
+    W = WL.gen_w(wl, n=50)
+    A = np.zeros((3, wl.k)); A[0, 0] = 1.0; A[1, 517] = 1.0; A[2, wl.k - 1] = -1.0
+    got = oracle.mm(WL.to_f16_bits(A), "f16", W, "f16")
+    w = np_f16(W)
+    assert np.array_equal(got[0], w[:, 0])
+    assert np.array_equal(got[1], w[:, 517])
+    assert np.array_equal(got[2], -w[:, wl.k - 1])
+
+
+def test_zero_a_gives_positive_zero():
+    W = WL.gen_matrix((7, 64), "bf16", ("normal", 0.02), 41)
+    got = oracle.mm(np.zeros((2, 64), np.uint16), "bf16", W, "bf16")
+    assert np.all(got == 0) and not np.any(np.signbit(got))
+
+
+def test_thread_count_does_not_change_bits():
+    wl = WL.WORKLOADS["gemv_k896"]
+    A = WL.gen_a(wl, 5)
+    W = WL.gen_w(wl, n=333)
+    c1 = oracle.mm(A, "f16", W, "f16", threads=1)
+    c7 = oracle.mm(A, "f16", W, "f16", threads=7)
+    assert np.array_equal(c1, c7)
+
+
+# ---------------------------------------------------------------------------
+# top-k
+# ---------------------------------------------------------------------------
+
+def test_topk_golden():
+    for line in golden_lines("topk_ties.txt"):
+        body = line.split(":", 1)[1]
+        vals, k, idx, top = [s.strip() for s in body.split(";")]
+        logits = np.array([[float(v) for v in vals.split()]])
+        gi, gv = oracle.topk(logits, int(k))
+        assert gi[0].tolist() == [int(x) for x in idx.split()]
+        ev = [float(x) for x in top.split()]
+        assert gv[0].tolist() == ev
+        assert np.signbit(gv[0]).tolist() == np.signbit(ev).tolist()
+
+
+def test_topk_matches_python_sorted_with_many_ties():
+    rng = np.random.default_rng(5)
+    for trial in range(20):
+        n = int(rng.integers(10, 300))
+        k = int(rng.integers(1, min(n, 32) + 1))
+        logits = rng.integers(-4, 5, size=(3, n)).astype(np.float64) / 4  # heavy ties
+        logits[logits == 0] *= rng.choice([-1.0, 1.0], size=int((logits == 0).sum()))
+        gi, gv = oracle.topk(logits, k)
+        for r in range(3):
+            order = sorted(range(n), key=lambda j: (-logits[r, j], j))[:k]
+            assert gi[r].tolist() == order
+            assert np.array_equal(gv[r], logits[r, order])
