@@ -1,0 +1,188 @@
+/*
+ * skinny.h -- C ABI of the MI355X (gfx950) weight-streaming skinny matmul.
+ *
+ * The operation is C[m,n] = A[m,k] . W[k,n] for small-to-moderate m, the
+ * product the nx_batchscale_kat page asks about ("is the matmul amortising
+ * across m?"): W is read from HBM once per call for all m rows.  Around it sit
+ * the two steps the Strata PR #109 page ("What", router bullet) batches over a
+ * decode window -- a multi-row GEMV and a per-row top-10 -- and the f16 dequant
+ * of a block-quantised weight from the opus r35 track A page (section 1,
+ * `dq_f16`), fused into the weight load path.
+ *
+ * Layouts (all row-major, element strides):
+ *   A  [m][lda]   f16 or bf16 rows ("tokens"); lda >= k
+ *   W  [n][k]     the weight stored k-contiguous: stored row j is logical
+ *                 column j of W[k,n].  f16, bf16, or Q8_0 (see below)
+ *   C  [m][ldc]   f32, f16 or bf16; ldc >= n
+ * Q8_0-style weights are two arrays: codes int8 [n][k] and scales f16
+ * [n][k/32]; weight (j, kk) is RNE_f16(scale[j][kk/32] * code[j][kk]).
+ *
+ * Paths: m <= 16 runs a multi-row GEMV (every W byte read once for all rows);
+ * m >= 17 runs an f16/bf16 MFMA GEMM with a tile chosen by the plan.
+ * Guarantees (bitwise):
+ *   - row invariance in the GEMV regime: row i of C at any m <= 16 equals the
+ *     m = 1 call on that row (Strata PR #109, "What": outputs of the batched
+ *     window are bit-identical to the per-token calls);
+ *   - tile invariance and M invariance in the GEMM regime: every tile, and
+ *     every m >= 17, gives the same bits for the same A row (opus r35 track A,
+ *     section 2 and "verification": all tiles memcmp-equal);
+ *   - the fused Q8_0 path equals skinny_dequant_q8_0_run followed by the f16
+ *     path on the dequantised weight.
+ * Across the two regimes results agree to rounding only.
+ *
+ * Memory and threading:
+ *   - every device pointer is owned by the caller; the library keeps none;
+ *   - a plan is host memory only, immutable after creation, and may be used
+ *     from several threads and streams at once;
+ *   - the run calls allocate nothing, never synchronise, and only enqueue
+ *     kernels on `stream` (a hipStream_t; NULL = the null stream), so they can
+ *     be captured in a HIP graph;
+ *   - the optional workspace is caller-owned scratch; two runs in flight at
+ *     once must not share one workspace.
+ * Errors: every argument is checked on the host before any HIP call; on an
+ * error nothing is enqueued and nothing is written.  The library never aborts
+ * and prints nothing unless SKINNY_LOG=1 is set.  Non-finite inputs are
+ * outside the contract (they propagate as IEEE arithmetic makes them).
+ */
+#ifndef SKINNY_H
+#define SKINNY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SKINNY_ABI_VERSION 1
+
+#if defined(__GNUC__)
+#define SKINNY_API __attribute__((visibility("default")))
+#else
+#define SKINNY_API
+#endif
+
+typedef enum skinny_status {
+  SKINNY_OK = 0,
+  SKINNY_ERR_INVALID_ARG = 1, /* null pointer, bad struct_size, m/n/k/topk out of range */
+  SKINNY_ERR_UNSUPPORTED = 2, /* dtype combination or flag the library does not implement */
+  SKINNY_ERR_ALIGNMENT = 3,   /* pointer not 16-byte aligned or stride not a multiple of 8 */
+  SKINNY_ERR_SHAPE = 4,       /* k not a multiple of 8 (32 for Q8_0), stride < row length */
+  SKINNY_ERR_HIP = 5,         /* the HIP runtime reported an error (device query or launch) */
+  SKINNY_ERR_WORKSPACE = 6    /* workspace missing or smaller than skinny_mm_workspace_size */
+} skinny_status;
+
+typedef enum skinny_dtype {
+  SKINNY_F16 = 1,
+  SKINNY_BF16 = 2,
+  SKINNY_F32 = 3,
+  SKINNY_Q8_0 = 4
+} skinny_dtype;
+
+/* desc.flags */
+#define SKINNY_FORCE_GEMV 0x1u /* use the GEMV for every m (m must stay <= 16) */
+#define SKINNY_FORCE_GEMM 0x2u /* use the MFMA GEMM for every m, including m <= 16 */
+
+#define SKINNY_GEMV_MAX_M 16
+#define SKINNY_TOPK_MAX 32
+
+/* Problem description, copied into the plan.
+ *   struct_size  sizeof(skinny_mm_desc), for ABI versioning
+ *   a_dtype      SKINNY_F16 or SKINNY_BF16
+ *   w_dtype      SKINNY_F16 / SKINNY_Q8_0 (with f16 A) or SKINNY_BF16 (with bf16 A)
+ *   c_dtype      SKINNY_F32, SKINNY_F16 or SKINNY_BF16 (rounded to nearest even)
+ *   max_m        largest m any run will pass (>= 1)
+ *   n, k         output columns and reduction length (n >= 1; k >= 8, k % 8 == 0,
+ *                k % 32 == 0 for Q8_0)
+ *   lda, ldc     row strides of A and C in elements; 0 means dense (k and n);
+ *                otherwise >= the row length and a multiple of 8
+ *   flags        SKINNY_FORCE_* (tests and benchmarks); 0 normally
+ *   tile_id      -1: the plan's tile selector; >= 0: force that GEMM tile
+ *                (see skinny_gemm_tile_count)
+ *   num_cus      0: query the current HIP device; > 0: plan for that many
+ *                compute units without touching the device (host-only use) */
+typedef struct skinny_mm_desc {
+  uint32_t struct_size;
+  int32_t a_dtype;
+  int32_t w_dtype;
+  int32_t c_dtype;
+  int64_t max_m;
+  int64_t n;
+  int64_t k;
+  int64_t lda;
+  int64_t ldc;
+  uint32_t flags;
+  int32_t tile_id;
+  int32_t num_cus;
+} skinny_mm_desc;
+
+typedef struct skinny_plan skinny_plan;
+
+/* Validate `desc` and build a plan: the GEMV work split (fixed by n and k
+ * only, so every m sees the same per-row arithmetic) and the GEMM tile for
+ * each m (opus r35 track A, section 2: a tile whose tail block is up to half
+ * padding loses, so the selector avoids it).  Host memory only. */
+SKINNY_API skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan);
+
+/* Free a plan (NULL is ignored).  Runs already enqueued are unaffected. */
+SKINNY_API void skinny_mm_plan_destroy(skinny_plan* plan);
+
+/* Bytes of device workspace a run with this plan needs (0 when none); valid
+ * for every m <= max_m, for skinny_mm_run and gemv_topk_run alike. */
+SKINNY_API skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_t* bytes);
+
+/* C[0:m, 0:n] = A[0:m, :] . W  (nx_batchscale_kat: the product with fp32
+ * accumulation; Strata PR #109 "What": every W byte read once for the window).
+ *   m          1 <= m <= max_m
+ *   A, W, C    device pointers (16-byte aligned); w_scales: Q8_0 scales
+ *              f16 [n][k/32] (16-byte aligned), else must be NULL
+ *   workspace  device scratch of >= skinny_mm_workspace_size bytes (may be
+ *              NULL when that size is 0)
+ *   stream     hipStream_t (NULL = null stream)
+ * Writes rows 0..m-1 of C, columns 0..n-1 only. */
+SKINNY_API skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
+                            const void* w_scales, void* C, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Router step (Strata PR #109, "What": the multi-row router GEMV into fp32
+ * logits, then one multi-row top-k launch with one block per token).
+ * The plan's c_dtype must be SKINNY_F32.
+ *   logits     f32 [m][ldc] out (the full product)
+ *   topk_idx   int32 [m][topk] out: the topk largest logits of each row,
+ *              value descending, equal values (IEEE ==, so -0 == +0) by lower
+ *              column index first
+ *   topk_val   f32 [m][topk] out: those logits, bit-for-bit
+ *   topk       1 <= topk <= min(n, SKINNY_TOPK_MAX) */
+SKINNY_API skinny_status gemv_topk_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
+                            const void* w_scales, float* logits, int32_t* topk_idx,
+                            float* topk_val, int32_t topk, void* workspace,
+                            size_t workspace_bytes, void* stream);
+
+/* Standalone Q8_0-style dequant (opus r35 track A, section 1: `dq_f16`):
+ * out[j][kk] = RNE_f16(f32(d[j][kk/32]) * f32(qs[j][kk])), the same
+ * arithmetic the fused paths use.
+ *   n >= 1, k >= 32 and k % 32 == 0; qs int8 [n][k], d f16 [n][k/32],
+ *   out f16 [n][k]; all device pointers, 16-byte aligned. */
+SKINNY_API skinny_status skinny_dequant_q8_0_run(int64_t n, int64_t k, const void* qs, const void* d,
+                                      void* out, void* stream);
+
+/* Human-readable description of what a run with this m would launch: path,
+ * tile or GEMV split, grid.  Writes a NUL-terminated string (truncated to
+ * len). */
+SKINNY_API skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf, size_t len);
+
+/* Number of GEMM tiles and the name of tile `tile_id` ("TMxTN_wWMxWN"). */
+SKINNY_API int32_t skinny_gemm_tile_count(void);
+SKINNY_API const char* skinny_gemm_tile_name(int32_t tile_id);
+
+/* Static text for a status code. */
+SKINNY_API const char* skinny_status_string(skinny_status status);
+
+/* SKINNY_ABI_VERSION of the built library. */
+SKINNY_API int32_t skinny_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SKINNY_H */

@@ -1,0 +1,264 @@
+"""Thin Python binding of libskinny.so, the MI355X weight-streaming skinny matmul.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI (include/skinny.h).  PyTorch supplies device memory
+and the current stream; nothing here computes a result, and there is no CPU
+fallback -- importing this package fails loudly when the library is missing.
+
+    C = mm(A, W)                       # f16/bf16 rows x [n][k] weight
+    C = mm(A, (qs, d))                 # Q8_0-style weight: int8 codes, f16 scales
+    logits, idx, val = gemv_topk(A, W, topk=10)
+    w16 = dequant_q8_0(qs, d)
+
+W is stored [n][k] (k-contiguous): stored row j is column j of the logical
+W[k, n] in C[m, n] = A[m, k] . W[k, n].
+"""
+import ctypes
+import os
+import threading
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libskinny.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m row_gemv_decode_amd.build` "
+        "(or __graft_entry__.build()); there is no fallback implementation")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+# --- C ABI mirror -----------------------------------------------------------
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_SHAPE, ERR_HIP, ERR_WORKSPACE = range(7)
+F16, BF16, F32, Q8_0 = 1, 2, 3, 4
+FORCE_GEMV, FORCE_GEMM = 0x1, 0x2
+GEMV_MAX_M = 16
+TOPK_MAX = 32
+
+EXPORTS = (
+    "skinny_mm_plan", "skinny_mm_plan_destroy", "skinny_mm_workspace_size", "skinny_mm_run",
+    "gemv_topk_run", "skinny_dequant_q8_0_run", "skinny_mm_plan_info", "skinny_gemm_tile_count",
+    "skinny_gemm_tile_name", "skinny_status_string", "skinny_abi_version",
+)
+
+
+class MMDesc(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", ctypes.c_uint32),
+        ("a_dtype", ctypes.c_int32),
+        ("w_dtype", ctypes.c_int32),
+        ("c_dtype", ctypes.c_int32),
+        ("max_m", ctypes.c_int64),
+        ("n", ctypes.c_int64),
+        ("k", ctypes.c_int64),
+        ("lda", ctypes.c_int64),
+        ("ldc", ctypes.c_int64),
+        ("flags", ctypes.c_uint32),
+        ("tile_id", ctypes.c_int32),
+        ("num_cus", ctypes.c_int32),
+    ]
+
+
+_vp, _i64, _i32, _sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+_lib.skinny_mm_plan.argtypes = [ctypes.POINTER(MMDesc), ctypes.POINTER(_vp)]
+_lib.skinny_mm_plan.restype = ctypes.c_int
+_lib.skinny_mm_plan_destroy.argtypes = [_vp]
+_lib.skinny_mm_plan_destroy.restype = None
+_lib.skinny_mm_workspace_size.argtypes = [_vp, ctypes.POINTER(_sz)]
+_lib.skinny_mm_workspace_size.restype = ctypes.c_int
+_lib.skinny_mm_run.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
+_lib.skinny_mm_run.restype = ctypes.c_int
+_lib.gemv_topk_run.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]
+_lib.gemv_topk_run.restype = ctypes.c_int
+_lib.skinny_dequant_q8_0_run.argtypes = [_i64, _i64, _vp, _vp, _vp, _vp]
+_lib.skinny_dequant_q8_0_run.restype = ctypes.c_int
+_lib.skinny_mm_plan_info.argtypes = [_vp, _i64, ctypes.c_char_p, _sz]
+_lib.skinny_mm_plan_info.restype = ctypes.c_int
+_lib.skinny_gemm_tile_count.argtypes = []
+_lib.skinny_gemm_tile_count.restype = _i32
+_lib.skinny_gemm_tile_name.argtypes = [_i32]
+_lib.skinny_gemm_tile_name.restype = ctypes.c_char_p
+_lib.skinny_status_string.argtypes = [ctypes.c_int]
+_lib.skinny_status_string.restype = ctypes.c_char_p
+_lib.skinny_abi_version.argtypes = []
+_lib.skinny_abi_version.restype = _i32
+
+
+class SkinnyError(RuntimeError):
+    def __init__(self, status: int, where: str = ""):
+        self.status = int(status)
+        msg = _lib.skinny_status_string(self.status).decode()
+        super().__init__(f"{where}: {msg} (status {self.status})" if where else msg)
+
+
+def _check(status: int, where: str):
+    if status != OK:
+        raise SkinnyError(status, where)
+
+
+def lib() -> ctypes.CDLL:
+    return _lib
+
+
+def abi_version() -> int:
+    return int(_lib.skinny_abi_version())
+
+
+def gemm_tiles():
+    return [_lib.skinny_gemm_tile_name(i).decode() for i in range(_lib.skinny_gemm_tile_count())]
+
+
+# --- torch plumbing ---------------------------------------------------------
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t, what):
+    torch = _torch()
+    if t == torch.float16:
+        return F16
+    if t == torch.bfloat16:
+        return BF16
+    if t == torch.float32:
+        return F32
+    raise TypeError(f"{what}: unsupported dtype {t}")
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+class Plan:
+    """A skinny_mm_plan: host-only, immutable, reusable across streams."""
+
+    def __init__(self, n, k, max_m, a_dtype=F16, w_dtype=F16, c_dtype=F32, lda=0, ldc=0,
+                 flags=0, tile_id=-1, num_cus=0):
+        d = MMDesc(ctypes.sizeof(MMDesc), a_dtype, w_dtype, c_dtype, max_m, n, k, lda, ldc,
+                   flags, tile_id, num_cus)
+        h = ctypes.c_void_p()
+        _check(_lib.skinny_mm_plan(ctypes.byref(d), ctypes.byref(h)), "skinny_mm_plan")
+        self._h = h
+        self.n, self.k, self.max_m = n, k, max_m
+        self.a_dtype, self.w_dtype, self.c_dtype = a_dtype, w_dtype, c_dtype
+        self.lda, self.ldc = lda or k, ldc or n
+        sz = ctypes.c_size_t()
+        _check(_lib.skinny_mm_workspace_size(self._h, ctypes.byref(sz)), "skinny_mm_workspace_size")
+        self.workspace_bytes = int(sz.value)
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self, m: int) -> str:
+        buf = ctypes.create_string_buffer(256)
+        _check(_lib.skinny_mm_plan_info(self._h, m, buf, 256), "skinny_mm_plan_info")
+        return buf.value.decode()
+
+    def workspace(self, device):
+        """A cached device workspace for this plan (None when none is needed)."""
+        if self.workspace_bytes == 0:
+            return None
+        return _workspace(device, self.workspace_bytes)
+
+    def run(self, m, A, W, C, scales=None, workspace=None, stream=None):
+        ws = workspace if workspace is not None else self.workspace(A.device)
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        _check(_lib.skinny_mm_run(self._h, m, _ptr(A), _ptr(W), _ptr(scales), _ptr(C), _ptr(ws),
+                                  nbytes, _stream(stream)), "skinny_mm_run")
+
+    def run_topk(self, m, A, W, logits, idx, val, topk, scales=None, workspace=None, stream=None):
+        ws = workspace if workspace is not None else self.workspace(A.device)
+        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        _check(_lib.gemv_topk_run(self._h, m, _ptr(A), _ptr(W), _ptr(scales), _ptr(logits),
+                                  _ptr(idx), _ptr(val), topk, _ptr(ws), nbytes, _stream(stream)),
+               "gemv_topk_run")
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.skinny_mm_plan_destroy(h)
+            self._h = None
+
+
+_ws_lock = threading.Lock()
+_ws_cache = {}
+
+
+def _workspace(device, nbytes):
+    torch = _torch()
+    key = (str(device), threading.get_ident())
+    with _ws_lock:
+        buf = _ws_cache.get(key)
+        if buf is None or buf.numel() < nbytes:
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+            _ws_cache[key] = buf
+        return buf
+
+
+_plan_cache = {}
+
+
+def _weight_kind(W):
+    torch = _torch()
+    if isinstance(W, tuple):
+        qs, d = W
+        if qs.dtype != torch.int8 or d.dtype != torch.float16:
+            raise TypeError("Q8_0 weight is (int8 codes [n][k], float16 scales [n][k/32])")
+        return Q8_0, qs, d
+    return _dtype_code(W.dtype, "W"), W, None
+
+
+def get_plan(n, k, max_m, a_dtype, w_dtype, c_dtype, flags=0, tile_id=-1) -> Plan:
+    key = (n, k, max_m, a_dtype, w_dtype, c_dtype, flags, tile_id)
+    p = _plan_cache.get(key)
+    if p is None:
+        p = Plan(n, k, max_m, a_dtype, w_dtype, c_dtype, flags=flags, tile_id=tile_id)
+        _plan_cache[key] = p
+    return p
+
+
+def mm(A, W, out=None, out_dtype=None, flags=0, tile_id=-1, max_m=None, stream=None):
+    """C = A . W^T_storage for A [m][k] (f16/bf16, contiguous rows) and W [n][k]
+    (same dtype), or W = (qs int8 [n][k], d f16 [n][k/32]) for Q8_0."""
+    torch = _torch()
+    wk, Wt, scales = _weight_kind(W)
+    m, k = A.shape
+    n = Wt.shape[0]
+    if out is None:
+        out = torch.empty((m, n), dtype=out_dtype or torch.float32, device=A.device)
+    plan = get_plan(n, k, max_m or m, _dtype_code(A.dtype, "A"), wk, _dtype_code(out.dtype, "C"),
+                    flags, tile_id)
+    plan.run(m, A, Wt, out, scales=scales, stream=stream)
+    return out
+
+
+def gemv_topk(A, W, topk=10, flags=0, max_m=None, stream=None):
+    """(logits f32 [m][n], idx int32 [m][topk], val f32 [m][topk]) of the router step."""
+    torch = _torch()
+    wk, Wt, scales = _weight_kind(W)
+    m, k = A.shape
+    n = Wt.shape[0]
+    logits = torch.empty((m, n), dtype=torch.float32, device=A.device)
+    idx = torch.empty((m, topk), dtype=torch.int32, device=A.device)
+    val = torch.empty((m, topk), dtype=torch.float32, device=A.device)
+    plan = get_plan(n, k, max_m or m, _dtype_code(A.dtype, "A"), wk, F32, flags)
+    plan.run_topk(m, A, Wt, logits, idx, val, topk, scales=scales, stream=stream)
+    return logits, idx, val
+
+
+def dequant_q8_0(qs, d, out=None, stream=None):
+    """f16 [n][k] weight of a Q8_0-style (codes, scales) pair."""
+    torch = _torch()
+    n, k = qs.shape
+    if out is None:
+        out = torch.empty((n, k), dtype=torch.float16, device=qs.device)
+    _check(_lib.skinny_dequant_q8_0_run(n, k, _ptr(qs), _ptr(d), _ptr(out), _stream(stream)),
+           "skinny_dequant_q8_0_run")
+    return out

@@ -1,0 +1,348 @@
+// abi.cpp -- the C ABI declared in include/skinny.h: argument validation (all
+// on the host, before any HIP call), the plan (GEMV split and GEMM tile
+// selection) and dispatch to the kernels in gemv.hip / gemm.hip.
+#include <hip/hip_runtime_api.h>
+
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+
+#include "internal.h"
+#include "skinny.h"
+
+using namespace skinny;
+
+struct skinny_plan {
+  skinny_mm_desc d;   // normalised copy (lda/ldc filled in)
+  int num_cus;
+  int w_kind;         // WK_*
+  int c_kind;         // CK_*
+  // GEMV work split, a function of k only (row invariance across m)
+  int gemv_T;
+  int gemv_S;
+  // GEMV columns per wave, a function of n, S and the CU count
+  int gemv_cpw;
+};
+
+namespace {
+
+bool log_enabled() {
+  static const int on = [] {
+    const char* s = std::getenv("SKINNY_LOG");
+    return (s != nullptr && s[0] == '1') ? 1 : 0;
+  }();
+  return on != 0;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+int to_wkind(int dt) { return dt == SKINNY_F16 ? WK_F16 : dt == SKINNY_BF16 ? WK_BF16 : WK_Q8; }
+int to_ckind(int dt) { return dt == SKINNY_F32 ? CK_F32 : dt == SKINNY_F16 ? CK_F16 : CK_BF16; }
+
+// k split of the GEMV: each wave covers 64*T chunks of eight elements; T in
+// {1, 2} (registers hold T * m * 16 bytes of A per lane).  Pick the T that
+// wastes the fewest chunk slots, then the one with fewer splits.
+void gemv_split(int64_t k, int* T_out, int* S_out) {
+  const int64_t nchunks = k / 8;
+  int bestT = 2;
+  int64_t bestS = (nchunks + 127) / 128;
+  int64_t bestWaste = bestS * 128 - nchunks;
+  const int64_t S1 = (nchunks + 63) / 64;
+  const int64_t waste1 = S1 * 64 - nchunks;
+  if (waste1 < bestWaste) {
+    bestT = 1;
+    bestS = S1;
+    bestWaste = waste1;
+  }
+  *T_out = bestT;
+  *S_out = (int)bestS;
+}
+
+// columns per wave: enough waves for about one per SIMD (4 per CU), but at
+// most kGemvCpwMax columns so the wave's weight loads all fit in registers
+int gemv_cols_per_wave(int64_t n, int S, int num_cus) {
+  const int64_t target_waves = 4LL * num_cus;
+  int64_t cpw = (n * S) / (target_waves > 0 ? target_waves : 1);
+  if (cpw < 1) cpw = 1;
+  if (cpw > kGemvCpwMax) cpw = kGemvCpwMax;
+  return (int)cpw;
+}
+
+bool use_gemv(const skinny_plan* p, int64_t m) {
+  if (p->d.flags & SKINNY_FORCE_GEMV) return true;
+  if (p->d.flags & SKINNY_FORCE_GEMM) return false;
+  return m <= kGemvMaxM;
+}
+
+// GEMM tile selector.  Cost = (number of rounds of resident blocks) x (work
+// of one block at the tile's efficiency).  Padded tail tiles are counted in
+// full, which is what makes a tile whose last row-block is mostly padding lose
+// (opus r35 track A, section 2, big-N GEMMs: a 128-row tile loses whenever
+// M % 128 is 1..64).  Ties go to the earlier (larger) tile.
+double tile_efficiency(const GemmTileInfo& t) {
+  const int wtm = t.tm / t.wm;
+  const int wtn = t.tn / t.wn;
+  const int area = wtm * wtn;  // outputs per wave
+  if (area >= 128 * 64) return 1.0;
+  if (area >= 64 * 64) return 0.85;
+  if (area >= 32 * 96) return 0.75;
+  if (area >= 32 * 64) return 0.65;
+  return 0.5;
+}
+
+int select_tile(const skinny_plan* p, int64_t m) {
+  if (p->d.tile_id >= 0) return p->d.tile_id;
+  const int64_t n = p->d.n;
+  int best = 0;
+  double best_cost = 0.0;
+  for (int id = 0; id < gemm_tile_count(); ++id) {
+    const GemmTileInfo& t = gemm_tile(id);
+    const int64_t blocks = ((m + t.tm - 1) / t.tm) * ((n + t.tn - 1) / t.tn);
+    const int waves_per_block = t.wm * t.wn;
+    int64_t resident = (int64_t)p->num_cus * (8 / waves_per_block > 2 ? 2 : 8 / waves_per_block);
+    if (resident < 1) resident = 1;
+    const int64_t rounds = (blocks + resident - 1) / resident;
+    const double cost = (double)rounds * (double)t.tm * (double)t.tn / tile_efficiency(t);
+    if (id == 0 || cost < best_cost * (1.0 - 1e-9)) {
+      best = id;
+      best_cost = cost;
+    }
+  }
+  return best;
+}
+
+size_t gemv_workspace_bytes(const skinny_plan* p, int64_t m) {
+  if (p->gemv_S <= 1) return 0;
+  return (size_t)p->gemv_S * (size_t)m * (size_t)p->d.n * sizeof(float);
+}
+
+size_t workspace_bytes_for(const skinny_plan* p, int64_t m) {
+  return use_gemv(p, m) ? gemv_workspace_bytes(p, m) : 0;
+}
+
+skinny_status hip_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_ERR_HIP; }
+
+GemvArgs gemv_args(const skinny_plan* p, const void* A, const void* W, const void* scales, void* C,
+                   int64_t ldc, void* workspace) {
+  GemvArgs g;
+  g.A = (const uint16_t*)A;
+  g.lda = p->d.lda;
+  g.W = W;
+  g.scales = (const uint16_t*)scales;
+  g.n = p->d.n;
+  g.k = p->d.k;
+  g.nchunks = (int32_t)(p->d.k / 8);
+  g.S = p->gemv_S;
+  g.cpw = p->gemv_cpw;
+  g.waves_per_split = (int32_t)((p->d.n + p->gemv_cpw - 1) / p->gemv_cpw);
+  g.C = C;
+  g.ldc = ldc;
+  g.partial = (float*)workspace;
+  return g;
+}
+
+GemmArgs gemm_args(const skinny_plan* p, int64_t m, const void* A, const void* W,
+                   const void* scales, void* C, int64_t ldc) {
+  GemmArgs g;
+  g.A = (const uint16_t*)A;
+  g.lda = p->d.lda;
+  g.W = W;
+  g.scales = (const uint16_t*)scales;
+  g.M = m;
+  g.N = p->d.n;
+  g.K = p->d.k;
+  g.C = C;
+  g.ldc = ldc;
+  return g;
+}
+
+// checks shared by skinny_mm_run and gemv_topk_run
+skinny_status check_run(const skinny_plan* p, int64_t m, const void* A, const void* W,
+                        const void* scales, const void* C, const void* workspace,
+                        size_t workspace_bytes) {
+  if (p == nullptr) return SKINNY_ERR_INVALID_ARG;
+  if (m < 1 || m > p->d.max_m) return SKINNY_ERR_INVALID_ARG;
+  if (A == nullptr || W == nullptr || C == nullptr) return SKINNY_ERR_INVALID_ARG;
+  const bool q8 = p->d.w_dtype == SKINNY_Q8_0;
+  if (q8 != (scales != nullptr)) return SKINNY_ERR_INVALID_ARG;
+  if (!aligned16(A) || !aligned16(W) || !aligned16(C) || (q8 && !aligned16(scales)))
+    return SKINNY_ERR_ALIGNMENT;
+  const size_t need = workspace_bytes_for(p, m);
+  if (need > 0) {
+    if (workspace == nullptr || workspace_bytes < need) return SKINNY_ERR_WORKSPACE;
+    if (!aligned16(workspace)) return SKINNY_ERR_ALIGNMENT;
+  }
+  return SKINNY_OK;
+}
+
+// enqueue C = A . W for m rows (GEMV partials stay in the workspace when the
+// plan splits k and `keep_partials` is set)
+skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const void* W,
+                         const void* scales, void* C, int64_t ldc, int c_kind, void* workspace,
+                         bool keep_partials, hipStream_t stream) {
+  if (use_gemv(p, m)) {
+    GemvArgs g = gemv_args(p, A, W, scales, C, ldc, workspace);
+    if (p->gemv_S > 1) {
+      hipError_t e = launch_gemv(g, (int)m, p->gemv_T, p->w_kind, 3, stream);
+      if (e != hipSuccess) return SKINNY_ERR_HIP;
+      if (keep_partials) return SKINNY_OK;
+      return hip_status(launch_split_reduce((const float*)workspace, p->gemv_S, (int)m, p->d.n, C, ldc,
+                                            c_kind, stream));
+    }
+    return hip_status(launch_gemv(g, (int)m, p->gemv_T, p->w_kind, c_kind, stream));
+  }
+  GemmArgs g = gemm_args(p, m, A, W, scales, C, ldc);
+  return hip_status(launch_gemm(select_tile(p, m), g, p->w_kind, c_kind, stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t skinny_abi_version(void) { return SKINNY_ABI_VERSION; }
+
+const char* skinny_status_string(skinny_status s) {
+  switch (s) {
+    case SKINNY_OK: return "ok";
+    case SKINNY_ERR_INVALID_ARG: return "invalid argument";
+    case SKINNY_ERR_UNSUPPORTED: return "unsupported dtype combination or flag";
+    case SKINNY_ERR_ALIGNMENT: return "pointer or stride misaligned";
+    case SKINNY_ERR_SHAPE: return "unsupported shape";
+    case SKINNY_ERR_HIP: return "HIP runtime error";
+    case SKINNY_ERR_WORKSPACE: return "workspace missing or too small";
+  }
+  return "unknown status";
+}
+
+int32_t skinny_gemm_tile_count(void) { return gemm_tile_count(); }
+
+const char* skinny_gemm_tile_name(int32_t tile_id) {
+  if (tile_id < 0 || tile_id >= gemm_tile_count()) return nullptr;
+  return gemm_tile(tile_id).name;
+}
+
+skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan) {
+  if (desc == nullptr || out_plan == nullptr) return SKINNY_ERR_INVALID_ARG;
+  if (desc->struct_size < sizeof(skinny_mm_desc)) return SKINNY_ERR_INVALID_ARG;
+  skinny_mm_desc d = *desc;
+
+  if (d.a_dtype != SKINNY_F16 && d.a_dtype != SKINNY_BF16) return SKINNY_ERR_UNSUPPORTED;
+  if (d.a_dtype == SKINNY_F16 && d.w_dtype != SKINNY_F16 && d.w_dtype != SKINNY_Q8_0)
+    return SKINNY_ERR_UNSUPPORTED;
+  if (d.a_dtype == SKINNY_BF16 && d.w_dtype != SKINNY_BF16) return SKINNY_ERR_UNSUPPORTED;
+  if (d.c_dtype != SKINNY_F32 && d.c_dtype != SKINNY_F16 && d.c_dtype != SKINNY_BF16)
+    return SKINNY_ERR_UNSUPPORTED;
+  if (d.max_m < 1 || d.n < 1 || d.k < 8) return SKINNY_ERR_INVALID_ARG;
+  if (d.max_m > (1LL << 31) - 1 || d.n > (1LL << 31) - 1 || d.k > (1LL << 31) - 1)
+    return SKINNY_ERR_INVALID_ARG;
+  if (d.k % 8 != 0) return SKINNY_ERR_SHAPE;
+  if (d.w_dtype == SKINNY_Q8_0 && d.k % 32 != 0) return SKINNY_ERR_SHAPE;
+  if (d.lda == 0) d.lda = d.k;
+  if (d.ldc == 0) d.ldc = d.n;
+  if (d.lda < d.k || d.ldc < d.n) return SKINNY_ERR_SHAPE;
+  if (d.lda % 8 != 0 || d.ldc % 8 != 0) return SKINNY_ERR_ALIGNMENT;
+  if (d.flags & ~(SKINNY_FORCE_GEMV | SKINNY_FORCE_GEMM)) return SKINNY_ERR_UNSUPPORTED;
+  if ((d.flags & SKINNY_FORCE_GEMV) && (d.flags & SKINNY_FORCE_GEMM)) return SKINNY_ERR_INVALID_ARG;
+  if ((d.flags & SKINNY_FORCE_GEMV) && d.max_m > kGemvMaxM) return SKINNY_ERR_INVALID_ARG;
+  if (d.tile_id < -1 || d.tile_id >= gemm_tile_count()) return SKINNY_ERR_INVALID_ARG;
+  if (d.num_cus < 0) return SKINNY_ERR_INVALID_ARG;
+
+  int cus = d.num_cus;
+  if (cus == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return SKINNY_ERR_HIP;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+      return SKINNY_ERR_HIP;
+    if (cus < 1) return SKINNY_ERR_HIP;
+  }
+
+  skinny_plan* p = new (std::nothrow) skinny_plan;
+  if (p == nullptr) return SKINNY_ERR_INVALID_ARG;
+  p->d = d;
+  p->num_cus = cus;
+  p->w_kind = to_wkind(d.w_dtype);
+  p->c_kind = to_ckind(d.c_dtype);
+  gemv_split(d.k, &p->gemv_T, &p->gemv_S);
+  p->gemv_cpw = gemv_cols_per_wave(d.n, p->gemv_S, cus);
+  if (log_enabled()) {
+    std::fprintf(stderr, "[skinny] plan n=%lld k=%lld max_m=%lld gemv T=%d S=%d cpw=%d cus=%d\n",
+                 (long long)d.n, (long long)d.k, (long long)d.max_m, p->gemv_T, p->gemv_S,
+                 p->gemv_cpw, cus);
+  }
+  *out_plan = p;
+  return SKINNY_OK;
+}
+
+void skinny_mm_plan_destroy(skinny_plan* plan) { delete plan; }
+
+skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_t* bytes) {
+  if (plan == nullptr || bytes == nullptr) return SKINNY_ERR_INVALID_ARG;
+  size_t need = 0;
+  const int64_t mm = plan->d.max_m < kGemvMaxM ? plan->d.max_m : kGemvMaxM;
+  // the GEMV is used for m <= 16 (or every m when forced); its need grows with m
+  if (!(plan->d.flags & SKINNY_FORCE_GEMM)) need = gemv_workspace_bytes(plan, mm);
+  *bytes = need;
+  return SKINNY_OK;
+}
+
+skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
+                            const void* w_scales, void* C, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  skinny_status st = check_run(plan, m, A, W, w_scales, C, workspace, workspace_bytes);
+  if (st != SKINNY_OK) return st;
+  return enqueue_mm(plan, m, A, W, w_scales, C, plan->d.ldc, plan->c_kind, workspace, false,
+                    (hipStream_t)stream);
+}
+
+skinny_status gemv_topk_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
+                            const void* w_scales, float* logits, int32_t* topk_idx,
+                            float* topk_val, int32_t topk, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  skinny_status st = check_run(plan, m, A, W, w_scales, logits, workspace, workspace_bytes);
+  if (st != SKINNY_OK) return st;
+  if (plan->d.c_dtype != SKINNY_F32) return SKINNY_ERR_UNSUPPORTED;
+  if (topk_idx == nullptr || topk_val == nullptr) return SKINNY_ERR_INVALID_ARG;
+  if (topk < 1 || topk > SKINNY_TOPK_MAX || topk > plan->d.n) return SKINNY_ERR_INVALID_ARG;
+  if (!aligned16(topk_idx) || !aligned16(topk_val)) return SKINNY_ERR_ALIGNMENT;
+
+  hipStream_t s = (hipStream_t)stream;
+  const bool split = use_gemv(plan, m) && plan->gemv_S > 1;
+  st = enqueue_mm(plan, m, A, W, w_scales, logits, plan->d.ldc, CK_F32, workspace, true, s);
+  if (st != SKINNY_OK) return st;
+  return hip_status(launch_topk(split ? (const float*)workspace : nullptr, plan->gemv_S, (int)m,
+                                plan->d.n, logits, plan->d.ldc, topk_idx, topk_val, topk, s));
+}
+
+skinny_status skinny_dequant_q8_0_run(int64_t n, int64_t k, const void* qs, const void* d,
+                                      void* out, void* stream) {
+  if (qs == nullptr || d == nullptr || out == nullptr) return SKINNY_ERR_INVALID_ARG;
+  if (n < 1 || k < 32 || n > (1LL << 31) - 1 || k > (1LL << 31) - 1) return SKINNY_ERR_INVALID_ARG;
+  if (k % 32 != 0) return SKINNY_ERR_SHAPE;
+  if (!aligned16(qs) || !aligned16(d) || !aligned16(out)) return SKINNY_ERR_ALIGNMENT;
+  return hip_status(launch_dequant_q8_0(n, k, (const int8_t*)qs, (const uint16_t*)d, (uint16_t*)out,
+                                        (hipStream_t)stream));
+}
+
+skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf, size_t len) {
+  if (plan == nullptr || buf == nullptr || len == 0) return SKINNY_ERR_INVALID_ARG;
+  if (m < 1 || m > plan->d.max_m) return SKINNY_ERR_INVALID_ARG;
+  if (use_gemv(plan, m)) {
+    const int64_t wps = (plan->d.n + plan->gemv_cpw - 1) / plan->gemv_cpw;
+    const int64_t waves = wps * plan->gemv_S;
+    std::snprintf(buf, len,
+                  "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld reduce=%s workspace=%zu",
+                  (long long)m, plan->gemv_T, plan->gemv_S, plan->gemv_cpw, (long long)waves,
+                  (long long)((waves + kGemvWavesPerBlock - 1) / kGemvWavesPerBlock),
+                  plan->gemv_S > 1 ? "yes" : "no", gemv_workspace_bytes(plan, m));
+  } else {
+    const int id = select_tile(plan, m);
+    const GemmTileInfo& t = gemm_tile(id);
+    const int64_t blocks = ((m + t.tm - 1) / t.tm) * ((plan->d.n + t.tn - 1) / t.tn);
+    std::snprintf(buf, len, "path=gemm m=%lld tile=%d name=%s blocks=%lld threads=%d", (long long)m,
+                  id, t.name, (long long)blocks, 64 * t.wm * t.wn);
+  }
+  return SKINNY_OK;
+}
+
+}  // extern "C"

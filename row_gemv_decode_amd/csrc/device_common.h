@@ -1,0 +1,74 @@
+// device_common.h -- small device-side helpers shared by the library's kernels
+// (gfx950 only).  Nothing here is shared with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "internal.h"
+
+namespace skinny {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 h8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+// Reinterpret a dword as two f16 / two bf16.  Always pass a plain scalar:
+// applying __builtin_bit_cast directly to an ext-vector element expression
+// (v.y, v.z, ...) reads element 0 with this compiler, so every cast of a
+// vector lane goes through these by-value helpers.
+__device__ __forceinline__ h2_t as_h2(uint32_t u) { return __builtin_bit_cast(h2_t, u); }
+__device__ __forceinline__ b2_t as_b2(uint32_t u) { return __builtin_bit_cast(b2_t, u); }
+__device__ __forceinline__ uint32_t h2_bits(h2_t h) { return __builtin_bit_cast(uint32_t, h); }
+
+__device__ __forceinline__ _Float16 half_from_bits(uint16_t b) {
+  return __builtin_bit_cast(_Float16, b);
+}
+
+// ---------------------------------------------------------------------------
+// Q8_0-style dequant of eight consecutive codes of one 32-block (opus r35
+// track A, section 1: block-quantised weights become f16 through `dq_f16`).
+// Each weight is RNE_f16(d * q): the code is converted to f16 exactly
+// (|q| <= 128) and one IEEE f16 multiply rounds the exact product once, to
+// nearest even, with the product's sign (so d < 0, q = 0 gives -0).  Every
+// path of the library -- the standalone dequant kernel, the fused GEMV and the
+// fused GEMM B-loader -- calls this one function, so their weights are equal
+// bit for bit.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ h2_t q8_pair(uint32_t two_codes_lo16, _Float16 d) {
+  const int8_t q0 = (int8_t)(two_codes_lo16 & 0xff);
+  const int8_t q1 = (int8_t)((two_codes_lo16 >> 8) & 0xff);
+  h2_t q = {(_Float16)(int16_t)q0, (_Float16)(int16_t)q1};
+  h2_t s = {d, d};
+  return s * q;
+}
+
+// eight codes (two dwords, little-endian bytes) -> eight f16 packed in 4 dwords
+__device__ __forceinline__ u32x4 q8_dequant8(u32x2 codes, _Float16 d) {
+  const uint32_t c0 = codes[0];
+  const uint32_t c1 = codes[1];
+  u32x4 out;
+  out[0] = h2_bits(q8_pair(c0, d));
+  out[1] = h2_bits(q8_pair(c0 >> 16, d));
+  out[2] = h2_bits(q8_pair(c1, d));
+  out[3] = h2_bits(q8_pair(c1 >> 16, d));
+  return out;
+}
+
+// fp32 -> stored output element, round to nearest even
+template <int CK>
+__device__ __forceinline__ void store_out(void* base, int64_t idx, float v) {
+  if constexpr (CK == CK_F32) {
+    ((float*)base)[idx] = v;
+  } else if constexpr (CK == CK_F16) {
+    ((_Float16*)base)[idx] = (_Float16)v;
+  } else {
+    ((__bf16*)base)[idx] = (__bf16)v;
+  }
+}
+
+}  // namespace skinny

@@ -1,0 +1,466 @@
+// gemv.hip -- multi-row GEMV, split-k reduction, per-row top-k and the
+// standalone Q8_0 dequant, for gfx950 (MI355X).
+//
+// What is computed (the pages print no code for any of it):
+//   C[r][j] = sum_kk A[r][kk] * W[j][kk] for r < m <= 16, W stored [n][k]
+//   (nx_batchscale_kat: the product must read W once for all m rows, so that
+//   us_per_row falls with m; Strata PR #109, "What": the router GEMV reads its
+//   weight once for the whole window, with each token's accumulators in
+//   exactly the single-token order).
+//
+// Design (MI355X-first, not the pages' CUDA kernel):
+//   * One wavefront owns a k-range of 64*T chunks of eight elements, chunk
+//     c = split*64*T + t*64 + lane, and a run of consecutive columns.  Every
+//     W load is a coalesced 16-byte load (a wave reads 1 KiB contiguous per
+//     instruction); all W loads of the wave are issued before any arithmetic,
+//     so the whole weight is in flight at once (the stream is tiny compared
+//     with the HBM latency-bandwidth product).
+//   * The wave's A slice is loaded once into registers and reused for every
+//     column, so the k loop reads no LDS.
+//   * Products use v_dot2_f32_{f16,bf16}: two products per lane per
+//     instruction into an fp32 accumulator, chunk by chunk in increasing k.
+//   * The 64 per-lane partials of each (row, column) are combined by a fixed
+//     six-level tree: lanes l ^ 15, l ^ 7 (DPP row mirrors), l ^ 2, l ^ 1 (DPP
+//     quad permutes), l ^ 16 and l ^ 32 (v_permlane16/32_swap).  The first
+//     levels are "transposed": a lane keeps half of its values and receives
+//     the partner's copy of that half, so reducing G columns x M rows costs
+//     about 3 * G * M instructions instead of 6 * G * M.  The tree is the same
+//     for every value, hence the same for every m.
+//   * Nothing in the split, the tree or the per-lane order depends on m, so
+//     row r of any call equals the m = 1 call bit for bit.
+#include "device_common.h"
+#include "internal.h"
+
+namespace skinny {
+
+namespace {
+
+constexpr int ctz_pow2(int x) { return x <= 1 ? 0 : 1 + ctz_pow2(x >> 1); }
+constexpr int next_pow2(int x) { return x <= 1 ? 1 : 2 * next_pow2((x + 1) / 2); }
+
+// columns reduced together: keeps G*M <= 32 values per lane
+template <int M>
+struct GemvShape {
+  static constexpr int G = (32 / next_pow2(M)) < 4 ? (32 / next_pow2(M)) : 4;
+  static constexpr int P = M * G;
+  static constexpr int P2 = next_pow2(P);
+  static constexpr int LV = ctz_pow2(P2);  // transposed levels (<= 6)
+};
+
+__device__ __forceinline__ float fbits(uint32_t u) { return __builtin_bit_cast(float, u); }
+__device__ __forceinline__ uint32_t ubits(float f) { return __builtin_bit_cast(uint32_t, f); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float x) {
+  return fbits(__builtin_amdgcn_update_dpp(0u, ubits(x), CTRL, 0xF, 0xF, false));
+}
+
+// DPP controls: row_mirror (l ^ 15 in a row of 16), row_half_mirror (l ^ 7),
+// quad_perm [2,3,0,1] (l ^ 2), quad_perm [1,0,3,2] (l ^ 1)
+constexpr int kDppRowMirror = 0x140;
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppXor2 = 0x4E;
+constexpr int kDppXor1 = 0xB1;
+
+// level L of the fixed tree: partner lane and the lane bit that picks the kept half
+template <int L>
+struct Level;
+template <> struct Level<0> { static constexpr int bit = 3; static constexpr int dpp = kDppRowMirror; };
+template <> struct Level<1> { static constexpr int bit = 2; static constexpr int dpp = kDppRowHalfMirror; };
+template <> struct Level<2> { static constexpr int bit = 1; static constexpr int dpp = kDppXor2; };
+template <> struct Level<3> { static constexpr int bit = 0; static constexpr int dpp = kDppXor1; };
+template <> struct Level<4> { static constexpr int bit = 4; static constexpr int dpp = -16; };  // permlane16 swap
+template <> struct Level<5> { static constexpr int bit = 5; static constexpr int dpp = -32; };  // permlane32 swap
+
+// One tree level.  CUR live values enter; if the level is transposed (L < LV)
+// CUR/2 leave, else CUR == 1 and every lane keeps the full sum.
+template <int L, int LV, int CUR, int NV>
+__device__ __forceinline__ void tree_level(float (&v)[NV], int lane, int& idx) {
+  constexpr int bit = Level<L>::bit;
+  constexpr int ctrl = Level<L>::dpp;
+  if constexpr (L < LV) {
+    constexpr int H = CUR / 2;
+    const bool hi = (lane >> bit) & 1;
+    if constexpr (ctrl >= 0) {
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        const float mine = hi ? v[i + H] : v[i];
+        const float send = hi ? v[i] : v[i + H];
+        v[i] = mine + dpp_mov<ctrl>(send);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < H; ++i) {
+        // swaps the upper half of the first operand's lane pairs with the
+        // lower half of the second's: afterwards the low lanes hold
+        // (v[i] of lane, v[i] of partner) and the high lanes
+        // (v[i+H] of partner, v[i+H] of lane)
+        auto r = (ctrl == -16)
+                     ? __builtin_amdgcn_permlane16_swap(ubits(v[i]), ubits(v[i + H]), false, false)
+                     : __builtin_amdgcn_permlane32_swap(ubits(v[i]), ubits(v[i + H]), false, false);
+        v[i] = fbits(r[0]) + fbits(r[1]);
+      }
+    }
+    if (hi) idx += H;
+  } else {
+    if constexpr (ctrl >= 0) {
+      v[0] = v[0] + dpp_mov<ctrl>(v[0]);
+    } else {
+      auto r = (ctrl == -16) ? __builtin_amdgcn_permlane16_swap(ubits(v[0]), ubits(v[0]), false, false)
+                             : __builtin_amdgcn_permlane32_swap(ubits(v[0]), ubits(v[0]), false, false);
+      v[0] = fbits(r[0]) + fbits(r[1]);
+    }
+  }
+}
+
+template <int LV>
+constexpr int plain_lane_mask() {
+  constexpr int bits[6] = {3, 2, 1, 0, 4, 5};
+  int mask = 0;
+  for (int L = LV; L < 6; ++L) mask |= 1 << bits[L];
+  return mask;
+}
+
+// live values entering level L
+constexpr int live_at(int L, int LV, int NV) { return L <= LV ? (NV >> L) : 1; }
+
+// Reduce NV = 2^LV values per lane over the 64 lanes.  Afterwards v[0] of a
+// lane holds the full sum of value `idx`; the lanes with (lane & mask) == 0
+// hold each value exactly once.
+template <int LV, int NV>
+__device__ __forceinline__ float wave_tree(float (&v)[NV], int lane, int& idx) {
+  idx = 0;
+  tree_level<0, LV, live_at(0, LV, NV)>(v, lane, idx);
+  tree_level<1, LV, live_at(1, LV, NV)>(v, lane, idx);
+  tree_level<2, LV, live_at(2, LV, NV)>(v, lane, idx);
+  tree_level<3, LV, live_at(3, LV, NV)>(v, lane, idx);
+  tree_level<4, LV, live_at(4, LV, NV)>(v, lane, idx);
+  tree_level<5, LV, live_at(5, LV, NV)>(v, lane, idx);
+  return v[0];
+}
+
+template <int WK>
+__device__ __forceinline__ float dot8(const u32x4& a, const u32x4& w, float acc) {
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t ap = a[p];
+    const uint32_t wp = w[p];
+    if constexpr (WK == WK_BF16) {
+      acc = __builtin_amdgcn_fdot2_f32_bf16(as_b2(ap), as_b2(wp), acc, false);
+    } else {
+      acc = __builtin_amdgcn_fdot2(as_h2(ap), as_h2(wp), acc, false);
+    }
+  }
+  return acc;
+}
+
+// Raw weight registers of one (column, chunk): 16 bytes of f16/bf16, or 8
+// bytes of codes plus the block's scale for Q8_0.
+template <int WK>
+struct WChunk {
+  u32x4 v;
+};
+template <>
+struct WChunk<WK_Q8> {
+  u32x2 codes;
+  uint16_t scale;
+};
+
+template <int WK>
+__device__ __forceinline__ void load_w(WChunk<WK>& dst, const GemvArgs& g, int64_t j, int chunk) {
+  if constexpr (WK == WK_Q8) {
+    const int8_t* wq = (const int8_t*)g.W;
+    dst.codes = *(const u32x2*)(wq + j * g.k + (int64_t)chunk * 8);
+    dst.scale = g.scales[j * (g.k >> 5) + (chunk >> 2)];
+  } else {
+    const uint16_t* w16 = (const uint16_t*)g.W;
+    dst.v = *(const u32x4*)(w16 + j * g.k + (int64_t)chunk * 8);
+  }
+}
+
+template <int WK>
+__device__ __forceinline__ void zero_w(WChunk<WK>& dst) {
+  if constexpr (WK == WK_Q8) {
+    dst.codes = u32x2{0u, 0u};
+    dst.scale = 0;
+  } else {
+    dst.v = u32x4{0u, 0u, 0u, 0u};
+  }
+}
+
+template <int WK>
+__device__ __forceinline__ u32x4 w_as_halves(const WChunk<WK>& w) {
+  if constexpr (WK == WK_Q8) {
+    return q8_dequant8(w.codes, half_from_bits(w.scale));
+  } else {
+    return w.v;
+  }
+}
+
+template <int M, int T, int WK, int OUT>
+__global__ __launch_bounds__(64 * kGemvWavesPerBlock) void gemv_rows_kernel(GemvArgs g) {
+  using Shape = GemvShape<M>;
+  constexpr int G = Shape::G;
+  constexpr int P = Shape::P;
+  constexpr int P2 = Shape::P2;
+  constexpr int LV = Shape::LV;
+  static_assert(LV <= 6, "at most 64 values per lane");
+
+  const int lane = threadIdx.x & 63;
+  const int gw = blockIdx.x * kGemvWavesPerBlock + (threadIdx.x >> 6);
+  const int s = gw / g.waves_per_split;
+  if (s >= g.S) return;  // whole wave leaves; the kernel has no barriers
+  const int wc = gw - s * g.waves_per_split;
+  const int64_t j0 = (int64_t)wc * g.cpw;
+  const int ncol = (int)min((int64_t)g.cpw, g.n - j0);
+
+  int chunk[T];
+  bool valid[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    chunk[t] = s * 64 * T + t * 64 + lane;
+    valid[t] = chunk[t] < g.nchunks;
+  }
+
+  // every weight load of the wave, issued before anything else waits
+  WChunk<WK> w[kGemvCpwMax][T];
+#pragma unroll
+  for (int c = 0; c < kGemvCpwMax; ++c) {
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      if (c < ncol && valid[t]) {
+        load_w<WK>(w[c][t], g, j0 + c, chunk[t]);
+      } else {
+        zero_w<WK>(w[c][t]);
+      }
+    }
+  }
+
+  // the wave's A slice, kept in registers for all its columns
+  u32x4 a[T][M];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+#pragma unroll
+    for (int r = 0; r < M; ++r) {
+      a[t][r] = valid[t] ? *(const u32x4*)(g.A + (int64_t)r * g.lda + (int64_t)chunk[t] * 8)
+                         : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  constexpr int plain_mask = plain_lane_mask<LV>();
+  const bool writer_lane = (lane & plain_mask) == 0;
+
+#pragma unroll
+  for (int c0 = 0; c0 < kGemvCpwMax; c0 += G) {
+    if (c0 >= ncol) break;
+    float v[P2];
+#pragma unroll
+    for (int gi = 0; gi < G; ++gi) {
+      u32x4 wh[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) wh[t] = w_as_halves<WK>(w[(c0 + gi) < kGemvCpwMax ? (c0 + gi) : 0][t]);
+#pragma unroll
+      for (int r = 0; r < M; ++r) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc = dot8<WK>(a[t][r], wh[t], acc);
+        v[gi * M + r] = acc;
+      }
+    }
+#pragma unroll
+    for (int i = P; i < P2; ++i) v[i] = 0.0f;
+
+    int idx;
+    const float sum = wave_tree<LV>(v, lane, idx);
+    const int gi = idx / M;
+    const int r = idx - gi * M;
+    if (writer_lane && idx < P && c0 + gi < ncol) {
+      const int64_t j = j0 + c0 + gi;
+      if constexpr (OUT == 3) {
+        g.partial[((int64_t)s * M + r) * g.n + j] = sum;
+      } else {
+        store_out<OUT>(g.C, (int64_t)r * g.ldc + j, sum);
+      }
+    }
+  }
+}
+
+// --- kernel table ----------------------------------------------------------
+typedef void (*gemv_fn)(GemvArgs);
+
+template <int M, int T, int WK>
+struct GemvRow {
+  static constexpr gemv_fn out[4] = {gemv_rows_kernel<M, T, WK, 0>, gemv_rows_kernel<M, T, WK, 1>,
+                                     gemv_rows_kernel<M, T, WK, 2>, gemv_rows_kernel<M, T, WK, 3>};
+};
+
+template <int T, int WK, int... Ms>
+const gemv_fn* gemv_row_ptr(int m) {
+  const gemv_fn* tbl[] = {GemvRow<Ms, T, WK>::out...};
+  return tbl[m - 1];
+}
+
+template <int T, int WK>
+const gemv_fn* gemv_table(int m) {
+  return gemv_row_ptr<T, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m);
+}
+
+// --- split-k reduction -----------------------------------------------------
+template <int CK>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ partial, int S,
+                                                           int m, int64_t n, void* C, int64_t ldc) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= (int64_t)m * n) return;
+  const int64_t r = e / n;
+  const int64_t j = e - r * n;
+  float acc = partial[r * n + j];
+  for (int s = 1; s < S; ++s) acc += partial[((int64_t)s * m + r) * n + j];
+  store_out<CK>(C, r * ldc + j, acc);
+}
+
+// --- top-k -----------------------------------------------------------------
+// (value desc, index asc): a strict total order over a row's entries
+__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+constexpr int kTopkCache = 16;  // values per lane kept in registers (n <= 1024)
+
+__global__ __launch_bounds__(64) void topk_rows_kernel(const float* __restrict__ partial, int S, int m,
+                                                       int64_t n, float* logits, int64_t ldl,
+                                                       int32_t* __restrict__ out_idx,
+                                                       float* __restrict__ out_val, int topk) {
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x;
+  float* row = logits + (int64_t)r * ldl;
+
+  // pass 0: materialise the row (reducing partials in split order when there
+  // are any); the first 64 * kTopkCache entries stay in registers
+  auto fetch = [&](int64_t j) -> float {
+    if (partial != nullptr) {
+      float x = partial[(int64_t)r * n + j];
+      for (int s = 1; s < S; ++s) x += partial[((int64_t)s * m + r) * n + j];
+      row[j] = x;
+      return x;
+    }
+    return row[j];
+  };
+  float cache[kTopkCache];
+#pragma unroll
+  for (int u = 0; u < kTopkCache; ++u) {
+    const int64_t j = lane + 64 * u;
+    cache[u] = j < n ? fetch(j) : 0.0f;
+  }
+  for (int64_t j = lane + 64 * kTopkCache; j < n; j += 64) (void)fetch(j);
+
+  float prev_v = 0.0f;
+  int prev_i = -1;  // -1: nothing selected yet
+  for (int t = 0; t < topk; ++t) {
+    float best_v = 0.0f;
+    int best_i = -1;
+    auto consider = [&](float x, int ji) {
+      const bool eligible = prev_i < 0 || ranks_before(prev_v, prev_i, x, ji);
+      if (eligible && (best_i < 0 || ranks_before(x, ji, best_v, best_i))) {
+        best_v = x;
+        best_i = ji;
+      }
+    };
+#pragma unroll
+    for (int u = 0; u < kTopkCache; ++u) {
+      const int64_t j = lane + 64 * u;
+      if (j < n) consider(cache[u], (int)j);
+    }
+    // entries beyond the cache: re-read what this same lane wrote in pass 0
+    for (int64_t j = lane + 64 * kTopkCache; j < n; j += 64) consider(row[j], (int)j);
+
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(best_v, off, 64);
+      const int oi = __shfl_xor(best_i, off, 64);
+      if (oi >= 0 && (best_i < 0 || ranks_before(ov, oi, best_v, best_i))) {
+        best_v = ov;
+        best_i = oi;
+      }
+    }
+    if (lane == 0) {
+      out_idx[(int64_t)r * topk + t] = best_i;
+      out_val[(int64_t)r * topk + t] = best_v;
+    }
+    prev_v = best_v;
+    prev_i = best_i;
+  }
+}
+
+// --- standalone dequant ----------------------------------------------------
+__global__ __launch_bounds__(256) void dequant_q8_0_kernel(const int8_t* __restrict__ qs,
+                                                           const uint16_t* __restrict__ d,
+                                                           uint16_t* __restrict__ out, int64_t n,
+                                                           int64_t k) {
+  const int64_t chunks_per_row = k >> 3;
+  const int64_t total = n * chunks_per_row;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t j = e / chunks_per_row;
+    const int64_t c = e - j * chunks_per_row;
+    const u32x2 codes = *(const u32x2*)(qs + j * k + c * 8);
+    const _Float16 scale = half_from_bits(d[j * (k >> 5) + (c >> 2)]);
+    *(u32x4*)(out + j * k + c * 8) = q8_dequant8(codes, scale);
+  }
+}
+
+}  // namespace
+
+hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_kind,
+                       hipStream_t stream) {
+  if (m < 1 || m > kGemvMaxM || (T != 1 && T != 2) || out_kind < 0 || out_kind > 3)
+    return hipErrorInvalidValue;
+  const gemv_fn* row = nullptr;
+  if (T == 1) {
+    row = w_kind == WK_F16 ? gemv_table<1, WK_F16>(m)
+        : w_kind == WK_BF16 ? gemv_table<1, WK_BF16>(m) : gemv_table<1, WK_Q8>(m);
+  } else {
+    row = w_kind == WK_F16 ? gemv_table<2, WK_F16>(m)
+        : w_kind == WK_BF16 ? gemv_table<2, WK_BF16>(m) : gemv_table<2, WK_Q8>(m);
+  }
+  const int64_t waves = (int64_t)args.S * args.waves_per_split;
+  const dim3 grid((unsigned)((waves + kGemvWavesPerBlock - 1) / kGemvWavesPerBlock));
+  hipLaunchKernelGGL(row[out_kind], grid, dim3(64 * kGemvWavesPerBlock), 0, stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_reduce(const float* partial, int S, int m, int64_t n, void* C,
+                               int64_t ldc, int c_kind, hipStream_t stream) {
+  const int64_t total = (int64_t)m * n;
+  const dim3 grid((unsigned)((total + 255) / 256));
+  switch (c_kind) {
+    case CK_F32:
+      hipLaunchKernelGGL(split_reduce_kernel<CK_F32>, grid, dim3(256), 0, stream, partial, S, m, n, C, ldc);
+      break;
+    case CK_F16:
+      hipLaunchKernelGGL(split_reduce_kernel<CK_F16>, grid, dim3(256), 0, stream, partial, S, m, n, C, ldc);
+      break;
+    default:
+      hipLaunchKernelGGL(split_reduce_kernel<CK_BF16>, grid, dim3(256), 0, stream, partial, S, m, n, C, ldc);
+      break;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_topk(const float* partial, int S, int m, int64_t n, float* logits, int64_t ldl,
+                       int32_t* idx, float* val, int topk, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)m), dim3(64), 0, stream, partial, S, m, n,
+                     logits, ldl, idx, val, topk);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_q8_0(int64_t n, int64_t k, const int8_t* qs, const uint16_t* d,
+                               uint16_t* out, hipStream_t stream) {
+  const int64_t total = n * (k >> 3);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(dequant_q8_0_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, qs, d, out,
+                     n, k);
+  return hipGetLastError();
+}
+
+}  // namespace skinny

@@ -1,0 +1,87 @@
+// internal.h -- host-side interfaces between the C ABI (abi.cpp) and the
+// kernel translation units (gemv.hip, gemm.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace skinny {
+
+// weight storage kinds and output kinds (kernel template parameters)
+enum WKind : int { WK_F16 = 0, WK_BF16 = 1, WK_Q8 = 2 };
+enum CKind : int { CK_F32 = 0, CK_F16 = 1, CK_BF16 = 2 };
+
+// ---------------------------------------------------------------------------
+// Multi-row GEMV (m <= 16).  One wavefront owns a k-range of 64*T chunks of
+// eight elements (chunk c = split*64*T + t*64 + lane) and a run of `cpw`
+// consecutive columns; its A slice lives in registers for the whole wave.
+// The k split (T, S) depends on k only, so the per-row arithmetic is the same
+// for every m.
+// ---------------------------------------------------------------------------
+constexpr int kGemvMaxM = 16;
+constexpr int kGemvCpwMax = 8;     // columns per wave, upper bound
+constexpr int kGemvWavesPerBlock = 4;
+
+struct GemvArgs {
+  const uint16_t* A;       // [m][lda] f16/bf16 bits
+  int64_t lda;
+  const void* W;           // [n][k] f16/bf16 bits, or int8 codes for Q8_0
+  const uint16_t* scales;  // Q8_0 scales [n][k/32] (f16 bits), else null
+  int64_t n;
+  int64_t k;
+  int32_t nchunks;          // k / 8
+  int32_t S;                // number of k splits
+  int32_t cpw;              // columns per wave (1..kGemvCpwMax)
+  int32_t waves_per_split;  // ceil(n / cpw)
+  void* C;                  // [m][ldc] output (when S == 1)
+  int64_t ldc;
+  float* partial;           // [S][m][n] fp32 partial sums (when S > 1)
+};
+
+// out_kind: 0 f32, 1 f16, 2 bf16, 3 = fp32 partials into args.partial
+hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_kind,
+                       hipStream_t stream);
+
+// C[r][j] = sum over s = 0..S-1, in that order, of partial[s][r][j]
+hipError_t launch_split_reduce(const float* partial, int S, int m, int64_t n, void* C,
+                               int64_t ldc, int c_kind, hipStream_t stream);
+
+// Per-row top-k with blockIdx.x = row.  When S >= 1 and `partial` is set, the
+// logits are first reduced from the partials (same order as
+// launch_split_reduce) and written to `logits`; otherwise they are read from
+// `logits`.
+hipError_t launch_topk(const float* partial, int S, int m, int64_t n, float* logits,
+                       int64_t ldl, int32_t* idx, float* val, int topk, hipStream_t stream);
+
+hipError_t launch_dequant_q8_0(int64_t n, int64_t k, const int8_t* qs, const uint16_t* d,
+                               uint16_t* out, hipStream_t stream);
+
+// ---------------------------------------------------------------------------
+// MFMA GEMM (v_mfma_f32_32x32x16_{f16,bf16} for every tile, K-tiles of 32 in
+// increasing k, so every tile gives the same bits).
+// ---------------------------------------------------------------------------
+struct GemmArgs {
+  const uint16_t* A;       // [M][lda]
+  int64_t lda;
+  const void* W;           // [N][K] (f16/bf16 bits, or int8 codes)
+  const uint16_t* scales;  // Q8_0 scales [N][K/32]
+  int64_t M;
+  int64_t N;
+  int64_t K;
+  void* C;                 // [M][ldc]
+  int64_t ldc;
+};
+
+struct GemmTileInfo {
+  int tm, tn, wm, wn;  // block tile and wave grid (each wave owns (tm/wm) x (tn/wn))
+  const char* name;
+};
+
+int gemm_tile_count();
+const GemmTileInfo& gemm_tile(int id);
+
+hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind,
+                       hipStream_t stream);
+
+}  // namespace skinny
