@@ -1,0 +1,414 @@
+"""Benchmark of the weight-streaming skinny matmul on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--rounds R] [--no-sweep] [--no-cpu]
+
+Headline step (the router workload, Strata PR #109 "What"): one decode
+window sweep -- gemv_topk_run at m = 1, 2, 4, 8, 16 rows, each on a cold copy
+of the bf16 router weight [256 x 5120] -- so `value` is the weight bytes the
+step streams per second (weight-GB/s), with us_per_row for every m alongside
+(nx_batchscale_kat: print every m, not one ratio).
+
+Timing: inputs are resident in HBM before the timed region.  Each weight
+copy comes from a rotating pool larger than the 256 MiB Infinity Cache, so
+every call streams its weight from HBM.  The K timed steps are captured once
+as a HIP graph (the library's runs allocate nothing and never synchronise, so
+they capture) and replayed between two events after a synchronize, which
+removes Python's per-launch cost from a region whose kernels take a few
+microseconds each.
+
+The sweep times every workload at every m the same way (min and median over
+interleaved rounds, opus r35 track A section 2's method), and reports
+us_per_row, weight-GB/s, HBM and MFMA roofline fractions.
+
+cpu_baseline: the CPU oracle (fp64, plain C) timed on this host's cores on a
+bounded sample of the headline step; its outputs also check the GPU's on the
+same sample (the run exits non-zero on a mismatch).
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense f16/bf16 MFMA, published
+POOL_BYTES = 640 << 20       # rotating weight pool, > 256 MiB Infinity Cache
+HEADLINE = "router_topk"
+HEADLINE_MS = (1, 2, 4, 8, 16)
+TOPK = 10
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=200)
+    p.add_argument("--warmup", type=int, default=20)
+    p.add_argument("--rounds", type=int, default=9)
+    p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--no-cpu", action="store_true")
+    p.add_argument("--cpu-seconds", type=float, default=10.0)
+    return p.parse_args()
+
+
+# ---------------------------------------------------------------------------
+# inputs
+# ---------------------------------------------------------------------------
+class Inputs:
+    """Device copies of one workload: a pool of weight copies and one A."""
+
+    def __init__(self, wl, torch, max_rows, pool_bytes=POOL_BYTES):
+        import numpy as np
+        import workloads as WL
+
+        self.wl = wl
+        W = WL.gen_w(wl)
+        A = WL.gen_a(wl, max_rows)
+        self.A_bits = A
+        self.W_bits = W
+
+        def dev16(bits, kind):
+            t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+            return t.view(torch.bfloat16 if kind == "bf16" else torch.float16).cuda()
+
+        self.A = dev16(A, wl.a_kind)
+        copies = max(2, int(pool_bytes // max(1, wl.w_bytes)))
+        if wl.w_kind == "q8_0":
+            qs, d = W
+            q0 = torch.from_numpy(qs).cuda()
+            d0 = dev16(d, "f16")
+            self.W = [(q0.clone(), d0.clone()) for _ in range(copies)]
+        else:
+            w0 = dev16(W, wl.w_kind)
+            self.W = [w0.clone() for _ in range(copies)]
+        self.scales = None
+
+
+def dtype_codes(sk, wl):
+    a = sk.BF16 if wl.a_kind == "bf16" else sk.F16
+    w = {"f16": sk.F16, "bf16": sk.BF16, "q8_0": sk.Q8_0}[wl.w_kind]
+    c = sk.F32 if wl.c_kind == "f32" else sk.F16
+    return a, w, c
+
+
+def call_bytes(wl, m, with_topk=False):
+    """Algorithmic HBM bytes of one call: the weight once, A once, C once."""
+    c_elem = 4 if wl.c_kind == "f32" else 2
+    b = wl.w_bytes + m * wl.k * 2 + m * wl.n * c_elem
+    if with_topk:
+        b += m * TOPK * 8
+    return b
+
+
+# ---------------------------------------------------------------------------
+# timing helpers
+# ---------------------------------------------------------------------------
+def capture(torch, fn, count):
+    """Capture `count` calls fn(i) into one HIP graph.
+
+    The caller must keep every tensor fn touches alive for as long as the
+    graph is replayed: torch.cuda.graph() empties the allocator cache when a
+    capture starts, so a buffer freed after an earlier capture can be unmapped
+    while that earlier graph still writes to it."""
+    g = torch.cuda.CUDAGraph()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        for i in range(2):  # warm the path on the capture stream
+            fn(i)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g, stream=s):
+            for i in range(count):
+                fn(i)
+    torch.cuda.synchronize()
+    return g
+
+
+def time_graph(torch, g, count, rounds):
+    """Per-call microseconds of a graph of `count` calls: (min, median) over rounds."""
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    g.replay()
+    torch.cuda.synchronize()
+    res = []
+    for _ in range(rounds):
+        e0.record()
+        g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        res.append(e0.elapsed_time(e1) * 1e3 / count)
+    res.sort()
+    return res[0], res[len(res) // 2]
+
+
+# ---------------------------------------------------------------------------
+# the headline step
+# ---------------------------------------------------------------------------
+class RouterStep:
+    def __init__(self, sk, torch, inp):
+        wl = inp.wl
+        self.inp = inp
+        self.plan = sk.Plan(wl.n, wl.k, max(HEADLINE_MS), sk.BF16, sk.BF16, sk.F32)
+        self.ws = self.plan.workspace(inp.A.device)
+        self.out = {}
+        for m in HEADLINE_MS:
+            self.out[m] = (torch.empty((m, wl.n), dtype=torch.float32, device="cuda"),
+                           torch.empty((m, TOPK), dtype=torch.int32, device="cuda"),
+                           torch.empty((m, TOPK), dtype=torch.float32, device="cuda"))
+        self.calls = 0
+
+    def call(self, m, copy):
+        lg, idx, val = self.out[m]
+        self.plan.run_topk(m, self.inp.A[:m], self.inp.W[copy % len(self.inp.W)], lg, idx, val, TOPK,
+                           workspace=self.ws)
+
+    def step(self, i):
+        base = i * len(HEADLINE_MS)
+        for j, m in enumerate(HEADLINE_MS):
+            self.call(m, base + j)
+
+    def bytes_per_step(self):
+        return sum(call_bytes(self.inp.wl, m, True) for m in HEADLINE_MS)
+
+    def weight_bytes_per_step(self):
+        return self.inp.wl.w_bytes * len(HEADLINE_MS)
+
+
+# ---------------------------------------------------------------------------
+# sweep over every workload and m
+# ---------------------------------------------------------------------------
+def sweep(sk, torch, rounds):
+    import workloads as WL
+
+    rows = []
+    for name, wl in WL.WORKLOADS.items():
+        inp = Inputs(wl, torch, max(wl.ms))
+        a, w, c = dtype_codes(sk, wl)
+        plan = sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c)
+        ws = plan.workspace(inp.A.device)
+        cdt = torch.float32 if wl.c_kind == "f32" else torch.float16
+        graphs = {}
+        keep = []  # every tensor a captured graph touches, alive until the graphs go
+        for m in wl.ms:
+            C = torch.empty((m, wl.n), dtype=cdt, device="cuda")
+            keep.append(C)
+            Am = inp.A[:m]
+            L = min(len(inp.W), 256)
+
+            if wl.w_kind == "q8_0":
+                def fn(i, m=m, C=C, Am=Am):
+                    qs, d = inp.W[i % len(inp.W)]
+                    plan.run(m, Am, qs, C, scales=d, workspace=ws)
+            elif wl.topk:
+                lg = C
+                idx = torch.empty((m, wl.topk), dtype=torch.int32, device="cuda")
+                val = torch.empty((m, wl.topk), dtype=torch.float32, device="cuda")
+                keep += [idx, val]
+
+                def fn(i, m=m, Am=Am, lg=lg, idx=idx, val=val):
+                    plan.run_topk(m, Am, inp.W[i % len(inp.W)], lg, idx, val, wl.topk, workspace=ws)
+            else:
+                def fn(i, m=m, C=C, Am=Am):
+                    plan.run(m, Am, inp.W[i % len(inp.W)], C, workspace=ws)
+            keep.append(fn)
+            graphs[m] = (capture(torch, fn, L), L)
+        # interleave rounds across m (the min over interleaved rounds)
+        per = {m: [] for m in wl.ms}
+        for _ in range(rounds):
+            for m in wl.ms:
+                g, L = graphs[m]
+                per[m].append(time_graph(torch, g, L, 1)[0])
+        for m in wl.ms:
+            ts = sorted(per[m])
+            t_min, t_med = ts[0], ts[len(ts) // 2]
+            nbytes = call_bytes(wl, m, bool(wl.topk))
+            flops = 2.0 * m * wl.n * wl.k
+            row = {
+                "workload": name, "m": m, "path": plan.info(m).split()[0].split("=")[1],
+                "plan": plan.info(m), "us_per_call_min": round(t_min, 3),
+                "us_per_call_median": round(t_med, 3), "us_per_row": round(t_min / m, 4),
+                "weight_GBps": round(wl.w_bytes / t_min / 1e3, 1),
+                "hbm_frac": round(nbytes / t_min / 1e3 / HBM_PEAK_GBS, 4),
+                "TFLOPs": round(flops / t_min / 1e6, 2),
+                "mfma_frac": round(flops / t_min / 1e6 / MFMA_F16_PEAK_TFLOPS, 4),
+            }
+            rows.append(row)
+            log(f"  {name:12s} m={m:5d} {t_min:8.3f} us (med {t_med:8.3f})  us/row {t_min / m:8.4f}"
+                f"  W {row['weight_GBps']:8.1f} GB/s  hbm {row['hbm_frac']:.3f}  "
+                f"{row['TFLOPs']:8.1f} TF/s  mfma {row['mfma_frac']:.3f}  [{row['plan']}]")
+        torch.cuda.synchronize()
+        del graphs
+        del keep, inp
+        torch.cuda.empty_cache()
+    return rows
+
+
+# ---------------------------------------------------------------------------
+# CPU baseline (the oracle, as it stands) + parity on the same sample
+# ---------------------------------------------------------------------------
+def cpu_baseline(torch, step, budget_s):
+    import numpy as np
+
+    import oracle
+
+    wl = step.inp.wl
+    A = step.inp.A_bits
+    W = step.inp.W_bits
+    threads = oracle.default_threads()
+    # parity of the GPU's headline outputs on this sample (fresh call on copy 0)
+    ok = True
+    for m in HEADLINE_MS:
+        step.call(m, 0)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    done_steps = 0
+    while True:
+        for m in HEADLINE_MS:
+            ref = oracle.mm(A[:m], "bf16", W, "bf16", threads=threads)
+            oi, _ = oracle.topk(ref, TOPK)
+            if done_steps == 0:
+                lg, idx, _ = step.out[m]
+                got = lg.cpu().numpy().astype(np.float64)
+                err = float(np.max(np.abs(got - ref)) / np.max(np.abs(ref)))
+                gi, _ = oracle.topk(got, TOPK)
+                if err > 2e-3 or not np.array_equal(idx.cpu().numpy(), gi):
+                    ok = False
+                    log(f"PARITY FAIL router m={m}: rel err {err:.3e}")
+        done_steps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    gbps = step.weight_bytes_per_step() * done_steps / dt / 1e9
+    return {
+        "value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "sample": f"{done_steps} headline steps (router m=1,2,4,8,16 + top-10), fp64 oracle, "
+                  f"{dt:.1f} s wall",
+    }, ok
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU: the library has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import row_gemv_decode_amd as sk
+    import workloads as WL
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    props = torch.cuda.get_device_properties(0)
+    log(f"device: {props.name}, {props.multi_processor_count} CUs")
+
+    wl = WL.WORKLOADS[HEADLINE]
+    inp = Inputs(wl, torch, max(HEADLINE_MS))
+    step = RouterStep(sk, torch, inp)
+    for m in HEADLINE_MS:
+        log(f"  plan m={m}: {step.plan.info(m)}")
+
+    # warmup: W untimed steps (eager), then the K-step graph
+    for i in range(args.warmup):
+        step.step(i)
+    torch.cuda.synchronize()
+    K = args.steps
+    g = capture(torch, lambda i: step.step(i + args.warmup), K)
+
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    ms_total = e0.elapsed_time(e1)
+    ms_per_step = ms_total / K
+    value = step.weight_bytes_per_step() / (ms_per_step / 1e3) / 1e9
+    launches = len(HEADLINE_MS) * K
+    # the dominant kernel: the router GEMV (one launch per call)
+    us_per_launch = ms_total * 1e3 / launches
+    alg_bytes = step.bytes_per_step() / len(HEADLINE_MS)
+    achieved = alg_bytes / us_per_launch / 1e3
+    log(f"headline: {ms_per_step * 1e3:.2f} us/step, {value:.1f} weight-GB/s, "
+        f"{us_per_launch:.3f} us/call")
+
+    # per-m lines of the headline workload (same timing, one graph per m)
+    per_m = []
+    for m in HEADLINE_MS:
+        L = min(len(inp.W), 256)
+        gm = capture(torch, lambda i, m=m: step.call(m, i), L)
+        t_min, t_med = time_graph(torch, gm, L, args.rounds)
+        per_m.append({"m": m, "us_per_call": round(t_min, 3), "us_per_call_median": round(t_med, 3),
+                      "us_per_row": round(t_min / m, 4),
+                      "weight_GBps": round(wl.w_bytes / t_min / 1e3, 1)})
+        del gm
+    log("per m: " + ", ".join(f"m={r['m']}: {r['us_per_row']} us/row" for r in per_m))
+
+    sweep_rows = [] if args.no_sweep else sweep(sk, torch, args.rounds)
+
+    cpu = None
+    parity_ok = True
+    if not args.no_cpu:
+        cpu, parity_ok = cpu_baseline(torch, step, args.cpu_seconds)
+        log(f"cpu oracle: {cpu['value']} GB/s on {cpu['cores']} threads ({cpu['sample']})")
+
+    derived = {}
+    rows0 = [r for r in sweep_rows if r["workload"] == "gemv_k896"]
+    if rows0:
+        u = {r["m"]: r["us_per_row"] for r in rows0}
+        if 1 in u and 8 in u:
+            derived["gemv_k896_us_per_row_ratio_m1_over_m8"] = round(u[1] / u[8], 3)
+    g2048 = [r for r in sweep_rows if r["workload"] == "wide_n7680" and r["m"] == 2048]
+    if g2048:
+        derived["f16_gemm_TFLOPs_M2048"] = g2048[0]["TFLOPs"]
+        derived["f16_gemm_mfma_frac_M2048"] = g2048[0]["mfma_frac"]
+
+    out = {
+        "metric": "us_per_row & weight-GB/s vs m (1..16); f16 GEMM TFLOP/s at M=2048; % of peak",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {
+            "workload": "router GEMV + top-10: W bf16 [256 x 5120], A bf16 ~N(0,1), "
+                        "fp32 logits; one step = m in (1,2,4,8,16), cold weight each call",
+            "n": wl.n, "k": wl.k, "m_sweep": list(HEADLINE_MS), "topk": TOPK,
+            "timing": "K steps captured as one HIP graph, replayed between events",
+        },
+        "roofline": {
+            "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "kernel": "router gemv_topk call", "alg_bytes_per_launch": round(alg_bytes, 1),
+            "us_per_launch": round(us_per_launch, 4),
+        },
+        "cpu_baseline": cpu,
+        "per_m": per_m,
+        "derived": derived,
+        "sweep": sweep_rows,
+        "parity_ok": parity_ok,
+    }
+    print(json.dumps(out), flush=True)
+    if not parity_ok:
+        sys.exit(1)
+
+
+if __name__ == "__main__":
+    main()

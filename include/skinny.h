@@ -66,7 +66,7 @@ typedef enum skinny_status {
   SKINNY_OK = 0,
   SKINNY_ERR_INVALID_ARG = 1, /* null pointer, bad struct_size, m/n/k/topk out of range */
   SKINNY_ERR_UNSUPPORTED = 2, /* dtype combination or flag the library does not implement */
-  SKINNY_ERR_ALIGNMENT = 3,   /* pointer not 16-byte aligned or stride not a multiple of 8 */
+  SKINNY_ERR_ALIGNMENT = 3,   /* pointer not 16-byte aligned or lda not a multiple of 8 */
   SKINNY_ERR_SHAPE = 4,       /* k not a multiple of 8 (32 for Q8_0), stride < row length */
   SKINNY_ERR_HIP = 5,         /* the HIP runtime reported an error (device query or launch) */
   SKINNY_ERR_WORKSPACE = 6    /* workspace missing or smaller than skinny_mm_workspace_size */
@@ -95,7 +95,8 @@ typedef enum skinny_dtype {
  *   n, k         output columns and reduction length (n >= 1; k >= 8, k % 8 == 0,
  *                k % 32 == 0 for Q8_0)
  *   lda, ldc     row strides of A and C in elements; 0 means dense (k and n);
- *                otherwise >= the row length and a multiple of 8
+ *                otherwise >= the row length; lda a multiple of 8 (A rows are
+ *                read 16 bytes at a time), ldc any value >= n
  *   flags        SKINNY_FORCE_* (tests and benchmarks); 0 normally
  *   tile_id      -1: the plan's tile selector; >= 0: force that GEMM tile
  *                (see skinny_gemm_tile_count)
@@ -127,8 +128,14 @@ SKINNY_API skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan*
 /* Free a plan (NULL is ignored).  Runs already enqueued are unaffected. */
 SKINNY_API void skinny_mm_plan_destroy(skinny_plan* plan);
 
-/* Bytes of device workspace a run with this plan needs (0 when none); valid
- * for every m <= max_m, for skinny_mm_run and gemv_topk_run alike. */
+/* Bytes of device workspace a run with this plan may need (0 when none);
+ * enough for every m <= max_m, for skinny_mm_run and gemv_topk_run alike.
+ * The workspace holds the GEMV's fp32 partial sums when the plan splits k
+ * and the arrival counters that let the last wave of a split (and the last
+ * block of a top-k launch) finish the call inside the same kernel.  It must be
+ * zero-filled once before its first use; every completed run leaves it ready
+ * for the next (its counters back at zero).  A run that needs no workspace
+ * (GEMM path, or an unsplit GEMV without top-k) ignores it. */
 SKINNY_API skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_t* bytes);
 
 /* C[0:m, 0:n] = A[0:m, :] . W  (nx_batchscale_kat: the product with fp32
@@ -136,8 +143,9 @@ SKINNY_API skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_
  *   m          1 <= m <= max_m
  *   A, W, C    device pointers (16-byte aligned); w_scales: Q8_0 scales
  *              f16 [n][k/32] (16-byte aligned), else must be NULL
- *   workspace  device scratch of >= skinny_mm_workspace_size bytes (may be
- *              NULL when that size is 0)
+ *   workspace  zero-initialised device scratch of >= skinny_mm_workspace_size
+ *              bytes (may be NULL when that size is 0); one launch finishes the
+ *              call, including the reduction over k splits
  *   stream     hipStream_t (NULL = null stream)
  * Writes rows 0..m-1 of C, columns 0..n-1 only. */
 SKINNY_API skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
@@ -145,8 +153,11 @@ SKINNY_API skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const
                             size_t workspace_bytes, void* stream);
 
 /* Router step (Strata PR #109, "What": the multi-row router GEMV into fp32
- * logits, then one multi-row top-k launch with one block per token).
- * The plan's c_dtype must be SKINNY_F32.
+ * logits and a multi-row top-k).  In the GEMV regime both run in ONE launch:
+ * the last block to finish takes the top-k of every row.  In the GEMM regime
+ * a second launch (one wave per row) takes the top-k.  The workspace is
+ * required (see skinny_mm_workspace_size).  The plan's c_dtype must be
+ * SKINNY_F32.
  *   logits     f32 [m][ldc] out (the full product)
  *   topk_idx   int32 [m][topk] out: the topk largest logits of each row,
  *              value descending, equal values (IEEE ==, so -0 == +0) by lower

@@ -15,7 +15,6 @@ W[k, n] in C[m, n] = A[m, k] . W[k, n].
 """
 import ctypes
 import os
-import threading
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libskinny.so")
@@ -151,6 +150,7 @@ class Plan:
         sz = ctypes.c_size_t()
         _check(_lib.skinny_mm_workspace_size(self._h, ctypes.byref(sz)), "skinny_mm_workspace_size")
         self.workspace_bytes = int(sz.value)
+        self._ws = {}
 
     @property
     def handle(self):
@@ -162,10 +162,17 @@ class Plan:
         return buf.value.decode()
 
     def workspace(self, device):
-        """A cached device workspace for this plan (None when none is needed)."""
+        """This plan's own zero-initialised device workspace (None when none is
+        needed).  Each plan keeps its own: the counters of one plan's layout
+        must not be overwritten by another plan's partial sums."""
         if self.workspace_bytes == 0:
             return None
-        return _workspace(device, self.workspace_bytes)
+        key = str(device)
+        ws = self._ws.get(key)
+        if ws is None:
+            ws = _torch().zeros(self.workspace_bytes, dtype=_torch().uint8, device=device)
+            self._ws[key] = ws
+        return ws
 
     def run(self, m, A, W, C, scales=None, workspace=None, stream=None):
         ws = workspace if workspace is not None else self.workspace(A.device)
@@ -182,24 +189,20 @@ class Plan:
 
     def __del__(self):
         h = getattr(self, "_h", None)
-        if h is not None and h.value:
-            _lib.skinny_mm_plan_destroy(h)
+        if h is not None and h.value and _lib is not None:
+            try:
+                _lib.skinny_mm_plan_destroy(h)
+            except Exception:  # interpreter shutdown
+                pass
             self._h = None
 
 
-_ws_lock = threading.Lock()
-_ws_cache = {}
-
-
-def _workspace(device, nbytes):
+def new_workspace(plan, device):
+    """A fresh zero-filled workspace for `plan` (None when it needs none)."""
     torch = _torch()
-    key = (str(device), threading.get_ident())
-    with _ws_lock:
-        buf = _ws_cache.get(key)
-        if buf is None or buf.numel() < nbytes:
-            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
-            _ws_cache[key] = buf
-        return buf
+    if plan.workspace_bytes == 0:
+        return None
+    return torch.zeros(plan.workspace_bytes, dtype=torch.uint8, device=device)
 
 
 _plan_cache = {}

@@ -94,17 +94,15 @@ double tile_efficiency(const GemmTileInfo& t) {
 int select_tile(const skinny_plan* p, int64_t m) {
   if (p->d.tile_id >= 0) return p->d.tile_id;
   const int64_t n = p->d.n;
-  int best = 0;
+  int best = -1;
   double best_cost = 0.0;
   for (int id = 0; id < gemm_tile_count(); ++id) {
     const GemmTileInfo& t = gemm_tile(id);
+    if (t.wm * t.wn != 4) continue;  // one- and two-wave tiles: tests only
     const int64_t blocks = ((m + t.tm - 1) / t.tm) * ((n + t.tn - 1) / t.tn);
-    const int waves_per_block = t.wm * t.wn;
-    int64_t resident = (int64_t)p->num_cus * (8 / waves_per_block > 2 ? 2 : 8 / waves_per_block);
-    if (resident < 1) resident = 1;
-    const int64_t rounds = (blocks + resident - 1) / resident;
+    const int64_t rounds = (blocks + p->num_cus - 1) / p->num_cus;
     const double cost = (double)rounds * (double)t.tm * (double)t.tn / tile_efficiency(t);
-    if (id == 0 || cost < best_cost * (1.0 - 1e-9)) {
+    if (best < 0 || cost < best_cost * (1.0 - 1e-9)) {
       best = id;
       best_cost = cost;
     }
@@ -112,13 +110,32 @@ int select_tile(const skinny_plan* p, int64_t m) {
   return best;
 }
 
-size_t gemv_workspace_bytes(const skinny_plan* p, int64_t m) {
-  if (p->gemv_S <= 1) return 0;
-  return (size_t)p->gemv_S * (size_t)m * (size_t)p->d.n * sizeof(float);
+// GEMV workspace: [fp32 partials S x m x n, when S > 1] [arrival counters:
+// one per column range, then one for finished blocks].  The counters must be
+// zero before the first call; every call leaves them at zero.
+constexpr size_t kWsAlign = 256;
+
+size_t round_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
+
+int64_t gemv_waves_per_split(const skinny_plan* p) { return (p->d.n + p->gemv_cpw - 1) / p->gemv_cpw; }
+
+size_t gemv_partial_bytes(const skinny_plan* p, int64_t m) {
+  return p->gemv_S > 1 ? round_up((size_t)p->gemv_S * (size_t)m * (size_t)p->d.n * sizeof(float)) : 0;
 }
 
-size_t workspace_bytes_for(const skinny_plan* p, int64_t m) {
-  return use_gemv(p, m) ? gemv_workspace_bytes(p, m) : 0;
+size_t gemv_counter_bytes(const skinny_plan* p) {
+  return round_up((size_t)(gemv_waves_per_split(p) + 1) * sizeof(uint32_t));
+}
+
+// bytes a run needs: the split partials (and their counters) when k is split,
+// the block counter when the run also does the top-k
+size_t workspace_bytes_for(const skinny_plan* p, int64_t m, bool topk) {
+  if (!use_gemv(p, m)) return 0;
+  if (p->gemv_S <= 1 && !topk) return 0;
+  // counters sit after the partials sized for the plan's largest GEMV m, so
+  // their offset is the same for every m
+  const int64_t mm = p->d.max_m < kGemvMaxM ? p->d.max_m : kGemvMaxM;
+  return gemv_partial_bytes(p, mm) + gemv_counter_bytes(p);
 }
 
 skinny_status hip_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_ERR_HIP; }
@@ -135,10 +152,17 @@ GemvArgs gemv_args(const skinny_plan* p, const void* A, const void* W, const voi
   g.nchunks = (int32_t)(p->d.k / 8);
   g.S = p->gemv_S;
   g.cpw = p->gemv_cpw;
-  g.waves_per_split = (int32_t)((p->d.n + p->gemv_cpw - 1) / p->gemv_cpw);
+  g.waves_per_split = (int32_t)gemv_waves_per_split(p);
   g.C = C;
   g.ldc = ldc;
-  g.partial = (float*)workspace;
+  const int64_t mm = p->d.max_m < kGemvMaxM ? p->d.max_m : kGemvMaxM;
+  char* ws = (char*)workspace;
+  g.partial = (ws != nullptr && p->gemv_S > 1) ? (float*)ws : nullptr;
+  g.counters = ws != nullptr ? (uint32_t*)(ws + gemv_partial_bytes(p, mm)) : nullptr;
+  g.done = ws != nullptr ? g.counters + gemv_waves_per_split(p) : nullptr;
+  g.topk_idx = nullptr;
+  g.topk_val = nullptr;
+  g.topk = 0;
   return g;
 }
 
@@ -160,7 +184,7 @@ GemmArgs gemm_args(const skinny_plan* p, int64_t m, const void* A, const void* W
 // checks shared by skinny_mm_run and gemv_topk_run
 skinny_status check_run(const skinny_plan* p, int64_t m, const void* A, const void* W,
                         const void* scales, const void* C, const void* workspace,
-                        size_t workspace_bytes) {
+                        size_t workspace_bytes, bool topk) {
   if (p == nullptr) return SKINNY_ERR_INVALID_ARG;
   if (m < 1 || m > p->d.max_m) return SKINNY_ERR_INVALID_ARG;
   if (A == nullptr || W == nullptr || C == nullptr) return SKINNY_ERR_INVALID_ARG;
@@ -168,7 +192,7 @@ skinny_status check_run(const skinny_plan* p, int64_t m, const void* A, const vo
   if (q8 != (scales != nullptr)) return SKINNY_ERR_INVALID_ARG;
   if (!aligned16(A) || !aligned16(W) || !aligned16(C) || (q8 && !aligned16(scales)))
     return SKINNY_ERR_ALIGNMENT;
-  const size_t need = workspace_bytes_for(p, m);
+  const size_t need = workspace_bytes_for(p, m, topk);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return SKINNY_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SKINNY_ERR_ALIGNMENT;
@@ -176,24 +200,31 @@ skinny_status check_run(const skinny_plan* p, int64_t m, const void* A, const vo
   return SKINNY_OK;
 }
 
-// enqueue C = A . W for m rows (GEMV partials stay in the workspace when the
-// plan splits k and `keep_partials` is set)
+// waves per GEMV block: 4 spreads the waves over the most CUs; a top-k launch
+// with more than 4 rows uses 8 so the last block has a wave per row
+int gemv_waves_per_block(int64_t m, bool topk) { return (topk && m > 4) ? 8 : 4; }
+
+// enqueue C = A . W for m rows (plus the top-k when idx/val are given)
 skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const void* W,
                          const void* scales, void* C, int64_t ldc, int c_kind, void* workspace,
-                         bool keep_partials, hipStream_t stream) {
+                         int32_t* topk_idx, float* topk_val, int32_t topk, hipStream_t stream) {
+  const bool want_topk = topk_idx != nullptr;
   if (use_gemv(p, m)) {
     GemvArgs g = gemv_args(p, A, W, scales, C, ldc, workspace);
-    if (p->gemv_S > 1) {
-      hipError_t e = launch_gemv(g, (int)m, p->gemv_T, p->w_kind, 3, stream);
-      if (e != hipSuccess) return SKINNY_ERR_HIP;
-      if (keep_partials) return SKINNY_OK;
-      return hip_status(launch_split_reduce((const float*)workspace, p->gemv_S, (int)m, p->d.n, C, ldc,
-                                            c_kind, stream));
+    int out_kind = c_kind;
+    if (want_topk) {
+      g.topk_idx = topk_idx;
+      g.topk_val = topk_val;
+      g.topk = topk;
+      out_kind = 3;
     }
-    return hip_status(launch_gemv(g, (int)m, p->gemv_T, p->w_kind, c_kind, stream));
+    return hip_status(launch_gemv(g, (int)m, p->gemv_T, p->w_kind, out_kind,
+                                  gemv_waves_per_block(m, want_topk), stream));
   }
   GemmArgs g = gemm_args(p, m, A, W, scales, C, ldc);
-  return hip_status(launch_gemm(select_tile(p, m), g, p->w_kind, c_kind, stream));
+  skinny_status st = hip_status(launch_gemm(select_tile(p, m), g, p->w_kind, c_kind, stream));
+  if (st != SKINNY_OK || !want_topk) return st;
+  return hip_status(launch_topk((const float*)C, (int)m, p->d.n, ldc, topk_idx, topk_val, topk, stream));
 }
 
 }  // namespace
@@ -241,7 +272,7 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   if (d.lda == 0) d.lda = d.k;
   if (d.ldc == 0) d.ldc = d.n;
   if (d.lda < d.k || d.ldc < d.n) return SKINNY_ERR_SHAPE;
-  if (d.lda % 8 != 0 || d.ldc % 8 != 0) return SKINNY_ERR_ALIGNMENT;
+  if (d.lda % 8 != 0) return SKINNY_ERR_ALIGNMENT;  // A rows are read 16 bytes at a time
   if (d.flags & ~(SKINNY_FORCE_GEMV | SKINNY_FORCE_GEMM)) return SKINNY_ERR_UNSUPPORTED;
   if ((d.flags & SKINNY_FORCE_GEMV) && (d.flags & SKINNY_FORCE_GEMM)) return SKINNY_ERR_INVALID_ARG;
   if ((d.flags & SKINNY_FORCE_GEMV) && d.max_m > kGemvMaxM) return SKINNY_ERR_INVALID_ARG;
@@ -278,40 +309,34 @@ void skinny_mm_plan_destroy(skinny_plan* plan) { delete plan; }
 
 skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_t* bytes) {
   if (plan == nullptr || bytes == nullptr) return SKINNY_ERR_INVALID_ARG;
-  size_t need = 0;
   const int64_t mm = plan->d.max_m < kGemvMaxM ? plan->d.max_m : kGemvMaxM;
-  // the GEMV is used for m <= 16 (or every m when forced); its need grows with m
-  if (!(plan->d.flags & SKINNY_FORCE_GEMM)) need = gemv_workspace_bytes(plan, mm);
-  *bytes = need;
+  // the largest need of any run: a GEMV m (when the plan may use the GEMV)
+  // with the top-k counters
+  *bytes = workspace_bytes_for(plan, mm, true);
   return SKINNY_OK;
 }
 
 skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
                             const void* w_scales, void* C, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  skinny_status st = check_run(plan, m, A, W, w_scales, C, workspace, workspace_bytes);
+  skinny_status st = check_run(plan, m, A, W, w_scales, C, workspace, workspace_bytes, false);
   if (st != SKINNY_OK) return st;
-  return enqueue_mm(plan, m, A, W, w_scales, C, plan->d.ldc, plan->c_kind, workspace, false,
-                    (hipStream_t)stream);
+  return enqueue_mm(plan, m, A, W, w_scales, C, plan->d.ldc, plan->c_kind, workspace, nullptr, nullptr,
+                    0, (hipStream_t)stream);
 }
 
 skinny_status gemv_topk_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
                             const void* w_scales, float* logits, int32_t* topk_idx,
                             float* topk_val, int32_t topk, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  skinny_status st = check_run(plan, m, A, W, w_scales, logits, workspace, workspace_bytes);
+  skinny_status st = check_run(plan, m, A, W, w_scales, logits, workspace, workspace_bytes, true);
   if (st != SKINNY_OK) return st;
   if (plan->d.c_dtype != SKINNY_F32) return SKINNY_ERR_UNSUPPORTED;
   if (topk_idx == nullptr || topk_val == nullptr) return SKINNY_ERR_INVALID_ARG;
   if (topk < 1 || topk > SKINNY_TOPK_MAX || topk > plan->d.n) return SKINNY_ERR_INVALID_ARG;
   if (!aligned16(topk_idx) || !aligned16(topk_val)) return SKINNY_ERR_ALIGNMENT;
-
-  hipStream_t s = (hipStream_t)stream;
-  const bool split = use_gemv(plan, m) && plan->gemv_S > 1;
-  st = enqueue_mm(plan, m, A, W, w_scales, logits, plan->d.ldc, CK_F32, workspace, true, s);
-  if (st != SKINNY_OK) return st;
-  return hip_status(launch_topk(split ? (const float*)workspace : nullptr, plan->gemv_S, (int)m,
-                                plan->d.n, logits, plan->d.ldc, topk_idx, topk_val, topk, s));
+  return enqueue_mm(plan, m, A, W, w_scales, logits, plan->d.ldc, CK_F32, workspace, topk_idx, topk_val,
+                    topk, (hipStream_t)stream);
 }
 
 skinny_status skinny_dequant_q8_0_run(int64_t n, int64_t k, const void* qs, const void* d,
@@ -328,13 +353,13 @@ skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf,
   if (plan == nullptr || buf == nullptr || len == 0) return SKINNY_ERR_INVALID_ARG;
   if (m < 1 || m > plan->d.max_m) return SKINNY_ERR_INVALID_ARG;
   if (use_gemv(plan, m)) {
-    const int64_t wps = (plan->d.n + plan->gemv_cpw - 1) / plan->gemv_cpw;
-    const int64_t waves = wps * plan->gemv_S;
+    const int64_t waves = gemv_waves_per_split(plan) * plan->gemv_S;
     std::snprintf(buf, len,
-                  "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld reduce=%s workspace=%zu",
+                  "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld/%lld split_reduce=%s "
+                  "workspace=%zu",
                   (long long)m, plan->gemv_T, plan->gemv_S, plan->gemv_cpw, (long long)waves,
-                  (long long)((waves + kGemvWavesPerBlock - 1) / kGemvWavesPerBlock),
-                  plan->gemv_S > 1 ? "yes" : "no", gemv_workspace_bytes(plan, m));
+                  (long long)((waves + 3) / 4), (long long)((waves + 7) / 8),
+                  plan->gemv_S > 1 ? "in-kernel" : "none", workspace_bytes_for(plan, m, true));
   } else {
     const int id = select_tile(plan, m);
     const GemmTileInfo& t = gemm_tile(id);

@@ -50,6 +50,25 @@ struct GemvShape {
 __device__ __forceinline__ float fbits(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t ubits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
+// Device-coherent accesses for data handed from one workgroup to another in
+// the same launch.  Relaxed agent-scope atomic stores/loads compile to plain
+// global stores/loads with the sc1 (device scope) bit: they are coherent
+// across the XCDs' L2 caches without the whole-L2 write-back and invalidate
+// that an agent-scope fence costs.  A writer waits for its stores to complete
+// (s_waitcnt) before it counts itself in with an atomic; the reader issues its
+// loads only after its atomic returned the final count.
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ float ld_dev(const float* p) {
+  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void wait_mem() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);  // every outstanding load and store of this wave completed
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return fbits(__builtin_amdgcn_update_dpp(0u, ubits(x), CTRL, 0xF, 0xF, false));
@@ -197,8 +216,159 @@ __device__ __forceinline__ u32x4 w_as_halves(const WChunk<WK>& w) {
   }
 }
 
-template <int M, int T, int WK, int OUT>
-__global__ __launch_bounds__(64 * kGemvWavesPerBlock) void gemv_rows_kernel(GemvArgs g) {
+// ---------------------------------------------------------------------------
+// Per-row top-k by one wavefront (Strata PR #109, "What": one multi-row top-10
+// over the window's tokens).  Order: value descending, equal values (IEEE ==,
+// so -0 == +0) by lower column first; the winning lane writes the logit's own
+// bits.
+//
+// Fast path (n <= 64 * NC): lane l holds columns l, l + 64, ... in NC
+// registers and sorts them once (a stable odd-even transposition sort, so
+// equal values keep increasing columns).  Each round is then branch-free: the
+// wave maximum of the lanes' heads (DPP / permlane max), the smallest column
+// among heads equal to it (DPP / permlane min), and the owner pops its head.
+// Generic path (larger n): each round rescans the row.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ float wave_max_f32(float v) {
+  v = fmaxf(v, dpp_mov<kDppXor1>(v));
+  v = fmaxf(v, dpp_mov<kDppXor2>(v));
+  v = fmaxf(v, dpp_mov<kDppRowHalfMirror>(v));
+  v = fmaxf(v, dpp_mov<kDppRowMirror>(v));
+  auto r16 = __builtin_amdgcn_permlane16_swap(ubits(v), ubits(v), false, false);
+  v = fmaxf(fbits(r16[0]), fbits(r16[1]));
+  auto r32 = __builtin_amdgcn_permlane32_swap(ubits(v), ubits(v), false, false);
+  v = fmaxf(fbits(r32[0]), fbits(r32[1]));
+  return v;
+}
+
+template <int CTRL>
+__device__ __forceinline__ int dpp_mov_i(int x) {
+  return (int)__builtin_amdgcn_update_dpp(0u, (uint32_t)x, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ int wave_min_i32(int v) {
+  v = min(v, dpp_mov_i<kDppXor1>(v));
+  v = min(v, dpp_mov_i<kDppXor2>(v));
+  v = min(v, dpp_mov_i<kDppRowHalfMirror>(v));
+  v = min(v, dpp_mov_i<kDppRowMirror>(v));
+  auto r16 = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = min((int)r16[0], (int)r16[1]);
+  auto r32 = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = min((int)r32[0], (int)r32[1]);
+  return v;
+}
+
+// (v, j) comes after (pv, pj) in the order above
+__device__ __forceinline__ bool after(float v, int j, float pv, int pj) {
+  return v < pv || (v == pv && j > pj);
+}
+
+template <int NC>
+__device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int topk, int32_t* out_idx,
+                                                   float* out_val, int lane) {
+  constexpr int kNone = 0x7fffffff;
+  float v[NC];
+  int jj[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    const int j = lane + 64 * u;
+    const bool ok = j < n;
+    v[u] = ok ? ld_dev(row + j) : -__builtin_inff();
+    jj[u] = ok ? j : kNone;
+  }
+  // stable sort of the lane's slots into rank order
+#pragma unroll
+  for (int round = 0; round < NC; ++round) {
+#pragma unroll
+    for (int u = round & 1; u + 1 < NC; u += 2) {
+      const bool swap = after(v[u], jj[u], v[u + 1], jj[u + 1]);
+      const float tv = v[u];
+      const int tj = jj[u];
+      v[u] = swap ? v[u + 1] : v[u];
+      jj[u] = swap ? jj[u + 1] : jj[u];
+      v[u + 1] = swap ? tv : v[u + 1];
+      jj[u + 1] = swap ? tj : jj[u + 1];
+    }
+  }
+  for (int t = 0; t < topk; ++t) {
+    const float wmax = wave_max_f32(v[0]);
+    const int wj = wave_min_i32(v[0] == wmax ? jj[0] : kNone);
+    const bool mine = jj[0] == wj;
+    if (mine) {
+      out_idx[t] = wj;
+      out_val[t] = v[0];
+    }
+#pragma unroll
+    for (int u = 0; u + 1 < NC; ++u) {
+      v[u] = mine ? v[u + 1] : v[u];
+      jj[u] = mine ? jj[u + 1] : jj[u];
+    }
+    v[NC - 1] = mine ? -__builtin_inff() : v[NC - 1];
+    jj[NC - 1] = mine ? kNone : jj[NC - 1];
+  }
+}
+
+__device__ __noinline__ void wave_topk_row_generic(const float* row, int n, int topk, int32_t* out_idx,
+                                                   float* out_val, int lane) {
+  float prev_v = 0.0f;
+  int prev_j = -1;
+  for (int t = 0; t < topk; ++t) {
+    float best = -__builtin_inff();
+    for (int j = lane; j < n; j += 64) {
+      const float x = ld_dev(row + j);
+      if (prev_j < 0 || after(x, j, prev_v, prev_j)) best = fmaxf(best, x);
+    }
+    const float wmax = wave_max_f32(best);
+    int cand = 0x7fffffff;
+    float cand_v = 0.0f;
+    for (int j = lane; j < n; j += 64) {
+      const float x = ld_dev(row + j);
+      if (x == wmax && (prev_j < 0 || after(x, j, prev_v, prev_j)) && j < cand) {
+        cand = j;
+        cand_v = x;
+      }
+    }
+    const int wj = wave_min_i32(cand);
+    if (cand == wj) {
+      out_idx[t] = wj;
+      out_val[t] = cand_v;
+    }
+    prev_v = wmax;
+    prev_j = wj;
+  }
+}
+
+__device__ __forceinline__ void wave_topk_row(const float* row, int n, int topk, int32_t* out_idx,
+                                              float* out_val, int lane) {
+  if (n <= 64) {
+    wave_topk_row_regs<1>(row, n, topk, out_idx, out_val, lane);
+  } else if (n <= 128) {
+    wave_topk_row_regs<2>(row, n, topk, out_idx, out_val, lane);
+  } else if (n <= 256) {
+    wave_topk_row_regs<4>(row, n, topk, out_idx, out_val, lane);
+  } else if (n <= 512) {
+    wave_topk_row_regs<8>(row, n, topk, out_idx, out_val, lane);
+  } else if (n <= 1024) {
+    wave_topk_row_regs<16>(row, n, topk, out_idx, out_val, lane);
+  } else {
+    wave_topk_row_generic(row, n, topk, out_idx, out_val, lane);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The GEMV kernel.  M rows (template), T chunk slots per lane, weight kind WK,
+// output kind CK; TOPK adds the router's top-k in the same launch.
+//
+// Epilogue when the plan splits k (S > 1): each wave writes its fp32 sums to
+// partial[s][r][j], makes them visible device-wide, and counts itself in on
+// its column range; the wave that arrives last adds the S partials in the
+// fixed order s = 0..S-1 and writes C.  No wave ever waits for another.  With
+// TOPK every workgroup counts itself in once its C is visible; the last one
+// runs the top-k of every row.  The counters live in the caller's workspace,
+// start at zero and are left at zero.
+// ---------------------------------------------------------------------------
+template <int M, int T, int WK, int CK, bool TOPK>
+__global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(GemvArgs g) {
   using Shape = GemvShape<M>;
   constexpr int G = Shape::G;
   constexpr int P = Shape::P;
@@ -207,80 +377,127 @@ __global__ __launch_bounds__(64 * kGemvWavesPerBlock) void gemv_rows_kernel(Gemv
   static_assert(LV <= 6, "at most 64 values per lane");
 
   const int lane = threadIdx.x & 63;
-  const int gw = blockIdx.x * kGemvWavesPerBlock + (threadIdx.x >> 6);
+  const int wave = threadIdx.x >> 6;
+  const int wpb = blockDim.x >> 6;
+  const int gw = blockIdx.x * wpb + wave;
   const int s = gw / g.waves_per_split;
-  if (s >= g.S) return;  // whole wave leaves; the kernel has no barriers
-  const int wc = gw - s * g.waves_per_split;
+  const bool active = s < g.S;  // trailing waves of the last block have no columns
+  const int wc = active ? gw - s * g.waves_per_split : 0;
   const int64_t j0 = (int64_t)wc * g.cpw;
-  const int ncol = (int)min((int64_t)g.cpw, g.n - j0);
+  const int ncol = active ? (int)min((int64_t)g.cpw, g.n - j0) : 0;
 
-  int chunk[T];
-  bool valid[T];
-#pragma unroll
-  for (int t = 0; t < T; ++t) {
-    chunk[t] = s * 64 * T + t * 64 + lane;
-    valid[t] = chunk[t] < g.nchunks;
-  }
-
-  // every weight load of the wave, issued before anything else waits
-  WChunk<WK> w[kGemvCpwMax][T];
-#pragma unroll
-  for (int c = 0; c < kGemvCpwMax; ++c) {
+  if (active) {
+    int chunk[T];
+    bool valid[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      if (c < ncol && valid[t]) {
-        load_w<WK>(w[c][t], g, j0 + c, chunk[t]);
-      } else {
-        zero_w<WK>(w[c][t]);
+      chunk[t] = s * 64 * T + t * 64 + lane;
+      valid[t] = chunk[t] < g.nchunks;
+    }
+
+    // every weight load of the wave, issued before anything else waits
+    WChunk<WK> w[kGemvCpwMax][T];
+#pragma unroll
+    for (int c = 0; c < kGemvCpwMax; ++c) {
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        if (c < ncol && valid[t]) {
+          load_w<WK>(w[c][t], g, j0 + c, chunk[t]);
+        } else {
+          zero_w<WK>(w[c][t]);
+        }
       }
     }
-  }
 
-  // the wave's A slice, kept in registers for all its columns
-  u32x4 a[T][M];
+    // the wave's A slice, kept in registers for all its columns
+    u32x4 a[T][M];
 #pragma unroll
-  for (int t = 0; t < T; ++t) {
-#pragma unroll
-    for (int r = 0; r < M; ++r) {
-      a[t][r] = valid[t] ? *(const u32x4*)(g.A + (int64_t)r * g.lda + (int64_t)chunk[t] * 8)
-                         : u32x4{0u, 0u, 0u, 0u};
-    }
-  }
-
-  constexpr int plain_mask = plain_lane_mask<LV>();
-  const bool writer_lane = (lane & plain_mask) == 0;
-
-#pragma unroll
-  for (int c0 = 0; c0 < kGemvCpwMax; c0 += G) {
-    if (c0 >= ncol) break;
-    float v[P2];
-#pragma unroll
-    for (int gi = 0; gi < G; ++gi) {
-      u32x4 wh[T];
-#pragma unroll
-      for (int t = 0; t < T; ++t) wh[t] = w_as_halves<WK>(w[(c0 + gi) < kGemvCpwMax ? (c0 + gi) : 0][t]);
+    for (int t = 0; t < T; ++t) {
 #pragma unroll
       for (int r = 0; r < M; ++r) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int t = 0; t < T; ++t) acc = dot8<WK>(a[t][r], wh[t], acc);
-        v[gi * M + r] = acc;
+        a[t][r] = valid[t] ? *(const u32x4*)(g.A + (int64_t)r * g.lda + (int64_t)chunk[t] * 8)
+                           : u32x4{0u, 0u, 0u, 0u};
       }
     }
-#pragma unroll
-    for (int i = P; i < P2; ++i) v[i] = 0.0f;
 
-    int idx;
-    const float sum = wave_tree<LV>(v, lane, idx);
-    const int gi = idx / M;
-    const int r = idx - gi * M;
-    if (writer_lane && idx < P && c0 + gi < ncol) {
-      const int64_t j = j0 + c0 + gi;
-      if constexpr (OUT == 3) {
-        g.partial[((int64_t)s * M + r) * g.n + j] = sum;
-      } else {
-        store_out<OUT>(g.C, (int64_t)r * g.ldc + j, sum);
+    constexpr int plain_mask = plain_lane_mask<LV>();
+    const bool writer_lane = (lane & plain_mask) == 0;
+
+#pragma unroll
+    for (int c0 = 0; c0 < kGemvCpwMax; c0 += G) {
+      if (c0 >= ncol) break;
+      float v[P2];
+#pragma unroll
+      for (int gi = 0; gi < G; ++gi) {
+        u32x4 wh[T];
+#pragma unroll
+        for (int t = 0; t < T; ++t) wh[t] = w_as_halves<WK>(w[(c0 + gi) < kGemvCpwMax ? (c0 + gi) : 0][t]);
+#pragma unroll
+        for (int r = 0; r < M; ++r) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int t = 0; t < T; ++t) acc = dot8<WK>(a[t][r], wh[t], acc);
+          v[gi * M + r] = acc;
+        }
       }
+#pragma unroll
+      for (int i = P; i < P2; ++i) v[i] = 0.0f;
+
+      int idx;
+      const float sum = wave_tree<LV>(v, lane, idx);
+      const int gi = idx / M;
+      const int r = idx - gi * M;
+      if (writer_lane && idx < P && c0 + gi < ncol) {
+        const int64_t j = j0 + c0 + gi;
+        if (g.S > 1) {
+          st_dev(g.partial + ((int64_t)s * M + r) * g.n + j, sum);
+        } else if constexpr (TOPK) {
+          st_dev((float*)g.C + (int64_t)r * g.ldc + j, sum);  // read by the top-k block
+        } else {
+          store_out<CK>(g.C, (int64_t)r * g.ldc + j, sum);
+        }
+      }
+    }
+
+    if (g.S > 1) {
+      wait_mem();  // this wave's partials have reached the device-coherent level
+      uint32_t old = 0;
+      if (lane == 0) old = atomicAdd(&g.counters[wc], 1u);
+      old = __shfl(old, 0, 64);
+      if (old == (uint32_t)(g.S - 1)) {
+        // every split of this column range has counted in: add them in order
+        for (int e = lane; e < M * ncol; e += 64) {
+          const int r = e / ncol;
+          const int64_t j = j0 + (e - r * ncol);
+          float acc = ld_dev(g.partial + (int64_t)r * g.n + j);
+          for (int q = 1; q < g.S; ++q) acc += ld_dev(g.partial + ((int64_t)q * M + r) * g.n + j);
+          if constexpr (TOPK) {
+            st_dev((float*)g.C + (int64_t)r * g.ldc + j, acc);
+          } else {
+            store_out<CK>(g.C, (int64_t)r * g.ldc + j, acc);
+          }
+        }
+        if (lane == 0) g.counters[wc] = 0u;  // ready for the next call
+      }
+    }
+  }
+
+  if constexpr (TOPK) {
+    wait_mem();  // this wave's logits have reached the device-coherent level
+    __syncthreads();
+    __shared__ int last_block;
+    if (threadIdx.x == 0) {
+      const uint32_t old = atomicAdd(g.done, 1u);
+      last_block = (old == gridDim.x - 1) ? 1 : 0;
+    }
+    __syncthreads();
+    if (last_block) {
+      // every block has counted in, so every row of logits is complete
+      const float* Cf = (const float*)g.C;
+      for (int r = wave; r < M; r += wpb)
+        wave_topk_row(Cf + (int64_t)r * g.ldc, (int)g.n, g.topk, g.topk_idx + (int64_t)r * g.topk,
+                      g.topk_val + (int64_t)r * g.topk, lane);
+      if (threadIdx.x == 0) *g.done = 0u;  // ready for the next call
     }
   }
 }
@@ -288,10 +505,13 @@ __global__ __launch_bounds__(64 * kGemvWavesPerBlock) void gemv_rows_kernel(Gemv
 // --- kernel table ----------------------------------------------------------
 typedef void (*gemv_fn)(GemvArgs);
 
+// [0..2] = C kind f32/f16/bf16, [3] = f32 logits + top-k
 template <int M, int T, int WK>
 struct GemvRow {
-  static constexpr gemv_fn out[4] = {gemv_rows_kernel<M, T, WK, 0>, gemv_rows_kernel<M, T, WK, 1>,
-                                     gemv_rows_kernel<M, T, WK, 2>, gemv_rows_kernel<M, T, WK, 3>};
+  static constexpr gemv_fn out[4] = {gemv_rows_kernel<M, T, WK, CK_F32, false>,
+                                     gemv_rows_kernel<M, T, WK, CK_F16, false>,
+                                     gemv_rows_kernel<M, T, WK, CK_BF16, false>,
+                                     gemv_rows_kernel<M, T, WK, CK_F32, true>};
 };
 
 template <int T, int WK, int... Ms>
@@ -305,90 +525,13 @@ const gemv_fn* gemv_table(int m) {
   return gemv_row_ptr<T, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m);
 }
 
-// --- split-k reduction -----------------------------------------------------
-template <int CK>
-__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ partial, int S,
-                                                           int m, int64_t n, void* C, int64_t ldc) {
-  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  if (e >= (int64_t)m * n) return;
-  const int64_t r = e / n;
-  const int64_t j = e - r * n;
-  float acc = partial[r * n + j];
-  for (int s = 1; s < S; ++s) acc += partial[((int64_t)s * m + r) * n + j];
-  store_out<CK>(C, r * ldc + j, acc);
-}
-
-// --- top-k -----------------------------------------------------------------
-// (value desc, index asc): a strict total order over a row's entries
-__device__ __forceinline__ bool ranks_before(float va, int ia, float vb, int ib) {
-  return va > vb || (va == vb && ia < ib);
-}
-
-constexpr int kTopkCache = 16;  // values per lane kept in registers (n <= 1024)
-
-__global__ __launch_bounds__(64) void topk_rows_kernel(const float* __restrict__ partial, int S, int m,
-                                                       int64_t n, float* logits, int64_t ldl,
-                                                       int32_t* __restrict__ out_idx,
+// --- standalone top-k (rows produced by the GEMM path) -----------------------
+__global__ __launch_bounds__(64) void topk_rows_kernel(const float* __restrict__ logits, int64_t n,
+                                                       int64_t ldl, int32_t* __restrict__ out_idx,
                                                        float* __restrict__ out_val, int topk) {
   const int r = blockIdx.x;
-  const int lane = threadIdx.x;
-  float* row = logits + (int64_t)r * ldl;
-
-  // pass 0: materialise the row (reducing partials in split order when there
-  // are any); the first 64 * kTopkCache entries stay in registers
-  auto fetch = [&](int64_t j) -> float {
-    if (partial != nullptr) {
-      float x = partial[(int64_t)r * n + j];
-      for (int s = 1; s < S; ++s) x += partial[((int64_t)s * m + r) * n + j];
-      row[j] = x;
-      return x;
-    }
-    return row[j];
-  };
-  float cache[kTopkCache];
-#pragma unroll
-  for (int u = 0; u < kTopkCache; ++u) {
-    const int64_t j = lane + 64 * u;
-    cache[u] = j < n ? fetch(j) : 0.0f;
-  }
-  for (int64_t j = lane + 64 * kTopkCache; j < n; j += 64) (void)fetch(j);
-
-  float prev_v = 0.0f;
-  int prev_i = -1;  // -1: nothing selected yet
-  for (int t = 0; t < topk; ++t) {
-    float best_v = 0.0f;
-    int best_i = -1;
-    auto consider = [&](float x, int ji) {
-      const bool eligible = prev_i < 0 || ranks_before(prev_v, prev_i, x, ji);
-      if (eligible && (best_i < 0 || ranks_before(x, ji, best_v, best_i))) {
-        best_v = x;
-        best_i = ji;
-      }
-    };
-#pragma unroll
-    for (int u = 0; u < kTopkCache; ++u) {
-      const int64_t j = lane + 64 * u;
-      if (j < n) consider(cache[u], (int)j);
-    }
-    // entries beyond the cache: re-read what this same lane wrote in pass 0
-    for (int64_t j = lane + 64 * kTopkCache; j < n; j += 64) consider(row[j], (int)j);
-
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(best_v, off, 64);
-      const int oi = __shfl_xor(best_i, off, 64);
-      if (oi >= 0 && (best_i < 0 || ranks_before(ov, oi, best_v, best_i))) {
-        best_v = ov;
-        best_i = oi;
-      }
-    }
-    if (lane == 0) {
-      out_idx[(int64_t)r * topk + t] = best_i;
-      out_val[(int64_t)r * topk + t] = best_v;
-    }
-    prev_v = best_v;
-    prev_i = best_i;
-  }
+  wave_topk_row(logits + (int64_t)r * ldl, (int)n, topk, out_idx + (int64_t)r * topk,
+                out_val + (int64_t)r * topk, threadIdx.x);
 }
 
 // --- standalone dequant ----------------------------------------------------
@@ -411,8 +554,9 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const int8_t* __restr
 }  // namespace
 
 hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_kind,
-                       hipStream_t stream) {
-  if (m < 1 || m > kGemvMaxM || (T != 1 && T != 2) || out_kind < 0 || out_kind > 3)
+                       int waves_per_block, hipStream_t stream) {
+  if (m < 1 || m > kGemvMaxM || (T != 1 && T != 2) || out_kind < 0 || out_kind > 3 ||
+      waves_per_block < 1 || waves_per_block > kGemvMaxWavesPerBlock)
     return hipErrorInvalidValue;
   const gemv_fn* row = nullptr;
   if (T == 1) {
@@ -423,33 +567,15 @@ hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_k
         : w_kind == WK_BF16 ? gemv_table<2, WK_BF16>(m) : gemv_table<2, WK_Q8>(m);
   }
   const int64_t waves = (int64_t)args.S * args.waves_per_split;
-  const dim3 grid((unsigned)((waves + kGemvWavesPerBlock - 1) / kGemvWavesPerBlock));
-  hipLaunchKernelGGL(row[out_kind], grid, dim3(64 * kGemvWavesPerBlock), 0, stream, args);
+  const dim3 grid((unsigned)((waves + waves_per_block - 1) / waves_per_block));
+  hipLaunchKernelGGL(row[out_kind], grid, dim3(64 * waves_per_block), 0, stream, args);
   return hipGetLastError();
 }
 
-hipError_t launch_split_reduce(const float* partial, int S, int m, int64_t n, void* C,
-                               int64_t ldc, int c_kind, hipStream_t stream) {
-  const int64_t total = (int64_t)m * n;
-  const dim3 grid((unsigned)((total + 255) / 256));
-  switch (c_kind) {
-    case CK_F32:
-      hipLaunchKernelGGL(split_reduce_kernel<CK_F32>, grid, dim3(256), 0, stream, partial, S, m, n, C, ldc);
-      break;
-    case CK_F16:
-      hipLaunchKernelGGL(split_reduce_kernel<CK_F16>, grid, dim3(256), 0, stream, partial, S, m, n, C, ldc);
-      break;
-    default:
-      hipLaunchKernelGGL(split_reduce_kernel<CK_BF16>, grid, dim3(256), 0, stream, partial, S, m, n, C, ldc);
-      break;
-  }
-  return hipGetLastError();
-}
-
-hipError_t launch_topk(const float* partial, int S, int m, int64_t n, float* logits, int64_t ldl,
-                       int32_t* idx, float* val, int topk, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)m), dim3(64), 0, stream, partial, S, m, n,
-                     logits, ldl, idx, val, topk);
+hipError_t launch_topk(const float* logits, int m, int64_t n, int64_t ldl, int32_t* idx, float* val,
+                       int topk, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)m), dim3(64), 0, stream, logits, n, ldl, idx, val,
+                     topk);
   return hipGetLastError();
 }
 

@@ -21,7 +21,7 @@ enum CKind : int { CK_F32 = 0, CK_F16 = 1, CK_BF16 = 2 };
 // ---------------------------------------------------------------------------
 constexpr int kGemvMaxM = 16;
 constexpr int kGemvCpwMax = 8;     // columns per wave, upper bound
-constexpr int kGemvWavesPerBlock = 4;
+constexpr int kGemvMaxWavesPerBlock = 8;
 
 struct GemvArgs {
   const uint16_t* A;       // [m][lda] f16/bf16 bits
@@ -34,25 +34,23 @@ struct GemvArgs {
   int32_t S;                // number of k splits
   int32_t cpw;              // columns per wave (1..kGemvCpwMax)
   int32_t waves_per_split;  // ceil(n / cpw)
-  void* C;                  // [m][ldc] output (when S == 1)
+  void* C;                  // [m][ldc] output
   int64_t ldc;
-  float* partial;           // [S][m][n] fp32 partial sums (when S > 1)
+  float* partial;           // [S][m][n] fp32 partial sums (S > 1)
+  uint32_t* counters;       // [waves_per_split] arrivals per column range (S > 1), zero between calls
+  uint32_t* done;           // blocks finished (top-k), zero between calls
+  int32_t* topk_idx;        // [m][topk] (top-k launches)
+  float* topk_val;          // [m][topk]
+  int32_t topk;
 };
 
-// out_kind: 0 f32, 1 f16, 2 bf16, 3 = fp32 partials into args.partial
+// out_kind: 0 f32, 1 f16, 2 bf16 (C), 3 = f32 logits + top-k in the same launch
 hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_kind,
-                       hipStream_t stream);
+                       int waves_per_block, hipStream_t stream);
 
-// C[r][j] = sum over s = 0..S-1, in that order, of partial[s][r][j]
-hipError_t launch_split_reduce(const float* partial, int S, int m, int64_t n, void* C,
-                               int64_t ldc, int c_kind, hipStream_t stream);
-
-// Per-row top-k with blockIdx.x = row.  When S >= 1 and `partial` is set, the
-// logits are first reduced from the partials (same order as
-// launch_split_reduce) and written to `logits`; otherwise they are read from
-// `logits`.
-hipError_t launch_topk(const float* partial, int S, int m, int64_t n, float* logits,
-                       int64_t ldl, int32_t* idx, float* val, int topk, hipStream_t stream);
+// Per-row top-k of f32 rows already in memory, blockIdx.x = row.
+hipError_t launch_topk(const float* logits, int m, int64_t n, int64_t ldl, int32_t* idx, float* val,
+                       int topk, hipStream_t stream);
 
 hipError_t launch_dequant_q8_0(int64_t n, int64_t k, const int8_t* qs, const uint16_t* d,
                                uint16_t* out, hipStream_t stream);

@@ -112,3 +112,95 @@ def test_q8_gemv_parity_and_fused_equals_unfused(m):
     C2 = sk.mm(to_dev(A, "f16"), w16, out_dtype=torch.float16, max_m=16)
     torch.cuda.synchronize()
     assert np.array_equal(bits_of(C), bits_of(C2))
+
+
+def _topk_case(m, n, k, seed, dup_cols=(), one_hot=False, max_m=16, flags=0):
+    """Router-style inputs; dup_cols lists (src, dst) weight rows to duplicate
+    (equal logits -> ties); one_hot makes A rows one-hot so logits are exact."""
+    W = WL.gen_matrix((n, k), "bf16", ("normal", 0.02), seed)
+    for src, dst in dup_cols:
+        W[dst] = W[src]
+    if one_hot:
+        A = np.zeros((m, k), np.uint16)
+        for r in range(m):
+            A[r, (7 * r) % k] = 0x3F80  # bf16 1.0
+    else:
+        A = WL.gen_matrix((m, k), "bf16", ("normal", 1.0), seed + 1)
+    logits, idx, val = sk.gemv_topk(to_dev(A, "bf16"), to_dev(W, "bf16"), topk=10, max_m=max_m,
+                                    flags=flags)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    ref = oracle.mm(A, "bf16", W, "bf16")
+    assert rel_err(lg, ref) <= REL_TOL
+    oi, ov = oracle.topk(lg.astype(np.float64), 10)
+    assert np.array_equal(idx.cpu().numpy(), oi)
+    assert np.array_equal(val.cpu().numpy().view(np.uint32), ov.astype(np.float32).view(np.uint32))
+    return lg, idx.cpu().numpy()
+
+
+@pytest.mark.parametrize("m", [1, 3, 8, 16])
+def test_topk_ties_break_to_lower_index(m):
+    # many duplicated weight rows: equal logits everywhere in the top of the list
+    dups = [(5, 200), (5, 17), (40, 41), (40, 3), (100, 250), (100, 101), (9, 10)]
+    lg, idx = _topk_case(m, 256, 5120, 301, dup_cols=dups)
+    for src, dst in dups:
+        assert np.array_equal(lg[:, src].view(np.uint32), lg[:, dst].view(np.uint32))
+
+
+def test_topk_exact_logits_one_hot():
+    # one-hot rows: logits are weight values exactly, so fp32 cannot reorder them
+    _topk_case(4, 256, 5120, 311, one_hot=True)
+
+
+@pytest.mark.parametrize("n", [10, 130, 1100, 1500])
+def test_topk_rows_beyond_register_cache(n):
+    # n > 1024 exercises the re-read path of the top-k; n = 10 takes every column
+    _topk_case(5, n, 512, 321 + n)
+
+
+def test_topk_on_gemm_path():
+    # m > 16: the MFMA GEMM writes the logits, a second launch takes the top-k
+    _topk_case(20, 256, 5120, 331, max_m=20)
+
+
+def test_repeated_calls_leave_counters_ready():
+    wl = WL.WORKLOADS["router_topk"]
+    W = to_dev(WL.gen_w(wl), "bf16")
+    A = to_dev(WL.gen_a(wl, 16), "bf16")
+    plan = sk.Plan(wl.n, wl.k, 16, sk.BF16, sk.BF16, sk.F32)
+    ws = sk.new_workspace(plan, A.device)
+    outs = []
+    for rep in range(4):
+        for m in (16, 3, 1):
+            lg = torch.empty((m, wl.n), dtype=torch.float32, device="cuda")
+            idx = torch.empty((m, 10), dtype=torch.int32, device="cuda")
+            val = torch.empty((m, 10), dtype=torch.float32, device="cuda")
+            plan.run_topk(m, A[:m], W, lg, idx, val, 10, workspace=ws)
+            outs.append((m, lg, idx))
+    torch.cuda.synchronize()
+    # the counters (the 1280-byte tail after the partials: 256 column ranges
+    # plus the block counter, rounded up to 256 bytes) are back at zero
+    nonzero_tail = ws[-1280:].cpu().numpy()
+    assert not np.any(nonzero_tail), nonzero_tail[np.nonzero(nonzero_tail)][:8]
+    first = {}
+    for m, lg, idx in outs:
+        key = m
+        if key not in first:
+            first[key] = (lg.cpu().numpy().view(np.uint32), idx.cpu().numpy())
+        else:
+            assert np.array_equal(lg.cpu().numpy().view(np.uint32), first[key][0])
+            assert np.array_equal(idx.cpu().numpy(), first[key][1])
+    # and row invariance holds through the fused path too
+    l16, l1 = first[16][0], first[1][0]
+    assert np.array_equal(l16[:1], l1)
+
+
+def test_mm_run_equals_gemv_topk_logits():
+    wl = WL.WORKLOADS["router_topk"]
+    W = to_dev(WL.gen_w(wl), "bf16")
+    A = to_dev(WL.gen_a(wl, 16), "bf16")
+    for m in (1, 7, 16):
+        C = sk.mm(A[:m], W, out_dtype=torch.float32, max_m=16)
+        lg, _, _ = sk.gemv_topk(A[:m], W, topk=10, max_m=16)
+        torch.cuda.synchronize()
+        assert np.array_equal(C.cpu().numpy().view(np.uint32), lg.cpu().numpy().view(np.uint32))
