@@ -57,7 +57,55 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--only", default=None, metavar="WORKLOAD:M[:TILE]",
+                   help="profiling mode: run one workload at one m (optionally a forced GEMM "
+                        "tile id) --steps times eagerly, print its timing and exit")
     return p.parse_args()
+
+
+def run_only(spec, steps, warmup):
+    """Profiling mode: `steps` eager calls of one workload at one m (each on the
+    next cold weight copy), for rocprofv3 kernel traces and counter passes."""
+    import torch
+
+    import row_gemv_decode_amd as sk
+    import workloads as WL
+
+    parts = spec.split(":")
+    wl = WL.WORKLOADS[parts[0]]
+    m = int(parts[1])
+    tile = int(parts[2]) if len(parts) > 2 else -1
+    inp = Inputs(wl, torch, m)
+    a, w, c = dtype_codes(sk, wl)
+    plan = sk.Plan(wl.n, wl.k, max(m, max(wl.ms)), a, w, c, tile_id=tile)
+    ws = plan.workspace(inp.A.device)
+    cdt = torch.float32 if wl.c_kind == "f32" else torch.float16
+    C = torch.empty((m, wl.n), dtype=cdt, device="cuda")
+    idx = torch.empty((m, TOPK), dtype=torch.int32, device="cuda")
+    val = torch.empty((m, TOPK), dtype=torch.float32, device="cuda")
+
+    def call(i):
+        W = inp.W[i % len(inp.W)]
+        if wl.w_kind == "q8_0":
+            plan.run(m, inp.A[:m], W[0], C, scales=W[1], workspace=ws)
+        elif wl.topk:
+            plan.run_topk(m, inp.A[:m], W, C, idx, val, TOPK, workspace=ws)
+        else:
+            plan.run(m, inp.A[:m], W, C, workspace=ws)
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(steps):
+        call(warmup + i)
+    e1.record()
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / steps
+    print(json.dumps({"only": spec, "plan": plan.info(m), "calls": steps,
+                      "us_per_call_eager": round(us, 3)}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -298,6 +346,9 @@ def cpu_baseline(torch, step, budget_s):
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.only:
+        run_only(args.only, args.steps, args.warmup)
+        return
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)

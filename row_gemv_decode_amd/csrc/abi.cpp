@@ -277,6 +277,9 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   if ((d.flags & SKINNY_FORCE_GEMV) && (d.flags & SKINNY_FORCE_GEMM)) return SKINNY_ERR_INVALID_ARG;
   if ((d.flags & SKINNY_FORCE_GEMV) && d.max_m > kGemvMaxM) return SKINNY_ERR_INVALID_ARG;
   if (d.tile_id < -1 || d.tile_id >= gemm_tile_count()) return SKINNY_ERR_INVALID_ARG;
+  // the GEMM addresses a block's rows through 32-bit buffer offsets
+  const bool may_gemm = !(d.flags & SKINNY_FORCE_GEMV) && (d.max_m > kGemvMaxM || (d.flags & SKINNY_FORCE_GEMM));
+  if (may_gemm && (d.k > kGemmMaxK || d.lda > kGemmMaxK)) return SKINNY_ERR_SHAPE;
   if (d.num_cus < 0) return SKINNY_ERR_INVALID_ARG;
 
   int cus = d.num_cus;

@@ -7,23 +7,39 @@
 //   * opus r35 track A, section 2 ("gemm_f16 tiles"): a family of tiles
 //     TM x TN whose results are bitwise identical, chosen per M.  Here every
 //     tile issues the same instruction, v_mfma_f32_32x32x16_{f16,bf16}, with
-//     the same k traversal (LDS k-tiles of 32 = two MFMA steps, in increasing
-//     k, into one accumulator per output), and every tile origin is a multiple
-//     of 32 rows and columns, so an output element sees the same arithmetic
-//     under every tile and every M (tile- and M-invariance).
+//     the same operand layout, and accumulates every output in one register
+//     over k = 0, 16, 32, ... in increasing order, and every tile origin is a
+//     multiple of 32 rows and columns.  So an output element sees the same
+//     arithmetic under every tile and every M (tile- and M-invariance).
 //   * the same section's tail rule (a 128-row tile whose last block is up to
 //     half padding loses): rows past M are zero-filled in LDS and masked on
 //     store; the plan's selector counts padded tiles when it picks a tile.
 //   * opus r35 track A, section 1 (`dq_f16` before the router GEMM): the Q8_0
-//     B-loader dequantises each 32-wide k-tile of a weight row (one block, one
-//     scale) straight into the f16 LDS tile with the same function as the
-//     standalone dequant, so no separate dequant pass or f16 copy exists.
+//     B-loader dequantises each k-tile of a weight row straight into the f16
+//     LDS tile with the same function as the standalone dequant, so no
+//     separate dequant pass or f16 copy of the weight exists.
 //   * Strata PR #109 ("Measured"): results must not depend on a split of the
-//     reduction; there is no split-k here.
-// Tiles are chosen for 64-wide wavefronts: each wave owns (TM/WM) x (TN/WN)
-// of 32x32 MFMA blocks; A/W k-tiles go global -> registers -> LDS (double
-// buffered, XOR-swizzled 16-byte chunks so each MFMA operand read is
-// bank-conflict free), one barrier per k-tile.
+//     reduction; there is no split-k.
+//
+// Structure (64-wide wavefronts, 4 waves in a 2 x 2 grid for the main tiles):
+//   * k-tiles of 64 (four MFMA steps per barrier);
+//   * global loads run two k-tiles ahead (16-byte, coalesced: 8 lanes cover
+//     one 128-byte row segment) into two register sets; a tile's registers
+//     are written to the other LDS buffer half way through the MFMAs of the
+//     tile before it, so a k-tile and a half of MFMA work hides their latency
+//     (256 x 256 tiles, whose accumulators fill the register file, keep one
+//     set: loaded at the start of a tile, written after its MFMAs);
+//   * blocks are renumbered so that each XCD (blocks b, b + 8, ... share one)
+//     runs a contiguous range of tiles in column-major order: the weight
+//     columns an XCD needs stay in its own L2 instead of all eight;
+//   * LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r is
+//     stored at c ^ ((r >> 1) & 7), so the sixteen rows read by sixteen
+//     consecutive lanes at one logical chunk hit sixteen different 16-byte
+//     bank groups (conflict-free for 64 banks; the bank-conflict counter
+//     measured the plain r & 7 swizzle at one stall per two accesses);
+//   * MFMA operand fragments are read for step ks + 1 while step ks's MFMAs
+//     run; the accumulators of a 128 x 128 wave tile (256 fp32 per lane) live
+//     in the accumulation registers.
 #include "device_common.h"
 #include "internal.h"
 
@@ -31,12 +47,19 @@ namespace skinny {
 
 namespace {
 
-constexpr int kBK = 32;        // k per LDS tile: two 32x32x16 MFMA steps
-constexpr int kCPR = kBK / 8;  // 16-byte chunks per tile row
+// buffer resource word 3 for raw (unstrided) 32-bit buffers on gfx9-family
+// parts; out-of-range offsets read as zero
+constexpr int kBufferFlags = 0x00020000;
 
-// chunk c of tile row r lives at chunk (c ^ swz(r)); eight consecutive rows
-// read at the same logical chunk then hit eight different 16-byte bank groups
-__device__ __forceinline__ int swz(int r) { return (r >> 1) & 3; }
+constexpr int kBK = 64;        // k per LDS tile: four 32x32x16 MFMA steps
+constexpr int kCPR = kBK / 8;  // 16-byte chunks per tile row (8)
+constexpr int kSteps = kBK / 16;
+
+// LDS rows are 128 bytes; gfx950 serves 16 lanes of a ds_read_b128 per cycle
+// from 64 banks (256 bytes), i.e. two rows.  Chunk c of row r goes to
+// c ^ ((r >> 1) & 7): the 16 rows read by 16 consecutive lanes at one logical
+// chunk then cover all 16 bank groups of the two-row window.
+__device__ __forceinline__ int swz(int r) { return (r >> 1) & 7; }
 
 __device__ __forceinline__ h8_t as_h8(u32x4 v) { return __builtin_bit_cast(h8_t, v); }
 __device__ __forceinline__ b8_t as_b8(u32x4 v) { return __builtin_bit_cast(b8_t, v); }
@@ -60,9 +83,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   constexpr int A_CHUNKS = TM * kCPR;
   constexpr int A_ITERS = (A_CHUNKS + NT - 1) / NT;
-  // Q8_0 rows arrive as two 16-code halves per k-tile; f16/bf16 rows as four chunks
-  constexpr int B_UNITS = (WK == WK_Q8) ? TN * 2 : TN * kCPR;
+  // Q8_0 rows arrive as 16-code quarters of a 64-wide k-tile; f16/bf16 rows as 8 chunks
+  constexpr int B_UNITS = (WK == WK_Q8) ? TN * 4 : TN * kCPR;
   constexpr int B_ITERS = (B_UNITS + NT - 1) / NT;
+  static_assert(A_CHUNKS % NT == 0 && (WK == WK_Q8 || B_UNITS % NT == 0),
+                "tile rows must split evenly over the block");
+  // register sets for staged k-tiles: two (prefetch distance 2) unless the
+  // accumulators of a 256 x 256 tile leave no room, then one (distance 1)
+  constexpr int NSETS = (TM + TN >= 512) ? 1 : 2;
 
   __shared__ u32x4 sA[2][A_CHUNKS];
   __shared__ u32x4 sB[2][TN * kCPR];
@@ -73,83 +101,119 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
   const int wm = wid / WN;
   const int wn = wid - wm * WN;
 
-  const int64_t tiles_n = (g.N + TN - 1) / TN;
-  const int64_t bm = blockIdx.x / tiles_n;
-  const int64_t bn = blockIdx.x - bm * tiles_n;
+  // XCD-aware renumbering: hardware block b runs on XCD b % 8; give XCD x the
+  // tiles [x * per, (x + 1) * per) of a column-major tile order (the last
+  // XCDs may get one fewer), so neighbouring tiles on an XCD share W columns
+  const int64_t tiles_m = (g.M + TM - 1) / TM;
+  const int64_t nblocks = (int64_t)gridDim.x;
+  const int64_t per = (nblocks + 7) / 8;
+  const int64_t xcd = blockIdx.x & 7;
+  const int64_t full = nblocks - 8 * (per - 1);  // XCDs that get `per` tiles
+  const int64_t local = blockIdx.x >> 3;
+  const int64_t t = xcd < full ? xcd * per + local : full * per + (xcd - full) * (per - 1) + local;
+  const int64_t bn = t / tiles_m;
+  const int64_t bm = t - bn * tiles_m;
   const int64_t row0 = bm * TM;
   const int64_t col0 = bn * TN;
 
   const uint16_t* __restrict__ A = g.A;
-  const int64_t K = g.K;
+  const int64_t K = g.K;  // <= 2^20 (checked by the plan), so offsets fit in 32 bits
   const int nk = (int)((K + kBK - 1) / kBK);
 
-  u32x4 ra[A_ITERS];
-  u32x4 rb[B_ITERS];
-  uint16_t rs[B_ITERS];  // Q8_0 scale of each staged half-row
+  u32x4 ra[NSETS][A_ITERS];
+  u32x4 rb[NSETS][B_ITERS];
+  uint16_t rs[NSETS][B_ITERS];  // Q8_0 scale of each staged quarter-row
 
-  auto load_tiles = [&](int kt) {
-    const int64_t k0 = (int64_t)kt * kBK;
+  // Loads go through buffer resources covering exactly this block's rows of
+  // A and W: a row past M or N lies outside the resource and reads as zero
+  // (hardware range check), so no load is predicated and the number of loads
+  // in flight is the same on every path -- the compiler's vmcnt waits then
+  // count exactly.  Each thread keeps one 32-bit offset per operand; the
+  // per-iteration row stride and the k-tile origin are scalar offsets.
+  // Chunks past K (only when K % 64 != 0) are zeroed by a select.
+  const int64_t rows_a = (g.M - row0) < TM ? (g.M - row0) : TM;
+  const int64_t rows_b = (g.N - col0) < TN ? (g.N - col0) : TN;
+  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(A + row0 * g.lda), (short)0, (int)(((rows_a - 1) * g.lda + K) * 2), kBufferFlags);
+  const int a_r = tid / kCPR;
+  const int a_c = tid - a_r * kCPR;
+  const int voff_a = (int)((a_r * g.lda + a_c * 8) * 2);
+  const bool k_tail = (K % kBK) != 0;
+
+  __amdgpu_buffer_rsrc_t rsrc_b;
+  __amdgpu_buffer_rsrc_t rsrc_s;
+  int voff_b, voff_s = 0, b_c;
+  if constexpr (WK == WK_Q8) {
+    rsrc_b = __builtin_amdgcn_make_buffer_rsrc((void*)((const int8_t*)g.W + col0 * K), (short)0,
+                                               (int)(rows_b * K), kBufferFlags);
+    rsrc_s = __builtin_amdgcn_make_buffer_rsrc((void*)(g.scales + col0 * (K >> 5)), (short)0,
+                                               (int)(rows_b * (K >> 5) * 2), kBufferFlags);
+    const int b_r = tid >> 2;
+    b_c = tid & 3;  // which 16-code quarter of the 64-wide k-tile
+    voff_b = (int)(b_r * K + b_c * 16);
+    voff_s = (int)((b_r * (K >> 5) + (b_c >> 1)) * 2);
+  } else {
+    rsrc_b = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)g.W + col0 * K), (short)0,
+                                               (int)(rows_b * K * 2), kBufferFlags);
+    rsrc_s = rsrc_b;
+    const int b_r = tid / kCPR;
+    b_c = tid - b_r * kCPR;
+    voff_b = (int)((b_r * K + b_c * 8) * 2);
+  }
+
+  auto load_tiles = [&](int kt, int set) {
+    const int k0 = kt * kBK;
 #pragma unroll
     for (int i = 0; i < A_ITERS; ++i) {
-      const int q = tid + i * NT;
-      const int r = q / kCPR;
-      const int c = q - r * kCPR;
-      const int64_t gr = row0 + r;
-      const int64_t kc = k0 + c * 8;
-      const bool ok = (q < A_CHUNKS) && gr < g.M && kc < K;
-      ra[i] = ok ? *(const u32x4*)(A + gr * g.lda + kc) : u32x4{0u, 0u, 0u, 0u};
+      const int soff = (int)(((int64_t)i * (NT / kCPR) * g.lda + k0) * 2);
+      u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a, soff, 0));
+      if (k_tail && k0 + a_c * 8 >= K) v = u32x4{0u, 0u, 0u, 0u};
+      ra[set][i] = v;
     }
 #pragma unroll
     for (int i = 0; i < B_ITERS; ++i) {
-      const int q = tid + i * NT;
       if constexpr (WK == WK_Q8) {
-        const int r = q >> 1;
-        const int h = q & 1;
-        const int64_t gr = col0 + r;
-        const bool ok = (q < B_UNITS) && gr < g.N;  // K % 32 == 0, so k0 < K covers the row
-        const int8_t* wq = (const int8_t*)g.W;
-        rb[i] = ok ? *(const u32x4*)(wq + gr * K + k0 + h * 16) : u32x4{0u, 0u, 0u, 0u};
-        rs[i] = ok ? g.scales[gr * (K >> 5) + (k0 >> 5)] : (uint16_t)0;
+        const int soff = (int)((int64_t)i * (NT / 4) * K + k0);
+        const int soff_s = (int)(((int64_t)i * (NT / 4) * (K >> 5) + (k0 >> 5)) * 2);
+        u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, soff, 0));
+        uint16_t sc = __builtin_amdgcn_raw_buffer_load_b16(rsrc_s, voff_s, soff_s, 0);
+        if (k_tail && k0 + b_c * 16 >= K) {
+          v = u32x4{0u, 0u, 0u, 0u};
+          sc = 0;
+        }
+        rb[set][i] = v;
+        rs[set][i] = sc;
       } else {
-        const int r = q / kCPR;
-        const int c = q - r * kCPR;
-        const int64_t gr = col0 + r;
-        const int64_t kc = k0 + c * 8;
-        const bool ok = (q < B_UNITS) && gr < g.N && kc < K;
-        const uint16_t* w16 = (const uint16_t*)g.W;
-        rb[i] = ok ? *(const u32x4*)(w16 + gr * K + kc) : u32x4{0u, 0u, 0u, 0u};
+        const int soff = (int)(((int64_t)i * (NT / kCPR) * K + k0) * 2);
+        u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, soff, 0));
+        if (k_tail && k0 + b_c * 8 >= K) v = u32x4{0u, 0u, 0u, 0u};
+        rb[set][i] = v;
       }
     }
   };
 
-  auto store_tiles = [&](int buf) {
+  auto store_tiles = [&](int buf, int set) {
 #pragma unroll
     for (int i = 0; i < A_ITERS; ++i) {
-      const int q = tid + i * NT;
-      if (q < A_CHUNKS) {
-        const int r = q / kCPR;
-        const int c = q - r * kCPR;
-        sA[buf][r * kCPR + (c ^ swz(r))] = ra[i];
-      }
+      const int r = a_r + i * (NT / kCPR);
+      sA[buf][r * kCPR + (a_c ^ swz(r))] = ra[set][i];
     }
 #pragma unroll
     for (int i = 0; i < B_ITERS; ++i) {
-      const int q = tid + i * NT;
-      if (q < B_UNITS) {
-        if constexpr (WK == WK_Q8) {
-          const int r = q >> 1;
-          const int h = q & 1;
-          const _Float16 d = half_from_bits(rs[i]);
-          const u32x4 codes = rb[i];
-          const u32x2 lo = {(uint32_t)codes[0], (uint32_t)codes[1]};
-          const u32x2 hi = {(uint32_t)codes[2], (uint32_t)codes[3]};
-          sB[buf][r * kCPR + ((2 * h) ^ swz(r))] = q8_dequant8(lo, d);
-          sB[buf][r * kCPR + ((2 * h + 1) ^ swz(r))] = q8_dequant8(hi, d);
-        } else {
-          const int r = q / kCPR;
-          const int c = q - r * kCPR;
-          sB[buf][r * kCPR + (c ^ swz(r))] = rb[i];
-        }
+      if constexpr (WK == WK_Q8) {
+        const int r = (tid >> 2) + i * (NT / 4);
+        // a last, partial pass (TN * 4 not a multiple of the block) loaded
+        // rows past the tile, which read as zero; they are not stored
+        if (B_UNITS % NT != 0 && r >= TN) continue;
+        const _Float16 d = half_from_bits(rs[set][i]);
+        const u32x4 codes = rb[set][i];
+        const u32x2 lo = {(uint32_t)codes[0], (uint32_t)codes[1]};
+        const u32x2 hi = {(uint32_t)codes[2], (uint32_t)codes[3]};
+        sB[buf][r * kCPR + ((2 * b_c) ^ swz(r))] = q8_dequant8(lo, d);
+        sB[buf][r * kCPR + ((2 * b_c + 1) ^ swz(r))] = q8_dequant8(hi, d);
+      } else {
+        const int r = (tid / kCPR) + i * (NT / kCPR);
+        sB[buf][r * kCPR + (b_c ^ swz(r))] = rb[set][i];
       }
     }
   };
@@ -162,39 +226,72 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
-  load_tiles(0);
-  store_tiles(0);
-  __syncthreads();
-
   const int lrow = lane & 31;
   const int lk = lane >> 5;  // which 8-wide half of an MFMA k-step this lane feeds
 
-  for (int kt = 0; kt < nk; ++kt) {
+  // LDS word index of this lane's fragment rows (the chunk is added per step)
+  int a_row[FM];
+  int b_row[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) a_row[i] = wm * WTM + i * 32 + lrow;
+#pragma unroll
+  for (int j = 0; j < FN; ++j) b_row[j] = wn * WTN + j * 32 + lrow;
+
+  auto read_frags = [&](int buf, int ks, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
+    const int c = ks * 2 + lk;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = sA[buf][a_row[i] * kCPR + (c ^ swz(a_row[i]))];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bf[j] = sB[buf][b_row[j] * kCPR + (c ^ swz(b_row[j]))];
+  };
+
+  // pipeline: tile kt is in LDS buffer kt & 1 when its MFMAs run.  With two
+  // register sets, tile kt + 1 sits in set (kt + 1) & 1 and is written to the
+  // other buffer half way through tile kt, while tile kt + 2 is loaded into
+  // set kt & 1 (emptied during tile kt - 1) at the start of tile kt.  With one
+  // set, tile kt + 1 is loaded at the start of tile kt and written after its
+  // last MFMA step.
+  load_tiles(0, 0);
+  if constexpr (NSETS == 2) load_tiles(nk > 1 ? 1 : 0, 1);
+  store_tiles(0, 0);
+  __syncthreads();
+
+  constexpr int kStoreAfter = (NSETS == 2) ? kSteps / 2 - 1 : kSteps - 1;
+  auto tile_step = [&](int kt, int set_next) {
     const int cur = kt & 1;
-    if (kt + 1 < nk) load_tiles(kt + 1);
+    // the prefetch is issued on every tile (past the end it re-reads the last
+    // tile and is never stored) so the count of loads in flight never varies
+    if constexpr (NSETS == 2) {
+      load_tiles(kt + 2 < nk ? kt + 2 : nk - 1, set_next ^ 1);
+    } else {
+      load_tiles(kt + 1 < nk ? kt + 1 : nk - 1, 0);
+    }
+    // fragments of step ks + 1 are read while step ks's MFMAs run (a single
+    // fragment set for the 256 x 256 tile, whose registers are full)
+    constexpr int NF = (NSETS == 2) ? 2 : 1;
+    u32x4 af[NF][FM];
+    u32x4 bf[NF][FN];
+    read_frags(cur, 0, af[0], bf[0]);
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int c = ks * 2 + lk;
-      u32x4 af[FM];
-      u32x4 bf[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        const int r = wm * WTM + i * 32 + lrow;
-        af[i] = sA[cur][r * kCPR + (c ^ swz(r))];
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const int r = wn * WTN + j * 32 + lrow;
-        bf[j] = sB[cur][r * kCPR + (c ^ swz(r))];
-      }
+    for (int ks = 0; ks < kSteps; ++ks) {
+      if (NF == 2 && ks + 1 < kSteps) read_frags(cur, ks + 1, af[(ks + 1) % NF], bf[(ks + 1) % NF]);
+      if (NF == 1 && ks > 0) read_frags(cur, ks, af[0], bf[0]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(af[i], bf[j], acc[i][j]);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(af[ks % NF][i], bf[ks % NF][j], acc[i][j]);
+      if (ks == kStoreAfter && kt + 1 < nk) store_tiles(cur ^ 1, NSETS == 2 ? set_next : 0);
     }
-    if (kt + 1 < nk) store_tiles(cur ^ 1);
     __syncthreads();
+  };
+
+  // unrolled by two so the register sets are named at compile time
+  int kt = 0;
+  for (; kt + 1 < nk; kt += 2) {
+    tile_step(kt, 1);
+    tile_step(kt + 1, 0);
   }
+  if (kt < nk) tile_step(kt, 1);
 
   // 32x32 accumulator layout: lane owns column (lane & 31); register v holds
   // row 8 * (v / 4) + 4 * (lane / 32) + (v % 4)
@@ -237,7 +334,9 @@ TileEntry make_tile(const char* name) {
 
 const TileEntry* tiles() {
   static const TileEntry table[] = {
+      make_tile<256, 256, 2, 2>("256x256_w2x2"),
       make_tile<256, 128, 2, 2>("256x128_w2x2"),
+      make_tile<128, 256, 2, 2>("128x256_w2x2"),
       make_tile<128, 128, 2, 2>("128x128_w2x2"),
       make_tile<128, 64, 2, 2>("128x64_w2x2"),
       make_tile<64, 128, 2, 2>("64x128_w2x2"),
@@ -250,7 +349,7 @@ const TileEntry* tiles() {
   return table;
 }
 
-constexpr int kTileCount = 9;
+constexpr int kTileCount = 11;
 
 }  // namespace
 

@@ -59,6 +59,10 @@ hipError_t launch_dequant_q8_0(int64_t n, int64_t k, const int8_t* qs, const uin
 // MFMA GEMM (v_mfma_f32_32x32x16_{f16,bf16} for every tile, K-tiles of 32 in
 // increasing k, so every tile gives the same bits).
 // ---------------------------------------------------------------------------
+// largest k (and lda) the GEMM path takes: a block's rows of A and W are
+// addressed with 32-bit byte offsets
+constexpr int64_t kGemmMaxK = 1 << 20;
+
 struct GemmArgs {
   const uint16_t* A;       // [M][lda]
   int64_t lda;
