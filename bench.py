@@ -57,34 +57,90 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
-    p.add_argument("--only", default=None, metavar="WORKLOAD:M[:TILE]",
-                   help="profiling mode: run one workload at one m (optionally a forced GEMM "
-                        "tile id) --steps times eagerly, print its timing and exit")
+    p.add_argument("--tiles", default=None, metavar="WORKLOAD",
+                   help="time every GEMM tile at every m > 16 of WORKLOAD (cold weights, "
+                        "HIP-graph replay, min of 5) and print one JSON line per m; the "
+                        "measurements behind the tile selector's cost table")
+    p.add_argument("--only", default=None, metavar="WORKLOAD:M[,M...][:TILE]",
+                   help="profiling mode: run one workload at the given m values (cycled; "
+                        "optionally a forced GEMM tile id) --steps times eagerly, print the "
+                        "timing and exit.  'copy:BYTES' runs a plain device copy of BYTES "
+                        "instead (the calibration for the HBM byte counters)")
     return p.parse_args()
 
 
+def run_tiles(name):
+    """Time every GEMM tile at every m > 16 of one workload."""
+    import torch
+
+    import row_gemv_decode_amd as sk
+    import workloads as WL
+
+    wl = WL.WORKLOADS[name]
+    inp = Inputs(wl, torch, max(wl.ms), pool_bytes=512 << 20)
+    a, w, c = dtype_codes(sk, wl)
+    cdt = torch.float32 if wl.c_kind == "f32" else torch.float16
+    for m in [x for x in wl.ms if x > 16]:
+        C = torch.empty((m, wl.n), dtype=cdt, device="cuda")
+        row = {"workload": name, "m": m, "us": {}}
+        for tid, tname in enumerate(sk.gemm_tiles()):
+            plan = sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c, tile_id=tid)
+            L = min(len(inp.W), 64)
+
+            def fn(i, plan=plan):
+                W = inp.W[i % len(inp.W)]
+                if wl.w_kind == "q8_0":
+                    plan.run(m, inp.A[:m], W[0], C, scales=W[1])
+                else:
+                    plan.run(m, inp.A[:m], W, C)
+            g = capture(torch, fn, L)
+            row["us"][tname] = round(time_graph(torch, g, L, 5)[0], 2)
+            del g
+        row["selector"] = sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c).info(m)
+        print(json.dumps(row), flush=True)
+        del C
+
+
 def run_only(spec, steps, warmup):
-    """Profiling mode: `steps` eager calls of one workload at one m (each on the
-    next cold weight copy), for rocprofv3 kernel traces and counter passes."""
+    """Profiling mode: `steps` eager calls of one workload (m values cycled,
+    each call on the next cold weight copy), for rocprofv3 kernel traces and
+    counter passes; or a plain copy of a known size for calibration."""
     import torch
 
     import row_gemv_decode_amd as sk
     import workloads as WL
 
     parts = spec.split(":")
+    if parts[0] == "copy":
+        nbytes = int(parts[1])
+        src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").random_()
+        dst = torch.empty_like(src)
+        for _ in range(warmup):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / steps
+        print(json.dumps({"only": spec, "bytes_read": nbytes, "bytes_written": nbytes,
+                          "us_per_copy": round(us, 2)}), flush=True)
+        return
     wl = WL.WORKLOADS[parts[0]]
-    m = int(parts[1])
+    ms = [int(x) for x in parts[1].split(",")]
     tile = int(parts[2]) if len(parts) > 2 else -1
-    inp = Inputs(wl, torch, m)
+    inp = Inputs(wl, torch, max(ms))
     a, w, c = dtype_codes(sk, wl)
-    plan = sk.Plan(wl.n, wl.k, max(m, max(wl.ms)), a, w, c, tile_id=tile)
+    plan = sk.Plan(wl.n, wl.k, max(max(ms), max(wl.ms)), a, w, c, tile_id=tile)
     ws = plan.workspace(inp.A.device)
     cdt = torch.float32 if wl.c_kind == "f32" else torch.float16
-    C = torch.empty((m, wl.n), dtype=cdt, device="cuda")
-    idx = torch.empty((m, TOPK), dtype=torch.int32, device="cuda")
-    val = torch.empty((m, TOPK), dtype=torch.float32, device="cuda")
+    outs = {m: (torch.empty((m, wl.n), dtype=cdt, device="cuda"),
+                torch.empty((m, TOPK), dtype=torch.int32, device="cuda"),
+                torch.empty((m, TOPK), dtype=torch.float32, device="cuda")) for m in ms}
 
     def call(i):
+        m = ms[i % len(ms)]
+        C, idx, val = outs[m]
         W = inp.W[i % len(inp.W)]
         if wl.w_kind == "q8_0":
             plan.run(m, inp.A[:m], W[0], C, scales=W[1], workspace=ws)
@@ -104,8 +160,9 @@ def run_only(spec, steps, warmup):
     e1.record()
     torch.cuda.synchronize()
     us = e0.elapsed_time(e1) * 1e3 / steps
-    print(json.dumps({"only": spec, "plan": plan.info(m), "calls": steps,
-                      "us_per_call_eager": round(us, 3)}), flush=True)
+    alg = sum(call_bytes(wl, m, bool(wl.topk)) for m in ms) / len(ms)
+    print(json.dumps({"only": spec, "plans": {m: plan.info(m) for m in ms}, "calls": steps,
+                      "us_per_call_eager": round(us, 3), "alg_bytes_per_call": alg}), flush=True)
 
 
 # ---------------------------------------------------------------------------
@@ -303,6 +360,40 @@ def sweep(sk, torch, rounds):
 # ---------------------------------------------------------------------------
 # CPU baseline (the oracle, as it stands) + parity on the same sample
 # ---------------------------------------------------------------------------
+COUNTERS = os.path.join(ROOT, "profiles", "router_gemv_topk_counters.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "row_gemv_decode_amd", "csrc", f)
+                  for f in ("gemv.hip", "device_common.h", "internal.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the router kernel from the committed rocprofv3
+    counter passes (FETCH_SIZE and WRITE_SIZE, each scaled by what it reads
+    for a plain copy of known size); None when the kernel sources changed
+    since the counters were taken, or when there is no measurement."""
+    try:
+        kv = {}
+        with open(COUNTERS) as f:
+            for line in f:
+                if "=" in line and not line.startswith("#"):
+                    k, v = line.split("=", 1)
+                    kv[k.strip()] = v.strip()
+        if kv.get("kernel_source_sha256") != kernel_source_hash():
+            return None
+        return float(kv["traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(torch, step, budget_s):
     import numpy as np
 
@@ -348,6 +439,9 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.only:
         run_only(args.only, args.steps, args.warmup)
+        return
+    if args.tiles:
+        run_tiles(args.tiles)
         return
     if args.gpus != 1 or world != 1:
         print(f"bench.py measures one GPU: the library has no multi-GPU path "
@@ -446,7 +540,7 @@ def main():
         },
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+            "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
             "kernel": "router gemv_topk call", "alg_bytes_per_launch": round(alg_bytes, 1),
             "us_per_launch": round(us_per_launch, 4),
         },

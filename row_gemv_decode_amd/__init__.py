@@ -16,6 +16,12 @@ W[k, n] in C[m, n] = A[m, k] . W[k, n].
 import ctypes
 import os
 
+# torch first: it brings its own HIP runtime (soname libamdhip64.so.7); loaded
+# afterwards, libskinny.so binds to that same runtime, so torch's streams and
+# device memory are the library's.  Loaded the other way round the process
+# would hold two HIP runtimes that do not share devices or streams.
+import torch  # noqa: F401
+
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libskinny.so")
 

@@ -75,34 +75,64 @@ bool use_gemv(const skinny_plan* p, int64_t m) {
   return m <= kGemvMaxM;
 }
 
-// GEMM tile selector.  Cost = (number of rounds of resident blocks) x (work
-// of one block at the tile's efficiency).  Padded tail tiles are counted in
-// full, which is what makes a tile whose last row-block is mostly padding lose
-// (opus r35 track A, section 2, big-N GEMMs: a 128-row tile loses whenever
-// M % 128 is 1..64).  Ties go to the earlier (larger) tile.
-double tile_efficiency(const GemmTileInfo& t) {
-  const int wtm = t.tm / t.wm;
-  const int wtn = t.tn / t.wn;
-  const int area = wtm * wtn;  // outputs per wave
-  if (area >= 128 * 64) return 1.0;
-  if (area >= 64 * 64) return 0.85;
-  if (area >= 32 * 96) return 0.75;
-  if (area >= 32 * 64) return 0.65;
-  return 0.5;
+// GEMM tile selector (opus r35 track A, section 2: the tile is chosen per
+// M, and a tile whose last row-block is mostly padding loses -- a 128-row
+// tile loses whenever M % 128 is 1..64).  Here the choice comes from a cost
+// model fitted to MI355X measurements of every tile (K = 2560, cold weights):
+//   t    time of one block per 64-wide k-tile when it runs alone on a CU (us)
+//   c    blocks of the tile one CU holds at once (LDS and registers)
+//   u    how much of a CU one block keeps busy: c blocks sharing a CU each
+//        run max(1, c_eff * u) times slower
+// est = rounds * t * max(1, c_eff * u) * k-tiles, with rounds = ceil(blocks /
+// (CUs * c)) and c_eff = min(c, ceil(blocks / CUs)).  Padded blocks count in
+// full, which is what makes a half-padded tail tile lose.
+struct TileCost {
+  double t;
+  int c;
+  double u;
+};
+
+const TileCost& tile_cost(int id) {
+  // indexed like the tile table in gemm.hip
+  static const TileCost kCost[] = {
+      {2.415, 1, 1.00},  // 256x256_w2x2
+      {2.455, 1, 1.00},  // 256x256_w2x4
+      {1.110, 1, 1.00},  // 256x128_w4x2
+      {1.515, 1, 1.00},  // 256x128_w2x2
+      {1.600, 1, 1.00},  // 128x256_w2x2
+      {0.910, 2, 0.72},  // 128x128_w2x2
+      {0.665, 3, 0.54},  // 128x64_w2x2
+      {0.680, 3, 0.54},  // 64x128_w2x2
+      {0.650, 4, 0.43},  // 64x64_w2x2
+      {0.800, 2, 0.60},  // 128x96_w4x1
+      {0.885, 2, 0.70},  // 64x96_w2x1
+      {1.185, 2, 0.70},  // 32x96_w1x1
+      {0.735, 3, 0.60},  // 32x64_w1x2
+  };
+  static_assert(sizeof(kCost) / sizeof(kCost[0]) == 13, "one cost row per tile");
+  return kCost[id];
+}
+
+double tile_estimate(const skinny_plan* p, int id, int64_t m) {
+  const GemmTileInfo& t = gemm_tile(id);
+  const TileCost& tc = tile_cost(id);
+  const int64_t blocks = ((m + t.tm - 1) / t.tm) * ((p->d.n + t.tn - 1) / t.tn);
+  const int64_t cus = p->num_cus;
+  const int64_t rounds = (blocks + cus * tc.c - 1) / (cus * tc.c);
+  int64_t c_eff = (blocks + cus - 1) / cus;
+  if (c_eff > tc.c) c_eff = tc.c;
+  const double share = (double)c_eff * tc.u;
+  const int64_t ktiles = (p->d.k + 63) / 64;
+  return (double)rounds * tc.t * (share > 1.0 ? share : 1.0) * (double)ktiles;
 }
 
 int select_tile(const skinny_plan* p, int64_t m) {
   if (p->d.tile_id >= 0) return p->d.tile_id;
-  const int64_t n = p->d.n;
-  int best = -1;
+  int best = 0;
   double best_cost = 0.0;
   for (int id = 0; id < gemm_tile_count(); ++id) {
-    const GemmTileInfo& t = gemm_tile(id);
-    if (t.wm * t.wn != 4) continue;  // one- and two-wave tiles: tests only
-    const int64_t blocks = ((m + t.tm - 1) / t.tm) * ((n + t.tn - 1) / t.tn);
-    const int64_t rounds = (blocks + p->num_cus - 1) / p->num_cus;
-    const double cost = (double)rounds * (double)t.tm * (double)t.tn / tile_efficiency(t);
-    if (best < 0 || cost < best_cost * (1.0 - 1e-9)) {
+    const double cost = tile_estimate(p, id, m);
+    if (id == 0 || cost < best_cost * (1.0 - 1e-9)) {
       best = id;
       best_cost = cost;
     }
@@ -367,8 +397,9 @@ skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf,
     const int id = select_tile(plan, m);
     const GemmTileInfo& t = gemm_tile(id);
     const int64_t blocks = ((m + t.tm - 1) / t.tm) * ((plan->d.n + t.tn - 1) / t.tn);
-    std::snprintf(buf, len, "path=gemm m=%lld tile=%d name=%s blocks=%lld threads=%d", (long long)m,
-                  id, t.name, (long long)blocks, 64 * t.wm * t.wn);
+    std::snprintf(buf, len, "path=gemm m=%lld tile=%d name=%s blocks=%lld threads=%d est_us=%.1f",
+                  (long long)m, id, t.name, (long long)blocks, 64 * t.wm * t.wn,
+                  tile_estimate(plan, id, m));
   }
   return SKINNY_OK;
 }

@@ -88,9 +88,14 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
   constexpr int B_ITERS = (B_UNITS + NT - 1) / NT;
   static_assert(A_CHUNKS % NT == 0 && (WK == WK_Q8 || B_UNITS % NT == 0),
                 "tile rows must split evenly over the block");
-  // register sets for staged k-tiles: two (prefetch distance 2) unless the
-  // accumulators of a 256 x 256 tile leave no room, then one (distance 1)
-  constexpr int NSETS = (TM + TN >= 512) ? 1 : 2;
+  // register sets for staged k-tiles: two (prefetch distance 2) when the
+  // accumulators, both sets, the double-buffered fragments and some slack fit
+  // the per-wave register budget (512 registers per SIMD lane shared by the
+  // waves of one block on each SIMD), else one (distance 1)
+  constexpr int kRegBudget = 512 / ((NT + 255) / 256);
+  constexpr int kStageRegs = (A_ITERS + B_ITERS) * 4 + (WK == WK_Q8 ? B_ITERS : 0);
+  constexpr int kNeed2 = FM * FN * 16 + 2 * kStageRegs + 2 * (FM + FN) * 4 + 40;
+  constexpr int NSETS = kNeed2 <= kRegBudget ? 2 : 1;
 
   __shared__ u32x4 sA[2][A_CHUNKS];
   __shared__ u32x4 sB[2][TN * kCPR];
@@ -130,7 +135,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
   // in flight is the same on every path -- the compiler's vmcnt waits then
   // count exactly.  Each thread keeps one 32-bit offset per operand; the
   // per-iteration row stride and the k-tile origin are scalar offsets.
-  // Chunks past K (only when K % 64 != 0) are zeroed by a select.
+  // Chunks past K (only when K % 64 != 0) are zeroed by a select when they
+  // are written to LDS (a select right after the load would make the wave
+  // wait for that load at once).
   const int64_t rows_a = (g.M - row0) < TM ? (g.M - row0) : TM;
   const int64_t rows_b = (g.N - col0) < TN ? (g.N - col0) : TN;
   const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
@@ -166,37 +173,30 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < A_ITERS; ++i) {
       const int soff = (int)(((int64_t)i * (NT / kCPR) * g.lda + k0) * 2);
-      u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a, soff, 0));
-      if (k_tail && k0 + a_c * 8 >= K) v = u32x4{0u, 0u, 0u, 0u};
-      ra[set][i] = v;
+      ra[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a, soff, 0));
     }
 #pragma unroll
     for (int i = 0; i < B_ITERS; ++i) {
       if constexpr (WK == WK_Q8) {
         const int soff = (int)((int64_t)i * (NT / 4) * K + k0);
         const int soff_s = (int)(((int64_t)i * (NT / 4) * (K >> 5) + (k0 >> 5)) * 2);
-        u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, soff, 0));
-        uint16_t sc = __builtin_amdgcn_raw_buffer_load_b16(rsrc_s, voff_s, soff_s, 0);
-        if (k_tail && k0 + b_c * 16 >= K) {
-          v = u32x4{0u, 0u, 0u, 0u};
-          sc = 0;
-        }
-        rb[set][i] = v;
-        rs[set][i] = sc;
+        rb[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, soff, 0));
+        rs[set][i] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_s, voff_s, soff_s, 0);
       } else {
         const int soff = (int)(((int64_t)i * (NT / kCPR) * K + k0) * 2);
-        u32x4 v = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, soff, 0));
-        if (k_tail && k0 + b_c * 8 >= K) v = u32x4{0u, 0u, 0u, 0u};
-        rb[set][i] = v;
+        rb[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, soff, 0));
       }
     }
   };
 
-  auto store_tiles = [&](int buf, int set) {
+  auto store_tiles = [&](int buf, int set, int kt) {
+    const int k0 = kt * kBK;
+    const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
     for (int i = 0; i < A_ITERS; ++i) {
       const int r = a_r + i * (NT / kCPR);
-      sA[buf][r * kCPR + (a_c ^ swz(r))] = ra[set][i];
+      const bool keep = !k_tail || k0 + a_c * 8 < K;
+      sA[buf][r * kCPR + (a_c ^ swz(r))] = keep ? ra[set][i] : zero;
     }
 #pragma unroll
     for (int i = 0; i < B_ITERS; ++i) {
@@ -205,15 +205,17 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
         // a last, partial pass (TN * 4 not a multiple of the block) loaded
         // rows past the tile, which read as zero; they are not stored
         if (B_UNITS % NT != 0 && r >= TN) continue;
-        const _Float16 d = half_from_bits(rs[set][i]);
-        const u32x4 codes = rb[set][i];
+        const bool keep = !k_tail || k0 + b_c * 16 < K;
+        const _Float16 d = half_from_bits(keep ? rs[set][i] : (uint16_t)0);
+        const u32x4 codes = keep ? rb[set][i] : zero;
         const u32x2 lo = {(uint32_t)codes[0], (uint32_t)codes[1]};
         const u32x2 hi = {(uint32_t)codes[2], (uint32_t)codes[3]};
         sB[buf][r * kCPR + ((2 * b_c) ^ swz(r))] = q8_dequant8(lo, d);
         sB[buf][r * kCPR + ((2 * b_c + 1) ^ swz(r))] = q8_dequant8(hi, d);
       } else {
         const int r = (tid / kCPR) + i * (NT / kCPR);
-        sB[buf][r * kCPR + (b_c ^ swz(r))] = rb[set][i];
+        const bool keep = !k_tail || k0 + b_c * 8 < K;
+        sB[buf][r * kCPR + (b_c ^ swz(r))] = keep ? rb[set][i] : zero;
       }
     }
   };
@@ -253,34 +255,34 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
   // last MFMA step.
   load_tiles(0, 0);
   if constexpr (NSETS == 2) load_tiles(nk > 1 ? 1 : 0, 1);
-  store_tiles(0, 0);
+  store_tiles(0, 0, 0);
   __syncthreads();
 
   constexpr int kStoreAfter = (NSETS == 2) ? kSteps / 2 - 1 : kSteps - 1;
+
   auto tile_step = [&](int kt, int set_next) {
     const int cur = kt & 1;
     // the prefetch is issued on every tile (past the end it re-reads the last
-    // tile and is never stored) so the count of loads in flight never varies
+    // tile) and the store on every tile (past the end into a buffer nobody
+    // reads), so a tile is one straight-line block with a fixed count of
+    // loads in flight
     if constexpr (NSETS == 2) {
       load_tiles(kt + 2 < nk ? kt + 2 : nk - 1, set_next ^ 1);
     } else {
       load_tiles(kt + 1 < nk ? kt + 1 : nk - 1, 0);
     }
-    // fragments of step ks + 1 are read while step ks's MFMAs run (a single
-    // fragment set for the 256 x 256 tile, whose registers are full)
-    constexpr int NF = (NSETS == 2) ? 2 : 1;
-    u32x4 af[NF][FM];
-    u32x4 bf[NF][FN];
+    // fragments of step ks + 1 are read while step ks's MFMAs run
+    u32x4 af[2][FM];
+    u32x4 bf[2][FN];
     read_frags(cur, 0, af[0], bf[0]);
 #pragma unroll
     for (int ks = 0; ks < kSteps; ++ks) {
-      if (NF == 2 && ks + 1 < kSteps) read_frags(cur, ks + 1, af[(ks + 1) % NF], bf[(ks + 1) % NF]);
-      if (NF == 1 && ks > 0) read_frags(cur, ks, af[0], bf[0]);
+      if (ks + 1 < kSteps) read_frags(cur, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(af[ks % NF][i], bf[ks % NF][j], acc[i][j]);
-      if (ks == kStoreAfter && kt + 1 < nk) store_tiles(cur ^ 1, NSETS == 2 ? set_next : 0);
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(af[ks & 1][i], bf[ks & 1][j], acc[i][j]);
+      if (ks == kStoreAfter) store_tiles(cur ^ 1, NSETS == 2 ? set_next : 0, kt + 1);
     }
     __syncthreads();
   };
@@ -335,6 +337,8 @@ TileEntry make_tile(const char* name) {
 const TileEntry* tiles() {
   static const TileEntry table[] = {
       make_tile<256, 256, 2, 2>("256x256_w2x2"),
+      make_tile<256, 256, 2, 4>("256x256_w2x4"),
+      make_tile<256, 128, 4, 2>("256x128_w4x2"),
       make_tile<256, 128, 2, 2>("256x128_w2x2"),
       make_tile<128, 256, 2, 2>("128x256_w2x2"),
       make_tile<128, 128, 2, 2>("128x128_w2x2"),
@@ -349,7 +353,7 @@ const TileEntry* tiles() {
   return table;
 }
 
-constexpr int kTileCount = 11;
+constexpr int kTileCount = 13;
 
 }  // namespace
 

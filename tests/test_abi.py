@@ -1,0 +1,243 @@
+"""The C ABI on the host (CPU only): the library loads, exports every entry
+point include/skinny.h declares, validates every argument before any HIP
+call, and plans the documented GEMV split and GEMM tile for each shape.
+
+Plans are made with num_cus = 256 (an MI355X), which skips the device query,
+so nothing here touches a GPU; runs are only called with arguments that fail
+validation, which returns before any launch.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import row_gemv_decode_amd as sk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "skinny.h")
+L = sk.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return re.findall(r"SKINNY_API\s+[\w\s\*]+?\b(\w+)\s*\(", text)
+
+
+def plan(n=4864, k=896, max_m=16, a=sk.F16, w=sk.F16, c=sk.F32, **kw):
+    kw.setdefault("num_cus", 256)
+    return sk.Plan(n, k, max_m, a, w, c, **kw)
+
+
+def plan_status(**fields):
+    d = sk.MMDesc(ctypes.sizeof(sk.MMDesc), sk.F16, sk.F16, sk.F32, 16, 4864, 896, 0, 0, 0, -1, 256)
+    for name, value in fields.items():
+        setattr(d, name, value)
+    h = ctypes.c_void_p()
+    st = L.skinny_mm_plan(ctypes.byref(d), ctypes.byref(h))
+    if st == sk.OK:
+        L.skinny_mm_plan_destroy(h)
+    return st
+
+
+def test_exports_every_declared_symbol():
+    names = declared_functions()
+    assert len(names) == 11, names
+    assert set(names) == set(sk.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_abi_version_and_status_strings():
+    assert sk.abi_version() == 1
+    for st in range(7):
+        assert L.skinny_status_string(st)
+    assert L.skinny_status_string(99) == b"unknown status"
+    assert ctypes.sizeof(sk.MMDesc) == 72  # layout shared with the C header
+
+
+def test_tile_table():
+    names = sk.gemm_tiles()
+    assert len(names) == L.skinny_gemm_tile_count() == 13
+    for nm in names:
+        tm, rest = nm.split("x", 1)
+        tn, w = rest.split("_w")
+        wm, wn = w.split("x")
+        assert int(tm) % (32 * int(wm)) == 0 and int(tn) % (32 * int(wn)) == 0
+    assert L.skinny_gemm_tile_name(-1) is None and L.skinny_gemm_tile_name(13) is None
+
+
+@pytest.mark.parametrize("fields,status", [
+    (dict(struct_size=8), sk.ERR_INVALID_ARG),
+    (dict(a_dtype=sk.F32), sk.ERR_UNSUPPORTED),
+    (dict(a_dtype=sk.F16, w_dtype=sk.BF16), sk.ERR_UNSUPPORTED),
+    (dict(a_dtype=sk.BF16, w_dtype=sk.F16), sk.ERR_UNSUPPORTED),
+    (dict(a_dtype=sk.BF16, w_dtype=sk.Q8_0), sk.ERR_UNSUPPORTED),
+    (dict(c_dtype=sk.Q8_0), sk.ERR_UNSUPPORTED),
+    (dict(max_m=0), sk.ERR_INVALID_ARG),
+    (dict(n=0), sk.ERR_INVALID_ARG),
+    (dict(k=4), sk.ERR_INVALID_ARG),
+    (dict(k=900), sk.ERR_SHAPE),
+    (dict(w_dtype=sk.Q8_0, k=904), sk.ERR_SHAPE),
+    (dict(lda=800), sk.ERR_SHAPE),
+    (dict(lda=900), sk.ERR_ALIGNMENT),
+    (dict(ldc=100), sk.ERR_SHAPE),
+    (dict(flags=0x4), sk.ERR_UNSUPPORTED),
+    (dict(flags=sk.FORCE_GEMV | sk.FORCE_GEMM), sk.ERR_INVALID_ARG),
+    (dict(flags=sk.FORCE_GEMV, max_m=17), sk.ERR_INVALID_ARG),
+    (dict(tile_id=13), sk.ERR_INVALID_ARG),
+    (dict(tile_id=-2), sk.ERR_INVALID_ARG),
+    (dict(num_cus=-1), sk.ERR_INVALID_ARG),
+    (dict(max_m=64, k=(1 << 20) + 8), sk.ERR_SHAPE),          # GEMM path: k <= 2^20
+    (dict(max_m=16, k=(1 << 20) + 8), sk.OK),                 # GEMV only: fine
+    (dict(ldc=4870), sk.OK),                                   # any ldc >= n
+    (dict(lda=904), sk.OK),
+])
+def test_plan_validation(fields, status):
+    assert plan_status(**fields) == status
+
+
+def test_plan_null_arguments():
+    h = ctypes.c_void_p()
+    assert L.skinny_mm_plan(None, ctypes.byref(h)) == sk.ERR_INVALID_ARG
+    d = sk.MMDesc(ctypes.sizeof(sk.MMDesc), sk.F16, sk.F16, sk.F32, 16, 64, 64, 0, 0, 0, -1, 256)
+    assert L.skinny_mm_plan(ctypes.byref(d), None) == sk.ERR_INVALID_ARG
+    L.skinny_mm_plan_destroy(None)  # ignored
+
+
+@pytest.mark.parametrize("k,T,S", [(896, 2, 1), (5120, 2, 5), (2560, 1, 5), (8, 1, 1), (1024, 2, 1),
+                                   (1032, 1, 3), (16384, 2, 16)])
+def test_gemv_split_depends_on_k_only(k, T, S):
+    for n in (1, 256, 4864):
+        for m in (1, 7, 16):
+            info = plan(n=n, k=k).info(m)
+            assert f"T={T} S={S}" in info, info
+
+
+def test_paths_by_m():
+    p = plan(max_m=64)
+    for m in range(1, 17):
+        assert p.info(m).startswith("path=gemv")
+    for m in (17, 31, 64):
+        assert p.info(m).startswith("path=gemm")
+    assert plan(max_m=8, flags=sk.FORCE_GEMM).info(3).startswith("path=gemm")
+    assert plan(max_m=16, flags=sk.FORCE_GEMV).info(16).startswith("path=gemv")
+
+
+def test_workspace_sizes():
+    # router: S = 5 splits x 16 rows x 256 columns of fp32, then 257 counters
+    # (one per column range, one for blocks), each region rounded to 256 bytes
+    assert plan(n=256, k=5120, a=sk.BF16, w=sk.BF16).workspace_bytes == 5 * 16 * 256 * 4 + 1280
+    # unsplit GEMV: only the counters (used by the top-k launch)
+    assert plan(n=4864, k=896).workspace_bytes == 1280 * 4  # 1217 counters -> 4868 -> 5120
+    # GEMM-only plan: none
+    assert plan(max_m=64, flags=sk.FORCE_GEMM).workspace_bytes == 0
+
+
+@pytest.mark.parametrize("n,k,m,tile", [
+    (7680, 2560, 150, "64x64_w2x2"),
+    (7680, 2560, 448, "128x64_w2x2"),
+    (7680, 2560, 700, "128x96_w4x1"),
+    (7680, 2560, 1050, "128x96_w4x1"),
+    (7680, 2560, 2048, "256x128_w4x2"),
+    (96, 2560, 2048, "64x64_w2x2"),
+])
+def test_tile_selector_picks(n, k, m, tile):
+    assert f"name={tile} " in plan(n=n, k=k, max_m=2048).info(m)
+
+
+def _est(info):
+    return float(info.split("est_us=")[1])
+
+
+def test_tile_cost_counts_padded_tail_blocks():
+    """opus r35 track A, section 2: a tile whose last row-block is mostly
+    padding loses.  The cost model charges a padded tail block in full: one
+    row past a multiple of the tile costs a whole extra row of blocks."""
+    for tid, name in enumerate(sk.gemm_tiles()):
+        tm = int(name.split("x")[0])
+        p = plan(n=7680, k=2560, max_m=4096, tile_id=tid)
+        m = 8 * tm
+        assert _est(p.info(m + 1)) >= _est(p.info(m)), name
+        # padded rows cost nothing extra until the next block boundary
+        assert _est(p.info(m + 1)) == _est(p.info(m + tm)), name
+
+
+def test_tile_selector_half_padded_example():
+    # the page's example: M = 192 leaves a 64-row tail (half padding) on a
+    # 128-row tile; the selector takes a 64-row tile there
+    info = plan(n=7680, k=2560, max_m=2048).info(192)
+    assert int(info.split("name=")[1].split("x")[0]) == 64, info
+
+
+def test_forced_tile_is_used():
+    for tid, name in enumerate(sk.gemm_tiles()):
+        assert f"tile={tid} name={name} " in plan(max_m=64, tile_id=tid).info(40)
+
+
+# --- run validation (returns before any HIP call) ---------------------------
+P16 = ctypes.c_void_p(1 << 20)   # aligned, never dereferenced
+P16b = ctypes.c_void_p(2 << 20)
+P16c = ctypes.c_void_p(3 << 20)
+ODD = ctypes.c_void_p((1 << 20) + 2)
+
+
+def run(p, m, A=P16, W=P16b, S=None, C=P16c, ws=None, nbytes=0):
+    return L.skinny_mm_run(p.handle if p is not None else None, m, A, W, S, C, ws, nbytes, None)
+
+
+def test_run_validation():
+    p = plan()
+    assert run(None, 1) == sk.ERR_INVALID_ARG
+    assert run(p, 0) == sk.ERR_INVALID_ARG
+    assert run(p, 17) == sk.ERR_INVALID_ARG
+    assert run(p, 1, A=None) == sk.ERR_INVALID_ARG
+    assert run(p, 1, W=None) == sk.ERR_INVALID_ARG
+    assert run(p, 1, C=None) == sk.ERR_INVALID_ARG
+    assert run(p, 1, S=P16) == sk.ERR_INVALID_ARG          # scales only for Q8_0
+    assert run(p, 1, A=ODD) == sk.ERR_ALIGNMENT
+    assert run(p, 1, W=ODD) == sk.ERR_ALIGNMENT
+    assert run(p, 1, C=ODD) == sk.ERR_ALIGNMENT
+    q = plan(n=512, k=2560, w=sk.Q8_0, c=sk.F16)
+    assert run(q, 1) == sk.ERR_INVALID_ARG                 # Q8_0 needs scales
+    assert run(q, 1, S=ODD) == sk.ERR_ALIGNMENT
+    # split-k GEMV: partials need the workspace
+    assert run(q, 4, S=P16, ws=None, nbytes=0) == sk.ERR_WORKSPACE
+    assert run(q, 4, S=P16, ws=P16, nbytes=q.workspace_bytes - 16) == sk.ERR_WORKSPACE
+    assert run(q, 4, S=P16, ws=ODD, nbytes=q.workspace_bytes) == sk.ERR_ALIGNMENT
+
+
+def topk_run(p, m, logits=P16c, idx=P16, val=P16b, k=10, ws=P16, nbytes=1 << 20):
+    return L.gemv_topk_run(p.handle, m, P16, P16b, None, logits, idx, val, k, ws, nbytes, None)
+
+
+def test_topk_validation():
+    p = plan(n=256, k=5120, a=sk.BF16, w=sk.BF16)
+    assert topk_run(p, 1, idx=None) == sk.ERR_INVALID_ARG
+    assert topk_run(p, 1, val=None) == sk.ERR_INVALID_ARG
+    assert topk_run(p, 1, k=0) == sk.ERR_INVALID_ARG
+    assert topk_run(p, 1, k=33) == sk.ERR_INVALID_ARG
+    assert topk_run(p, 1, idx=ODD) == sk.ERR_ALIGNMENT
+    assert topk_run(p, 1, ws=None, nbytes=0) == sk.ERR_WORKSPACE
+    small = plan(n=8, k=64)
+    assert topk_run(small, 1, k=9) == sk.ERR_INVALID_ARG   # topk > n
+    f16out = plan(n=256, k=5120, a=sk.BF16, w=sk.BF16, c=sk.F16)
+    assert topk_run(f16out, 1) == sk.ERR_UNSUPPORTED
+
+
+def test_dequant_validation():
+    f = L.skinny_dequant_q8_0_run
+    assert f(0, 64, P16, P16b, P16c, None) == sk.ERR_INVALID_ARG
+    assert f(4, 16, P16, P16b, P16c, None) == sk.ERR_INVALID_ARG
+    assert f(4, 80, P16, P16b, P16c, None) == sk.ERR_SHAPE
+    assert f(4, 64, None, P16b, P16c, None) == sk.ERR_INVALID_ARG
+    assert f(4, 64, ODD, P16b, P16c, None) == sk.ERR_ALIGNMENT
+
+
+def test_plan_info_validation():
+    p = plan()
+    buf = ctypes.create_string_buffer(8)
+    assert L.skinny_mm_plan_info(p.handle, 0, buf, 8) == sk.ERR_INVALID_ARG
+    assert L.skinny_mm_plan_info(p.handle, 1, None, 8) == sk.ERR_INVALID_ARG
+    assert L.skinny_mm_plan_info(p.handle, 1, buf, 8) == sk.OK  # truncated, NUL-terminated
+    assert len(buf.value) == 7
