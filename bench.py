@@ -16,6 +16,10 @@ they capture) and replayed between two events after a synchronize, which
 removes Python's per-launch cost from a region whose kernels take a few
 microseconds each.
 
+The roofline object is the step's dominant kernel, the router GEMV: the same
+K cold-weight steps captured with only the GEMV launch of each call, timed
+the same way (algorithmic bytes W + A + logits per launch / launch time).
+
 The sweep times every workload at every m the same way (min and median over
 interleaved rounds, opus r35 track A section 2's method), and reports
 us_per_row, weight-GB/s, HBM and MFMA roofline fractions.
@@ -276,13 +280,22 @@ class RouterStep:
         self.plan.run_topk(m, self.inp.A[:m], self.inp.W[copy % len(self.inp.W)], lg, idx, val, TOPK,
                            workspace=self.ws)
 
-    def step(self, i):
+    def gemv_call(self, m, copy):
+        # the step's dominant kernel alone: the GEMV launch of the same call
+        lg, _, _ = self.out[m]
+        self.plan.run(m, self.inp.A[:m], self.inp.W[copy % len(self.inp.W)], lg, workspace=self.ws)
+
+    def step(self, i, fn=None):
+        fn = fn or self.call
         base = i * len(HEADLINE_MS)
         for j, m in enumerate(HEADLINE_MS):
-            self.call(m, base + j)
+            fn(m, base + j)
 
     def bytes_per_step(self):
         return sum(call_bytes(self.inp.wl, m, True) for m in HEADLINE_MS)
+
+    def gemv_bytes_per_step(self):
+        return sum(call_bytes(self.inp.wl, m, False) for m in HEADLINE_MS)
 
     def weight_bytes_per_step(self):
         return self.inp.wl.w_bytes * len(HEADLINE_MS)
@@ -480,13 +493,24 @@ def main():
     ms_total = e0.elapsed_time(e1)
     ms_per_step = ms_total / K
     value = step.weight_bytes_per_step() / (ms_per_step / 1e3) / 1e9
-    launches = len(HEADLINE_MS) * K
-    # the dominant kernel: the router GEMV (one launch per call)
-    us_per_launch = ms_total * 1e3 / launches
-    alg_bytes = step.bytes_per_step() / len(HEADLINE_MS)
-    achieved = alg_bytes / us_per_launch / 1e3
+    us_per_call = ms_total * 1e3 / (len(HEADLINE_MS) * K)
     log(f"headline: {ms_per_step * 1e3:.2f} us/step, {value:.1f} weight-GB/s, "
-        f"{us_per_launch:.3f} us/call")
+        f"{us_per_call:.3f} us/call")
+    del g
+
+    # the dominant kernel, the router GEMV, timed alone: the same K steps of
+    # cold-weight calls with only the GEMV launch of each call
+    gk = capture(torch, lambda i: step.step(i + args.warmup, step.gemv_call), K)
+    torch.cuda.synchronize()
+    e0.record()
+    gk.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    us_per_launch = e0.elapsed_time(e1) * 1e3 / (len(HEADLINE_MS) * K)
+    alg_bytes = step.gemv_bytes_per_step() / len(HEADLINE_MS)
+    achieved = alg_bytes / us_per_launch / 1e3
+    log(f"router GEMV launch alone: {us_per_launch:.3f} us, {achieved:.1f} GB/s algorithmic")
+    del gk
 
     # per-m lines of the headline workload (same timing, one graph per m)
     per_m = []
@@ -541,7 +565,8 @@ def main():
         "roofline": {
             "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": measured_traffic(),
-            "kernel": "router gemv_topk call", "alg_bytes_per_launch": round(alg_bytes, 1),
+            "kernel": "gemv_rows_kernel (the router GEMV launch of each call)",
+            "alg_bytes_per_launch": round(alg_bytes, 1),
             "us_per_launch": round(us_per_launch, 4),
         },
         "cpu_baseline": cpu,

@@ -131,12 +131,12 @@ SKINNY_API void skinny_mm_plan_destroy(skinny_plan* plan);
 
 /* Bytes of device workspace a run with this plan may need (0 when none);
  * enough for every m <= max_m, for skinny_mm_run and gemv_topk_run alike.
- * The workspace holds the GEMV's fp32 partial sums when the plan splits k
- * and the arrival counters that let the last wave of a split (and the last
- * block of a top-k launch) finish the call inside the same kernel.  It must be
- * zero-filled once before its first use; every completed run leaves it ready
- * for the next (its counters back at zero).  A run that needs no workspace
- * (GEMM path, or an unsplit GEMV without top-k) ignores it. */
+ * Only a GEMV whose k is split into more pieces than one workgroup sums
+ * (k > 8192 for 16-bit weights) needs it: it holds that GEMV's fp32 partial
+ * sums and the arrival counters that let the last wave of each column range
+ * finish the sum inside the same kernel.  It must be zero-filled once before
+ * its first use; every completed run leaves it ready for the next (its
+ * counters back at zero).  A run that needs no workspace ignores it. */
 SKINNY_API skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_t* bytes);
 
 /* C[0:m, 0:n] = A[0:m, :] . W  (nx_batchscale_kat: the product with fp32
@@ -153,11 +153,9 @@ SKINNY_API skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const
                             const void* w_scales, void* C, void* workspace,
                             size_t workspace_bytes, void* stream);
 
-/* Router step (Strata PR #109, "What": the multi-row router GEMV into fp32
- * logits and a multi-row top-k).  In the GEMV regime both run in ONE launch:
- * the last block to finish takes the top-k of every row.  In the GEMM regime
- * a second launch (one wave per row) takes the top-k.  The workspace is
- * required (see skinny_mm_workspace_size).  The plan's c_dtype must be
+/* Router step (Strata PR #109, "What": one multi-row router GEMV launch into
+ * fp32 logits, then one multi-row top-k launch with a wavefront per row).
+ * The workspace is as for skinny_mm_run.  The plan's c_dtype must be
  * SKINNY_F32.
  *   logits     f32 [m][ldc] out (the full product)
  *   topk_idx   int32 [m][topk] out: the topk largest logits of each row,

@@ -41,22 +41,24 @@ int to_wkind(int dt) { return dt == SKINNY_F16 ? WK_F16 : dt == SKINNY_BF16 ? WK
 int to_ckind(int dt) { return dt == SKINNY_F32 ? CK_F32 : dt == SKINNY_F16 ? CK_F16 : CK_BF16; }
 
 // k split of the GEMV: each wave covers 64*T chunks of eight elements; T in
-// {1, 2} (registers hold T * m * 16 bytes of A per lane).  Pick the T that
-// wastes the fewest chunk slots, then the one with fewer splits.
+// {1, 2} (registers hold T * m * 16 bytes of A per lane).  Depends on k only.
 void gemv_split(int64_t k, int* T_out, int* S_out) {
   const int64_t nchunks = k / 8;
-  int bestT = 2;
-  int64_t bestS = (nchunks + 127) / 128;
-  int64_t bestWaste = bestS * 128 - nchunks;
-  const int64_t S1 = (nchunks + 63) / 64;
-  const int64_t waste1 = S1 * 64 - nchunks;
-  if (waste1 < bestWaste) {
-    bestT = 1;
-    bestS = S1;
-    bestWaste = waste1;
+  // candidates (T = 2 first, so it wins ties): the fewest idle chunk slots,
+  // preferring splits that one workgroup can sum
+  struct Cand {
+    int T;
+    int64_t S;
+  } cand[2] = {{2, (nchunks + 127) / 128}, {1, (nchunks + 63) / 64}};
+  int best = 0;
+  for (int i = 1; i < 2; ++i) {
+    const bool in_i = cand[i].S <= kGemvBlockSplitMax, in_b = cand[best].S <= kGemvBlockSplitMax;
+    const int64_t waste_i = cand[i].S * 64 * cand[i].T - nchunks;
+    const int64_t waste_b = cand[best].S * 64 * cand[best].T - nchunks;
+    if ((in_i && !in_b) || (in_i == in_b && waste_i < waste_b)) best = i;
   }
-  *T_out = bestT;
-  *S_out = (int)bestS;
+  *T_out = cand[best].T;
+  *S_out = (int)cand[best].S;
 }
 
 // columns per wave: enough waves for about one per SIMD (4 per CU), but at
@@ -140,28 +142,31 @@ int select_tile(const skinny_plan* p, int64_t m) {
   return best;
 }
 
-// GEMV workspace: [fp32 partials S x m x n, when S > 1] [arrival counters:
-// one per column range, then one for finished blocks].  The counters must be
-// zero before the first call; every call leaves them at zero.
+// GEMV workspace, needed only when the k splits are summed across
+// workgroups: [fp32 partials S x m x n] [one arrival counter per column
+// range].  The counters must be zero before the first call; every call leaves
+// them at zero.  Splits summed inside a workgroup need no workspace.
 constexpr size_t kWsAlign = 256;
 
 size_t round_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
 int64_t gemv_waves_per_split(const skinny_plan* p) { return (p->d.n + p->gemv_cpw - 1) / p->gemv_cpw; }
 
+bool gemv_global_split(const skinny_plan* p) { return p->gemv_S > kGemvBlockSplitMax; }
+
 size_t gemv_partial_bytes(const skinny_plan* p, int64_t m) {
-  return p->gemv_S > 1 ? round_up((size_t)p->gemv_S * (size_t)m * (size_t)p->d.n * sizeof(float)) : 0;
+  return gemv_global_split(p)
+             ? round_up((size_t)p->gemv_S * (size_t)m * (size_t)p->d.n * sizeof(float))
+             : 0;
 }
 
 size_t gemv_counter_bytes(const skinny_plan* p) {
-  return round_up((size_t)(gemv_waves_per_split(p) + 1) * sizeof(uint32_t));
+  return round_up((size_t)gemv_waves_per_split(p) * sizeof(uint32_t));
 }
 
-// bytes a run needs: the split partials (and their counters) when k is split,
-// the block counter when the run also does the top-k
-size_t workspace_bytes_for(const skinny_plan* p, int64_t m, bool topk) {
-  if (!use_gemv(p, m)) return 0;
-  if (p->gemv_S <= 1 && !topk) return 0;
+// bytes a run at m rows needs (the same with or without the top-k)
+size_t workspace_bytes_for(const skinny_plan* p, int64_t m) {
+  if (!use_gemv(p, m) || !gemv_global_split(p)) return 0;
   // counters sit after the partials sized for the plan's largest GEMV m, so
   // their offset is the same for every m
   const int64_t mm = p->d.max_m < kGemvMaxM ? p->d.max_m : kGemvMaxM;
@@ -183,16 +188,13 @@ GemvArgs gemv_args(const skinny_plan* p, const void* A, const void* W, const voi
   g.S = p->gemv_S;
   g.cpw = p->gemv_cpw;
   g.waves_per_split = (int32_t)gemv_waves_per_split(p);
+  g.cg_per_block = 0;
   g.C = C;
   g.ldc = ldc;
   const int64_t mm = p->d.max_m < kGemvMaxM ? p->d.max_m : kGemvMaxM;
   char* ws = (char*)workspace;
-  g.partial = (ws != nullptr && p->gemv_S > 1) ? (float*)ws : nullptr;
+  g.partial = (ws != nullptr && gemv_global_split(p)) ? (float*)ws : nullptr;
   g.counters = ws != nullptr ? (uint32_t*)(ws + gemv_partial_bytes(p, mm)) : nullptr;
-  g.done = ws != nullptr ? g.counters + gemv_waves_per_split(p) : nullptr;
-  g.topk_idx = nullptr;
-  g.topk_val = nullptr;
-  g.topk = 0;
   return g;
 }
 
@@ -214,7 +216,7 @@ GemmArgs gemm_args(const skinny_plan* p, int64_t m, const void* A, const void* W
 // checks shared by skinny_mm_run and gemv_topk_run
 skinny_status check_run(const skinny_plan* p, int64_t m, const void* A, const void* W,
                         const void* scales, const void* C, const void* workspace,
-                        size_t workspace_bytes, bool topk) {
+                        size_t workspace_bytes) {
   if (p == nullptr) return SKINNY_ERR_INVALID_ARG;
   if (m < 1 || m > p->d.max_m) return SKINNY_ERR_INVALID_ARG;
   if (A == nullptr || W == nullptr || C == nullptr) return SKINNY_ERR_INVALID_ARG;
@@ -222,7 +224,7 @@ skinny_status check_run(const skinny_plan* p, int64_t m, const void* A, const vo
   if (q8 != (scales != nullptr)) return SKINNY_ERR_INVALID_ARG;
   if (!aligned16(A) || !aligned16(W) || !aligned16(C) || (q8 && !aligned16(scales)))
     return SKINNY_ERR_ALIGNMENT;
-  const size_t need = workspace_bytes_for(p, m, topk);
+  const size_t need = workspace_bytes_for(p, m);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return SKINNY_ERR_WORKSPACE;
     if (!aligned16(workspace)) return SKINNY_ERR_ALIGNMENT;
@@ -230,26 +232,46 @@ skinny_status check_run(const skinny_plan* p, int64_t m, const void* A, const vo
   return SKINNY_OK;
 }
 
-// waves per GEMV block: 4 spreads the waves over the most CUs; a top-k launch
-// with more than 4 rows uses 8 so the last block has a wave per row
-int gemv_waves_per_block(int64_t m, bool topk) { return (topk && m > 4) ? 8 : 4; }
+// GEMV workgroup shape.  Splits summed inside a workgroup: S waves per column
+// range and as many ranges as fit in kGemvMaxWavesPerBlock waves.  Without a
+// split (or with splits summed across workgroups) 4 waves spread the work over
+// the most CUs.
+struct GemvBlock {
+  int waves;
+  int ranges;  // column ranges per workgroup (splits summed inside), else 0
+};
 
-// enqueue C = A . W for m rows (plus the top-k when idx/val are given)
+GemvBlock gemv_block(const skinny_plan* p) {
+  const int S = p->gemv_S;
+  const int plain = 4;
+  if (S == 1) return {plain, plain};
+  if (S <= kGemvBlockSplitMax) {
+    const int ranges = kGemvMaxWavesPerBlock / S;
+    return {ranges * S, ranges};
+  }
+  return {plain, 0};
+}
+
+int64_t gemv_blocks(const skinny_plan* p, const GemvBlock& b) {
+  const int64_t wps = gemv_waves_per_split(p);
+  if (b.ranges > 0) return (wps + b.ranges - 1) / b.ranges;
+  return (wps * p->gemv_S + b.waves - 1) / b.waves;
+}
+
+// enqueue C = A . W for m rows, then (when idx/val are given) the top-k launch
+// over the rows of C (Strata PR #109, "What": one multi-row GEMV launch and
+// one multi-row top-10 launch per window)
 skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const void* W,
                          const void* scales, void* C, int64_t ldc, int c_kind, void* workspace,
                          int32_t* topk_idx, float* topk_val, int32_t topk, hipStream_t stream) {
   const bool want_topk = topk_idx != nullptr;
   if (use_gemv(p, m)) {
     GemvArgs g = gemv_args(p, A, W, scales, C, ldc, workspace);
-    int out_kind = c_kind;
-    if (want_topk) {
-      g.topk_idx = topk_idx;
-      g.topk_val = topk_val;
-      g.topk = topk;
-      out_kind = 3;
-    }
-    return hip_status(launch_gemv(g, (int)m, p->gemv_T, p->w_kind, out_kind,
-                                  gemv_waves_per_block(m, want_topk), stream));
+    const GemvBlock b = gemv_block(p);
+    g.cg_per_block = b.ranges;
+    skinny_status st = hip_status(launch_gemv(g, (int)m, p->gemv_T, p->w_kind, c_kind, b.waves, stream));
+    if (st != SKINNY_OK || !want_topk) return st;
+    return hip_status(launch_topk((const float*)C, (int)m, p->d.n, ldc, topk_idx, topk_val, topk, stream));
   }
   GemmArgs g = gemm_args(p, m, A, W, scales, C, ldc);
   skinny_status st = hip_status(launch_gemm(select_tile(p, m), g, p->w_kind, c_kind, stream));
@@ -345,14 +367,14 @@ skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_t* bytes) {
   const int64_t mm = plan->d.max_m < kGemvMaxM ? plan->d.max_m : kGemvMaxM;
   // the largest need of any run: a GEMV m (when the plan may use the GEMV)
   // with the top-k counters
-  *bytes = workspace_bytes_for(plan, mm, true);
+  *bytes = workspace_bytes_for(plan, mm);
   return SKINNY_OK;
 }
 
 skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
                             const void* w_scales, void* C, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  skinny_status st = check_run(plan, m, A, W, w_scales, C, workspace, workspace_bytes, false);
+  skinny_status st = check_run(plan, m, A, W, w_scales, C, workspace, workspace_bytes);
   if (st != SKINNY_OK) return st;
   return enqueue_mm(plan, m, A, W, w_scales, C, plan->d.ldc, plan->c_kind, workspace, nullptr, nullptr,
                     0, (hipStream_t)stream);
@@ -362,7 +384,7 @@ skinny_status gemv_topk_run(const skinny_plan* plan, int64_t m, const void* A, c
                             const void* w_scales, float* logits, int32_t* topk_idx,
                             float* topk_val, int32_t topk, void* workspace,
                             size_t workspace_bytes, void* stream) {
-  skinny_status st = check_run(plan, m, A, W, w_scales, logits, workspace, workspace_bytes, true);
+  skinny_status st = check_run(plan, m, A, W, w_scales, logits, workspace, workspace_bytes);
   if (st != SKINNY_OK) return st;
   if (plan->d.c_dtype != SKINNY_F32) return SKINNY_ERR_UNSUPPORTED;
   if (topk_idx == nullptr || topk_val == nullptr) return SKINNY_ERR_INVALID_ARG;
@@ -387,12 +409,14 @@ skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf,
   if (m < 1 || m > plan->d.max_m) return SKINNY_ERR_INVALID_ARG;
   if (use_gemv(plan, m)) {
     const int64_t waves = gemv_waves_per_split(plan) * plan->gemv_S;
+    const GemvBlock b = gemv_block(plan);
     std::snprintf(buf, len,
-                  "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld/%lld split_reduce=%s "
+                  "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld x %d waves split_reduce=%s "
                   "workspace=%zu",
                   (long long)m, plan->gemv_T, plan->gemv_S, plan->gemv_cpw, (long long)waves,
-                  (long long)((waves + 3) / 4), (long long)((waves + 7) / 8),
-                  plan->gemv_S > 1 ? "in-kernel" : "none", workspace_bytes_for(plan, m, true));
+                  (long long)gemv_blocks(plan, b), b.waves,
+                  plan->gemv_S == 1 ? "none" : (gemv_global_split(plan) ? "global" : "in-block"),
+                  workspace_bytes_for(plan, m));
   } else {
     const int id = select_tile(plan, m);
     const GemmTileInfo& t = gemm_tile(id);

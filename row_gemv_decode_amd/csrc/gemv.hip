@@ -217,16 +217,18 @@ __device__ __forceinline__ u32x4 w_as_halves(const WChunk<WK>& w) {
 }
 
 // ---------------------------------------------------------------------------
-// Per-row top-k by one wavefront (Strata PR #109, "What": one multi-row top-10
-// over the window's tokens).  Order: value descending, equal values (IEEE ==,
-// so -0 == +0) by lower column first; the winning lane writes the logit's own
-// bits.
+// Per-row top-k, one wavefront per row (Strata PR #109, "What": one multi-row
+// top-10 launch over the window's tokens, the row taken from the block index).
+// Order: value descending, equal values (IEEE ==, so -0 == +0) by lower column
+// first; the result carries the logit's own bits.
 //
 // Fast path (n <= 64 * NC): lane l holds columns l, l + 64, ... in NC
-// registers and sorts them once (a stable odd-even transposition sort, so
-// equal values keep increasing columns).  Each round is then branch-free: the
-// wave maximum of the lanes' heads (DPP / permlane max), the smallest column
-// among heads equal to it (DPP / permlane min), and the owner pops its head.
+// registers, sorted once per lane (a stable odd-even transposition sort, so
+// equal values keep increasing columns).  Each round takes the wave maximum of
+// the lanes' heads (DPP / permlane max) and a ballot of the lanes whose head
+// equals it: one lane in the ballot owns the winner outright, several (a tie)
+// fall back to the smallest column among them.  The owner pops its head and
+// lane t keeps the t-th winner, so the results leave in one coalesced store.
 // Generic path (larger n): each round rescans the row.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ float wave_max_f32(float v) {
@@ -263,18 +265,19 @@ __device__ __forceinline__ bool after(float v, int j, float pv, int pj) {
   return v < pv || (v == pv && j > pj);
 }
 
+constexpr int kNoColumn = 0x7fffffff;
+
 template <int NC>
 __device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int topk, int32_t* out_idx,
                                                    float* out_val, int lane) {
-  constexpr int kNone = 0x7fffffff;
   float v[NC];
   int jj[NC];
 #pragma unroll
   for (int u = 0; u < NC; ++u) {
     const int j = lane + 64 * u;
     const bool ok = j < n;
-    v[u] = ok ? ld_dev(row + j) : -__builtin_inff();
-    jj[u] = ok ? j : kNone;
+    v[u] = ok ? row[j] : -__builtin_inff();
+    jj[u] = ok ? j : kNoColumn;
   }
   // stable sort of the lane's slots into rank order
 #pragma unroll
@@ -290,21 +293,32 @@ __device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int 
       jj[u + 1] = swap ? tj : jj[u + 1];
     }
   }
+  int res_j = 0;
+  float res_v = 0.0f;
   for (int t = 0; t < topk; ++t) {
     const float wmax = wave_max_f32(v[0]);
-    const int wj = wave_min_i32(v[0] == wmax ? jj[0] : kNone);
-    const bool mine = jj[0] == wj;
-    if (mine) {
-      out_idx[t] = wj;
-      out_val[t] = v[0];
+    uint64_t ball = __builtin_amdgcn_ballot_w64(v[0] == wmax);
+    if (__builtin_popcountll(ball) != 1) {  // wave-uniform; a tie, rare with continuous data
+      const int wj = wave_min_i32(((ball >> lane) & 1) ? jj[0] : kNoColumn);
+      ball = __builtin_amdgcn_ballot_w64(jj[0] == wj);
     }
+    const int owner = ball != 0 ? __builtin_ctzll(ball) : 0;
+    const int wj = __builtin_amdgcn_readlane(jj[0], owner);
+    const float wv = fbits((uint32_t)__builtin_amdgcn_readlane((int)ubits(v[0]), owner));
+    res_j = lane == t ? wj : res_j;
+    res_v = lane == t ? wv : res_v;
+    const bool mine = lane == owner;
 #pragma unroll
     for (int u = 0; u + 1 < NC; ++u) {
       v[u] = mine ? v[u + 1] : v[u];
       jj[u] = mine ? jj[u + 1] : jj[u];
     }
     v[NC - 1] = mine ? -__builtin_inff() : v[NC - 1];
-    jj[NC - 1] = mine ? kNone : jj[NC - 1];
+    jj[NC - 1] = mine ? kNoColumn : jj[NC - 1];
+  }
+  if (lane < topk) {
+    out_idx[lane] = res_j;
+    out_val[lane] = res_v;
   }
 }
 
@@ -315,14 +329,14 @@ __device__ __noinline__ void wave_topk_row_generic(const float* row, int n, int 
   for (int t = 0; t < topk; ++t) {
     float best = -__builtin_inff();
     for (int j = lane; j < n; j += 64) {
-      const float x = ld_dev(row + j);
+      const float x = row[j];
       if (prev_j < 0 || after(x, j, prev_v, prev_j)) best = fmaxf(best, x);
     }
     const float wmax = wave_max_f32(best);
-    int cand = 0x7fffffff;
+    int cand = kNoColumn;
     float cand_v = 0.0f;
     for (int j = lane; j < n; j += 64) {
-      const float x = ld_dev(row + j);
+      const float x = row[j];
       if (x == wmax && (prev_j < 0 || after(x, j, prev_v, prev_j)) && j < cand) {
         cand = j;
         cand_v = x;
@@ -357,17 +371,21 @@ __device__ __forceinline__ void wave_topk_row(const float* row, int n, int topk,
 
 // ---------------------------------------------------------------------------
 // The GEMV kernel.  M rows (template), T chunk slots per lane, weight kind WK,
-// output kind CK; TOPK adds the router's top-k in the same launch.
+// output kind CK.
 //
-// Epilogue when the plan splits k (S > 1): each wave writes its fp32 sums to
-// partial[s][r][j], makes them visible device-wide, and counts itself in on
-// its column range; the wave that arrives last adds the S partials in the
-// fixed order s = 0..S-1 and writes C.  No wave ever waits for another.  With
-// TOPK every workgroup counts itself in once its C is visible; the last one
-// runs the top-k of every row.  The counters live in the caller's workspace,
-// start at zero and are left at zero.
+// Wave -> work: with S <= kGemvBlockSplitMax k splits, a workgroup holds
+// cg_per_block column ranges and S waves per range (wave w: split w % S,
+// range w / S).  Each wave reduces its sums over its 64 lanes, parks them in
+// LDS, and after one barrier the block adds the S splits in the fixed order
+// s = 0..S-1 and writes C.  With more splits the waves of one range sit in
+// different workgroups: each writes its sums to partial[s][r][j], makes them
+// visible device-wide and counts itself in on its range; the wave that arrives
+// last adds the S partials in the same fixed order.  No wave ever waits for
+// another workgroup.  Either way row r sees the same arithmetic at every m.
+// The range counters live in the caller's workspace, start at zero and are
+// left at zero.
 // ---------------------------------------------------------------------------
-template <int M, int T, int WK, int CK, bool TOPK>
+template <int M, int T, int WK, int CK>
 __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(GemvArgs g) {
   using Shape = GemvShape<M>;
   constexpr int G = Shape::G;
@@ -376,13 +394,27 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
   constexpr int LV = Shape::LV;
   static_assert(LV <= 6, "at most 64 values per lane");
 
+  // sums of one block's waves: [wave][column of the wave][row]
+  __shared__ float red[kGemvMaxWavesPerBlock * kGemvCpwMax * M];
+
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int wpb = blockDim.x >> 6;
-  const int gw = blockIdx.x * wpb + wave;
-  const int s = gw / g.waves_per_split;
-  const bool active = s < g.S;  // trailing waves of the last block have no columns
-  const int wc = active ? gw - s * g.waves_per_split : 0;
+  const bool in_block = g.S <= kGemvBlockSplitMax;
+  int s, wc;
+  bool active;
+  if (in_block) {
+    const int cg = wave / g.S;
+    s = wave - cg * g.S;
+    wc = blockIdx.x * g.cg_per_block + cg;
+    active = cg < g.cg_per_block && wc < g.waves_per_split;
+  } else {
+    const int gw = blockIdx.x * wpb + wave;
+    s = gw / g.waves_per_split;
+    active = s < g.S;  // trailing waves of the last block have no columns
+    wc = active ? gw - s * g.waves_per_split : 0;
+  }
+  if (!active) wc = 0;
   const int64_t j0 = (int64_t)wc * g.cpw;
   const int ncol = active ? (int)min((int64_t)g.cpw, g.n - j0) : 0;
 
@@ -449,17 +481,17 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
       const int r = idx - gi * M;
       if (writer_lane && idx < P && c0 + gi < ncol) {
         const int64_t j = j0 + c0 + gi;
-        if (g.S > 1) {
-          st_dev(g.partial + ((int64_t)s * M + r) * g.n + j, sum);
-        } else if constexpr (TOPK) {
-          st_dev((float*)g.C + (int64_t)r * g.ldc + j, sum);  // read by the top-k block
-        } else {
+        if (g.S == 1) {
           store_out<CK>(g.C, (int64_t)r * g.ldc + j, sum);
+        } else if (in_block) {
+          red[(wave * kGemvCpwMax + c0 + gi) * M + r] = sum;
+        } else {
+          st_dev(g.partial + ((int64_t)s * M + r) * g.n + j, sum);
         }
       }
     }
 
-    if (g.S > 1) {
+    if (!in_block) {
       wait_mem();  // this wave's partials have reached the device-coherent level
       uint32_t old = 0;
       if (lane == 0) old = atomicAdd(&g.counters[wc], 1u);
@@ -471,33 +503,26 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
           const int64_t j = j0 + (e - r * ncol);
           float acc = ld_dev(g.partial + (int64_t)r * g.n + j);
           for (int q = 1; q < g.S; ++q) acc += ld_dev(g.partial + ((int64_t)q * M + r) * g.n + j);
-          if constexpr (TOPK) {
-            st_dev((float*)g.C + (int64_t)r * g.ldc + j, acc);
-          } else {
-            store_out<CK>(g.C, (int64_t)r * g.ldc + j, acc);
-          }
+          store_out<CK>(g.C, (int64_t)r * g.ldc + j, acc);
         }
         if (lane == 0) g.counters[wc] = 0u;  // ready for the next call
       }
     }
   }
 
-  if constexpr (TOPK) {
-    wait_mem();  // this wave's logits have reached the device-coherent level
-    __syncthreads();
-    __shared__ int last_block;
-    if (threadIdx.x == 0) {
-      const uint32_t old = atomicAdd(g.done, 1u);
-      last_block = (old == gridDim.x - 1) ? 1 : 0;
-    }
-    __syncthreads();
-    if (last_block) {
-      // every block has counted in, so every row of logits is complete
-      const float* Cf = (const float*)g.C;
-      for (int r = wave; r < M; r += wpb)
-        wave_topk_row(Cf + (int64_t)r * g.ldc, (int)g.n, g.topk, g.topk_idx + (int64_t)r * g.topk,
-                      g.topk_val + (int64_t)r * g.topk, lane);
-      if (threadIdx.x == 0) *g.done = 0u;  // ready for the next call
+  if (in_block && g.S > 1) {
+    __syncthreads();  // every wave's sums are in LDS
+    const int per_range = g.cpw * M;
+    for (int e = threadIdx.x; e < g.cg_per_block * per_range; e += blockDim.x) {
+      const int cg = e / per_range;
+      const int c = (e - cg * per_range) / M;
+      const int r = e - cg * per_range - c * M;
+      const int64_t j = (int64_t)(blockIdx.x * g.cg_per_block + cg) * g.cpw + c;
+      if (j >= g.n) continue;  // past the last column (or the last range)
+      const int w0 = cg * g.S;
+      float acc = red[(w0 * kGemvCpwMax + c) * M + r];
+      for (int q = 1; q < g.S; ++q) acc += red[((w0 + q) * kGemvCpwMax + c) * M + r];
+      store_out<CK>(g.C, (int64_t)r * g.ldc + j, acc);
     }
   }
 }
@@ -505,13 +530,12 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
 // --- kernel table ----------------------------------------------------------
 typedef void (*gemv_fn)(GemvArgs);
 
-// [0..2] = C kind f32/f16/bf16, [3] = f32 logits + top-k
+// indexed by C kind: f32, f16, bf16
 template <int M, int T, int WK>
 struct GemvRow {
-  static constexpr gemv_fn out[4] = {gemv_rows_kernel<M, T, WK, CK_F32, false>,
-                                     gemv_rows_kernel<M, T, WK, CK_F16, false>,
-                                     gemv_rows_kernel<M, T, WK, CK_BF16, false>,
-                                     gemv_rows_kernel<M, T, WK, CK_F32, true>};
+  static constexpr gemv_fn out[3] = {gemv_rows_kernel<M, T, WK, CK_F32>,
+                                     gemv_rows_kernel<M, T, WK, CK_F16>,
+                                     gemv_rows_kernel<M, T, WK, CK_BF16>};
 };
 
 template <int T, int WK, int... Ms>
@@ -525,7 +549,7 @@ const gemv_fn* gemv_table(int m) {
   return gemv_row_ptr<T, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m);
 }
 
-// --- standalone top-k (rows produced by the GEMM path) -----------------------
+// --- top-k launch: one wavefront per row, blockIdx.x = row -------------------
 __global__ __launch_bounds__(64) void topk_rows_kernel(const float* __restrict__ logits, int64_t n,
                                                        int64_t ldl, int32_t* __restrict__ out_idx,
                                                        float* __restrict__ out_val, int topk) {
@@ -555,7 +579,7 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const int8_t* __restr
 
 hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_kind,
                        int waves_per_block, hipStream_t stream) {
-  if (m < 1 || m > kGemvMaxM || (T != 1 && T != 2) || out_kind < 0 || out_kind > 3 ||
+  if (m < 1 || m > kGemvMaxM || (T != 1 && T != 2) || out_kind < 0 || out_kind > 2 ||
       waves_per_block < 1 || waves_per_block > kGemvMaxWavesPerBlock)
     return hipErrorInvalidValue;
   const gemv_fn* row = nullptr;
@@ -566,8 +590,15 @@ hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_k
     row = w_kind == WK_F16 ? gemv_table<2, WK_F16>(m)
         : w_kind == WK_BF16 ? gemv_table<2, WK_BF16>(m) : gemv_table<2, WK_Q8>(m);
   }
-  const int64_t waves = (int64_t)args.S * args.waves_per_split;
-  const dim3 grid((unsigned)((waves + waves_per_block - 1) / waves_per_block));
+  int64_t blocks;
+  if (args.S <= kGemvBlockSplitMax) {
+    if (args.cg_per_block < 1 || args.cg_per_block * args.S != waves_per_block) return hipErrorInvalidValue;
+    blocks = (args.waves_per_split + args.cg_per_block - 1) / args.cg_per_block;
+  } else {
+    const int64_t waves = (int64_t)args.S * args.waves_per_split;
+    blocks = (waves + waves_per_block - 1) / waves_per_block;
+  }
+  const dim3 grid((unsigned)blocks);
   hipLaunchKernelGGL(row[out_kind], grid, dim3(64 * waves_per_block), 0, stream, args);
   return hipGetLastError();
 }

@@ -22,6 +22,9 @@ enum CKind : int { CK_F32 = 0, CK_F16 = 1, CK_BF16 = 2 };
 constexpr int kGemvMaxM = 16;
 constexpr int kGemvCpwMax = 8;     // columns per wave, upper bound
 constexpr int kGemvMaxWavesPerBlock = 8;
+// k splits up to this many are summed inside one workgroup (through LDS);
+// beyond it through fp32 partials in the caller's workspace
+constexpr int kGemvBlockSplitMax = 8;
 
 struct GemvArgs {
   const uint16_t* A;       // [m][lda] f16/bf16 bits
@@ -34,21 +37,20 @@ struct GemvArgs {
   int32_t S;                // number of k splits
   int32_t cpw;              // columns per wave (1..kGemvCpwMax)
   int32_t waves_per_split;  // ceil(n / cpw)
+  int32_t cg_per_block;     // S <= kGemvBlockSplitMax: column ranges per block (S waves each)
   void* C;                  // [m][ldc] output
   int64_t ldc;
-  float* partial;           // [S][m][n] fp32 partial sums (S > 1)
-  uint32_t* counters;       // [waves_per_split] arrivals per column range (S > 1), zero between calls
-  uint32_t* done;           // blocks finished (top-k), zero between calls
-  int32_t* topk_idx;        // [m][topk] (top-k launches)
-  float* topk_val;          // [m][topk]
-  int32_t topk;
+  float* partial;           // [S][m][n] fp32 partial sums (S > kGemvBlockSplitMax)
+  uint32_t* counters;       // [waves_per_split] arrivals per column range (S > kGemvBlockSplitMax),
+                            // zero between calls
 };
 
-// out_kind: 0 f32, 1 f16, 2 bf16 (C), 3 = f32 logits + top-k in the same launch
+// out_kind: 0 f32, 1 f16, 2 bf16 (C)
 hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_kind,
                        int waves_per_block, hipStream_t stream);
 
-// Per-row top-k of f32 rows already in memory, blockIdx.x = row.
+// Per-row top-k of f32 rows written by an earlier launch, one wavefront per
+// row (blockIdx.x = row).
 hipError_t launch_topk(const float* logits, int m, int64_t n, int64_t ldl, int32_t* idx, float* val,
                        int topk, hipStream_t stream);
 

@@ -106,7 +106,7 @@ def test_plan_null_arguments():
 
 
 @pytest.mark.parametrize("k,T,S", [(896, 2, 1), (5120, 2, 5), (2560, 1, 5), (8, 1, 1), (1024, 2, 1),
-                                   (1032, 1, 3), (16384, 2, 16)])
+                                   (1032, 1, 3), (16384, 2, 16), (4600, 2, 5), (8192, 2, 8), (8200, 1, 17)])
 def test_gemv_split_depends_on_k_only(k, T, S):
     for n in (1, 256, 4864):
         for m in (1, 7, 16):
@@ -125,13 +125,30 @@ def test_paths_by_m():
 
 
 def test_workspace_sizes():
-    # router: S = 5 splits x 16 rows x 256 columns of fp32, then 257 counters
-    # (one per column range, one for blocks), each region rounded to 256 bytes
-    assert plan(n=256, k=5120, a=sk.BF16, w=sk.BF16).workspace_bytes == 5 * 16 * 256 * 4 + 1280
-    # unsplit GEMV: only the counters (used by the top-k launch)
-    assert plan(n=4864, k=896).workspace_bytes == 1280 * 4  # 1217 counters -> 4868 -> 5120
+    # router: its 5 k splits are summed inside a workgroup; the top-k is a
+    # second launch: no workspace
+    assert plan(n=256, k=5120, a=sk.BF16, w=sk.BF16).workspace_bytes == 0
+    assert plan(n=4864, k=896).workspace_bytes == 0
+    # k = 16384: 16 splits are summed across workgroups through fp32 partials
+    # (16 splits x 16 rows x 256 columns), then 64 range counters (4 columns
+    # per wave) rounded to 256 B
+    assert plan(n=256, k=16384).workspace_bytes == 16 * 16 * 256 * 4 + 256
+    # the partials are sized for the plan's largest GEMV m
+    assert plan(n=256, k=16384, max_m=3).workspace_bytes == 16 * 3 * 256 * 4 + 256
     # GEMM-only plan: none
     assert plan(max_m=64, flags=sk.FORCE_GEMM).workspace_bytes == 0
+
+
+@pytest.mark.parametrize("k,S,shape,reduce", [
+    (896, 1, "x 4 waves", "none"),     # no split: 4 waves of separate columns
+    (2048, 2, "x 8 waves", "in-block"),  # 2 splits x 4 column ranges
+    (1032, 3, "x 6 waves", "in-block"),  # 3 splits x 2 ranges
+    (5120, 5, "x 5 waves", "in-block"),  # the router: one range of 5 splits
+    (16384, 16, "x 4 waves", "global"),  # too many splits for one workgroup
+])
+def test_gemv_block_shape(k, S, shape, reduce):
+    info = plan(n=256, k=k).info(4)
+    assert f"S={S} " in info and f"{shape} split_reduce={reduce} " in info, info
 
 
 @pytest.mark.parametrize("n,k,m,tile", [
@@ -201,10 +218,11 @@ def test_run_validation():
     q = plan(n=512, k=2560, w=sk.Q8_0, c=sk.F16)
     assert run(q, 1) == sk.ERR_INVALID_ARG                 # Q8_0 needs scales
     assert run(q, 1, S=ODD) == sk.ERR_ALIGNMENT
-    # split-k GEMV: partials need the workspace
-    assert run(q, 4, S=P16, ws=None, nbytes=0) == sk.ERR_WORKSPACE
-    assert run(q, 4, S=P16, ws=P16, nbytes=q.workspace_bytes - 16) == sk.ERR_WORKSPACE
-    assert run(q, 4, S=P16, ws=ODD, nbytes=q.workspace_bytes) == sk.ERR_ALIGNMENT
+    # splits summed across workgroups: partials need the workspace
+    g = plan(n=256, k=16384)
+    assert run(g, 4, ws=None, nbytes=0) == sk.ERR_WORKSPACE
+    assert run(g, 4, ws=P16, nbytes=g.workspace_bytes - 16) == sk.ERR_WORKSPACE
+    assert run(g, 4, ws=ODD, nbytes=g.workspace_bytes) == sk.ERR_ALIGNMENT
 
 
 def topk_run(p, m, logits=P16c, idx=P16, val=P16b, k=10, ws=P16, nbytes=1 << 20):
@@ -218,7 +236,8 @@ def test_topk_validation():
     assert topk_run(p, 1, k=0) == sk.ERR_INVALID_ARG
     assert topk_run(p, 1, k=33) == sk.ERR_INVALID_ARG
     assert topk_run(p, 1, idx=ODD) == sk.ERR_ALIGNMENT
-    assert topk_run(p, 1, ws=None, nbytes=0) == sk.ERR_WORKSPACE
+    g = plan(n=256, k=16384)  # splits summed across workgroups need the workspace
+    assert topk_run(g, 1, ws=None, nbytes=0) == sk.ERR_WORKSPACE
     small = plan(n=8, k=64)
     assert topk_run(small, 1, k=9) == sk.ERR_INVALID_ARG   # topk > n
     f16out = plan(n=256, k=5120, a=sk.BF16, w=sk.BF16, c=sk.F16)

@@ -164,33 +164,36 @@ def test_topk_on_gemm_path():
 
 
 def test_repeated_calls_leave_counters_ready():
-    wl = WL.WORKLOADS["router_topk"]
-    W = to_dev(WL.gen_w(wl), "bf16")
-    A = to_dev(WL.gen_a(wl, 16), "bf16")
-    plan = sk.Plan(wl.n, wl.k, 16, sk.BF16, sk.BF16, sk.F32)
+    """k = 16384 splits k across workgroups: the workspace counters must be back
+    at zero after every call, so repeated calls (with different m) reproduce
+    their first results bit for bit."""
+    n, k = 256, 16384
+    W = to_dev(WL.gen_matrix((n, k), "bf16", ("normal", 0.02), 501), "bf16")
+    A = to_dev(WL.gen_matrix((16, k), "bf16", ("normal", 1.0), 502), "bf16")
+    plan = sk.Plan(n, k, 16, sk.BF16, sk.BF16, sk.F32)
     ws = sk.new_workspace(plan, A.device)
+    assert ws is not None and "split_reduce=global" in plan.info(1)
     outs = []
     for rep in range(4):
         for m in (16, 3, 1):
-            lg = torch.empty((m, wl.n), dtype=torch.float32, device="cuda")
+            lg = torch.empty((m, n), dtype=torch.float32, device="cuda")
             idx = torch.empty((m, 10), dtype=torch.int32, device="cuda")
             val = torch.empty((m, 10), dtype=torch.float32, device="cuda")
             plan.run_topk(m, A[:m], W, lg, idx, val, 10, workspace=ws)
             outs.append((m, lg, idx))
     torch.cuda.synchronize()
-    # the counters (the 1280-byte tail after the partials: 256 column ranges
-    # plus the block counter, rounded up to 256 bytes) are back at zero
-    nonzero_tail = ws[-1280:].cpu().numpy()
-    assert not np.any(nonzero_tail), nonzero_tail[np.nonzero(nonzero_tail)][:8]
+    # the counters (the 256-byte tail after the partials: 64 column ranges of
+    # 4 columns) are back at zero
+    tail = ws[-256:].cpu().numpy()
+    assert not np.any(tail), tail[np.nonzero(tail)][:8]
     first = {}
     for m, lg, idx in outs:
-        key = m
-        if key not in first:
-            first[key] = (lg.cpu().numpy().view(np.uint32), idx.cpu().numpy())
+        if m not in first:
+            first[m] = (lg.cpu().numpy().view(np.uint32), idx.cpu().numpy())
         else:
-            assert np.array_equal(lg.cpu().numpy().view(np.uint32), first[key][0])
-            assert np.array_equal(idx.cpu().numpy(), first[key][1])
-    # and row invariance holds through the fused path too
+            assert np.array_equal(lg.cpu().numpy().view(np.uint32), first[m][0])
+            assert np.array_equal(idx.cpu().numpy(), first[m][1])
+    # and row invariance holds through the top-k path too
     l16, l1 = first[16][0], first[1][0]
     assert np.array_equal(l16[:1], l1)
 
@@ -204,3 +207,38 @@ def test_mm_run_equals_gemv_topk_logits():
         lg, _, _ = sk.gemv_topk(A[:m], W, topk=10, max_m=16)
         torch.cuda.synchronize()
         assert np.array_equal(C.cpu().numpy().view(np.uint32), lg.cpu().numpy().view(np.uint32))
+
+
+@pytest.mark.parametrize("n,k", [(300, 1032), (1001, 2048), (256, 16384), (37, 4096)])
+def test_split_shapes_parity_and_row_invariance(n, k):
+    """k splits summed inside a workgroup (k = 1032: 3 splits, 2048: 2, 4096:
+    4) and across workgroups (k = 16384: 16 splits), with ragged column
+    ranges; every row at m = 16 equals its m = 1 call bit for bit."""
+    print(f"split shapes n={n} k={k}", flush=True)
+    W = WL.gen_matrix((n, k), "f16", ("uniform", -0.05, 0.05), 401 + k)
+    A = WL.gen_matrix((16, k), "f16", ("normal", 1.0), 402 + k)
+    dW, dA = to_dev(W, "f16"), to_dev(A, "f16")
+    plan = sk.Plan(n, k, 16, sk.F16, sk.F16, sk.F32)
+    c16 = torch.empty((16, n), dtype=torch.float32, device="cuda")
+    plan.run(16, dA, dW, c16)
+    singles = []
+    for r in range(16):
+        c1 = torch.empty((1, n), dtype=torch.float32, device="cuda")
+        plan.run(1, dA[r:r + 1], dW, c1)
+        singles.append(c1)
+    torch.cuda.synchronize()
+    got = c16.cpu().numpy()
+    ref = oracle.mm(A, "f16", W, "f16")
+    assert rel_err(got, ref) <= REL_TOL
+    assert np.all(np.abs(got - ref) <= _f32_bound(A, "f16", W, "f16"))
+    single = torch.cat(singles).cpu().numpy().view(np.uint32)
+    assert np.array_equal(got.view(np.uint32), single)
+
+
+@pytest.mark.parametrize("m", [1, 6, 16])
+@pytest.mark.parametrize("k", [1032, 16384])
+def test_topk_with_split_shapes(m, k):
+    # the top-k handoff after splits summed inside (k = 1032) and across
+    # (k = 16384) workgroups
+    print(f"topk split m={m} k={k}", flush=True)
+    _topk_case(m, 300, k, 411 + k + m)
