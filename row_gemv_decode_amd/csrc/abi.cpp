@@ -23,6 +23,10 @@ struct skinny_plan {
   int gemv_S;
   // GEMV columns per wave, a function of n, S and the CU count
   int gemv_cpw;
+  // GEMM k split (ranges of gemm_kps k-tiles), a function of n, k and the CU
+  // count only (M-invariance within the plan)
+  int gemm_splits;
+  int gemm_kps;
 };
 
 namespace {
@@ -71,6 +75,24 @@ int gemv_cols_per_wave(int64_t n, int S, int num_cus) {
   return (int)cpw;
 }
 
+// GEMM k split: narrow N leaves most CUs idle at moderate M, so k is split
+// until the column tiles (of 64) times the splits reach an eighth of the CU
+// count (32 on 256 CUs), keeping at least four 64-wide k-tiles per split and
+// at most 16 splits.  Depends on n, k and the CU count only.
+void gemm_split(int64_t n, int64_t k, int num_cus, int* splits, int* kps) {
+  const int64_t nk = (k + 63) / 64;
+  const int64_t col_tiles = (n + 63) / 64;
+  int64_t target = num_cus / 8;
+  if (target < 8) target = 8;
+  int64_t s = (target + col_tiles - 1) / col_tiles;
+  if (s > nk / 4) s = nk / 4;
+  if (s > 16) s = 16;
+  if (s < 1) s = 1;
+  const int64_t per = (nk + s - 1) / s;
+  *kps = (int)per;
+  *splits = (int)((nk + per - 1) / per);
+}
+
 bool use_gemv(const skinny_plan* p, int64_t m) {
   if (p->d.flags & SKINNY_FORCE_GEMV) return true;
   if (p->d.flags & SKINNY_FORCE_GEMM) return false;
@@ -80,36 +102,39 @@ bool use_gemv(const skinny_plan* p, int64_t m) {
 // GEMM tile selector (opus r35 track A, section 2: the tile is chosen per
 // M, and a tile whose last row-block is mostly padding loses -- a 128-row
 // tile loses whenever M % 128 is 1..64).  Here the choice comes from a cost
-// model fitted to MI355X measurements of every tile (K = 2560, cold weights):
-//   t    time of one block per 64-wide k-tile when it runs alone on a CU (us)
-//   c    blocks of the tile one CU holds at once (LDS and registers)
-//   u    how much of a CU one block keeps busy: c blocks sharing a CU each
-//        run max(1, c_eff * u) times slower
-// est = rounds * t * max(1, c_eff * u) * k-tiles, with rounds = ceil(blocks /
-// (CUs * c)) and c_eff = min(c, ceil(blocks / CUs)).  Padded blocks count in
-// full, which is what makes a half-padded tail tile lose.
+// model fitted to MI355X measurements of every tile (K = 2560, N = 96 and
+// 7680, M = 150 .. 2048, cold weights):
+//   t      time of one block per 64-wide k-tile when it runs alone (us)
+//   c      blocks of the tile one CU holds at once (LDS)
+//   a      slow-down when the whole machine is busy: a round with b of its
+//          CUs * c slots filled runs 1 + a * b / (CUs * c) times slower
+//   sigma  slow-down of a round in which some CU holds two blocks
+// est = k-tiles per block * t * sum over rounds of round factors, with
+// rounds of CUs * c blocks.  Padded blocks count in full, which is what makes
+// a half-padded tail tile lose.
 struct TileCost {
   double t;
   int c;
-  double u;
+  double a;
+  double sigma;
 };
 
 const TileCost& tile_cost(int id) {
   // indexed like the tile table in gemm.hip
   static const TileCost kCost[] = {
-      {2.415, 1, 1.00},  // 256x256_w2x2
-      {2.455, 1, 1.00},  // 256x256_w2x4
-      {1.110, 1, 1.00},  // 256x128_w4x2
-      {1.515, 1, 1.00},  // 256x128_w2x2
-      {1.600, 1, 1.00},  // 128x256_w2x2
-      {0.910, 2, 0.72},  // 128x128_w2x2
-      {0.665, 3, 0.54},  // 128x64_w2x2
-      {0.680, 3, 0.54},  // 64x128_w2x2
-      {0.650, 4, 0.43},  // 64x64_w2x2
-      {0.800, 2, 0.60},  // 128x96_w4x1
-      {0.885, 2, 0.70},  // 64x96_w2x1
-      {1.185, 2, 0.70},  // 32x96_w1x1
-      {0.735, 3, 0.60},  // 32x64_w1x2
+      {1.7098, 1, 0.280, 1.000},  // 256x256_w2x2
+      {1.4204, 1, 0.360, 1.000},  // 256x256_w2x4
+      {0.8404, 1, 0.320, 1.000},  // 256x128_w4x2
+      {1.0466, 1, 0.240, 1.000},  // 256x128_w2x2
+      {1.0163, 1, 0.280, 1.000},  // 128x256_w2x2
+      {0.5247, 1, 0.440, 1.000},  // 128x128_w2x2
+      {0.4307, 2, 0.400, 1.425},  // 128x64_w2x2
+      {0.4411, 2, 0.900, 1.175},  // 64x128_w2x2
+      {0.2888, 2, 0.000, 2.175},  // 64x64_w2x2
+      {0.4583, 1, 0.340, 1.000},  // 128x96_w4x1
+      {0.5776, 2, 0.120, 1.225},  // 64x96_w2x1
+      {0.3722, 1, 0.000, 1.000},  // 32x96_w1x1
+      {0.2406, 2, 0.840, 1.000},  // 32x64_w1x2
   };
   static_assert(sizeof(kCost) / sizeof(kCost[0]) == 13, "one cost row per tile");
   return kCost[id];
@@ -118,14 +143,16 @@ const TileCost& tile_cost(int id) {
 double tile_estimate(const skinny_plan* p, int id, int64_t m) {
   const GemmTileInfo& t = gemm_tile(id);
   const TileCost& tc = tile_cost(id);
-  const int64_t blocks = ((m + t.tm - 1) / t.tm) * ((p->d.n + t.tn - 1) / t.tn);
+  const int64_t blocks = ((m + t.tm - 1) / t.tm) * ((p->d.n + t.tn - 1) / t.tn) * p->gemm_splits;
   const int64_t cus = p->num_cus;
-  const int64_t rounds = (blocks + cus * tc.c - 1) / (cus * tc.c);
-  int64_t c_eff = (blocks + cus - 1) / cus;
-  if (c_eff > tc.c) c_eff = tc.c;
-  const double share = (double)c_eff * tc.u;
-  const int64_t ktiles = (p->d.k + 63) / 64;
-  return (double)rounds * tc.t * (share > 1.0 ? share : 1.0) * (double)ktiles;
+  const int64_t slots = cus * tc.c;
+  double rounds = 0.0;
+  for (int64_t left = blocks; left > 0; left -= slots) {
+    const int64_t nb = left < slots ? left : slots;
+    const int64_t busiest = (nb + cus - 1) / cus;  // blocks on the busiest CU
+    rounds += (busiest >= 2 ? tc.sigma : 1.0) * (1.0 + tc.a * (double)nb / (double)slots);
+  }
+  return (double)p->gemm_kps * tc.t * rounds;
 }
 
 int select_tile(const skinny_plan* p, int64_t m) {
@@ -142,10 +169,12 @@ int select_tile(const skinny_plan* p, int64_t m) {
   return best;
 }
 
-// GEMV workspace, needed only when the k splits are summed across
-// workgroups: [fp32 partials S x m x n] [one arrival counter per column
-// range].  The counters must be zero before the first call; every call leaves
-// them at zero.  Splits summed inside a workgroup need no workspace.
+// Workspace: [one arrival counter per GEMV column range, when the GEMV's k
+// splits are summed across workgroups] [fp32 partial sums: the GEMV's
+// S x m x n in that case, or the GEMM's splits x m x n when the GEMM splits
+// k].  The counters come first so GEMM partials never overwrite them; they
+// must be zero before the first call and every call leaves them at zero.
+// Partial sums need no initial value.
 constexpr size_t kWsAlign = 256;
 
 size_t round_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
@@ -154,23 +183,26 @@ int64_t gemv_waves_per_split(const skinny_plan* p) { return (p->d.n + p->gemv_cp
 
 bool gemv_global_split(const skinny_plan* p) { return p->gemv_S > kGemvBlockSplitMax; }
 
+size_t gemv_counter_bytes(const skinny_plan* p) {
+  return gemv_global_split(p) ? round_up((size_t)gemv_waves_per_split(p) * sizeof(uint32_t)) : 0;
+}
+
 size_t gemv_partial_bytes(const skinny_plan* p, int64_t m) {
   return gemv_global_split(p)
              ? round_up((size_t)p->gemv_S * (size_t)m * (size_t)p->d.n * sizeof(float))
              : 0;
 }
 
-size_t gemv_counter_bytes(const skinny_plan* p) {
-  return round_up((size_t)gemv_waves_per_split(p) * sizeof(uint32_t));
+size_t gemm_partial_bytes(const skinny_plan* p, int64_t m) {
+  return p->gemm_splits > 1
+             ? round_up((size_t)p->gemm_splits * (size_t)m * (size_t)p->d.n * sizeof(float))
+             : 0;
 }
 
 // bytes a run at m rows needs (the same with or without the top-k)
 size_t workspace_bytes_for(const skinny_plan* p, int64_t m) {
-  if (!use_gemv(p, m) || !gemv_global_split(p)) return 0;
-  // counters sit after the partials sized for the plan's largest GEMV m, so
-  // their offset is the same for every m
-  const int64_t mm = p->d.max_m < kGemvMaxM ? p->d.max_m : kGemvMaxM;
-  return gemv_partial_bytes(p, mm) + gemv_counter_bytes(p);
+  const size_t part = use_gemv(p, m) ? gemv_partial_bytes(p, m) : gemm_partial_bytes(p, m);
+  return part > 0 ? gemv_counter_bytes(p) + part : 0;
 }
 
 skinny_status hip_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_ERR_HIP; }
@@ -193,13 +225,13 @@ GemvArgs gemv_args(const skinny_plan* p, const void* A, const void* W, const voi
   g.ldc = ldc;
   const int64_t mm = p->d.max_m < kGemvMaxM ? p->d.max_m : kGemvMaxM;
   char* ws = (char*)workspace;
-  g.partial = (ws != nullptr && gemv_global_split(p)) ? (float*)ws : nullptr;
-  g.counters = ws != nullptr ? (uint32_t*)(ws + gemv_partial_bytes(p, mm)) : nullptr;
+  g.counters = (ws != nullptr && gemv_global_split(p)) ? (uint32_t*)ws : nullptr;
+  g.partial = (ws != nullptr && gemv_global_split(p)) ? (float*)(ws + gemv_counter_bytes(p)) : nullptr;
   return g;
 }
 
 GemmArgs gemm_args(const skinny_plan* p, int64_t m, const void* A, const void* W,
-                   const void* scales, void* C, int64_t ldc) {
+                   const void* scales, void* C, int64_t ldc, void* workspace) {
   GemmArgs g;
   g.A = (const uint16_t*)A;
   g.lda = p->d.lda;
@@ -210,6 +242,11 @@ GemmArgs gemm_args(const skinny_plan* p, int64_t m, const void* A, const void* W
   g.K = p->d.k;
   g.C = C;
   g.ldc = ldc;
+  g.splits = p->gemm_splits;
+  g.kt_per_split = p->gemm_kps;
+  g.partial = (workspace != nullptr && p->gemm_splits > 1)
+                  ? (float*)((char*)workspace + gemv_counter_bytes(p))
+                  : nullptr;
   return g;
 }
 
@@ -273,8 +310,9 @@ skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const v
     if (st != SKINNY_OK || !want_topk) return st;
     return hip_status(launch_topk((const float*)C, (int)m, p->d.n, ldc, topk_idx, topk_val, topk, stream));
   }
-  GemmArgs g = gemm_args(p, m, A, W, scales, C, ldc);
+  GemmArgs g = gemm_args(p, m, A, W, scales, C, ldc, workspace);
   skinny_status st = hip_status(launch_gemm(select_tile(p, m), g, p->w_kind, c_kind, stream));
+  if (st == SKINNY_OK && g.splits > 1) st = hip_status(launch_splitk_reduce(g, c_kind, stream));
   if (st != SKINNY_OK || !want_topk) return st;
   return hip_status(launch_topk((const float*)C, (int)m, p->d.n, ldc, topk_idx, topk_val, topk, stream));
 }
@@ -351,6 +389,7 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   p->c_kind = to_ckind(d.c_dtype);
   gemv_split(d.k, &p->gemv_T, &p->gemv_S);
   p->gemv_cpw = gemv_cols_per_wave(d.n, p->gemv_S, cus);
+  gemm_split(d.n, d.k, cus, &p->gemm_splits, &p->gemm_kps);
   if (log_enabled()) {
     std::fprintf(stderr, "[skinny] plan n=%lld k=%lld max_m=%lld gemv T=%d S=%d cpw=%d cus=%d\n",
                  (long long)d.n, (long long)d.k, (long long)d.max_m, p->gemv_T, p->gemv_S,
@@ -364,10 +403,15 @@ void skinny_mm_plan_destroy(skinny_plan* plan) { delete plan; }
 
 skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_t* bytes) {
   if (plan == nullptr || bytes == nullptr) return SKINNY_ERR_INVALID_ARG;
-  const int64_t mm = plan->d.max_m < kGemvMaxM ? plan->d.max_m : kGemvMaxM;
-  // the largest need of any run: a GEMV m (when the plan may use the GEMV)
-  // with the top-k counters
-  *bytes = workspace_bytes_for(plan, mm);
+  // the largest need of any run: the GEMV at its largest m, or the GEMM at
+  // max_m (each needs the workspace only when it splits k across workgroups)
+  size_t need = 0;
+  const int64_t probe[2] = {plan->d.max_m < kGemvMaxM ? plan->d.max_m : kGemvMaxM, plan->d.max_m};
+  for (int64_t m : probe) {
+    const size_t b = workspace_bytes_for(plan, m);
+    need = b > need ? b : need;
+  }
+  *bytes = need;
   return SKINNY_OK;
 }
 
@@ -420,10 +464,13 @@ skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf,
   } else {
     const int id = select_tile(plan, m);
     const GemmTileInfo& t = gemm_tile(id);
-    const int64_t blocks = ((m + t.tm - 1) / t.tm) * ((plan->d.n + t.tn - 1) / t.tn);
-    std::snprintf(buf, len, "path=gemm m=%lld tile=%d name=%s blocks=%lld threads=%d est_us=%.1f",
-                  (long long)m, id, t.name, (long long)blocks, 64 * t.wm * t.wn,
-                  tile_estimate(plan, id, m));
+    const int64_t blocks =
+        ((m + t.tm - 1) / t.tm) * ((plan->d.n + t.tn - 1) / t.tn) * plan->gemm_splits;
+    std::snprintf(buf, len,
+                  "path=gemm m=%lld tile=%d name=%s splits=%d blocks=%lld threads=%d est_us=%.1f "
+                  "workspace=%zu",
+                  (long long)m, id, t.name, plan->gemm_splits, (long long)blocks, 64 * t.wm * t.wn,
+                  tile_estimate(plan, id, m), workspace_bytes_for(plan, m));
   }
   return SKINNY_OK;
 }

@@ -1,4 +1,5 @@
-// gemm.hip -- f16 / bf16 MFMA GEMM for the m >= 17 regime on gfx950 (MI355X).
+// gemm.hip -- MFMA GEMM (f16 / bf16 / Q8_0-style weights) for the m >= 17
+// regime on gfx950 (MI355X).
 //
 // C[M,N] = A[M,K] . W[K,N] with W stored [N][K] (both operands k-contiguous),
 // fp32 accumulation in the matrix cores, f32/f16/bf16 output.
@@ -12,34 +13,33 @@
 //     multiple of 32 rows and columns.  So an output element sees the same
 //     arithmetic under every tile and every M (tile- and M-invariance).
 //   * the same section's tail rule (a 128-row tile whose last block is up to
-//     half padding loses): rows past M are zero-filled in LDS and masked on
-//     store; the plan's selector counts padded tiles when it picks a tile.
-//   * opus r35 track A, section 1 (`dq_f16` before the router GEMM): the Q8_0
-//     B-loader dequantises each k-tile of a weight row straight into the f16
-//     LDS tile with the same function as the standalone dequant, so no
-//     separate dequant pass or f16 copy of the weight exists.
-//   * Strata PR #109 ("Measured"): results must not depend on a split of the
-//     reduction; there is no split-k.
+//     half padding loses): rows past M lie outside the block's buffer
+//     resource and reach only outputs that are never stored; the plan's
+//     selector counts padded tiles when it picks a tile.
+//   * opus r35 track A, section 1 (`dq_f16` before the router GEMM): Q8_0
+//     codes and scales are loaded into LDS as stored and each B fragment is
+//     dequantised as it is read, with the same function as the standalone
+//     dequant, so no separate dequant pass or f16 copy of the weight exists.
+//   * a plan may split k into `splits` ranges (fixed per plan from N, K and the
+//     CU count, never from M, so M-invariance holds within a plan); each range
+//     writes fp32 partial sums and a second launch adds them in range order.
+//     The split changes the rounding against an unsplit sum, never between
+//     tiles or calls.
 //
-// Structure (64-wide wavefronts, 4 waves in a 2 x 2 grid for the main tiles):
+// Structure (64-wide wavefronts, 1 to 8 waves per block):
 //   * k-tiles of 64 (four MFMA steps per barrier);
-//   * global loads run two k-tiles ahead (16-byte, coalesced: 8 lanes cover
-//     one 128-byte row segment) into two register sets; a tile's registers
-//     are written to the other LDS buffer half way through the MFMAs of the
-//     tile before it, so a k-tile and a half of MFMA work hides their latency
-//     (256 x 256 tiles, whose accumulators fill the register file, keep one
-//     set: loaded at the start of a tile, written after its MFMAs);
+//   * global loads go straight into LDS (buffer_load ... lds) through buffer
+//     resources that cover exactly the block's rows, NS k-tiles in flight; one
+//     barrier per k-tile (below);
 //   * blocks are renumbered so that each XCD (blocks b, b + 8, ... share one)
-//     runs a contiguous range of tiles in column-major order: the weight
-//     columns an XCD needs stay in its own L2 instead of all eight;
+//     runs a contiguous range of tiles, ordered so that the larger operand's
+//     tiles an XCD needs stay in its own L2 instead of all eight;
 //   * LDS rows are 128 bytes (eight 16-byte chunks); chunk c of row r is
 //     stored at c ^ ((r >> 1) & 7), so the sixteen rows read by sixteen
 //     consecutive lanes at one logical chunk hit sixteen different 16-byte
-//     bank groups (conflict-free for 64 banks; the bank-conflict counter
-//     measured the plain r & 7 swizzle at one stall per two accesses);
-//   * MFMA operand fragments are read for step ks + 1 while step ks's MFMAs
-//     run; the accumulators of a 128 x 128 wave tile (256 fp32 per lane) live
-//     in the accumulation registers.
+//     bank groups (the bank-conflict counter reads zero);
+//   * MFMA operand fragments are read ahead of their MFMAs: one k-step ahead
+//     for large wave tiles, one whole k-tile ahead for small ones.
 #include "device_common.h"
 #include "internal.h"
 
@@ -73,32 +73,116 @@ __device__ __forceinline__ f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
   }
 }
 
-template <int TM, int TN, int WM, int WN, int WK, int CK>
-__global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
-  constexpr int NT = 64 * WM * WN;
+// ---------------------------------------------------------------------------
+// The GEMM kernel: global loads go straight into LDS (buffer_load ... lds),
+// so NS k-tiles can be in flight without staging registers.  Per k-tile: wait until this wave's loads of tile kt have
+// landed (NS - 2 later tiles may stay in flight), one barrier (every wave's
+// part of tile kt is in LDS and every wave is done with tile kt - 1), issue
+// tile kt + NS - 1 into the stage tile kt - 1 used, run tile kt's MFMAs.
+// A lane's 16 bytes land at the wave's LDS base + 16 * lane, so the chunk
+// swizzle is applied on the global side: lane l of a load fills slot l % 8 of
+// row l / 8 with global chunk (l % 8) ^ swz(row).  Rows past M or N lie
+// outside the buffer resources: whatever their LDS slots hold reaches only
+// outputs that are never stored.  For a K % 64 != 0 shape the chunks past K
+// of the last k-tile are zeroed in LDS before its fragments are read.  The
+// MFMA sequence of every output is the same under every tile: same bits.
+// ---------------------------------------------------------------------------
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // vmcnt in bits [3:0] and [15:14]; expcnt (7) and lgkmcnt (15) not waited on
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// a workgroup barrier without the memory fence __syncthreads() adds (the
+// fence would wait for every load in flight); the signal fences keep the
+// compiler from moving LDS accesses across it
+__device__ __forceinline__ void barrier_only() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_barrier();
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
+// 32-bit LDS address of a __shared__ object
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(__attribute__((address_space(3))) const void*)p;
+}
+
+// buffer resource for raw 16-byte loads of `bytes` bytes from `base`
+__device__ __forceinline__ u32x4 buffer_rsrc(const void* base, int64_t bytes) {
+  const uint64_t b = (uint64_t)(uintptr_t)base;
+  return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xFFFFu, (uint32_t)bytes, (uint32_t)kBufferFlags};
+}
+
+// One 16-byte-per-lane load straight into LDS: lane l's bytes land at
+// lds + 16 * l.  Issued from asm so that the compiler neither counts it nor
+// orders LDS reads after it: the kernel waits for it explicitly (vmcnt and a
+// barrier) before any wave reads the stage.  There is no output register;
+// M0, which holds the LDS address, is restored before the asm ends.
+__device__ __forceinline__ void lds_dma16(const u32x4& rsrc, uint32_t lds, int voff, int soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dwordx4 %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+// the same for 4 bytes per lane (lane l's word lands at lds + 4 * l)
+__device__ __forceinline__ void lds_dma4(const u32x4& rsrc, uint32_t lds, int voff, int soff) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "buffer_load_dword %2, %3, %4 offen lds\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "s"(lds), "v"(voff), "s"(rsrc), "s"(soff)
+      : "memory");
+}
+
+
+// Q8_0 weights: each k-tile of a weight row is 64 codes (four 16-byte slots,
+// slot s of row r holding code piece s ^ q8_swz(r)) plus its two f16 scales
+// (one 32-bit word per row).  A B fragment is dequantised when it is read from
+// LDS, by the same function as every other path, so it equals the f16 weight.
+__device__ __forceinline__ int q8_swz(int r) { return (r >> 2) & 3; }
+
+template <int TM, int TN, int WM, int WN, int NS, bool XT, int WK, int CK>
+__global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
+  constexpr bool Q8 = WK == WK_Q8;
+  constexpr int NW = WM * WN;
   constexpr int WTM = TM / WM;
   constexpr int WTN = TN / WN;
   constexpr int FM = WTM / 32;
   constexpr int FN = WTN / 32;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
-  constexpr int A_CHUNKS = TM * kCPR;
-  constexpr int A_ITERS = (A_CHUNKS + NT - 1) / NT;
-  // Q8_0 rows arrive as 16-code quarters of a 64-wide k-tile; f16/bf16 rows as 8 chunks
-  constexpr int B_UNITS = (WK == WK_Q8) ? TN * 4 : TN * kCPR;
-  constexpr int B_ITERS = (B_UNITS + NT - 1) / NT;
-  static_assert(A_CHUNKS % NT == 0 && (WK == WK_Q8 || B_UNITS % NT == 0),
-                "tile rows must split evenly over the block");
-  // register sets for staged k-tiles: two (prefetch distance 2) when the
-  // accumulators, both sets, the double-buffered fragments and some slack fit
-  // the per-wave register budget (512 registers per SIMD lane shared by the
-  // waves of one block on each SIMD), else one (distance 1)
-  constexpr int kRegBudget = 512 / ((NT + 255) / 256);
-  constexpr int kStageRegs = (A_ITERS + B_ITERS) * 4 + (WK == WK_Q8 ? B_ITERS : 0);
-  constexpr int kNeed2 = FM * FN * 16 + 2 * kStageRegs + 2 * (FM + FN) * 4 + 40;
-  constexpr int NSETS = kNeed2 <= kRegBudget ? 2 : 1;
+  // one load instruction of one wave fills 8 rows of 16-bit data (64 lanes x
+  // 16 bytes), 16 rows of Q8_0 codes, or the scale words of 64 rows; a Q8_0
+  // stage rounds its code and scale rows up to whole instructions (rows past
+  // the tile are loaded and never read)
+  static_assert(TM % (8 * NW) == 0 && (Q8 || TN % (8 * NW) == 0), "tile rows must split evenly over the waves");
+  constexpr int A_ITERS = TM / (8 * NW);
+  constexpr int B_ITERS = Q8 ? (TN + 16 * NW - 1) / (16 * NW) : TN / (8 * NW);
+  constexpr int S_ITERS = Q8 ? (TN + 64 * NW - 1) / (64 * NW) : 0;
+  constexpr int LOADS = A_ITERS + B_ITERS + S_ITERS;  // per lane per k-tile
+  static_assert(NS >= 2 && (NS - 2) * LOADS < 64, "stages");
+  // XT: read the next k-tile's fragments during this one's MFMAs (small wave
+  // tiles; needs a third stage and (FM + FN) * 32 fragment registers)
+  constexpr bool kCrossTile = XT;
+  static_assert(!XT || (FM + FN <= 4 && NS >= 3), "cross-tile fragment reads");
+  constexpr int SA = TM * kCPR;                              // u32x4 per stage
+  constexpr int SB = Q8 ? B_ITERS * 16 * NW * 4 : TN * kCPR;  // u32x4 per stage
+  constexpr int SS = Q8 ? S_ITERS * 64 * NW : 1;              // scale words per stage
 
-  __shared__ u32x4 sA[2][A_CHUNKS];
-  __shared__ u32x4 sB[2][TN * kCPR];
+  __shared__ u32x4 sA[NS][SA];
+  __shared__ u32x4 sB[NS][SB];
+  __shared__ uint32_t sS[NS][SS];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -106,117 +190,110 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
   const int wm = wid / WN;
   const int wn = wid - wm * WN;
 
-  // XCD-aware renumbering: hardware block b runs on XCD b % 8; give XCD x the
-  // tiles [x * per, (x + 1) * per) of a column-major tile order (the last
-  // XCDs may get one fewer), so neighbouring tiles on an XCD share W columns
+  // XCD-aware renumbering: hardware block b runs on XCD b % 8; XCD x gets the
+  // tiles [x * per, (x + 1) * per) of one tile order (the last XCDs may get
+  // one fewer).  The order keeps the larger operand's tiles together on an
+  // XCD, so that XCD's L2 serves them to its blocks: column-major (blocks of
+  // one XCD share W columns) when N >= M, row-major (they share A rows) when
+  // M > N.  The order changes no result.
   const int64_t tiles_m = (g.M + TM - 1) / TM;
+  const int64_t tiles_n = (g.N + TN - 1) / TN;
   const int64_t nblocks = (int64_t)gridDim.x;
   const int64_t per = (nblocks + 7) / 8;
   const int64_t xcd = blockIdx.x & 7;
-  const int64_t full = nblocks - 8 * (per - 1);  // XCDs that get `per` tiles
+  const int64_t full = nblocks - 8 * (per - 1);
   const int64_t local = blockIdx.x >> 3;
-  const int64_t t = xcd < full ? xcd * per + local : full * per + (xcd - full) * (per - 1) + local;
-  const int64_t bn = t / tiles_m;
-  const int64_t bm = t - bn * tiles_m;
+  const int64_t tv = xcd < full ? xcd * per + local : full * per + (xcd - full) * (per - 1) + local;
+  // split-major: the blocks of one k range sit together, so neighbours share
+  // operand k-slices
+  const int64_t tiles = tiles_m * tiles_n;
+  const int split = (int)(tv / tiles);
+  const int64_t t = tv - (int64_t)split * tiles;
+  int64_t bm, bn;
+  if (g.M > g.N) {
+    bm = t / tiles_n;
+    bn = t - bm * tiles_n;
+  } else {
+    bn = t / tiles_m;
+    bm = t - bn * tiles_m;
+  }
   const int64_t row0 = bm * TM;
   const int64_t col0 = bn * TN;
 
-  const uint16_t* __restrict__ A = g.A;
   const int64_t K = g.K;  // <= 2^20 (checked by the plan), so offsets fit in 32 bits
-  const int nk = (int)((K + kBK - 1) / kBK);
-
-  u32x4 ra[NSETS][A_ITERS];
-  u32x4 rb[NSETS][B_ITERS];
-  uint16_t rs[NSETS][B_ITERS];  // Q8_0 scale of each staged quarter-row
-
-  // Loads go through buffer resources covering exactly this block's rows of
-  // A and W: a row past M or N lies outside the resource and reads as zero
-  // (hardware range check), so no load is predicated and the number of loads
-  // in flight is the same on every path -- the compiler's vmcnt waits then
-  // count exactly.  Each thread keeps one 32-bit offset per operand; the
-  // per-iteration row stride and the k-tile origin are scalar offsets.
-  // Chunks past K (only when K % 64 != 0) are zeroed by a select when they
-  // are written to LDS (a select right after the load would make the wave
-  // wait for that load at once).
+  const int nk_all = (int)((K + kBK - 1) / kBK);
+  // this block's k-tiles: [kb, kb + nk)
+  const int kb = split * g.kt_per_split;
+  const int nk = (nk_all - kb) < g.kt_per_split ? (nk_all - kb) : g.kt_per_split;
+  const bool last_split = kb + nk == nk_all;
   const int64_t rows_a = (g.M - row0) < TM ? (g.M - row0) : TM;
   const int64_t rows_b = (g.N - col0) < TN ? (g.N - col0) : TN;
-  const __amdgpu_buffer_rsrc_t rsrc_a = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)(A + row0 * g.lda), (short)0, (int)(((rows_a - 1) * g.lda + K) * 2), kBufferFlags);
-  const int a_r = tid / kCPR;
-  const int a_c = tid - a_r * kCPR;
-  const int voff_a = (int)((a_r * g.lda + a_c * 8) * 2);
-  const bool k_tail = (K % kBK) != 0;
+  const u32x4 rsrc_a = buffer_rsrc(g.A + row0 * g.lda, ((rows_a - 1) * g.lda + K) * 2);
+  const u32x4 rsrc_b = Q8 ? buffer_rsrc((const int8_t*)g.W + col0 * K, rows_b * K)
+                          : buffer_rsrc((const uint16_t*)g.W + col0 * K, rows_b * K * 2);
+  const u32x4 rsrc_s = Q8 ? buffer_rsrc(g.scales + col0 * (K >> 5), rows_b * (K >> 5) * 2) : rsrc_b;
+  const int wid_u = __builtin_amdgcn_readfirstlane(wid);
 
-  __amdgpu_buffer_rsrc_t rsrc_b;
-  __amdgpu_buffer_rsrc_t rsrc_s;
-  int voff_b, voff_s = 0, b_c;
-  if constexpr (WK == WK_Q8) {
-    rsrc_b = __builtin_amdgcn_make_buffer_rsrc((void*)((const int8_t*)g.W + col0 * K), (short)0,
-                                               (int)(rows_b * K), kBufferFlags);
-    rsrc_s = __builtin_amdgcn_make_buffer_rsrc((void*)(g.scales + col0 * (K >> 5)), (short)0,
-                                               (int)(rows_b * (K >> 5) * 2), kBufferFlags);
-    const int b_r = tid >> 2;
-    b_c = tid & 3;  // which 16-code quarter of the 64-wide k-tile
-    voff_b = (int)(b_r * K + b_c * 16);
-    voff_s = (int)((b_r * (K >> 5) + (b_c >> 1)) * 2);
-  } else {
-    rsrc_b = __builtin_amdgcn_make_buffer_rsrc((void*)((const uint16_t*)g.W + col0 * K), (short)0,
-                                               (int)(rows_b * K * 2), kBufferFlags);
-    rsrc_s = rsrc_b;
-    const int b_r = tid / kCPR;
-    b_c = tid - b_r * kCPR;
-    voff_b = (int)((b_r * K + b_c * 8) * 2);
+  // per-lane global offsets of each load (row r = 8 * (i * NW + wid) + lane / 8)
+  const int lr = lane >> 3;
+  const int ls = lane & 7;
+  int voff_a[A_ITERS];
+  int voff_b[B_ITERS];
+  int voff_s[S_ITERS > 0 ? S_ITERS : 1];
+#pragma unroll
+  for (int i = 0; i < A_ITERS; ++i) {
+    const int r = 8 * (i * NW + wid) + lr;
+    voff_a[i] = (int)(((int64_t)r * g.lda + (ls ^ swz(r)) * 8) * 2);
+  }
+#pragma unroll
+  for (int i = 0; i < B_ITERS; ++i) {
+    if constexpr (Q8) {
+      const int r = 16 * (i * NW + wid) + (lane >> 2);
+      voff_b[i] = (int)((int64_t)r * K + ((lane & 3) ^ q8_swz(r)) * 16);
+    } else {
+      const int r = 8 * (i * NW + wid) + lr;
+      voff_b[i] = (int)(((int64_t)r * K + (ls ^ swz(r)) * 8) * 2);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < S_ITERS; ++i) {
+    const int r = 64 * (i * NW + wid) + lane;
+    voff_s[i] = (int)((int64_t)r * (K >> 5) * 2);
   }
 
-  auto load_tiles = [&](int kt, int set) {
-    const int k0 = kt * kBK;
+  // k-tile kt (clamped to the last one, so every k-tile issues the same
+  // number of loads and the waits count exactly) into stage st
+  // local k-tile kt (0 .. nk - 1) into stage st
+  auto issue = [&](int st, int kt) {
+    const int kc = kb + (kt < nk ? kt : nk - 1);
+    const int koff = kc * kBK * 2;  // bytes of a 16-bit row
 #pragma unroll
-    for (int i = 0; i < A_ITERS; ++i) {
-      const int soff = (int)(((int64_t)i * (NT / kCPR) * g.lda + k0) * 2);
-      ra[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_a, voff_a, soff, 0));
-    }
+    for (int i = 0; i < A_ITERS; ++i)
+      lds_dma16(rsrc_a, lds_addr(&sA[st][(8 * (i * NW + wid_u)) * kCPR]), voff_a[i], koff);
+    if constexpr (Q8) {
 #pragma unroll
-    for (int i = 0; i < B_ITERS; ++i) {
-      if constexpr (WK == WK_Q8) {
-        const int soff = (int)((int64_t)i * (NT / 4) * K + k0);
-        const int soff_s = (int)(((int64_t)i * (NT / 4) * (K >> 5) + (k0 >> 5)) * 2);
-        rb[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, soff, 0));
-        rs[set][i] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_s, voff_s, soff_s, 0);
-      } else {
-        const int soff = (int)(((int64_t)i * (NT / kCPR) * K + k0) * 2);
-        rb[set][i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rsrc_b, voff_b, soff, 0));
-      }
+      for (int i = 0; i < B_ITERS; ++i)
+        lds_dma16(rsrc_b, lds_addr(&sB[st][(16 * (i * NW + wid_u)) * 4]), voff_b[i], kc * kBK);
+#pragma unroll
+      for (int i = 0; i < S_ITERS; ++i)
+        lds_dma4(rsrc_s, lds_addr(&sS[st][64 * (i * NW + wid_u)]), voff_s[i], kc * 4);
+    } else {
+#pragma unroll
+      for (int i = 0; i < B_ITERS; ++i)
+        lds_dma16(rsrc_b, lds_addr(&sB[st][(8 * (i * NW + wid_u)) * kCPR]), voff_b[i], koff);
     }
   };
 
-  auto store_tiles = [&](int buf, int set, int kt) {
-    const int k0 = kt * kBK;
-    const u32x4 zero = {0u, 0u, 0u, 0u};
-#pragma unroll
-    for (int i = 0; i < A_ITERS; ++i) {
-      const int r = a_r + i * (NT / kCPR);
-      const bool keep = !k_tail || k0 + a_c * 8 < K;
-      sA[buf][r * kCPR + (a_c ^ swz(r))] = keep ? ra[set][i] : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < B_ITERS; ++i) {
-      if constexpr (WK == WK_Q8) {
-        const int r = (tid >> 2) + i * (NT / 4);
-        // a last, partial pass (TN * 4 not a multiple of the block) loaded
-        // rows past the tile, which read as zero; they are not stored
-        if (B_UNITS % NT != 0 && r >= TN) continue;
-        const bool keep = !k_tail || k0 + b_c * 16 < K;
-        const _Float16 d = half_from_bits(keep ? rs[set][i] : (uint16_t)0);
-        const u32x4 codes = keep ? rb[set][i] : zero;
-        const u32x2 lo = {(uint32_t)codes[0], (uint32_t)codes[1]};
-        const u32x2 hi = {(uint32_t)codes[2], (uint32_t)codes[3]};
-        sB[buf][r * kCPR + ((2 * b_c) ^ swz(r))] = q8_dequant8(lo, d);
-        sB[buf][r * kCPR + ((2 * b_c + 1) ^ swz(r))] = q8_dequant8(hi, d);
-      } else {
-        const int r = (tid / kCPR) + i * (NT / kCPR);
-        const bool keep = !k_tail || k0 + b_c * 8 < K;
-        sB[buf][r * kCPR + (b_c ^ swz(r))] = keep ? rb[set][i] : zero;
-      }
+  // one B fragment: 8 weights of row `row` at k-chunk c (of 8) of a stage
+  auto read_b = [&](int st, int row, int c) -> u32x4 {
+    if constexpr (Q8) {
+      const uint32_t* codes = reinterpret_cast<const uint32_t*>(&sB[st][0]);
+      const int w = row * 16 + (((c >> 1) ^ q8_swz(row)) * 4) + (c & 1) * 2;
+      const u32x2 q = *reinterpret_cast<const u32x2*>(codes + w);
+      const uint32_t sc = sS[st][row];
+      return q8_dequant8(q, half_from_bits((uint16_t)((c >> 2) ? (sc >> 16) : sc)));
+    } else {
+      return sB[st][row * kCPR + (c ^ swz(row))];
     }
   };
 
@@ -229,9 +306,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
   const int lrow = lane & 31;
-  const int lk = lane >> 5;  // which 8-wide half of an MFMA k-step this lane feeds
-
-  // LDS word index of this lane's fragment rows (the chunk is added per step)
+  const int lk = lane >> 5;
   int a_row[FM];
   int b_row[FN];
 #pragma unroll
@@ -239,64 +314,120 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
 #pragma unroll
   for (int j = 0; j < FN; ++j) b_row[j] = wn * WTN + j * 32 + lrow;
 
-  auto read_frags = [&](int buf, int ks, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
-    const int c = ks * 2 + lk;
+  const bool k_tail = (K % kBK) != 0;
+
+  // prologue: tiles 0 .. NS - 2 into stages 0 .. NS - 2
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = sA[buf][a_row[i] * kCPR + (c ^ swz(a_row[i]))];
+  for (int st = 0; st < NS - 1; ++st) issue(st, st);
+
+  // K % 64 != 0: the last k-tile runs outside the loop, and there the
+  // fragments past K are zeroed (in both operands) before its MFMAs
+  auto mask_tail = [&](int ks, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
+    if (k_tail && last_split && (int64_t)(kb + nk - 1) * kBK + ks * 16 + lk * 8 >= K) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bf[j] = sB[buf][b_row[j] * kCPR + (c ^ swz(b_row[j]))];
+      for (int i = 0; i < FM; ++i) af[i] = zero;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) bf[j] = zero;
+    }
   };
 
-  // pipeline: tile kt is in LDS buffer kt & 1 when its MFMAs run.  With two
-  // register sets, tile kt + 1 sits in set (kt + 1) & 1 and is written to the
-  // other buffer half way through tile kt, while tile kt + 2 is loaded into
-  // set kt & 1 (emptied during tile kt - 1) at the start of tile kt.  With one
-  // set, tile kt + 1 is loaded at the start of tile kt and written after its
-  // last MFMA step.
-  load_tiles(0, 0);
-  if constexpr (NSETS == 2) load_tiles(nk > 1 ? 1 : 0, 1);
-  store_tiles(0, 0, 0);
-  __syncthreads();
-
-  constexpr int kStoreAfter = (NSETS == 2) ? kSteps / 2 - 1 : kSteps - 1;
-
-  auto tile_step = [&](int kt, int set_next) {
-    const int cur = kt & 1;
-    // the prefetch is issued on every tile (past the end it re-reads the last
-    // tile) and the store on every tile (past the end into a buffer nobody
-    // reads), so a tile is one straight-line block with a fixed count of
-    // loads in flight
-    if constexpr (NSETS == 2) {
-      load_tiles(kt + 2 < nk ? kt + 2 : nk - 1, set_next ^ 1);
+  if constexpr (kCrossTile) {
+    // Small wave tiles: one MFMA per fragment pair cannot hide an LDS read,
+    // so tile kt + 1's fragments (all four k-steps) are read while tile kt's
+    // MFMAs run on the fragments read one iteration earlier.  Iteration kt:
+    // wait for this lane's part of tile kt + 1 (NS - 3 later tiles may stay in
+    // flight), barrier (tile kt + 1 is in LDS; every wave has its tile-kt
+    // fragments in registers, so the stages of tiles kt - 1 and kt are free),
+    // refill the stage of tile kt - 1 with tile kt + NS - 1, read tile kt + 1,
+    // multiply tile kt.
+    u32x4 fa[2][kSteps][FM];
+    u32x4 fb[2][kSteps][FN];
+    auto read_tile = [&](int st, u32x4 (&ta)[kSteps][FM], u32x4 (&tb)[kSteps][FN]) {
+      const u32x4* a_s = sA[st];
+#pragma unroll
+      for (int ks = 0; ks < kSteps; ++ks) {
+        const int c = ks * 2 + lk;
+#pragma unroll
+        for (int i = 0; i < FM; ++i) ta[ks][i] = a_s[a_row[i] * kCPR + (c ^ swz(a_row[i]))];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) tb[ks][j] = read_b(st, b_row[j], c);
+      }
+    };
+    auto mma_tile = [&](u32x4 (&ta)[kSteps][FM], u32x4 (&tb)[kSteps][FN], bool last) {
+#pragma unroll
+      for (int ks = 0; ks < kSteps; ++ks) {
+        if (last) mask_tail(ks, ta[ks], tb[ks]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(ta[ks][i], tb[ks][j], acc[i][j]);
+      }
+    };
+    wait_vmcnt<(NS - 2) * LOADS>();  // tile 0
+    barrier_only();
+    read_tile(0, fa[0], fb[0]);
+    int stage = 0;  // stage of tile kt
+    int kt = 0;
+    // tiles 0 .. nk - 2, two per trip so the fragment sets are named at
+    // compile time; the body is one straight-line block
+    while (kt < nk - 1) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        wait_vmcnt<(NS - 3) * LOADS>();
+        barrier_only();
+        issue(stage == 0 ? NS - 1 : stage - 1, kt + NS - 1);
+        stage = stage + 1 == NS ? 0 : stage + 1;
+        read_tile(stage, fa[h ^ 1], fb[h ^ 1]);
+        mma_tile(fa[h], fb[h], false);
+        if (++kt == nk - 1) break;
+      }
+    }
+    // the last tile, read by the last trip (or the prologue)
+    if ((nk - 1) & 1) {
+      mma_tile(fa[1], fb[1], true);
     } else {
-      load_tiles(kt + 1 < nk ? kt + 1 : nk - 1, 0);
+      mma_tile(fa[0], fb[0], true);
     }
-    // fragments of step ks + 1 are read while step ks's MFMAs run
-    u32x4 af[2][FM];
-    u32x4 bf[2][FN];
-    read_frags(cur, 0, af[0], bf[0]);
+  } else {
+    // per k-tile: wait for this lane's part of tile kt (NS - 2 later tiles may
+    // stay in flight), barrier (every wave's part has landed, and every wave is
+    // done with the stage tile kt - 1 used), refill that stage with tile
+    // kt + NS - 1, then the MFMAs of tile kt
+    auto tile = [&](int kt, int st, bool last) {
+      wait_vmcnt<(NS - 2) * LOADS>();
+      barrier_only();
+      issue(st == 0 ? NS - 1 : st - 1, kt + NS - 1);
+      const u32x4* a_s = sA[st];
+      auto read_frags = [&](int ks, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
+        const int c = ks * 2 + lk;
 #pragma unroll
-    for (int ks = 0; ks < kSteps; ++ks) {
-      if (ks + 1 < kSteps) read_frags(cur, ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+        for (int i = 0; i < FM; ++i) af[i] = a_s[a_row[i] * kCPR + (c ^ swz(a_row[i]))];
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+        for (int j = 0; j < FN; ++j) bf[j] = read_b(st, b_row[j], c);
+      };
+      u32x4 af[2][FM];
+      u32x4 bf[2][FN];
+      read_frags(0, af[0], bf[0]);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(af[ks & 1][i], bf[ks & 1][j], acc[i][j]);
-      if (ks == kStoreAfter) store_tiles(cur ^ 1, NSETS == 2 ? set_next : 0, kt + 1);
+      for (int ks = 0; ks < kSteps; ++ks) {
+        if (ks + 1 < kSteps) read_frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
+        if (last) mask_tail(ks, af[ks & 1], bf[ks & 1]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(af[ks & 1][i], bf[ks & 1][j], acc[i][j]);
+      }
+    };
+    int stage = 0;
+    for (int kt = 0; kt < nk - 1; ++kt) {
+      tile(kt, stage, false);
+      stage = stage + 1 == NS ? 0 : stage + 1;
     }
-    __syncthreads();
-  };
-
-  // unrolled by two so the register sets are named at compile time
-  int kt = 0;
-  for (; kt + 1 < nk; kt += 2) {
-    tile_step(kt, 1);
-    tile_step(kt + 1, 0);
+    tile(nk - 1, stage, true);
   }
-  if (kt < nk) tile_step(kt, 1);
+  wait_vmcnt<0>();  // the re-reads past the end land before the block exits
 
-  // 32x32 accumulator layout: lane owns column (lane & 31); register v holds
-  // row 8 * (v / 4) + 4 * (lane / 32) + (v % 4)
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
@@ -305,9 +436,29 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
         const int64_t row = row0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
-        if (row < g.M && col < g.N) store_out<CK>(g.C, row * g.ldc + col, acc[i][j][v]);
+        if (row < g.M && col < g.N) {
+          if (g.splits > 1) {
+            g.partial[((int64_t)split * g.M + row) * g.N + col] = acc[i][j][v];
+          } else {
+            store_out<CK>(g.C, row * g.ldc + col, acc[i][j][v]);
+          }
+        }
       }
     }
+  }
+}
+
+// C[r][c] = partial[0][r][c] + partial[1][r][c] + ... in that order
+template <int CK>
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
+  const int64_t total = g.M * g.N;
+  const int64_t plane = total;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
+    const int64_t r = e / g.N;
+    const int64_t c = e - r * g.N;
+    float acc = g.partial[e];
+    for (int s = 1; s < g.splits; ++s) acc += g.partial[s * plane + e];
+    store_out<CK>(g.C, r * g.ldc + c, acc);
   }
 }
 
@@ -318,37 +469,44 @@ struct TileEntry {
   gemm_fn fn[3][3];  // [w_kind][c_kind]
 };
 
-template <int TM, int TN, int WM, int WN>
+// 16-bit weights run the multi-stage kernel with NS k-tiles in LDS (XT: the
+// next k-tile's fragments are read during this one's MFMAs); Q8_0 weights the
+// register-staged kernel (they are dequantised on their way into LDS).  Both
+// issue the same MFMA sequence for every output.
+template <int TM, int TN, int WM, int WN, int NS, bool XT>
 TileEntry make_tile(const char* name) {
   TileEntry e;
   e.info = GemmTileInfo{TM, TN, WM, WN, name};
-  e.fn[WK_F16][CK_F32] = gemm_kernel<TM, TN, WM, WN, WK_F16, CK_F32>;
-  e.fn[WK_F16][CK_F16] = gemm_kernel<TM, TN, WM, WN, WK_F16, CK_F16>;
-  e.fn[WK_F16][CK_BF16] = gemm_kernel<TM, TN, WM, WN, WK_F16, CK_BF16>;
-  e.fn[WK_BF16][CK_F32] = gemm_kernel<TM, TN, WM, WN, WK_BF16, CK_F32>;
-  e.fn[WK_BF16][CK_F16] = gemm_kernel<TM, TN, WM, WN, WK_BF16, CK_F16>;
-  e.fn[WK_BF16][CK_BF16] = gemm_kernel<TM, TN, WM, WN, WK_BF16, CK_BF16>;
-  e.fn[WK_Q8][CK_F32] = gemm_kernel<TM, TN, WM, WN, WK_Q8, CK_F32>;
-  e.fn[WK_Q8][CK_F16] = gemm_kernel<TM, TN, WM, WN, WK_Q8, CK_F16>;
-  e.fn[WK_Q8][CK_BF16] = gemm_kernel<TM, TN, WM, WN, WK_Q8, CK_BF16>;
+  e.fn[WK_F16][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_F16, CK_F32>;
+  e.fn[WK_F16][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_F16, CK_F16>;
+  e.fn[WK_F16][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_F16, CK_BF16>;
+  e.fn[WK_BF16][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_BF16, CK_F32>;
+  e.fn[WK_BF16][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_BF16, CK_F16>;
+  e.fn[WK_BF16][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_BF16, CK_BF16>;
+  e.fn[WK_Q8][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_Q8, CK_F32>;
+  e.fn[WK_Q8][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_Q8, CK_F16>;
+  e.fn[WK_Q8][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_Q8, CK_BF16>;
   return e;
 }
 
+// stage counts: (TM + TN) * 128 bytes of LDS per stage, at most 144 KiB per
+// block; the small tiles keep two blocks per CU.  XT where it measured faster
+// on MI355X (K = 2560, N = 96 and 7680).
 const TileEntry* tiles() {
   static const TileEntry table[] = {
-      make_tile<256, 256, 2, 2>("256x256_w2x2"),
-      make_tile<256, 256, 2, 4>("256x256_w2x4"),
-      make_tile<256, 128, 4, 2>("256x128_w4x2"),
-      make_tile<256, 128, 2, 2>("256x128_w2x2"),
-      make_tile<128, 256, 2, 2>("128x256_w2x2"),
-      make_tile<128, 128, 2, 2>("128x128_w2x2"),
-      make_tile<128, 64, 2, 2>("128x64_w2x2"),
-      make_tile<64, 128, 2, 2>("64x128_w2x2"),
-      make_tile<64, 64, 2, 2>("64x64_w2x2"),
-      make_tile<128, 96, 4, 1>("128x96_w4x1"),
-      make_tile<64, 96, 2, 1>("64x96_w2x1"),
-      make_tile<32, 96, 1, 1>("32x96_w1x1"),
-      make_tile<32, 64, 1, 2>("32x64_w1x2"),
+      make_tile<256, 256, 2, 2, 2, false>("256x256_w2x2"),
+      make_tile<256, 256, 2, 4, 2, false>("256x256_w2x4"),
+      make_tile<256, 128, 4, 2, 3, false>("256x128_w4x2"),
+      make_tile<256, 128, 2, 2, 3, false>("256x128_w2x2"),
+      make_tile<128, 256, 2, 2, 3, false>("128x256_w2x2"),
+      make_tile<128, 128, 2, 2, 4, true>("128x128_w2x2"),
+      make_tile<128, 64, 2, 2, 3, false>("128x64_w2x2"),
+      make_tile<64, 128, 2, 2, 3, false>("64x128_w2x2"),
+      make_tile<64, 64, 2, 2, 4, true>("64x64_w2x2"),
+      make_tile<128, 96, 4, 1, 5, true>("128x96_w4x1"),
+      make_tile<64, 96, 2, 1, 3, false>("64x96_w2x1"),
+      make_tile<32, 96, 1, 1, 5, true>("32x96_w1x1"),
+      make_tile<32, 64, 1, 2, 5, true>("32x64_w1x2"),
   };
   return table;
 }
@@ -366,10 +524,25 @@ hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind
   if (tile_id < 0 || tile_id >= kTileCount || w_kind < 0 || w_kind > 2 || c_kind < 0 || c_kind > 2)
     return hipErrorInvalidValue;
   const TileEntry& e = tiles()[tile_id];
-  const int64_t blocks = ((args.M + e.info.tm - 1) / e.info.tm) * ((args.N + e.info.tn - 1) / e.info.tn);
+  const int64_t nk = (args.K + kBK - 1) / kBK;
+  if (args.splits < 1 || args.kt_per_split < 1 || (int64_t)(args.splits - 1) * args.kt_per_split >= nk ||
+      (int64_t)args.splits * args.kt_per_split < nk || (args.splits > 1 && args.partial == nullptr))
+    return hipErrorInvalidValue;
+  const int64_t blocks =
+      ((args.M + e.info.tm - 1) / e.info.tm) * ((args.N + e.info.tn - 1) / e.info.tn) * args.splits;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
   hipLaunchKernelGGL(e.fn[w_kind][c_kind], dim3((unsigned)blocks), dim3(64 * e.info.wm * e.info.wn), 0,
                      stream, args);
+  return hipGetLastError();
+}
+
+hipError_t launch_splitk_reduce(const GemmArgs& args, int c_kind, hipStream_t stream) {
+  if (args.splits < 2 || args.partial == nullptr || c_kind < 0 || c_kind > 2) return hipErrorInvalidValue;
+  int64_t blocks = (args.M * args.N + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  const auto fn = c_kind == CK_F32 ? splitk_reduce_kernel<CK_F32>
+                : c_kind == CK_F16 ? splitk_reduce_kernel<CK_F16> : splitk_reduce_kernel<CK_BF16>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(256), 0, stream, args);
   return hipGetLastError();
 }
 

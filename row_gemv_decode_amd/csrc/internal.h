@@ -75,6 +75,9 @@ struct GemmArgs {
   int64_t K;
   void* C;                 // [M][ldc]
   int64_t ldc;
+  int32_t splits;          // k split into this many ranges of kt_per_split k-tiles
+  int32_t kt_per_split;
+  float* partial;          // [splits][M][N] fp32 partial sums (splits > 1)
 };
 
 struct GemmTileInfo {
@@ -87,5 +90,9 @@ const GemmTileInfo& gemm_tile(int id);
 
 hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind,
                        hipStream_t stream);
+
+// C = sum over s = 0..splits-1, in that order, of partial[s] (fp32), rounded
+// to the output kind
+hipError_t launch_splitk_reduce(const GemmArgs& args, int c_kind, hipStream_t stream);
 
 }  // namespace skinny

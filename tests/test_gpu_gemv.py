@@ -182,10 +182,10 @@ def test_repeated_calls_leave_counters_ready():
             plan.run_topk(m, A[:m], W, lg, idx, val, 10, workspace=ws)
             outs.append((m, lg, idx))
     torch.cuda.synchronize()
-    # the counters (the 256-byte tail after the partials: 64 column ranges of
-    # 4 columns) are back at zero
-    tail = ws[-256:].cpu().numpy()
-    assert not np.any(tail), tail[np.nonzero(tail)][:8]
+    # the counters (the first 256 bytes, before the partials: 64 column
+    # ranges of 4 columns) are back at zero
+    head = ws[:256].cpu().numpy()
+    assert not np.any(head), head[np.nonzero(head)][:8]
     first = {}
     for m, lg, idx in outs:
         if m not in first:
