@@ -271,31 +271,63 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
   const int64_t j0 = (int64_t)wc * g.cpw;
   const int ncol = active ? (int)min((int64_t)g.cpw, g.n - j0) : 0;
 
-  if (active) {
-    int chunk[T];
-    bool valid[T];
+  // Unsplit k (S = 1) with four or more rows: every wave of the block needs
+  // the same A slice (chunks 0 .. 64 T - 1 of every row), so the block loads
+  // it once into LDS and each wave reads its chunks from there, instead of
+  // every wave fetching all of A through its own load path.
+  constexpr bool kStageA = M >= 4;
+  __shared__ u32x4 sAr[kStageA ? M * 64 * T : 1];
+  const bool stage_a = kStageA && g.S == 1;
+  u32x4 a_share[kStageA ? (M * 64 * T + 255) / 256 : 1];
+  if (stage_a) {
+    // issued before the weight loads, so their latencies overlap
+#pragma unroll
+    for (int i = 0; i < (kStageA ? (M * 64 * T + 255) / 256 : 0); ++i) {
+      const int e = (int)threadIdx.x + i * (int)blockDim.x;
+      const int r = e / (64 * T);
+      const int c = e - r * (64 * T);
+      a_share[i] = (e < M * 64 * T && c < g.nchunks)
+                       ? *(const u32x4*)(g.A + (int64_t)r * g.lda + (int64_t)c * 8)
+                       : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  int chunk[T];
+  bool valid[T];
+#pragma unroll
+  for (int t = 0; t < T; ++t) {
+    chunk[t] = s * 64 * T + t * 64 + lane;
+    valid[t] = active && chunk[t] < g.nchunks;
+  }
+
+  // every weight load of the wave, issued before anything else waits
+  WChunk<WK> w[kGemvCpwMax][T];
+#pragma unroll
+  for (int c = 0; c < kGemvCpwMax; ++c) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      chunk[t] = s * 64 * T + t * 64 + lane;
-      valid[t] = chunk[t] < g.nchunks;
-    }
-
-    // every weight load of the wave, issued before anything else waits
-    WChunk<WK> w[kGemvCpwMax][T];
-#pragma unroll
-    for (int c = 0; c < kGemvCpwMax; ++c) {
-#pragma unroll
-      for (int t = 0; t < T; ++t) {
-        if (c < ncol && valid[t]) {
-          load_w<WK>(w[c][t], g, j0 + c, chunk[t]);
-        } else {
-          zero_w<WK>(w[c][t]);
-        }
+      if (c < ncol && valid[t]) {
+        load_w<WK>(w[c][t], g, j0 + c, chunk[t]);
+      } else {
+        zero_w<WK>(w[c][t]);
       }
     }
+  }
 
-    // the wave's A slice, kept in registers for all its columns
-    u32x4 a[T][M];
+  // the wave's A slice, kept in registers for all its columns
+  u32x4 a[T][M];
+  if (stage_a) {
+#pragma unroll
+    for (int i = 0; i < (kStageA ? (M * 64 * T + 255) / 256 : 0); ++i) {
+      const int e = (int)threadIdx.x + i * (int)blockDim.x;
+      if (e < M * 64 * T) sAr[e] = a_share[i];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < M; ++r) a[t][r] = sAr[(r * T + t) * 64 + lane];
+  } else {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
 #pragma unroll
@@ -304,6 +336,9 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
                            : u32x4{0u, 0u, 0u, 0u};
       }
     }
+  }
+
+  if (active) {
 
     constexpr int plain_mask = plain_lane_mask<LV>();
     const bool writer_lane = (lane & plain_mask) == 0;
@@ -405,8 +440,8 @@ hipError_t launch_gemv_kind(const GemvArgs& args, int m, int T, int out_kind, in
                             hipStream_t stream) {
   if (m < 1 || m > kGemvMaxM || (T != 1 && T != 2) || out_kind < 0 || out_kind > 2 ||
       waves_per_block < 1 || waves_per_block > kGemvMaxWavesPerBlock || args.cpw < 1 ||
-      args.cpw > kGemvCpwMax)
-    return hipErrorInvalidValue;
+      args.cpw > kGemvCpwMax || (args.S == 1 && waves_per_block < 4))
+    return hipErrorInvalidValue;  // (unsplit blocks stage A with at least 256 threads)
   // one column per pass when the wave owns fewer columns than a full group
   const int group = args.cpw < gemv_group_max(m) ? 0 : 1;
   const gemv_fn fn =
