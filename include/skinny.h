@@ -82,6 +82,13 @@ typedef enum skinny_dtype {
 /* desc.flags */
 #define SKINNY_FORCE_GEMV 0x1u /* use the GEMV for every m (m must stay <= 16) */
 #define SKINNY_FORCE_GEMM 0x2u /* use the MFMA GEMM for every m, including m <= 16 */
+/* A plan whose GEMM cuts k into chunks (narrow n) can run them as one block
+ * per chunk plus an ordered reduce launch, or as one launch that folds the
+ * chunk sums in the same order; both give the same bits and the plan picks
+ * the faster per m.  These flags force one shape (tests); with the second, a
+ * tile that cannot hold two accumulator sets falls back to the first. */
+#define SKINNY_GEMM_SPLIT_LAUNCH 0x4u
+#define SKINNY_GEMM_ONE_LAUNCH 0x8u
 
 #define SKINNY_GEMV_MAX_M 16
 #define SKINNY_TOPK_MAX 32

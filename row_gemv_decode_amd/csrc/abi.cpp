@@ -75,10 +75,12 @@ int gemv_cols_per_wave(int64_t n, int S, int num_cus) {
   return (int)cpw;
 }
 
-// GEMM k split: narrow N leaves most CUs idle at moderate M, so k is split
+// GEMM k split: narrow N leaves most CUs idle at moderate M, so the plan
+// also holds a k split, used at the m where the cost model prefers it: k is cut
 // until the column tiles (of 64) times the splits reach an eighth of the CU
 // count (32 on 256 CUs), keeping at least four 64-wide k-tiles per split and
-// at most 16 splits.  Depends on n, k and the CU count only.
+// at most 16 splits, with an even number of k-tiles per split.  Depends on n,
+// k and the CU count only.
 void gemm_split(int64_t n, int64_t k, int num_cus, int* splits, int* kps) {
   const int64_t nk = (k + 63) / 64;
   const int64_t col_tiles = (n + 63) / 64;
@@ -88,7 +90,8 @@ void gemm_split(int64_t n, int64_t k, int num_cus, int* splits, int* kps) {
   if (s > nk / 4) s = nk / 4;
   if (s > 16) s = 16;
   if (s < 1) s = 1;
-  const int64_t per = (nk + s - 1) / s;
+  int64_t per = (nk + s - 1) / s;
+  if (per % 2 != 0 && per < nk) ++per;  // even chunks: a chunked launch folds between tile pairs
   *kps = (int)per;
   *splits = (int)((nk + per - 1) / per);
 }
@@ -140,10 +143,12 @@ const TileCost& tile_cost(int id) {
   return kCost[id];
 }
 
-double tile_estimate(const skinny_plan* p, int id, int64_t m) {
+// estimated time of tile `id` at m rows when each of its blocks is repeated
+// `copies` times along k and covers `ktiles` 64-wide k-tiles
+double tile_estimate(const skinny_plan* p, int id, int64_t m, int64_t copies, int64_t ktiles) {
   const GemmTileInfo& t = gemm_tile(id);
   const TileCost& tc = tile_cost(id);
-  const int64_t blocks = ((m + t.tm - 1) / t.tm) * ((p->d.n + t.tn - 1) / t.tn) * p->gemm_splits;
+  const int64_t blocks = ((m + t.tm - 1) / t.tm) * ((p->d.n + t.tn - 1) / t.tn) * copies;
   const int64_t cus = p->num_cus;
   const int64_t slots = cus * tc.c;
   double rounds = 0.0;
@@ -152,18 +157,52 @@ double tile_estimate(const skinny_plan* p, int id, int64_t m) {
     const int64_t busiest = (nb + cus - 1) / cus;  // blocks on the busiest CU
     rounds += (busiest >= 2 ? tc.sigma : 1.0) * (1.0 + tc.a * (double)nb / (double)slots);
   }
-  return (double)p->gemm_kps * tc.t * rounds;
+  // Q8_0 weights are dequantised per fragment: about 1.65x the f16 time per
+  // k-tile on MI355X
+  const double kind = p->w_kind == WK_Q8 ? 1.65 : 1.0;
+  return (double)ktiles * tc.t * kind * rounds;
 }
 
-int select_tile(const skinny_plan* p, int64_t m) {
-  if (p->d.tile_id >= 0) return p->d.tile_id;
-  int best = 0;
-  double best_cost = 0.0;
-  for (int id = 0; id < gemm_tile_count(); ++id) {
-    const double cost = tile_estimate(p, id, m);
-    if (id == 0 || cost < best_cost * (1.0 - 1e-9)) {
-      best = id;
-      best_cost = cost;
+// the split launch's extra cost, fitted to MI355X runs (N = 96 and 512,
+// K = 2560): about 6 us for the short blocks' fixed costs and the reduce
+// launch, plus the fp32 partials written and read back at about 2 TB/s
+double reduce_estimate(const skinny_plan* p, int64_t m) {
+  const double bytes = (double)(p->gemm_splits + 1) * (double)m * (double)p->d.n * 4.0;
+  return 6.0 + bytes / 2.0e6;
+}
+
+struct GemmChoice {
+  int tile;
+  bool split;  // splits > 1: one block per chunk + the reduce launch
+  bool chunked;  // splits > 1 plan run as one chunk-folding launch
+  double est;
+};
+
+GemmChoice choose_gemm(const skinny_plan* p, int64_t m) {
+  const int64_t nk = (p->d.k + 63) / 64;
+  const int C = p->gemm_splits;
+  GemmChoice best{0, false, false, 0.0};
+  bool have = false;
+  const int first = p->d.tile_id >= 0 ? p->d.tile_id : 0;
+  const int last = p->d.tile_id >= 0 ? p->d.tile_id + 1 : gemm_tile_count();
+  for (int id = first; id < last; ++id) {
+    GemmChoice c[2];
+    int n = 0;
+    if (C == 1) {
+      c[n++] = GemmChoice{id, false, false, tile_estimate(p, id, m, 1, nk)};
+    } else {
+      const bool one_ok = gemm_tile_chunkable(id) && !(p->d.flags & SKINNY_GEMM_SPLIT_LAUNCH);
+      const bool split_ok = !(p->d.flags & SKINNY_GEMM_ONE_LAUNCH) || !gemm_tile_chunkable(id);
+      if (split_ok)
+        c[n++] = GemmChoice{id, true, false,
+                            tile_estimate(p, id, m, C, p->gemm_kps) + reduce_estimate(p, m)};
+      if (one_ok) c[n++] = GemmChoice{id, false, true, tile_estimate(p, id, m, 1, nk)};
+    }
+    for (int i = 0; i < n; ++i) {
+      if (!have || c[i].est < best.est * (1.0 - 1e-9)) {
+        best = c[i];
+        have = true;
+      }
     }
   }
   return best;
@@ -194,7 +233,7 @@ size_t gemv_partial_bytes(const skinny_plan* p, int64_t m) {
 }
 
 size_t gemm_partial_bytes(const skinny_plan* p, int64_t m) {
-  return p->gemm_splits > 1
+  return choose_gemm(p, m).split
              ? round_up((size_t)p->gemm_splits * (size_t)m * (size_t)p->d.n * sizeof(float))
              : 0;
 }
@@ -242,7 +281,7 @@ GemmArgs gemm_args(const skinny_plan* p, int64_t m, const void* A, const void* W
   g.K = p->d.k;
   g.C = C;
   g.ldc = ldc;
-  g.splits = p->gemm_splits;
+  g.splits = 1;
   g.kt_per_split = p->gemm_kps;
   g.partial = (workspace != nullptr && p->gemm_splits > 1)
                   ? (float*)((char*)workspace + gemv_counter_bytes(p))
@@ -311,7 +350,9 @@ skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const v
     return hip_status(launch_topk((const float*)C, (int)m, p->d.n, ldc, topk_idx, topk_val, topk, stream));
   }
   GemmArgs g = gemm_args(p, m, A, W, scales, C, ldc, workspace);
-  skinny_status st = hip_status(launch_gemm(select_tile(p, m), g, p->w_kind, c_kind, stream));
+  const GemmChoice gc = choose_gemm(p, m);
+  if (gc.split) g.splits = p->gemm_splits;
+  skinny_status st = hip_status(launch_gemm(gc.tile, g, p->w_kind, c_kind, gc.chunked, stream));
   if (st == SKINNY_OK && g.splits > 1) st = hip_status(launch_splitk_reduce(g, c_kind, stream));
   if (st != SKINNY_OK || !want_topk) return st;
   return hip_status(launch_topk((const float*)C, (int)m, p->d.n, ldc, topk_idx, topk_val, topk, stream));
@@ -363,7 +404,9 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   if (d.ldc == 0) d.ldc = d.n;
   if (d.lda < d.k || d.ldc < d.n) return SKINNY_ERR_SHAPE;
   if (d.lda % 8 != 0) return SKINNY_ERR_ALIGNMENT;  // A rows are read 16 bytes at a time
-  if (d.flags & ~(SKINNY_FORCE_GEMV | SKINNY_FORCE_GEMM)) return SKINNY_ERR_UNSUPPORTED;
+  if (d.flags & ~(SKINNY_FORCE_GEMV | SKINNY_FORCE_GEMM | SKINNY_GEMM_SPLIT_LAUNCH | SKINNY_GEMM_ONE_LAUNCH))
+    return SKINNY_ERR_UNSUPPORTED;
+  if ((d.flags & SKINNY_GEMM_SPLIT_LAUNCH) && (d.flags & SKINNY_GEMM_ONE_LAUNCH)) return SKINNY_ERR_INVALID_ARG;
   if ((d.flags & SKINNY_FORCE_GEMV) && (d.flags & SKINNY_FORCE_GEMM)) return SKINNY_ERR_INVALID_ARG;
   if ((d.flags & SKINNY_FORCE_GEMV) && d.max_m > kGemvMaxM) return SKINNY_ERR_INVALID_ARG;
   if (d.tile_id < -1 || d.tile_id >= gemm_tile_count()) return SKINNY_ERR_INVALID_ARG;
@@ -405,11 +448,15 @@ skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_t* bytes) {
   if (plan == nullptr || bytes == nullptr) return SKINNY_ERR_INVALID_ARG;
   // the largest need of any run: the GEMV at its largest m, or the GEMM at
   // max_m (each needs the workspace only when it splits k across workgroups)
-  size_t need = 0;
-  const int64_t probe[2] = {plan->d.max_m < kGemvMaxM ? plan->d.max_m : kGemvMaxM, plan->d.max_m};
-  for (int64_t m : probe) {
-    const size_t b = workspace_bytes_for(plan, m);
-    need = b > need ? b : need;
+  // (a GEMM that cuts k into chunks may use the split launch at any m, so
+  // its partials are sized for max_m)
+  size_t need = workspace_bytes_for(plan, plan->d.max_m < kGemvMaxM ? plan->d.max_m : kGemvMaxM);
+  const bool may_gemm = !(plan->d.flags & SKINNY_FORCE_GEMV) &&
+                        (plan->d.max_m > kGemvMaxM || (plan->d.flags & SKINNY_FORCE_GEMM));
+  if (may_gemm && plan->gemm_splits > 1) {
+    const size_t g = gemv_counter_bytes(plan) + round_up((size_t)plan->gemm_splits * (size_t)plan->d.max_m *
+                                                         (size_t)plan->d.n * sizeof(float));
+    need = g > need ? g : need;
   }
   *bytes = need;
   return SKINNY_OK;
@@ -462,15 +509,16 @@ skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf,
                   plan->gemv_S == 1 ? "none" : (gemv_global_split(plan) ? "global" : "in-block"),
                   workspace_bytes_for(plan, m));
   } else {
-    const int id = select_tile(plan, m);
-    const GemmTileInfo& t = gemm_tile(id);
+    const GemmChoice gc = choose_gemm(plan, m);
+    const GemmTileInfo& t = gemm_tile(gc.tile);
     const int64_t blocks =
-        ((m + t.tm - 1) / t.tm) * ((plan->d.n + t.tn - 1) / t.tn) * plan->gemm_splits;
+        ((m + t.tm - 1) / t.tm) * ((plan->d.n + t.tn - 1) / t.tn) * (gc.split ? plan->gemm_splits : 1);
     std::snprintf(buf, len,
-                  "path=gemm m=%lld tile=%d name=%s splits=%d blocks=%lld threads=%d est_us=%.1f "
-                  "workspace=%zu",
-                  (long long)m, id, t.name, plan->gemm_splits, (long long)blocks, 64 * t.wm * t.wn,
-                  tile_estimate(plan, id, m), workspace_bytes_for(plan, m));
+                  "path=gemm m=%lld tile=%d name=%s chunks=%d launch=%s blocks=%lld threads=%d "
+                  "est_us=%.1f workspace=%zu",
+                  (long long)m, gc.tile, t.name, plan->gemm_splits,
+                  gc.split ? "split" : (gc.chunked ? "one" : "plain"), (long long)blocks,
+                  64 * t.wm * t.wn, gc.est, workspace_bytes_for(plan, m));
   }
   return SKINNY_OK;
 }

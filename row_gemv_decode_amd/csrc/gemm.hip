@@ -40,6 +40,8 @@
 //     bank groups (the bank-conflict counter reads zero);
 //   * MFMA operand fragments are read ahead of their MFMAs: one k-step ahead
 //     for large wave tiles, one whole k-tile ahead for small ones.
+#include <type_traits>
+
 #include "device_common.h"
 #include "internal.h"
 
@@ -153,7 +155,7 @@ __device__ __forceinline__ void lds_dma4(const u32x4& rsrc, uint32_t lds, int vo
 // LDS, by the same function as every other path, so it equals the f16 weight.
 __device__ __forceinline__ int q8_swz(int r) { return (r >> 2) & 3; }
 
-template <int TM, int TN, int WM, int WN, int NS, bool XT, int WK, int CK>
+template <int TM, int TN, int WM, int WN, int NS, bool XT, bool CH, int WK, int CK>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
   constexpr bool Q8 = WK == WK_Q8;
   constexpr int NW = WM * WN;
@@ -222,9 +224,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
 
   const int64_t K = g.K;  // <= 2^20 (checked by the plan), so offsets fit in 32 bits
   const int nk_all = (int)((K + kBK - 1) / kBK);
-  // this block's k-tiles: [kb, kb + nk)
-  const int kb = split * g.kt_per_split;
-  const int nk = (nk_all - kb) < g.kt_per_split ? (nk_all - kb) : g.kt_per_split;
+  // this block's k-tiles: [kb, kb + nk) -- one chunk per block in a split
+  // launch, all of k otherwise (a chunked launch folds at chunk ends)
+  const int span = g.splits > 1 ? g.kt_per_split : nk_all;
+  const int kb = split * span;
+  const int nk = (nk_all - kb) < span ? (nk_all - kb) : span;
   const bool last_split = kb + nk == nk_all;
   const int64_t rows_a = (g.M - row0) < TM ? (g.M - row0) : TM;
   const int64_t rows_b = (g.N - col0) < TN ? (g.N - col0) : TN;
@@ -305,6 +309,28 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
 
+  // CH (one launch for a plan whose k is cut into chunks of kt_per_split
+  // k-tiles): acc holds the current chunk's sum, started from zero as a
+  // split block would; at each chunk end it is folded into tot -- the first
+  // chunk copied, later ones added in order -- exactly the additions the
+  // split-k reduce launch makes, so both launch shapes give the same bits.
+  f32x16 tot[CH ? FM : 1][CH ? FN : 1];
+  bool have_tot = false;
+  auto fold = [&]() {
+    if constexpr (CH) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            tot[i][j][v] = have_tot ? tot[i][j][v] + acc[i][j][v] : acc[i][j][v];
+            acc[i][j][v] = 0.0f;
+          }
+      have_tot = true;
+    }
+  };
+
   const int lrow = lane & 31;
   const int lk = lane >> 5;
   int a_row[FM];
@@ -369,19 +395,39 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
     read_tile(0, fa[0], fb[0]);
     int stage = 0;  // stage of tile kt
     int kt = 0;
-    // tiles 0 .. nk - 2, two per trip so the fragment sets are named at
-    // compile time; the body is one straight-line block
-    while (kt < nk - 1) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        wait_vmcnt<(NS - 3) * LOADS>();
-        barrier_only();
-        issue(stage == 0 ? NS - 1 : stage - 1, kt + NS - 1);
-        stage = stage + 1 == NS ? 0 : stage + 1;
-        read_tile(stage, fa[h ^ 1], fb[h ^ 1]);
-        mma_tile(fa[h], fb[h], false);
-        if (++kt == nk - 1) break;
+    // one trip: tile kt's MFMAs on fragment set H while tile kt + 1 is read
+    // into the other set
+    auto trip = [&](auto hc) {
+      constexpr int H = decltype(hc)::value;
+      wait_vmcnt<(NS - 3) * LOADS>();
+      barrier_only();
+      issue(stage == 0 ? NS - 1 : stage - 1, kt + NS - 1);
+      stage = stage + 1 == NS ? 0 : stage + 1;
+      read_tile(stage, fa[H ^ 1], fb[H ^ 1]);
+      mma_tile(fa[H], fb[H], false);
+      ++kt;
+    };
+    // tiles kt .. stop - 1 (kt even on entry): trips in pairs, so the loop
+    // body is one straight-line block with the fragment sets named at compile
+    // time and the loop has a single exit; an odd count leaves one trip after
+    auto run_to = [&](const int stop) {
+      while (kt + 1 < stop) {
+        trip(std::integral_constant<int, 0>{});
+        trip(std::integral_constant<int, 1>{});
       }
+      if (kt < stop) trip(std::integral_constant<int, 0>{});
+    };
+    if constexpr (CH) {
+      // chunks hold an even number of k-tiles, so kt is even at each chunk
+      // start; the fold sits between chunks; the global last tile is peeled
+      for (;;) {
+        const int cend = kt + g.kt_per_split < nk ? kt + g.kt_per_split : nk;
+        run_to(cend < nk ? cend : nk - 1);
+        if (cend == nk) break;
+        fold();
+      }
+    } else {
+      run_to(nk - 1);
     }
     // the last tile, read by the last trip (or the prologue)
     if ((nk - 1) & 1) {
@@ -389,6 +435,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
     } else {
       mma_tile(fa[0], fb[0], true);
     }
+    fold();
   } else {
     // per k-tile: wait for this lane's part of tile kt (NS - 2 later tiles may
     // stay in flight), barrier (every wave's part has landed, and every wave is
@@ -420,11 +467,19 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
       }
     };
     int stage = 0;
-    for (int kt = 0; kt < nk - 1; ++kt) {
-      tile(kt, stage, false);
-      stage = stage + 1 == NS ? 0 : stage + 1;
+    int kt = 0;
+    for (;;) {
+      const int cend = CH ? (kt + g.kt_per_split < nk ? kt + g.kt_per_split : nk) : nk;
+      const int stop = cend < nk ? cend : nk - 1;
+      for (; kt < stop; ++kt) {
+        tile(kt, stage, false);
+        stage = stage + 1 == NS ? 0 : stage + 1;
+      }
+      if (cend == nk) break;
+      fold();
     }
     tile(nk - 1, stage, true);
+    fold();
   }
   wait_vmcnt<0>();  // the re-reads past the end land before the block exits
 
@@ -437,7 +492,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
       for (int v = 0; v < 16; ++v) {
         const int64_t row = row0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
         if (row < g.M && col < g.N) {
-          if (g.splits > 1) {
+          if constexpr (CH) {
+            store_out<CK>(g.C, row * g.ldc + col, tot[i][j][v]);
+          } else if (g.splits > 1) {
             g.partial[((int64_t)split * g.M + row) * g.N + col] = acc[i][j][v];
           } else {
             store_out<CK>(g.C, row * g.ldc + col, acc[i][j][v]);
@@ -466,26 +523,43 @@ typedef void (*gemm_fn)(GemmArgs);
 
 struct TileEntry {
   GemmTileInfo info;
-  gemm_fn fn[3][3];  // [w_kind][c_kind]
+  gemm_fn fn[3][3];     // [w_kind][c_kind]
+  gemm_fn fn_ch[3][3];  // one launch over k chunks (null where the tile cannot hold two sums)
 };
 
 // 16-bit weights run the multi-stage kernel with NS k-tiles in LDS (XT: the
 // next k-tile's fragments are read during this one's MFMAs); Q8_0 weights the
 // register-staged kernel (they are dequantised on their way into LDS).  Both
 // issue the same MFMA sequence for every output.
+template <int TM, int TN, int WM, int WN, int NS, bool XT, bool CH>
+void fill_kinds(gemm_fn (&f)[3][3]) {
+  f[WK_F16][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_F16, CK_F32>;
+  f[WK_F16][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_F16, CK_F16>;
+  f[WK_F16][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_F16, CK_BF16>;
+  f[WK_BF16][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_BF16, CK_F32>;
+  f[WK_BF16][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_BF16, CK_F16>;
+  f[WK_BF16][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_BF16, CK_BF16>;
+  f[WK_Q8][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_Q8, CK_F32>;
+  f[WK_Q8][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_Q8, CK_F16>;
+  f[WK_Q8][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_Q8, CK_BF16>;
+}
+
+// the chunked one-launch variant keeps a second set of accumulators, so only
+// tiles with at most four 32 x 32 blocks per wave get it
+template <int TM, int TN, int WM, int WN>
+constexpr bool kChunkable = (TM / WM / 32) * (TN / WN / 32) <= 4;
+
 template <int TM, int TN, int WM, int WN, int NS, bool XT>
 TileEntry make_tile(const char* name) {
   TileEntry e;
   e.info = GemmTileInfo{TM, TN, WM, WN, name};
-  e.fn[WK_F16][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_F16, CK_F32>;
-  e.fn[WK_F16][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_F16, CK_F16>;
-  e.fn[WK_F16][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_F16, CK_BF16>;
-  e.fn[WK_BF16][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_BF16, CK_F32>;
-  e.fn[WK_BF16][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_BF16, CK_F16>;
-  e.fn[WK_BF16][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_BF16, CK_BF16>;
-  e.fn[WK_Q8][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_Q8, CK_F32>;
-  e.fn[WK_Q8][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_Q8, CK_F16>;
-  e.fn[WK_Q8][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, WK_Q8, CK_BF16>;
+  fill_kinds<TM, TN, WM, WN, NS, XT, false>(e.fn);
+  if constexpr (kChunkable<TM, TN, WM, WN>) {
+    fill_kinds<TM, TN, WM, WN, NS, XT, true>(e.fn_ch);
+  } else {
+    for (auto& row : e.fn_ch)
+      for (auto& f : row) f = nullptr;
+  }
   return e;
 }
 
@@ -519,20 +593,27 @@ int gemm_tile_count() { return kTileCount; }
 
 const GemmTileInfo& gemm_tile(int id) { return tiles()[id].info; }
 
-hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind,
+bool gemm_tile_chunkable(int id) { return tiles()[id].fn_ch[0][0] != nullptr; }
+
+hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind, bool chunked,
                        hipStream_t stream) {
   if (tile_id < 0 || tile_id >= kTileCount || w_kind < 0 || w_kind > 2 || c_kind < 0 || c_kind > 2)
     return hipErrorInvalidValue;
   const TileEntry& e = tiles()[tile_id];
   const int64_t nk = (args.K + kBK - 1) / kBK;
-  if (args.splits < 1 || args.kt_per_split < 1 || (int64_t)(args.splits - 1) * args.kt_per_split >= nk ||
-      (int64_t)args.splits * args.kt_per_split < nk || (args.splits > 1 && args.partial == nullptr))
+  if (args.splits < 1 || args.kt_per_split < 1 ||
+      (args.splits > 1 && ((int64_t)(args.splits - 1) * args.kt_per_split >= nk ||
+                           (int64_t)args.splits * args.kt_per_split < nk || args.partial == nullptr)))
     return hipErrorInvalidValue;
   const int64_t blocks =
       ((args.M + e.info.tm - 1) / e.info.tm) * ((args.N + e.info.tn - 1) / e.info.tn) * args.splits;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(e.fn[w_kind][c_kind], dim3((unsigned)blocks), dim3(64 * e.info.wm * e.info.wn), 0,
-                     stream, args);
+  // a chunked launch folds between pairs of k-tiles: chunks of even length
+  if (chunked && (args.splits != 1 || e.fn_ch[w_kind][c_kind] == nullptr ||
+                  (args.kt_per_split % 2 != 0 && args.kt_per_split < nk)))
+    return hipErrorInvalidValue;
+  hipLaunchKernelGGL(chunked ? e.fn_ch[w_kind][c_kind] : e.fn[w_kind][c_kind], dim3((unsigned)blocks),
+                     dim3(64 * e.info.wm * e.info.wn), 0, stream, args);
   return hipGetLastError();
 }
 

@@ -75,8 +75,8 @@ struct GemmArgs {
   int64_t K;
   void* C;                 // [M][ldc]
   int64_t ldc;
-  int32_t splits;          // k split into this many ranges of kt_per_split k-tiles
-  int32_t kt_per_split;
+  int32_t splits;          // blocks per tile: k split into this many ranges of
+  int32_t kt_per_split;    // kt_per_split k-tiles (also the chunk of a chunked launch)
   float* partial;          // [splits][M][N] fp32 partial sums (splits > 1)
 };
 
@@ -88,8 +88,11 @@ struct GemmTileInfo {
 int gemm_tile_count();
 const GemmTileInfo& gemm_tile(int id);
 
-hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind,
+// chunked: one launch over a k cut into chunks of kt_per_split k-tiles
+// (splits == 1), folding the chunk sums in order; needs a chunkable tile
+hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind, bool chunked,
                        hipStream_t stream);
+bool gemm_tile_chunkable(int tile_id);
 
 // C = sum over s = 0..splits-1, in that order, of partial[s] (fp32), rounded
 // to the output kind

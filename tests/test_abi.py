@@ -82,7 +82,7 @@ def test_tile_table():
     (dict(lda=800), sk.ERR_SHAPE),
     (dict(lda=900), sk.ERR_ALIGNMENT),
     (dict(ldc=100), sk.ERR_SHAPE),
-    (dict(flags=0x4), sk.ERR_UNSUPPORTED),
+    (dict(flags=0x10), sk.ERR_UNSUPPORTED),
     (dict(flags=sk.FORCE_GEMV | sk.FORCE_GEMM), sk.ERR_INVALID_ARG),
     (dict(flags=sk.FORCE_GEMV, max_m=17), sk.ERR_INVALID_ARG),
     (dict(tile_id=13), sk.ERR_INVALID_ARG),
@@ -164,21 +164,31 @@ def test_tile_selector_picks(n, k, m, tile):
     assert f"name={tile} " in plan(n=n, k=k, max_m=2048).info(m)
 
 
-@pytest.mark.parametrize("n,k,splits", [(96, 2560, 10), (512, 2560, 4), (7680, 2560, 1), (200, 512, 2),
-                                        (96, 64, 1), (4864, 896, 1)])
+@pytest.mark.parametrize("n,k,splits", [(96, 2560, 10), (256, 2560, 7), (512, 2560, 4), (7680, 2560, 1),
+                                        (200, 512, 2), (200, 64, 1), (4864, 896, 1)])
 def test_gemm_split_depends_on_n_k_only(n, k, splits):
     # narrow N splits k so that enough blocks exist at moderate M; the split
     # is fixed per plan (never per M), so rows stay M-invariant
     for m in (17, 300, 2048):
         info = plan(n=n, k=k, max_m=2048).info(m)
-        assert f" splits={splits} " in info, info
+        assert f" chunks={splits} " in info, info
 
 
 def test_gemm_split_workspace():
-    # splits x M x N fp32 partial sums, sized for max_m
-    p = plan(n=96, k=2560, max_m=2048)
-    assert p.workspace_bytes == 10 * 2048 * 96 * 4
-    assert p.info(17).endswith(" workspace=65280")  # 10 * 17 * 96 * 4, a multiple of 256
+    # chunks x M x N fp32 partial sums for the split launch, sized for max_m;
+    # the one-launch shape needs none
+    p = plan(n=512, k=2560, max_m=2048)
+    assert p.workspace_bytes == 4 * 2048 * 512 * 4
+    s = plan(n=512, k=2560, max_m=2048, flags=sk.GEMM_SPLIT_LAUNCH)
+    assert " launch=split " in s.info(17) and s.info(17).endswith(" workspace=139264")  # 4 * 17 * 512 * 4
+    o = plan(n=512, k=2560, max_m=2048, flags=sk.GEMM_ONE_LAUNCH)
+    assert " launch=one " in o.info(17) and o.info(17).endswith(" workspace=0")
+    # a tile without room for two accumulator sets always splits
+    big = plan(n=512, k=2560, max_m=2048, flags=sk.GEMM_ONE_LAUNCH, tile_id=0)
+    assert " launch=split " in big.info(300)
+    # narrow N: 10 chunks of 4 k-tiles
+    assert plan(n=96, k=2560, max_m=2048).workspace_bytes == 10 * 2048 * 96 * 4
+    assert plan_status(flags=sk.GEMM_SPLIT_LAUNCH | sk.GEMM_ONE_LAUNCH) == sk.ERR_INVALID_ARG
 
 
 def _est(info):
@@ -262,7 +272,7 @@ def test_run_validation():
     assert run(g, 16, ws=P16, nbytes=g.workspace_bytes - 16) == sk.ERR_WORKSPACE  # m = 16 needs it all
     assert run(g, 4, ws=ODD, nbytes=g.workspace_bytes) == sk.ERR_ALIGNMENT
     # a GEMM that splits k needs the workspace for its partial sums
-    h = plan(n=96, k=2560, max_m=64)
+    h = plan(n=512, k=2560, max_m=64, flags=sk.GEMM_SPLIT_LAUNCH)
     assert run(h, 40, ws=None, nbytes=0) == sk.ERR_WORKSPACE
     assert run(h, 64, ws=P16, nbytes=h.workspace_bytes - 16) == sk.ERR_WORKSPACE
 

@@ -159,3 +159,36 @@ def test_q8_gemm_full_size_and_fused_equals_unfused():
         rows = _sample_rows(M)
         ref = oracle.mm(A[rows], "f16", qs, "q8_0", w_scales=d)
         assert rel_err(C.float().cpu().numpy()[rows], ref) <= REL_TOL, M
+
+
+@pytest.mark.parametrize("w_kind", ["f16", "q8_0"])
+def test_chunked_one_launch_equals_split_launch(w_kind):
+    """A plan that cuts k into chunks gives the same bits whether each chunk
+    runs in its own block (partials + ordered reduce) or one block folds the
+    chunk sums in the same order; K = 2600 leaves a short last chunk."""
+    N, K = 256, 2560 if w_kind == "q8_0" else 2600
+    A = WL.gen_matrix((300, K), "f16", ("normal", 1.0), 601)
+    if w_kind == "q8_0":
+        qs, d = WL.gen_q8_0(N, K, 602, 603)
+        dW, scales, wk = to_dev(qs, "i8"), to_dev(d, "f16"), sk.Q8_0
+        ref_all = oracle.mm(A, "f16", qs, "q8_0", w_scales=d)
+    else:
+        W = WL.gen_matrix((N, K), "f16", ("normal", 0.02), 602)
+        dW, scales, wk = to_dev(W, "f16"), None, sk.F16
+        ref_all = oracle.mm(A, "f16", W, "f16")
+    dA = to_dev(A, "f16")
+    outs = {}
+    for flag in (sk.GEMM_SPLIT_LAUNCH, sk.GEMM_ONE_LAUNCH):
+        plan = sk.Plan(N, K, 300, sk.F16, wk, sk.F32, flags=flag)
+        ws = plan.workspace(dA.device)
+        for M in (17, 64, 300):
+            print(f"{w_kind} flag={flag} M={M}: {plan.info(M)}", flush=True)
+            C = torch.empty((M, N), dtype=torch.float32, device="cuda")
+            plan.run(M, dA[:M], dW, C, scales=scales, workspace=ws)
+            torch.cuda.synchronize()
+            outs[(flag, M)] = C.cpu().numpy()
+    for M in (17, 64, 300):
+        a, b = outs[(sk.GEMM_SPLIT_LAUNCH, M)], outs[(sk.GEMM_ONE_LAUNCH, M)]
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), M
+        assert np.array_equal(a.view(np.uint32), outs[(sk.GEMM_SPLIT_LAUNCH, 300)][:M].view(np.uint32)), M
+        assert rel_err(a, ref_all[:M]) <= REL_TOL
