@@ -16,32 +16,44 @@ namespace {
 // Per-row top-k, one wavefront per row (Strata PR #109, "What": one multi-row
 // top-10 launch over the window's tokens, the row taken from the block index).
 // Order: value descending, equal values (IEEE ==, so -0 == +0) by lower column
-// first; the result carries the logit's own bits.
+// first; the result carries the logit's own bits.  Logits are not NaN (a NaN
+// logit's rank is unspecified).
+//
+// Values are compared as order keys: the float's bits with the magnitude bits
+// of negative values flipped, read as a signed integer, and -0 mapped to +0's
+// key; for non-NaN values the key order is IEEE order and equal keys are
+// IEEE-equal values.  Integer keys let each reduction level be one DPP max.
 //
 // Fast path (n <= 64 * NC): lane l holds columns l, l + 64, ... in NC
 // registers, sorted once per lane (a stable odd-even transposition sort, so
 // equal values keep increasing columns).  Each round takes the wave maximum of
-// the lanes' heads (DPP / permlane max) and a ballot of the lanes whose head
-// equals it: one lane in the ballot owns the winner outright, several (a tie)
-// fall back to the smallest column among them.  The owner pops its head and
-// lane t keeps the t-th winner, so the results leave in one coalesced store.
+// the lanes' head keys and a ballot of the lanes whose head equals it: one
+// lane in the ballot owns the winner outright, several (a tie) fall back to
+// the smallest column among them.  The owner pops its head and lane t keeps
+// the t-th winner, so the results leave in one coalesced store.
 // Generic path (larger n): each round rescans the row.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ float wave_max_f32(float v) {
-  v = fmaxf(v, dpp_mov<kDppXor1>(v));
-  v = fmaxf(v, dpp_mov<kDppXor2>(v));
-  v = fmaxf(v, dpp_mov<kDppRowHalfMirror>(v));
-  v = fmaxf(v, dpp_mov<kDppRowMirror>(v));
-  auto r16 = __builtin_amdgcn_permlane16_swap(ubits(v), ubits(v), false, false);
-  v = fmaxf(fbits(r16[0]), fbits(r16[1]));
-  auto r32 = __builtin_amdgcn_permlane32_swap(ubits(v), ubits(v), false, false);
-  v = fmaxf(fbits(r32[0]), fbits(r32[1]));
-  return v;
+__device__ __forceinline__ int order_key(float x) {
+  uint32_t b = ubits(x);
+  if (b == 0x80000000u) b = 0u;  // -0 ranks with +0
+  return (int)(b ^ ((uint32_t)((int)b >> 31) & 0x7fffffffu));
 }
 
 template <int CTRL>
 __device__ __forceinline__ int dpp_mov_i(int x) {
   return (int)__builtin_amdgcn_update_dpp(0u, (uint32_t)x, CTRL, 0xF, 0xF, false);
+}
+
+__device__ __forceinline__ int wave_max_i32(int v) {
+  v = max(v, dpp_mov_i<kDppXor1>(v));
+  v = max(v, dpp_mov_i<kDppXor2>(v));
+  v = max(v, dpp_mov_i<kDppRowHalfMirror>(v));
+  v = max(v, dpp_mov_i<kDppRowMirror>(v));
+  auto r16 = __builtin_amdgcn_permlane16_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = max((int)r16[0], (int)r16[1]);
+  auto r32 = __builtin_amdgcn_permlane32_swap((uint32_t)v, (uint32_t)v, false, false);
+  v = max((int)r32[0], (int)r32[1]);
+  return v;
 }
 
 __device__ __forceinline__ int wave_min_i32(int v) {
@@ -56,23 +68,35 @@ __device__ __forceinline__ int wave_min_i32(int v) {
   return v;
 }
 
-// (v, j) comes after (pv, pj) in the order above
-__device__ __forceinline__ bool after(float v, int j, float pv, int pj) {
-  return v < pv || (v == pv && j > pj);
+// (key, j) comes after (pkey, pj) in the order above
+__device__ __forceinline__ bool after(int key, int j, int pkey, int pj) {
+  return key < pkey || (key == pkey && j > pj);
 }
 
 constexpr int kNoColumn = 0x7fffffff;
+constexpr int kNoKey = (int)0x80000000;  // below every non-NaN value's key
+
+// the float whose order key is `key` (-0 comes back as +0)
+__device__ __forceinline__ float key_value(int key) {
+  return fbits((uint32_t)key ^ ((uint32_t)(key >> 31) & 0x7fffffffu));
+}
 
 template <int NC>
 __device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int topk, int32_t* out_idx,
                                                    float* out_val, int lane) {
-  float v[NC];
+  int key[NC];
   int jj[NC];
+  float x[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {  // every load in flight before the first key
+    const int j = lane + 64 * u;
+    x[u] = j < n ? row[j] : 0.0f;
+  }
 #pragma unroll
   for (int u = 0; u < NC; ++u) {
     const int j = lane + 64 * u;
     const bool ok = j < n;
-    v[u] = ok ? row[j] : -__builtin_inff();
+    key[u] = ok ? order_key(x[u]) : kNoKey;
     jj[u] = ok ? j : kNoColumn;
   }
   // stable sort of the lane's slots into rank order
@@ -80,60 +104,62 @@ __device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int 
   for (int round = 0; round < NC; ++round) {
 #pragma unroll
     for (int u = round & 1; u + 1 < NC; u += 2) {
-      const bool swap = after(v[u], jj[u], v[u + 1], jj[u + 1]);
-      const float tv = v[u];
+      const bool swap = after(key[u], jj[u], key[u + 1], jj[u + 1]);
+      const int tk = key[u];
       const int tj = jj[u];
-      v[u] = swap ? v[u + 1] : v[u];
+      key[u] = swap ? key[u + 1] : key[u];
       jj[u] = swap ? jj[u + 1] : jj[u];
-      v[u + 1] = swap ? tv : v[u + 1];
+      key[u + 1] = swap ? tk : key[u + 1];
       jj[u + 1] = swap ? tj : jj[u + 1];
     }
   }
   int res_j = 0;
-  float res_v = 0.0f;
+  int res_k = 0;
   for (int t = 0; t < topk; ++t) {
-    const float wmax = wave_max_f32(v[0]);
-    uint64_t ball = __builtin_amdgcn_ballot_w64(v[0] == wmax);
+    const int kmax = wave_max_i32(key[0]);  // the same in every lane
+    uint64_t ball = __builtin_amdgcn_ballot_w64(key[0] == kmax);
     if (__builtin_popcountll(ball) != 1) {  // wave-uniform; a tie, rare with continuous data
       const int wj = wave_min_i32(((ball >> lane) & 1) ? jj[0] : kNoColumn);
       ball = __builtin_amdgcn_ballot_w64(jj[0] == wj);
     }
     const int owner = ball != 0 ? __builtin_ctzll(ball) : 0;
     const int wj = __builtin_amdgcn_readlane(jj[0], owner);
-    const float wv = fbits((uint32_t)__builtin_amdgcn_readlane((int)ubits(v[0]), owner));
     res_j = lane == t ? wj : res_j;
-    res_v = lane == t ? wv : res_v;
-    const bool mine = lane == owner;
+    res_k = lane == t ? kmax : res_k;
+    if (lane == owner) {  // the owner pops its head
 #pragma unroll
-    for (int u = 0; u + 1 < NC; ++u) {
-      v[u] = mine ? v[u + 1] : v[u];
-      jj[u] = mine ? jj[u + 1] : jj[u];
+      for (int u = 0; u + 1 < NC; ++u) {
+        key[u] = key[u + 1];
+        jj[u] = jj[u + 1];
+      }
+      key[NC - 1] = kNoKey;
+      jj[NC - 1] = kNoColumn;
     }
-    v[NC - 1] = mine ? -__builtin_inff() : v[NC - 1];
-    jj[NC - 1] = mine ? kNoColumn : jj[NC - 1];
   }
   if (lane < topk) {
     out_idx[lane] = res_j;
-    out_val[lane] = res_v;
+    // the key gives the value's bits back, except that a zero may be -0
+    out_val[lane] = res_k == 0 ? row[res_j] : key_value(res_k);
   }
 }
 
-__device__ __noinline__ void wave_topk_row_generic(const float* row, int n, int topk, int32_t* out_idx,
-                                                   float* out_val, int lane) {
-  float prev_v = 0.0f;
+__device__ void wave_topk_row_generic(const float* row, int n, int topk, int32_t* out_idx, float* out_val,
+                                      int lane) {
+  int prev_k = 0;
   int prev_j = -1;
   for (int t = 0; t < topk; ++t) {
-    float best = -__builtin_inff();
+    int best = kNoKey;
     for (int j = lane; j < n; j += 64) {
-      const float x = row[j];
-      if (prev_j < 0 || after(x, j, prev_v, prev_j)) best = fmaxf(best, x);
+      const int kx = order_key(row[j]);
+      if (prev_j < 0 || after(kx, j, prev_k, prev_j)) best = max(best, kx);
     }
-    const float wmax = wave_max_f32(best);
+    const int kmax = wave_max_i32(best);
     int cand = kNoColumn;
     float cand_v = 0.0f;
     for (int j = lane; j < n; j += 64) {
       const float x = row[j];
-      if (x == wmax && (prev_j < 0 || after(x, j, prev_v, prev_j)) && j < cand) {
+      const int kx = order_key(x);
+      if (kx == kmax && (prev_j < 0 || after(kx, j, prev_k, prev_j)) && j < cand) {
         cand = j;
         cand_v = x;
       }
@@ -143,35 +169,26 @@ __device__ __noinline__ void wave_topk_row_generic(const float* row, int n, int 
       out_idx[t] = wj;
       out_val[t] = cand_v;
     }
-    prev_v = wmax;
+    prev_k = kmax;
     prev_j = wj;
   }
 }
 
-__device__ __forceinline__ void wave_topk_row(const float* row, int n, int topk, int32_t* out_idx,
-                                              float* out_val, int lane) {
-  if (n <= 64) {
-    wave_topk_row_regs<1>(row, n, topk, out_idx, out_val, lane);
-  } else if (n <= 128) {
-    wave_topk_row_regs<2>(row, n, topk, out_idx, out_val, lane);
-  } else if (n <= 256) {
-    wave_topk_row_regs<4>(row, n, topk, out_idx, out_val, lane);
-  } else if (n <= 512) {
-    wave_topk_row_regs<8>(row, n, topk, out_idx, out_val, lane);
-  } else if (n <= 1024) {
-    wave_topk_row_regs<16>(row, n, topk, out_idx, out_val, lane);
-  } else {
-    wave_topk_row_generic(row, n, topk, out_idx, out_val, lane);
-  }
-}
-
 // --- top-k launch: one wavefront per row, blockIdx.x = row -------------------
+// NC > 0: rows of at most 64 * NC columns held in registers; NC == 0: generic
+template <int NC>
 __global__ __launch_bounds__(64) void topk_rows_kernel(const float* __restrict__ logits, int64_t n,
                                                        int64_t ldl, int32_t* __restrict__ out_idx,
                                                        float* __restrict__ out_val, int topk) {
   const int r = blockIdx.x;
-  wave_topk_row(logits + (int64_t)r * ldl, (int)n, topk, out_idx + (int64_t)r * topk,
-                out_val + (int64_t)r * topk, threadIdx.x);
+  const float* row = logits + (int64_t)r * ldl;
+  int32_t* oi = out_idx + (int64_t)r * topk;
+  float* ov = out_val + (int64_t)r * topk;
+  if constexpr (NC > 0) {
+    wave_topk_row_regs<NC>(row, (int)n, topk, oi, ov, threadIdx.x);
+  } else {
+    wave_topk_row_generic(row, (int)n, topk, oi, ov, threadIdx.x);
+  }
 }
 
 // --- standalone dequant ----------------------------------------------------
@@ -205,8 +222,14 @@ hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_k
 
 hipError_t launch_topk(const float* logits, int m, int64_t n, int64_t ldl, int32_t* idx, float* val,
                        int topk, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_rows_kernel, dim3((unsigned)m), dim3(64), 0, stream, logits, n, ldl, idx, val,
-                     topk);
+  typedef void (*topk_fn)(const float*, int64_t, int64_t, int32_t*, float*, int);
+  const topk_fn fn = n <= 64    ? topk_rows_kernel<1>
+                     : n <= 128 ? topk_rows_kernel<2>
+                     : n <= 256 ? topk_rows_kernel<4>
+                     : n <= 512 ? topk_rows_kernel<8>
+                     : n <= 1024 ? topk_rows_kernel<16>
+                                 : topk_rows_kernel<0>;
+  hipLaunchKernelGGL(fn, dim3((unsigned)m), dim3(64), 0, stream, logits, n, ldl, idx, val, topk);
   return hipGetLastError();
 }
 

@@ -114,10 +114,13 @@ def test_q8_gemv_parity_and_fused_equals_unfused(m):
     assert np.array_equal(bits_of(C), bits_of(C2))
 
 
-def _topk_case(m, n, k, seed, dup_cols=(), one_hot=False, max_m=16, flags=0):
+def _topk_case(m, n, k, seed, dup_cols=(), one_hot=False, max_m=16, flags=0, negative=False):
     """Router-style inputs; dup_cols lists (src, dst) weight rows to duplicate
-    (equal logits -> ties); one_hot makes A rows one-hot so logits are exact."""
+    (equal logits -> ties); one_hot makes A rows one-hot so logits are exact;
+    negative sets every weight's sign bit."""
     W = WL.gen_matrix((n, k), "bf16", ("normal", 0.02), seed)
+    if negative:
+        W = W | np.uint16(0x8000)
     for src, dst in dup_cols:
         W[dst] = W[src]
     if one_hot:
@@ -150,6 +153,13 @@ def test_topk_ties_break_to_lower_index(m):
 def test_topk_exact_logits_one_hot():
     # one-hot rows: logits are weight values exactly, so fp32 cannot reorder them
     _topk_case(4, 256, 5120, 311, one_hot=True)
+
+
+@pytest.mark.parametrize("n", [64, 100, 128, 500, 512, 1000, 1024])
+def test_topk_negative_logits_every_register_width(n):
+    # all logits negative (the order keys flip their magnitude bits), exact
+    # (one-hot rows), for each number of register slots per lane (1 .. 16)
+    _, idx = _topk_case(3, n, 256, 341 + n, one_hot=True, negative=True, dup_cols=((1, n - 1),))
 
 
 @pytest.mark.parametrize("n", [10, 130, 1100, 1500])
