@@ -14,6 +14,10 @@ the pages, which print none for these steps):
                  w = RNE_f16(d * q)
   topk        -- Strata PR #109, "What" (router top-10 per token), ties to the
                  lower index
+  cast_bf16   -- Strata PR #109, "What" (the bf16 cast of the window's rows):
+                 fp32 to bf16, round to nearest, ties to even
+  sigmoid, gate -- Strata PR #109, "What" (the shared expert's scalar gate: a
+                 multi-row GEMV, then a sigmoid): gate = 1 / (1 + e^-(a . w))
 """
 import ctypes
 import os
@@ -49,6 +53,12 @@ def _load():
     lib.oracle_mm.restype = ctypes.c_int
     lib.oracle_topk.argtypes = [i64, i64, vp, i64, i32, vp, vp]
     lib.oracle_topk.restype = ctypes.c_int
+    lib.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
+    lib.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_cast_f32_bf16.argtypes = [i64, vp, vp]
+    lib.oracle_cast_f32_bf16.restype = None
+    lib.oracle_sigmoid.argtypes = [i64, vp, vp]
+    lib.oracle_sigmoid.restype = None
     _lib = lib
     return lib
 
@@ -136,3 +146,29 @@ def topk(logits: np.ndarray, k: int):
     if rc != 0:
         raise ValueError(f"oracle_topk failed ({rc})")
     return idx, val
+
+
+def f64_to_bf16_rne(x: float) -> int:
+    return int(_load().oracle_f64_to_bf16_rne(float(x)))
+
+
+def cast_bf16(x: np.ndarray) -> np.ndarray:
+    """bf16 bits of every fp32 value of x, rounded to nearest, ties to even."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=np.uint16)
+    _load().oracle_cast_f32_bf16(x.size, _ptr(x), _ptr(out))
+    return out
+
+
+def sigmoid(x: np.ndarray) -> np.ndarray:
+    """fp64 1 / (1 + e^-x), elementwise."""
+    x = np.ascontiguousarray(x, dtype=np.float64)
+    y = np.empty(x.shape, dtype=np.float64)
+    _load().oracle_sigmoid(x.size, _ptr(x), _ptr(y))
+    return y
+
+
+def gate(A_f32: np.ndarray, W: np.ndarray, w_kind: str = "bf16", threads=None) -> np.ndarray:
+    """The scalar gate over fp32 rows: sigmoid(cast_bf16(A) . W) in fp64,
+    W stored [n][k] (n = 1 for a scalar gate)."""
+    return sigmoid(mm(cast_bf16(A_f32), "bf16", W, w_kind, threads=threads))

@@ -32,6 +32,11 @@
  *   - top-k: the Strata PR #109 page ("What", router bullet) takes a per-row
  *     top-10 of the router logits; ordered by value descending, equal values
  *     (IEEE ==, so -0 == +0) by lower index first.
+ *   - the window-row cast and the scalar gate: the Strata PR #109 page
+ *     ("What", the bf16 cast and shared-expert gate bullets) casts the
+ *     window's fp32 rows to bf16 and gates the shared expert with a
+ *     multi-row GEMV followed by a sigmoid; the cast rounds to nearest, ties
+ *     to even, and the sigmoid is the logistic function 1 / (1 + e^-x).
  */
 #include <math.h>
 #include <pthread.h>
@@ -125,6 +130,58 @@ uint16_t oracle_f64_to_f16_rne(double x) {
   }
   if (exp_field >= 31) return sign | 0x7c00;
   return sign | (uint16_t)((exp_field << 10) | (ri - 1024));
+}
+
+/* bfloat16 round to nearest, ties to even, by the same method as the f16
+ * encoder above.  bfloat16 keeps binary32's exponent range: normals from
+ * 2^-126 with 8 significant bits (spacing 2^(E-7) in [2^E, 2^(E+1))),
+ * subnormals with the fixed spacing 2^-133, largest finite (2 - 2^-7) * 2^127;
+ * anything that rounds past it is infinity. */
+uint16_t oracle_f64_to_bf16_rne(double x) {
+  uint16_t sign = signbit(x) ? 0x8000 : 0;
+  double ax = fabs(x);
+  if (isnan(x)) return 0x7fc0;
+  if (isinf(x)) return sign | 0x7f80;
+  if (ax == 0.0) return sign;
+
+  int e2;
+  (void)frexp(ax, &e2);
+  int E = e2 - 1;       /* ax in [2^E, 2^(E+1)) */
+  int quantum_exp = (E < -126) ? -133 : E - 7;
+  double units = ldexp(ax, -quantum_exp);
+  double lo = floor(units);
+  double frac = units - lo;
+  double r;
+  if (frac > 0.5) {
+    r = lo + 1.0;
+  } else if (frac < 0.5) {
+    r = lo;
+  } else {
+    r = (fmod(lo, 2.0) == 0.0) ? lo : lo + 1.0; /* tie: to even */
+  }
+  if (E < -126) {
+    /* r in [0, 128]; 128 is 2^-126, the smallest normal, pattern 0x0080 */
+    return sign | (uint16_t)r;
+  }
+  int exp_field = E + 127;
+  int ri = (int)r;   /* in [128, 256]; 256 carries into the next binade */
+  if (ri == 256) {
+    ri = 128;
+    exp_field += 1;
+  }
+  if (exp_field >= 255) return sign | 0x7f80;
+  return sign | (uint16_t)((exp_field << 7) | (ri - 128));
+}
+
+/* The window-row cast: out[i] = RNE_bf16(in[i]) for binary32 inputs (each is
+ * exact in fp64, so rounding the fp64 value is rounding the fp32 value). */
+void oracle_cast_f32_bf16(int64_t count, const float* in, uint16_t* out) {
+  for (int64_t i = 0; i < count; ++i) out[i] = oracle_f64_to_bf16_rne((double)in[i]);
+}
+
+/* The scalar gate's nonlinearity, elementwise: y[i] = 1 / (1 + e^-x[i]). */
+void oracle_sigmoid(int64_t count, const double* x, double* y) {
+  for (int64_t i = 0; i < count; ++i) y[i] = 1.0 / (1.0 + exp(-x[i]));
 }
 
 /* ---------------------------------------------------------------------------

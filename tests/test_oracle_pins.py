@@ -303,3 +303,77 @@ def test_topk_matches_python_sorted_with_many_ties():
             order = sorted(range(n), key=lambda j: (-logits[r, j], j))[:k]
             assert gi[r].tolist() == order
             assert np.array_equal(gv[r], logits[r, order])
+
+
+# --- the window-row cast and the scalar gate (Strata PR #109, "What": the bf16
+# cast of the window's rows; the shared expert's gate, a GEMV then a sigmoid)
+
+def _f32(bits):
+    return np.asarray(bits, dtype=np.uint32).view(np.float32)
+
+
+@pytest.mark.parametrize("value,bits", [
+    (1.0, 0x3F80),
+    (1.0 + 2.0 ** -8, 0x3F80),                  # halfway between 1 and 1 + 2^-7: to even
+    (1.0 + 3 * 2.0 ** -8, 0x3F82),              # halfway, odd lower neighbour: up
+    (1.0 + 2.0 ** -8 + 2.0 ** -20, 0x3F81),     # just above halfway: up
+    (-(1.0 + 2.0 ** -8), 0xBF80),
+    (-0.0, 0x8000),
+    (2.0 ** -133, 0x0001),                      # smallest subnormal
+    (2.0 ** -134, 0x0000),                      # halfway between 0 and it: to even (0)
+    (3 * 2.0 ** -134, 0x0002),                  # halfway between 1 and 2 units: to even (2)
+    (2.0 ** -126 - 2.0 ** -134, 0x0080),        # rounds up into the first normal
+    ((2 - 2.0 ** -7) * 2.0 ** 127, 0x7F7F),     # largest finite
+    ((2 - 2.0 ** -8) * 2.0 ** 127, 0x7F80),     # halfway past it, odd: to infinity
+    (float(np.finfo(np.float32).max), 0x7F80),
+])
+def test_bf16_rne_hand_values(value, bits):
+    assert oracle.f64_to_bf16_rne(value) == bits
+    assert oracle.cast_bf16(np.array([value], np.float32))[0] == bits
+
+
+def test_bf16_cast_keeps_every_finite_bf16_value():
+    # each finite bf16 value, widened to fp32 by numpy's bit placement, casts back to itself
+    pats = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((pats >> 7) & 0xFF) != 0xFF
+    x = (pats.astype(np.uint32) << 16).view(np.float32)
+    got = oracle.cast_bf16(x)
+    assert np.array_equal(got[finite], pats[finite])
+
+
+def test_bf16_cast_matches_torch_cpu_rne():
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(77)
+    raw = rng.integers(0, 2 ** 32, 200_000, dtype=np.uint64).astype(np.uint32)
+    raw = raw[((raw >> 23) & 0xFF) != 0xFF]  # finite fp32 patterns of every size
+    mags = np.ldexp(rng.random(50_000) + 0.5, rng.integers(-140, 128, 50_000)) * rng.choice([-1, 1], 50_000)
+    x = np.concatenate([_f32(raw), mags.astype(np.float32)])
+    want = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(oracle.cast_bf16(x), want)
+
+
+def test_sigmoid_closed_forms_and_library():
+    special = pytest.importorskip("scipy.special")
+    assert oracle.sigmoid(np.array([0.0]))[0] == 0.5
+    l3 = math.log(3.0)
+    y = oracle.sigmoid(np.array([l3, -l3]))
+    assert abs(y[0] - 0.75) < 1e-15 and abs(y[1] - 0.25) < 1e-15
+    x = np.random.default_rng(5).normal(0, 8, 10_000)
+    y, yn = oracle.sigmoid(x), oracle.sigmoid(-x)
+    assert np.max(np.abs(y + yn - 1.0)) < 1e-15
+    assert np.max(np.abs(y - special.expit(x))) < 1e-15
+    assert np.all(np.diff(oracle.sigmoid(np.sort(x))) >= 0)  # monotone
+
+
+def test_gate_hand_example():
+    # row 0: the cast drops 2^-8 from the first value, so a . w = 1 exactly;
+    # row 1: a . w = 0, the gate is one half; row 2: -ln-free check, 3 - 3 = 0
+    one_bf16 = 0x3F80
+    w = np.array([[one_bf16, 0x3F00, 0x4000, 0x4040, 0, 0, 0, 0]], np.uint16)  # 1, 0.5, 2, 3
+    A = np.array([[1 + 2.0 ** -8, 2.0, -0.5, 0.0, 9.0, 9.0, 9.0, 9.0],
+                  [1.0, 0.0, -0.5, 0.0, 0.0, 0.0, 0.0, 0.0],
+                  [0.0, 6.0, 0.0, -1.0, 0.0, 0.0, 0.0, 0.0]], np.float32)
+    g = oracle.gate(A, w)
+    assert g.shape == (3, 1)
+    assert abs(g[0, 0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
+    assert g[1, 0] == 0.5 and g[2, 0] == 0.5
