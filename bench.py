@@ -189,7 +189,10 @@ class Inputs:
             t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
             return t.view(torch.bfloat16 if kind == "bf16" else torch.float16).cuda()
 
-        self.A = dev16(A, wl.a_kind)
+        if wl.a_kind == "f32":
+            self.A = torch.from_numpy(np.ascontiguousarray(A, dtype=np.float32)).cuda()
+        else:
+            self.A = dev16(A, wl.a_kind)
         copies = max(2, int(pool_bytes // max(1, wl.w_bytes)))
         if wl.w_kind == "q8_0":
             qs, d = W
@@ -203,7 +206,8 @@ class Inputs:
 
 
 def dtype_codes(sk, wl):
-    a = sk.BF16 if wl.a_kind == "bf16" else sk.F16
+    # fp32 rows (the gate) reach the GEMV through the bf16 cast launch
+    a = sk.BF16 if wl.a_kind in ("bf16", "f32") else sk.F16
     w = {"f16": sk.F16, "bf16": sk.BF16, "q8_0": sk.Q8_0}[wl.w_kind]
     c = sk.F32 if wl.c_kind == "f32" else sk.F16
     return a, w, c
@@ -212,7 +216,8 @@ def dtype_codes(sk, wl):
 def call_bytes(wl, m, with_topk=False):
     """Algorithmic HBM bytes of one call: the weight once, A once, C once."""
     c_elem = 4 if wl.c_kind == "f32" else 2
-    b = wl.w_bytes + m * wl.k * 2 + m * wl.n * c_elem
+    a_elem = 4 if wl.a_kind == "f32" else 2
+    b = wl.w_bytes + m * wl.k * a_elem + m * wl.n * c_elem
     if with_topk:
         b += m * TOPK * 8
     return b
@@ -311,18 +316,26 @@ def sweep(sk, torch, rounds):
     for name, wl in WL.WORKLOADS.items():
         inp = Inputs(wl, torch, max(wl.ms))
         a, w, c = dtype_codes(sk, wl)
-        plan = sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c)
+        gate = wl.a_kind == "f32"  # the scalar gate: cast launch + GEMV with the sigmoid
+        plan = sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c, flags=sk.EPILOGUE_SIGMOID if gate else 0)
         ws = plan.workspace(inp.A.device)
         cdt = torch.float32 if wl.c_kind == "f32" else torch.float16
         graphs = {}
         keep = []  # every tensor a captured graph touches, alive until the graphs go
+        if gate:
+            A16 = torch.empty((max(wl.ms), wl.k), dtype=torch.bfloat16, device="cuda")
+            keep.append(A16)
         for m in wl.ms:
             C = torch.empty((m, wl.n), dtype=cdt, device="cuda")
             keep.append(C)
             Am = inp.A[:m]
             L = min(len(inp.W), 256)
 
-            if wl.w_kind == "q8_0":
+            if gate:
+                def fn(i, m=m, C=C, Am=Am):
+                    sk.cast_f32_bf16(Am, out=A16[:m])
+                    plan.run(m, A16[:m], inp.W[i % len(inp.W)], C, workspace=ws)
+            elif wl.w_kind == "q8_0":
                 def fn(i, m=m, C=C, Am=Am):
                     qs, d = inp.W[i % len(inp.W)]
                     plan.run(m, Am, qs, C, scales=d, workspace=ws)

@@ -89,6 +89,14 @@ typedef enum skinny_dtype {
  * tile that cannot hold two accumulator sets falls back to the first. */
 #define SKINNY_GEMM_SPLIT_LAUNCH 0x4u
 #define SKINNY_GEMM_ONE_LAUNCH 0x8u
+/* C = sigmoid(A . W) elementwise, sigmoid(x) = 1 / (1 + e^-x) in fp32 (the
+ * Strata PR #109 page, "What": the shared expert's scalar gate is a
+ * multi-row GEMV followed by a sigmoid; here the sigmoid is applied as the
+ * GEMV stores each output, so no second launch runs).  GEMV regime only: the
+ * plan needs max_m <= 16 and no SKINNY_FORCE_GEMM (else
+ * SKINNY_ERR_UNSUPPORTED), and gemv_topk_run rejects such a plan.  The
+ * sigmoid acts on each output alone, so row invariance holds. */
+#define SKINNY_EPILOGUE_SIGMOID 0x10u
 
 #define SKINNY_GEMV_MAX_M 16
 #define SKINNY_TOPK_MAX 32
@@ -138,12 +146,17 @@ SKINNY_API void skinny_mm_plan_destroy(skinny_plan* plan);
 
 /* Bytes of device workspace a run with this plan may need (0 when none);
  * enough for every m <= max_m, for skinny_mm_run and gemv_topk_run alike.
- * Only a GEMV whose k is split into more pieces than one workgroup sums
- * (k > 8192 for 16-bit weights) needs it: it holds that GEMV's fp32 partial
- * sums and the arrival counters that let the last wave of each column range
- * finish the sum inside the same kernel.  It must be zero-filled once before
- * its first use; every completed run leaves it ready for the next (its
- * counters back at zero).  A run that needs no workspace ignores it. */
+ * Two runs need it:
+ *   - a GEMV whose k is split into more pieces than one workgroup sums
+ *     (k > 8192 for 16-bit weights): it holds the arrival counters (first)
+ *     and the fp32 partial sums that let the last wave of each column range
+ *     finish the sum inside the same kernel;
+ *   - a GEMM whose plan cuts k into chunks (narrow n) and runs them as one
+ *     block per chunk: it holds the chunks' fp32 partial sums, which an
+ *     ordered reduce launch adds.
+ * It must be zero-filled once before its first use; every completed run
+ * leaves it ready for the next (its counters back at zero).  A run that needs
+ * no workspace ignores it. */
 SKINNY_API skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_t* bytes);
 
 /* C[0:m, 0:n] = A[0:m, :] . W  (nx_batchscale_kat: the product with fp32
@@ -182,6 +195,14 @@ SKINNY_API skinny_status gemv_topk_run(const skinny_plan* plan, int64_t m, const
  *   out f16 [n][k]; all device pointers, 16-byte aligned. */
 SKINNY_API skinny_status skinny_dequant_q8_0_run(int64_t n, int64_t k, const void* qs, const void* d,
                                       void* out, void* stream);
+
+/* The window-row cast (the Strata PR #109 page, "What": the window's fp32
+ * rows are cast to bf16 in one call, the rows being contiguous):
+ * out[i] = RNE_bf16(in[i]) for 0 <= i < count, round to nearest, ties to
+ * even; a NaN becomes a quiet NaN.  The result feeds a bf16 plan's A.
+ *   1 <= count <= 2^40; in: f32 [count], out: bf16 [count]; device pointers,
+ *   16-byte aligned, not overlapping (else SKINNY_ERR_INVALID_ARG). */
+SKINNY_API skinny_status skinny_cast_f32_bf16_run(int64_t count, const float* in, void* out, void* stream);
 
 /* Human-readable description of what a run with this m would launch: path,
  * tile or GEMV split, grid.  Writes a NUL-terminated string (truncated to

@@ -36,13 +36,14 @@ _lib = ctypes.CDLL(LIB_PATH)
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_SHAPE, ERR_HIP, ERR_WORKSPACE = range(7)
 F16, BF16, F32, Q8_0 = 1, 2, 3, 4
 FORCE_GEMV, FORCE_GEMM, GEMM_SPLIT_LAUNCH, GEMM_ONE_LAUNCH = 0x1, 0x2, 0x4, 0x8
+EPILOGUE_SIGMOID = 0x10
 GEMV_MAX_M = 16
 TOPK_MAX = 32
 
 EXPORTS = (
     "skinny_mm_plan", "skinny_mm_plan_destroy", "skinny_mm_workspace_size", "skinny_mm_run",
     "gemv_topk_run", "skinny_dequant_q8_0_run", "skinny_mm_plan_info", "skinny_gemm_tile_count",
-    "skinny_gemm_tile_name", "skinny_status_string", "skinny_abi_version",
+    "skinny_gemm_tile_name", "skinny_status_string", "skinny_abi_version", "skinny_cast_f32_bf16_run",
 )
 
 
@@ -76,6 +77,8 @@ _lib.gemv_topk_run.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _v
 _lib.gemv_topk_run.restype = ctypes.c_int
 _lib.skinny_dequant_q8_0_run.argtypes = [_i64, _i64, _vp, _vp, _vp, _vp]
 _lib.skinny_dequant_q8_0_run.restype = ctypes.c_int
+_lib.skinny_cast_f32_bf16_run.argtypes = [_i64, _vp, _vp, _vp]
+_lib.skinny_cast_f32_bf16_run.restype = ctypes.c_int
 _lib.skinny_mm_plan_info.argtypes = [_vp, _i64, ctypes.c_char_p, _sz]
 _lib.skinny_mm_plan_info.restype = ctypes.c_int
 _lib.skinny_gemm_tile_count.argtypes = []
@@ -270,4 +273,34 @@ def dequant_q8_0(qs, d, out=None, stream=None):
         out = torch.empty((n, k), dtype=torch.float16, device=qs.device)
     _check(_lib.skinny_dequant_q8_0_run(n, k, _ptr(qs), _ptr(d), _ptr(out), _stream(stream)),
            "skinny_dequant_q8_0_run")
+    return out
+
+
+def cast_f32_bf16(x, out=None, stream=None):
+    """bf16 copy of a contiguous fp32 tensor (round to nearest even), one launch."""
+    torch = _torch()
+    if x.dtype != torch.float32 or not x.is_contiguous():
+        raise TypeError("cast_f32_bf16 takes a contiguous float32 tensor")
+    if out is None:
+        out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
+    _check(_lib.skinny_cast_f32_bf16_run(x.numel(), _ptr(x), _ptr(out), _stream(stream)),
+           "skinny_cast_f32_bf16_run")
+    return out
+
+
+def gate(A, W, max_m=None, out=None, stream=None):
+    """Scalar gate of fp32 window rows: sigmoid(bf16(A) . W) for A [m][k] fp32
+    and W bf16 [n][k] (n = 1 for one gate per row): the cast launch, then the
+    GEMV with the sigmoid applied as it stores."""
+    torch = _torch()
+    m, k = A.shape
+    n = W.shape[0]
+    A16 = cast_f32_bf16(A, stream=stream)
+    if stream is not None:
+        A16.record_stream(stream)  # the temporary lives until the GEMV on that stream ran
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=A.device)
+    plan = get_plan(n, k, max_m or m, BF16, _dtype_code(W.dtype, "W"), _dtype_code(out.dtype, "C"),
+                    EPILOGUE_SIGMOID)
+    plan.run(m, A16, W, out, stream=stream)
     return out

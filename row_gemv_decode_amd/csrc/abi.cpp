@@ -262,6 +262,7 @@ GemvArgs gemv_args(const skinny_plan* p, const void* A, const void* W, const voi
   g.cg_per_block = 0;
   g.C = C;
   g.ldc = ldc;
+  g.epilogue = (p->d.flags & SKINNY_EPILOGUE_SIGMOID) ? kEpiSigmoid : kEpiNone;
   const int64_t mm = p->d.max_m < kGemvMaxM ? p->d.max_m : kGemvMaxM;
   char* ws = (char*)workspace;
   g.counters = (ws != nullptr && gemv_global_split(p)) ? (uint32_t*)ws : nullptr;
@@ -404,7 +405,11 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   if (d.ldc == 0) d.ldc = d.n;
   if (d.lda < d.k || d.ldc < d.n) return SKINNY_ERR_SHAPE;
   if (d.lda % 8 != 0) return SKINNY_ERR_ALIGNMENT;  // A rows are read 16 bytes at a time
-  if (d.flags & ~(SKINNY_FORCE_GEMV | SKINNY_FORCE_GEMM | SKINNY_GEMM_SPLIT_LAUNCH | SKINNY_GEMM_ONE_LAUNCH))
+  if (d.flags & ~(SKINNY_FORCE_GEMV | SKINNY_FORCE_GEMM | SKINNY_GEMM_SPLIT_LAUNCH | SKINNY_GEMM_ONE_LAUNCH |
+                  SKINNY_EPILOGUE_SIGMOID))
+    return SKINNY_ERR_UNSUPPORTED;
+  // the gate's sigmoid is applied by the GEMV only
+  if ((d.flags & SKINNY_EPILOGUE_SIGMOID) && (d.max_m > kGemvMaxM || (d.flags & SKINNY_FORCE_GEMM)))
     return SKINNY_ERR_UNSUPPORTED;
   if ((d.flags & SKINNY_GEMM_SPLIT_LAUNCH) && (d.flags & SKINNY_GEMM_ONE_LAUNCH)) return SKINNY_ERR_INVALID_ARG;
   if ((d.flags & SKINNY_FORCE_GEMV) && (d.flags & SKINNY_FORCE_GEMM)) return SKINNY_ERR_INVALID_ARG;
@@ -477,7 +482,7 @@ skinny_status gemv_topk_run(const skinny_plan* plan, int64_t m, const void* A, c
                             size_t workspace_bytes, void* stream) {
   skinny_status st = check_run(plan, m, A, W, w_scales, logits, workspace, workspace_bytes);
   if (st != SKINNY_OK) return st;
-  if (plan->d.c_dtype != SKINNY_F32) return SKINNY_ERR_UNSUPPORTED;
+  if (plan->d.c_dtype != SKINNY_F32 || (plan->d.flags & SKINNY_EPILOGUE_SIGMOID)) return SKINNY_ERR_UNSUPPORTED;
   if (topk_idx == nullptr || topk_val == nullptr) return SKINNY_ERR_INVALID_ARG;
   if (topk < 1 || topk > SKINNY_TOPK_MAX || topk > plan->d.n) return SKINNY_ERR_INVALID_ARG;
   if (!aligned16(topk_idx) || !aligned16(topk_val)) return SKINNY_ERR_ALIGNMENT;
@@ -495,6 +500,14 @@ skinny_status skinny_dequant_q8_0_run(int64_t n, int64_t k, const void* qs, cons
                                         (hipStream_t)stream));
 }
 
+skinny_status skinny_cast_f32_bf16_run(int64_t count, const float* in, void* out, void* stream) {
+  if (in == nullptr || out == nullptr || count < 1 || count > (1LL << 40)) return SKINNY_ERR_INVALID_ARG;
+  const uintptr_t i0 = reinterpret_cast<uintptr_t>(in), o0 = reinterpret_cast<uintptr_t>(out);
+  if (i0 < o0 + (uintptr_t)count * 2 && o0 < i0 + (uintptr_t)count * 4) return SKINNY_ERR_INVALID_ARG;
+  if (!aligned16(in) || !aligned16(out)) return SKINNY_ERR_ALIGNMENT;
+  return hip_status(launch_cast_f32_bf16(count, in, (uint16_t*)out, (hipStream_t)stream));
+}
+
 skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf, size_t len) {
   if (plan == nullptr || buf == nullptr || len == 0) return SKINNY_ERR_INVALID_ARG;
   if (m < 1 || m > plan->d.max_m) return SKINNY_ERR_INVALID_ARG;
@@ -503,10 +516,11 @@ skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf,
     const GemvBlock b = gemv_block(plan);
     std::snprintf(buf, len,
                   "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld x %d waves split_reduce=%s "
-                  "workspace=%zu",
+                  "%sworkspace=%zu",
                   (long long)m, plan->gemv_T, plan->gemv_S, plan->gemv_cpw, (long long)waves,
                   (long long)gemv_blocks(plan, b), b.waves,
                   plan->gemv_S == 1 ? "none" : (gemv_global_split(plan) ? "global" : "in-block"),
+                  (plan->d.flags & SKINNY_EPILOGUE_SIGMOID) ? "epilogue=sigmoid " : "",
                   workspace_bytes_for(plan, m));
   } else {
     const GemmChoice gc = choose_gemm(plan, m);

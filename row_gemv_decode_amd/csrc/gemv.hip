@@ -191,6 +191,37 @@ __global__ __launch_bounds__(64) void topk_rows_kernel(const float* __restrict__
   }
 }
 
+// --- window-row cast: fp32 -> bf16, round to nearest even --------------------
+// Eight values per thread and step: two 16-byte loads, one 16-byte store; the
+// count % 8 tail is converted one value per thread by the first workgroup.
+// The conversion is the compiler's float -> __bf16, the same one the bf16
+// output path of every kernel uses.
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void cast_f32_bf16_kernel(const float* __restrict__ in,
+                                                            uint16_t* __restrict__ out, int64_t count) {
+  const int64_t groups = count >> 3;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < groups; e += (int64_t)gridDim.x * 256) {
+    const f32x4 lo = *(const f32x4*)(in + e * 8);
+    const f32x4 hi = *(const f32x4*)(in + e * 8 + 4);
+    b8_t v;
+    v[0] = (__bf16)lo[0];
+    v[1] = (__bf16)lo[1];
+    v[2] = (__bf16)lo[2];
+    v[3] = (__bf16)lo[3];
+    v[4] = (__bf16)hi[0];
+    v[5] = (__bf16)hi[1];
+    v[6] = (__bf16)hi[2];
+    v[7] = (__bf16)hi[3];
+    *(u32x4*)(out + e * 8) = __builtin_bit_cast(u32x4, v);
+  }
+  const int64_t tail = count - (groups << 3);
+  if (blockIdx.x == 0 && (int64_t)threadIdx.x < tail) {
+    const int64_t i = (groups << 3) + threadIdx.x;
+    ((__bf16*)out)[i] = (__bf16)in[i];
+  }
+}
+
 // --- standalone dequant ----------------------------------------------------
 __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const int8_t* __restrict__ qs,
                                                            const uint16_t* __restrict__ d,
@@ -230,6 +261,15 @@ hipError_t launch_topk(const float* logits, int m, int64_t n, int64_t ldl, int32
                      : n <= 1024 ? topk_rows_kernel<16>
                                  : topk_rows_kernel<0>;
   hipLaunchKernelGGL(fn, dim3((unsigned)m), dim3(64), 0, stream, logits, n, ldl, idx, val, topk);
+  return hipGetLastError();
+}
+
+hipError_t launch_cast_f32_bf16(int64_t count, const float* in, uint16_t* out, hipStream_t stream) {
+  const int64_t groups = count >> 3;
+  int64_t blocks = (groups + 255) / 256;
+  if (blocks < 1) blocks = 1;
+  if (blocks > 2048) blocks = 2048;
+  hipLaunchKernelGGL(cast_f32_bf16_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, in, out, count);
   return hipGetLastError();
 }
 

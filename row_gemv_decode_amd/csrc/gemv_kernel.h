@@ -164,6 +164,13 @@ __device__ __forceinline__ float wave_tree(float (&v)[NV], int lane, int& idx) {
   return v[0];
 }
 
+// the value stored for a finished sum: the sum itself, or the scalar gate's
+// sigmoid of it (an IEEE divide of 1 by 1 + e^-x; the exponential is the
+// device library's expf)
+__device__ __forceinline__ float gemv_finish(const GemvArgs& g, float sum) {
+  return g.epilogue == kEpiSigmoid ? 1.0f / (1.0f + expf(-sum)) : sum;
+}
+
 template <int WK>
 __device__ __forceinline__ float dot8(const u32x4& a, const u32x4& w, float acc) {
 #pragma unroll
@@ -370,7 +377,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
       if (writer_lane && idx < P && c0 + gi < ncol) {
         const int64_t j = j0 + c0 + gi;
         if (g.S == 1) {
-          store_out<CK>(g.C, (int64_t)r * g.ldc + j, sum);
+          store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish(g, sum));
         } else if (in_block) {
           red[(wave * kGemvCpwMax + c0 + gi) * M + r] = sum;
         } else {
@@ -391,7 +398,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
           const int64_t j = j0 + (e - r * ncol);
           float acc = ld_dev(g.partial + (int64_t)r * g.n + j);
           for (int q = 1; q < g.S; ++q) acc += ld_dev(g.partial + ((int64_t)q * M + r) * g.n + j);
-          store_out<CK>(g.C, (int64_t)r * g.ldc + j, acc);
+          store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish(g, acc));
         }
         if (lane == 0) g.counters[wc] = 0u;  // ready for the next call
       }
@@ -410,7 +417,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
       const int w0 = cg * g.S;
       float acc = red[(w0 * kGemvCpwMax + c) * M + r];
       for (int q = 1; q < g.S; ++q) acc += red[((w0 + q) * kGemvCpwMax + c) * M + r];
-      store_out<CK>(g.C, (int64_t)r * g.ldc + j, acc);
+      store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish(g, acc));
     }
   }
 }

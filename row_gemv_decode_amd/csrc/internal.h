@@ -43,7 +43,11 @@ struct GemvArgs {
   float* partial;           // [S][m][n] fp32 partial sums (S > kGemvBlockSplitMax)
   uint32_t* counters;       // [waves_per_split] arrivals per column range (S > kGemvBlockSplitMax),
                             // zero between calls
+  int32_t epilogue;         // kEpiNone, or kEpiSigmoid: C = 1 / (1 + e^-sum)
 };
+
+constexpr int kEpiNone = 0;
+constexpr int kEpiSigmoid = 1;
 
 // out_kind: 0 f32, 1 f16, 2 bf16 (C)
 hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_kind,
@@ -53,6 +57,9 @@ hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_k
 // row (blockIdx.x = row).
 hipError_t launch_topk(const float* logits, int m, int64_t n, int64_t ldl, int32_t* idx, float* val,
                        int topk, hipStream_t stream);
+
+// out[i] = bf16(in[i]) (round to nearest even) for i < count
+hipError_t launch_cast_f32_bf16(int64_t count, const float* in, uint16_t* out, hipStream_t stream);
 
 hipError_t launch_dequant_q8_0(int64_t n, int64_t k, const int8_t* qs, const uint16_t* d,
                                uint16_t* out, hipStream_t stream);

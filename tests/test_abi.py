@@ -42,7 +42,7 @@ def plan_status(**fields):
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 11, names
+    assert len(names) == 12, names
     assert set(names) == set(sk.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -82,7 +82,10 @@ def test_tile_table():
     (dict(lda=800), sk.ERR_SHAPE),
     (dict(lda=900), sk.ERR_ALIGNMENT),
     (dict(ldc=100), sk.ERR_SHAPE),
-    (dict(flags=0x10), sk.ERR_UNSUPPORTED),
+    (dict(flags=0x20), sk.ERR_UNSUPPORTED),
+    (dict(flags=sk.EPILOGUE_SIGMOID), sk.OK),                          # the gate: GEMV regime
+    (dict(flags=sk.EPILOGUE_SIGMOID, max_m=17), sk.ERR_UNSUPPORTED),  # the GEMM has no sigmoid
+    (dict(flags=sk.EPILOGUE_SIGMOID | sk.FORCE_GEMM), sk.ERR_UNSUPPORTED),
     (dict(flags=sk.FORCE_GEMV | sk.FORCE_GEMM), sk.ERR_INVALID_ARG),
     (dict(flags=sk.FORCE_GEMV, max_m=17), sk.ERR_INVALID_ARG),
     (dict(tile_id=13), sk.ERR_INVALID_ARG),
@@ -295,6 +298,29 @@ def test_topk_validation():
     assert topk_run(small, 1, k=9) == sk.ERR_INVALID_ARG   # topk > n
     f16out = plan(n=256, k=5120, a=sk.BF16, w=sk.BF16, c=sk.F16)
     assert topk_run(f16out, 1) == sk.ERR_UNSUPPORTED
+    gated = plan(n=256, k=5120, a=sk.BF16, w=sk.BF16, flags=sk.EPILOGUE_SIGMOID)
+    assert topk_run(gated, 1) == sk.ERR_UNSUPPORTED      # no top-k of gate values
+
+
+@fake_pointers
+def test_cast_validation():
+    f = L.skinny_cast_f32_bf16_run
+    assert f(0, P16, P16b, None) == sk.ERR_INVALID_ARG
+    assert f((1 << 40) + 1, P16, P16b, None) == sk.ERR_INVALID_ARG
+    assert f(8, None, P16b, None) == sk.ERR_INVALID_ARG
+    assert f(8, P16, None, None) == sk.ERR_INVALID_ARG
+    assert f(8, ODD, P16b, None) == sk.ERR_ALIGNMENT
+    assert f(8, P16, ctypes.c_void_p((2 << 20) + 2), None) == sk.ERR_ALIGNMENT
+    base = 1 << 20
+    # overlapping ranges: in [base, base + 4 * count), out [o, o + 2 * count)
+    assert f(64, ctypes.c_void_p(base), ctypes.c_void_p(base + 128), None) == sk.ERR_INVALID_ARG
+    assert f(64, ctypes.c_void_p(base + 96), ctypes.c_void_p(base), None) == sk.ERR_INVALID_ARG
+
+
+def test_gate_plan_info():
+    g = plan(n=1, k=5120, a=sk.BF16, w=sk.BF16, flags=sk.EPILOGUE_SIGMOID)
+    assert " epilogue=sigmoid " in g.info(16) and "path=gemv" in g.info(16)
+    assert "epilogue" not in plan(n=1, k=5120, a=sk.BF16, w=sk.BF16).info(1)
 
 
 @fake_pointers

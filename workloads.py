@@ -19,6 +19,9 @@ The five workloads stand in for the pages' measurements:
   wide_n7680    -- opus r35 track A, section 2, big-N GEMMs with ragged M.
   q8_0_n512     -- opus r35 track A, section 1: a 512 x 2560 block-quantised
                    weight (the router that `dq_f16` dequantises), Q8_0-style.
+  scalar_gate   -- Strata PR #109 ("What"): the shared expert's scalar gate over
+                   the window's fp32 rows (n = 1, the router's k = 5120); the
+                   rows are kept in fp32 (A ~N(0,1) stored as float32).
 No dataset, prompt or model from the pages exists here or is recreated.
 """
 from dataclasses import dataclass
@@ -33,7 +36,7 @@ class Workload:
     index: int          # seed base c (seeds 1000*c + {0,1,2})
     n: int              # output columns (rows of the stored [n][k] weight)
     k: int              # reduction length
-    a_kind: str         # "f16" | "bf16"
+    a_kind: str         # "f16" | "bf16" | "f32"
     w_kind: str         # "f16" | "bf16" | "q8_0"
     c_kind: str         # "f32" | "f16"
     ms: Tuple[int, ...]  # row counts swept
@@ -60,6 +63,8 @@ WORKLOADS = {
                  (150, 192, 306, 448, 520, 700, 1050, 1983, 2048), ("normal", 0.02)),
         Workload("q8_0_n512", 4, 512, 2560, "f16", "q8_0", "f16", (1, 4, 16, 306, 2048),
                  ("q8_0", 1e-3, 2e-3)),
+        Workload("scalar_gate", 5, 1, 5120, "f32", "bf16", "f32", (1, 2, 4, 8, 16),
+                 ("normal", 0.02)),
     )
 }
 
@@ -78,6 +83,9 @@ def to_bf16_bits(x: np.ndarray) -> np.ndarray:
 
 
 def to_bits(x: np.ndarray, kind: str) -> np.ndarray:
+    """The storage form: f16 / bf16 bit patterns, or float32 values for "f32"."""
+    if kind == "f32":
+        return np.asarray(x, dtype=np.float32)
     return to_bf16_bits(x) if kind == "bf16" else to_f16_bits(x)
 
 
@@ -108,7 +116,7 @@ def gen_w(wl: Workload, n: Optional[int] = None):
 
 
 def gen_a(wl: Workload, rows: int) -> np.ndarray:
-    """A [rows][k] ~N(0,1) as bits.  Smaller m take a prefix of these rows, so the
+    """A [rows][k] ~N(0,1) as bits (float32 values for an "f32" workload).  Smaller m take a prefix of these rows, so the
     same token rows appear at every m."""
     return to_bits(draw((rows, wl.k), ("normal", 1.0), 1000 * wl.index + 1), wl.a_kind)
 
