@@ -135,8 +135,11 @@ def run_only(spec, steps, warmup):
     tile = int(parts[2]) if len(parts) > 2 else -1
     inp = Inputs(wl, torch, max(ms))
     a, w, c = dtype_codes(sk, wl)
-    plan = sk.Plan(wl.n, wl.k, max(max(ms), max(wl.ms)), a, w, c, tile_id=tile)
+    gate = wl.a_kind == "f32"  # the scalar gate: cast launch + GEMV with the sigmoid
+    plan = sk.Plan(wl.n, wl.k, max(max(ms), max(wl.ms)), a, w, c, tile_id=tile,
+                   flags=sk.EPILOGUE_SIGMOID if gate else 0)
     ws = plan.workspace(inp.A.device)
+    A16 = torch.empty((max(ms), wl.k), dtype=torch.bfloat16, device="cuda") if gate else None
     cdt = torch.float32 if wl.c_kind == "f32" else torch.float16
     outs = {m: (torch.empty((m, wl.n), dtype=cdt, device="cuda"),
                 torch.empty((m, TOPK), dtype=torch.int32, device="cuda"),
@@ -146,7 +149,10 @@ def run_only(spec, steps, warmup):
         m = ms[i % len(ms)]
         C, idx, val = outs[m]
         W = inp.W[i % len(inp.W)]
-        if wl.w_kind == "q8_0":
+        if gate:
+            sk.cast_f32_bf16(inp.A[:m], out=A16[:m])
+            plan.run(m, A16[:m], W, C, workspace=ws)
+        elif wl.w_kind == "q8_0":
             plan.run(m, inp.A[:m], W[0], C, scales=W[1], workspace=ws)
         elif wl.topk:
             plan.run_topk(m, inp.A[:m], W, C, idx, val, TOPK, workspace=ws)

@@ -92,8 +92,9 @@ typedef enum skinny_dtype {
 /* C = sigmoid(A . W) elementwise, sigmoid(x) = 1 / (1 + e^-x) in fp32 (the
  * Strata PR #109 page, "What": the shared expert's scalar gate is a
  * multi-row GEMV followed by a sigmoid; here the sigmoid is applied as the
- * GEMV stores each output, so no second launch runs).  GEMV regime only: the
- * plan needs max_m <= 16 and no SKINNY_FORCE_GEMM (else
+ * GEMV stores each output, so no second launch runs).  GEMV regime only, for
+ * the gate's bf16 weight: the plan needs max_m <= 16, no SKINNY_FORCE_GEMM,
+ * w_dtype SKINNY_BF16 and c_dtype SKINNY_F32 or SKINNY_F16 (else
  * SKINNY_ERR_UNSUPPORTED), and gemv_topk_run rejects such a plan.  The
  * sigmoid acts on each output alone, so row invariance holds. */
 #define SKINNY_EPILOGUE_SIGMOID 0x10u

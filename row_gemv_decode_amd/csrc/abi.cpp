@@ -408,8 +408,11 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   if (d.flags & ~(SKINNY_FORCE_GEMV | SKINNY_FORCE_GEMM | SKINNY_GEMM_SPLIT_LAUNCH | SKINNY_GEMM_ONE_LAUNCH |
                   SKINNY_EPILOGUE_SIGMOID))
     return SKINNY_ERR_UNSUPPORTED;
-  // the gate's sigmoid is applied by the GEMV only
-  if ((d.flags & SKINNY_EPILOGUE_SIGMOID) && (d.max_m > kGemvMaxM || (d.flags & SKINNY_FORCE_GEMM)))
+  // the gate's sigmoid is applied by the GEMV only, for bf16 weights and an
+  // f32 or f16 gate
+  if ((d.flags & SKINNY_EPILOGUE_SIGMOID) &&
+      (d.max_m > kGemvMaxM || (d.flags & SKINNY_FORCE_GEMM) || d.w_dtype != SKINNY_BF16 ||
+       d.c_dtype == SKINNY_BF16))
     return SKINNY_ERR_UNSUPPORTED;
   if ((d.flags & SKINNY_GEMM_SPLIT_LAUNCH) && (d.flags & SKINNY_GEMM_ONE_LAUNCH)) return SKINNY_ERR_INVALID_ARG;
   if ((d.flags & SKINNY_FORCE_GEMV) && (d.flags & SKINNY_FORCE_GEMM)) return SKINNY_ERR_INVALID_ARG;

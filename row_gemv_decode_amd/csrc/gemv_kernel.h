@@ -166,9 +166,15 @@ __device__ __forceinline__ float wave_tree(float (&v)[NV], int lane, int& idx) {
 
 // the value stored for a finished sum: the sum itself, or the scalar gate's
 // sigmoid of it (an IEEE divide of 1 by 1 + e^-x; the exponential is the
-// device library's expf)
-__device__ __forceinline__ float gemv_finish(const GemvArgs& g, float sum) {
-  return g.epilogue == kEpiSigmoid ? 1.0f / (1.0f + expf(-sum)) : sum;
+// device library's expf).  EPI is a template argument, so the plain kernels
+// carry no trace of the gate.
+template <int EPI>
+__device__ __forceinline__ float gemv_finish(float sum) {
+  if constexpr (EPI == kEpiSigmoid) {
+    return 1.0f / (1.0f + expf(-sum));
+  } else {
+    return sum;
+  }
 }
 
 template <int WK>
@@ -246,7 +252,7 @@ __device__ __forceinline__ u32x4 w_as_halves(const WChunk<WK>& w) {
 // The range counters live in the caller's workspace, start at zero and are
 // left at zero.
 // ---------------------------------------------------------------------------
-template <int M, int T, int WK, int CK, int G>
+template <int M, int T, int WK, int CK, int G, int EPI>
 __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(GemvArgs g) {
   using Shape = GemvShape<M, G>;
   constexpr int P = Shape::P;
@@ -377,7 +383,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
       if (writer_lane && idx < P && c0 + gi < ncol) {
         const int64_t j = j0 + c0 + gi;
         if (g.S == 1) {
-          store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish(g, sum));
+          store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish<EPI>(sum));
         } else if (in_block) {
           red[(wave * kGemvCpwMax + c0 + gi) * M + r] = sum;
         } else {
@@ -398,7 +404,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
           const int64_t j = j0 + (e - r * ncol);
           float acc = ld_dev(g.partial + (int64_t)r * g.n + j);
           for (int q = 1; q < g.S; ++q) acc += ld_dev(g.partial + ((int64_t)q * M + r) * g.n + j);
-          store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish(g, acc));
+          store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish<EPI>(acc));
         }
         if (lane == 0) g.counters[wc] = 0u;  // ready for the next call
       }
@@ -417,7 +423,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
       const int w0 = cg * g.S;
       float acc = red[(w0 * kGemvCpwMax + c) * M + r];
       for (int q = 1; q < g.S; ++q) acc += red[((w0 + q) * kGemvCpwMax + c) * M + r];
-      store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish(g, acc));
+      store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish<EPI>(acc));
     }
   }
 }
@@ -430,15 +436,32 @@ template <int M, int T, int WK>
 struct GemvRow {
   static constexpr int GM = gemv_group_max(M);
   static constexpr gemv_fn out[2][3] = {
-      {gemv_rows_kernel<M, T, WK, CK_F32, 1>, gemv_rows_kernel<M, T, WK, CK_F16, 1>,
-       gemv_rows_kernel<M, T, WK, CK_BF16, 1>},
-      {gemv_rows_kernel<M, T, WK, CK_F32, GM>, gemv_rows_kernel<M, T, WK, CK_F16, GM>,
-       gemv_rows_kernel<M, T, WK, CK_BF16, GM>}};
+      {gemv_rows_kernel<M, T, WK, CK_F32, 1, kEpiNone>, gemv_rows_kernel<M, T, WK, CK_F16, 1, kEpiNone>,
+       gemv_rows_kernel<M, T, WK, CK_BF16, 1, kEpiNone>},
+      {gemv_rows_kernel<M, T, WK, CK_F32, GM, kEpiNone>, gemv_rows_kernel<M, T, WK, CK_F16, GM, kEpiNone>,
+       gemv_rows_kernel<M, T, WK, CK_BF16, GM, kEpiNone>}};
+};
+
+// the scalar gate's kernels (sigmoid epilogue; f32 or f16 gate values)
+template <int M, int T, int WK>
+struct GemvGateRow {
+  static constexpr int GM = gemv_group_max(M);
+  static constexpr gemv_fn out[2][3] = {
+      {gemv_rows_kernel<M, T, WK, CK_F32, 1, kEpiSigmoid>, gemv_rows_kernel<M, T, WK, CK_F16, 1, kEpiSigmoid>,
+       nullptr},
+      {gemv_rows_kernel<M, T, WK, CK_F32, GM, kEpiSigmoid>, gemv_rows_kernel<M, T, WK, CK_F16, GM, kEpiSigmoid>,
+       nullptr}};
 };
 
 template <int T, int WK, int... Ms>
 gemv_fn gemv_pick(int m, int group, int out_kind) {
   const gemv_fn(*tbl[])[3] = {GemvRow<Ms, T, WK>::out...};
+  return tbl[m - 1][group][out_kind];
+}
+
+template <int T, int WK, int... Ms>
+gemv_fn gemv_pick_gate(int m, int group, int out_kind) {
+  const gemv_fn(*tbl[])[3] = {GemvGateRow<Ms, T, WK>::out...};
   return tbl[m - 1][group][out_kind];
 }
 
@@ -451,9 +474,16 @@ hipError_t launch_gemv_kind(const GemvArgs& args, int m, int T, int out_kind, in
     return hipErrorInvalidValue;  // (unsplit blocks stage A with at least 256 threads)
   // one column per pass when the wave owns fewer columns than a full group
   const int group = args.cpw < gemv_group_max(m) ? 0 : 1;
-  const gemv_fn fn =
-      T == 1 ? gemv_pick<1, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind)
-             : gemv_pick<2, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind);
+  gemv_fn fn = nullptr;
+  if (args.epilogue == kEpiNone) {
+    fn = T == 1 ? gemv_pick<1, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind)
+                : gemv_pick<2, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind);
+  } else if constexpr (WK == WK_BF16) {  // the gate: bf16 weights only
+    if (args.epilogue == kEpiSigmoid)
+      fn = T == 1 ? gemv_pick_gate<1, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind)
+                  : gemv_pick_gate<2, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind);
+  }
+  if (fn == nullptr) return hipErrorInvalidValue;
   int64_t blocks;
   if (args.S <= kGemvBlockSplitMax) {
     if (args.cg_per_block < 1 || args.cg_per_block * args.S != waves_per_block) return hipErrorInvalidValue;

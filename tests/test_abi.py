@@ -83,9 +83,11 @@ def test_tile_table():
     (dict(lda=900), sk.ERR_ALIGNMENT),
     (dict(ldc=100), sk.ERR_SHAPE),
     (dict(flags=0x20), sk.ERR_UNSUPPORTED),
-    (dict(flags=sk.EPILOGUE_SIGMOID), sk.OK),                          # the gate: GEMV regime
-    (dict(flags=sk.EPILOGUE_SIGMOID, max_m=17), sk.ERR_UNSUPPORTED),  # the GEMM has no sigmoid
-    (dict(flags=sk.EPILOGUE_SIGMOID | sk.FORCE_GEMM), sk.ERR_UNSUPPORTED),
+    (dict(flags=sk.EPILOGUE_SIGMOID, a_dtype=sk.BF16, w_dtype=sk.BF16), sk.OK),  # the gate
+    (dict(flags=sk.EPILOGUE_SIGMOID), sk.ERR_UNSUPPORTED),            # f16 weights: no gate
+    (dict(flags=sk.EPILOGUE_SIGMOID, a_dtype=sk.BF16, w_dtype=sk.BF16, c_dtype=sk.BF16), sk.ERR_UNSUPPORTED),
+    (dict(flags=sk.EPILOGUE_SIGMOID, a_dtype=sk.BF16, w_dtype=sk.BF16, max_m=17), sk.ERR_UNSUPPORTED),
+    (dict(flags=sk.EPILOGUE_SIGMOID | sk.FORCE_GEMM, a_dtype=sk.BF16, w_dtype=sk.BF16), sk.ERR_UNSUPPORTED),
     (dict(flags=sk.FORCE_GEMV | sk.FORCE_GEMM), sk.ERR_INVALID_ARG),
     (dict(flags=sk.FORCE_GEMV, max_m=17), sk.ERR_INVALID_ARG),
     (dict(tile_id=13), sk.ERR_INVALID_ARG),
