@@ -20,11 +20,14 @@
 //     codes and scales are loaded into LDS as stored and each B fragment is
 //     dequantised as it is read, with the same function as the standalone
 //     dequant, so no separate dequant pass or f16 copy of the weight exists.
-//   * a plan may split k into `splits` ranges (fixed per plan from N, K and the
-//     CU count, never from M, so M-invariance holds within a plan); each range
-//     writes fp32 partial sums and a second launch adds them in range order.
-//     The split changes the rounding against an unsplit sum, never between
-//     tiles or calls.
+//   * a plan may cut k into chunks (fixed per plan from N, K and the CU
+//     count, never from M, so M-invariance holds within a plan).  Each m then
+//     runs either one block per chunk writing fp32 partial sums, added in
+//     chunk order by a second launch, or one launch whose blocks walk all
+//     chunks and fold each chunk's sum into a running total at the chunk's
+//     end -- the same additions in the same order, so both give the same
+//     bits.  Chunking changes the rounding against an unchunked sum, never
+//     between tiles, launch shapes or calls.
 //
 // Structure (64-wide wavefronts, 1 to 8 waves per block):
 //   * k-tiles of 64 (four MFMA steps per barrier);
