@@ -21,8 +21,12 @@ struct skinny_plan {
   // GEMV work split, a function of k only (row invariance across m)
   int gemv_T;
   int gemv_S;
-  // GEMV columns per wave, a function of n, S and the CU count
+  // GEMV columns per wave: gemv_cpw from n, S and the CU count (the
+  // arrival counters of a k split across workgroups are laid out by it), and
+  // the launch shape each m uses, gemv_cpw_m[m] (a column's arithmetic does not
+  // depend on how many columns a wave owns, so it may change with m)
   int gemv_cpw;
+  int gemv_cpw_m[kGemvMaxM + 1];
   // GEMM k split (ranges of gemm_kps k-tiles), a function of n, k and the CU
   // count only (M-invariance within the plan)
   int gemm_splits;
@@ -65,10 +69,10 @@ void gemv_split(int64_t k, int* T_out, int* S_out) {
   *S_out = (int)cand[best].S;
 }
 
-// columns per wave: enough waves for about one per SIMD (4 per CU), but at
+// columns per wave: enough for about `waves_per_cu` waves per CU, but at
 // most kGemvCpwMax columns so the wave's weight loads all fit in registers
-int gemv_cols_per_wave(int64_t n, int S, int num_cus) {
-  const int64_t target_waves = 4LL * num_cus;
+int gemv_cols_per_wave(int64_t n, int S, int num_cus, int waves_per_cu) {
+  const int64_t target_waves = (int64_t)waves_per_cu * num_cus;
   int64_t cpw = (n * S) / (target_waves > 0 ? target_waves : 1);
   if (cpw < 1) cpw = 1;
   if (cpw > kGemvCpwMax) cpw = kGemvCpwMax;
@@ -218,12 +222,18 @@ constexpr size_t kWsAlign = 256;
 
 size_t round_up(size_t x) { return (x + kWsAlign - 1) / kWsAlign * kWsAlign; }
 
-int64_t gemv_waves_per_split(const skinny_plan* p) { return (p->d.n + p->gemv_cpw - 1) / p->gemv_cpw; }
-
 bool gemv_global_split(const skinny_plan* p) { return p->gemv_S > kGemvBlockSplitMax; }
 
+// column ranges (waves per k split) of the launch for m rows
+int64_t gemv_waves_per_split(const skinny_plan* p, int64_t m) {
+  const int cpw = p->gemv_cpw_m[m < kGemvMaxM ? m : kGemvMaxM];
+  return (p->d.n + cpw - 1) / cpw;
+}
+
 size_t gemv_counter_bytes(const skinny_plan* p) {
-  return gemv_global_split(p) ? round_up((size_t)gemv_waves_per_split(p) * sizeof(uint32_t)) : 0;
+  return gemv_global_split(p)
+             ? round_up((size_t)((p->d.n + p->gemv_cpw - 1) / p->gemv_cpw) * sizeof(uint32_t))
+             : 0;
 }
 
 size_t gemv_partial_bytes(const skinny_plan* p, int64_t m) {
@@ -246,8 +256,8 @@ size_t workspace_bytes_for(const skinny_plan* p, int64_t m) {
 
 skinny_status hip_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_ERR_HIP; }
 
-GemvArgs gemv_args(const skinny_plan* p, const void* A, const void* W, const void* scales, void* C,
-                   int64_t ldc, void* workspace) {
+GemvArgs gemv_args(const skinny_plan* p, int64_t m, const void* A, const void* W, const void* scales,
+                   void* C, int64_t ldc, void* workspace) {
   GemvArgs g;
   g.A = (const uint16_t*)A;
   g.lda = p->d.lda;
@@ -257,8 +267,8 @@ GemvArgs gemv_args(const skinny_plan* p, const void* A, const void* W, const voi
   g.k = p->d.k;
   g.nchunks = (int32_t)(p->d.k / 8);
   g.S = p->gemv_S;
-  g.cpw = p->gemv_cpw;
-  g.waves_per_split = (int32_t)gemv_waves_per_split(p);
+  g.cpw = p->gemv_cpw_m[m < kGemvMaxM ? m : kGemvMaxM];
+  g.waves_per_split = (int32_t)gemv_waves_per_split(p, m);
   g.cg_per_block = 0;
   g.C = C;
   g.ldc = ldc;
@@ -329,8 +339,8 @@ GemvBlock gemv_block(const skinny_plan* p) {
   return {plain, 0};
 }
 
-int64_t gemv_blocks(const skinny_plan* p, const GemvBlock& b) {
-  const int64_t wps = gemv_waves_per_split(p);
+int64_t gemv_blocks(const skinny_plan* p, const GemvBlock& b, int64_t m) {
+  const int64_t wps = gemv_waves_per_split(p, m);
   if (b.ranges > 0) return (wps + b.ranges - 1) / b.ranges;
   return (wps * p->gemv_S + b.waves - 1) / b.waves;
 }
@@ -343,7 +353,7 @@ skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const v
                          int32_t* topk_idx, float* topk_val, int32_t topk, hipStream_t stream) {
   const bool want_topk = topk_idx != nullptr;
   if (use_gemv(p, m)) {
-    GemvArgs g = gemv_args(p, A, W, scales, C, ldc, workspace);
+    GemvArgs g = gemv_args(p, m, A, W, scales, C, ldc, workspace);
     const GemvBlock b = gemv_block(p);
     g.cg_per_block = b.ranges;
     skinny_status st = hip_status(launch_gemv(g, (int)m, p->gemv_T, p->w_kind, c_kind, b.waves, stream));
@@ -439,7 +449,16 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   p->w_kind = to_wkind(d.w_dtype);
   p->c_kind = to_ckind(d.c_dtype);
   gemv_split(d.k, &p->gemv_T, &p->gemv_S);
-  p->gemv_cpw = gemv_cols_per_wave(d.n, p->gemv_S, cus);
+  // about four waves per CU as the base; a k split inside the workgroup runs
+  // about eight per CU, which hides more latency (measured on MI355X at
+  // n x k = 4864 x 896, 2048 x 2048, 8192 x 1024, 1024 x 4096, 14336 x 4096),
+  // except that an unsplit k at m > 8 keeps the base: there each workgroup
+  // stages all m rows of A in LDS, and fewer, wider workgroups load less of it
+  p->gemv_cpw = gemv_cols_per_wave(d.n, p->gemv_S, cus, 4);
+  for (int m = 0; m <= kGemvMaxM; ++m) {
+    const bool base = p->gemv_S > kGemvBlockSplitMax || (p->gemv_S == 1 && m > 8);
+    p->gemv_cpw_m[m] = base ? p->gemv_cpw : gemv_cols_per_wave(d.n, p->gemv_S, cus, 8);
+  }
   gemm_split(d.n, d.k, cus, &p->gemm_splits, &p->gemm_kps);
   if (log_enabled()) {
     std::fprintf(stderr, "[skinny] plan n=%lld k=%lld max_m=%lld gemv T=%d S=%d cpw=%d cus=%d\n",
@@ -515,13 +534,13 @@ skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf,
   if (plan == nullptr || buf == nullptr || len == 0) return SKINNY_ERR_INVALID_ARG;
   if (m < 1 || m > plan->d.max_m) return SKINNY_ERR_INVALID_ARG;
   if (use_gemv(plan, m)) {
-    const int64_t waves = gemv_waves_per_split(plan) * plan->gemv_S;
+    const int64_t waves = gemv_waves_per_split(plan, m) * plan->gemv_S;
     const GemvBlock b = gemv_block(plan);
     std::snprintf(buf, len,
                   "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld x %d waves split_reduce=%s "
                   "%sworkspace=%zu",
-                  (long long)m, plan->gemv_T, plan->gemv_S, plan->gemv_cpw, (long long)waves,
-                  (long long)gemv_blocks(plan, b), b.waves,
+                  (long long)m, plan->gemv_T, plan->gemv_S, plan->gemv_cpw_m[m], (long long)waves,
+                  (long long)gemv_blocks(plan, b, m), b.waves,
                   plan->gemv_S == 1 ? "none" : (gemv_global_split(plan) ? "global" : "in-block"),
                   (plan->d.flags & SKINNY_EPILOGUE_SIGMOID) ? "epilogue=sigmoid " : "",
                   workspace_bytes_for(plan, m));

@@ -179,6 +179,18 @@ def test_gemm_split_depends_on_n_k_only(n, k, splits):
         assert f" chunks={splits} " in info, info
 
 
+@pytest.mark.parametrize("n,k,m,cpw", [
+    (4864, 896, 1, 2), (4864, 896, 8, 2), (4864, 896, 9, 4), (4864, 896, 16, 4),  # unsplit k
+    (2048, 2048, 16, 2), (1024, 4096, 1, 2),                                      # k split in the workgroup
+    (256, 5120, 1, 1), (256, 5120, 16, 1),                                        # the router
+    (256, 16384, 1, 4), (4864, 16384, 16, 8),                                     # k split across workgroups
+])
+def test_gemv_columns_per_wave_by_m(n, k, m, cpw):
+    # about eight waves per CU when k is split in the workgroup (and for an
+    # unsplit k up to m = 8), four otherwise; never more than eight columns
+    assert f" cpw={cpw} " in plan(n=n, k=k).info(m)
+
+
 def test_gemm_split_workspace():
     # chunks x M x N fp32 partial sums for the split launch, sized for max_m;
     # the one-launch shape needs none
