@@ -82,13 +82,15 @@ def test_gemm_strided_a():
     assert rel_err(C.cpu().numpy(), oracle.mm(A, "f16", W, "f16")) <= REL_TOL
 
 
-@pytest.mark.parametrize("M,N,K", [(150, 200, 512), (150, 200, 520)])
+@pytest.mark.parametrize("M,N,K", [(150, 200, 512), (150, 200, 520), (300, 2048, 520)])
 def test_gemm_every_tile_bitwise_equal(M, N, K):
+    """Every tile gives the same bits: N = 200 with k cut into chunks (the
+    plan's chunk launch per tile), N = 2048 with k whole."""
     A, W = _inputs(M, N, K, 7)
     dA, dW = to_dev(A, "f16"), to_dev(W, "f16")
     outs = []
     for tid in range(len(sk.gemm_tiles())):
-        print(f"tile {tid} {sk.gemm_tiles()[tid]} K={K}", flush=True)
+        print(f"tile {tid} {sk.gemm_tiles()[tid]} N={N} K={K}", flush=True)
         C = sk.mm(dA, dW, out_dtype=torch.float32, tile_id=tid)
         torch.cuda.synchronize()
         outs.append(C.cpu().numpy().view(np.uint32))
