@@ -508,7 +508,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
   }
 }
 
-// C[r][c] = partial[0][r][c] + partial[1][r][c] + ... in that order
+// C[r][c] = partial[0][r][c] + partial[1][r][c] + ... in that order.  All of
+// an element's partials are loaded before the first add (one memory round
+// trip instead of one per chunk); the adds keep the chunk order.
+constexpr int kMaxSplits = 16;  // the plan cuts k into at most this many chunks
+
 template <int CK>
 __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   const int64_t total = g.M * g.N;
@@ -516,8 +520,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (int64_t)gridDim.x * 256) {
     const int64_t r = e / g.N;
     const int64_t c = e - r * g.N;
-    float acc = g.partial[e];
-    for (int s = 1; s < g.splits; ++s) acc += g.partial[s * plane + e];
+    float part[kMaxSplits];
+#pragma unroll
+    for (int s = 0; s < kMaxSplits; ++s) part[s] = s < g.splits ? g.partial[s * plane + e] : 0.0f;
+    float acc = part[0];
+#pragma unroll
+    for (int s = 1; s < kMaxSplits; ++s)
+      if (s < g.splits) acc += part[s];
     store_out<CK>(g.C, r * g.ldc + c, acc);
   }
 }
@@ -621,7 +630,8 @@ hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind
 }
 
 hipError_t launch_splitk_reduce(const GemmArgs& args, int c_kind, hipStream_t stream) {
-  if (args.splits < 2 || args.partial == nullptr || c_kind < 0 || c_kind > 2) return hipErrorInvalidValue;
+  if (args.splits < 2 || args.splits > kMaxSplits || args.partial == nullptr || c_kind < 0 || c_kind > 2)
+    return hipErrorInvalidValue;
   int64_t blocks = (args.M * args.N + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   const auto fn = c_kind == CK_F32 ? splitk_reduce_kernel<CK_F32>
