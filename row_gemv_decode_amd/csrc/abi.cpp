@@ -156,10 +156,14 @@ double tile_estimate(const skinny_plan* p, int id, int64_t m, int64_t copies, in
   const int64_t cus = p->num_cus;
   const int64_t slots = cus * tc.c;
   double rounds = 0.0;
+  // sigma was fitted on blocks of 40 k-tiles; two short blocks on one CU mostly
+  // overlap their fixed latencies, so the penalty shrinks with the block
+  const double short_block = ktiles < 40 ? (double)ktiles / 40.0 : 1.0;
+  const double sigma = 1.0 + (tc.sigma - 1.0) * short_block;
   for (int64_t left = blocks; left > 0; left -= slots) {
     const int64_t nb = left < slots ? left : slots;
     const int64_t busiest = (nb + cus - 1) / cus;  // blocks on the busiest CU
-    rounds += (busiest >= 2 ? tc.sigma : 1.0) * (1.0 + tc.a * (double)nb / (double)slots);
+    rounds += (busiest >= 2 ? sigma : 1.0) * (1.0 + tc.a * (double)nb / (double)slots);
   }
   // Q8_0 weights are dequantised per fragment: about 1.65x the f16 time per
   // k-tile on MI355X
