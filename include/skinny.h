@@ -166,10 +166,12 @@ SKINNY_API skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_
  *   A, W, C    device pointers (16-byte aligned); w_scales: Q8_0 scales
  *              f16 [n][k/32] (16-byte aligned), else must be NULL
  *   workspace  zero-initialised device scratch of >= skinny_mm_workspace_size
- *              bytes (may be NULL when that size is 0); one launch finishes the
- *              call, including the reduction over k splits
+ *              bytes (may be NULL when that size is 0)
  *   stream     hipStream_t (NULL = null stream)
- * Writes rows 0..m-1 of C, columns 0..n-1 only. */
+ * Enqueues one launch (the GEMV, whose k splits are summed inside it, or the
+ * GEMM), or two when the plan's GEMM runs its k chunks as separate blocks
+ * (the second adds the chunks in order).  Writes rows 0..m-1 of C, columns
+ * 0..n-1 only. */
 SKINNY_API skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
                             const void* w_scales, void* C, void* workspace,
                             size_t workspace_bytes, void* stream);
