@@ -109,8 +109,9 @@ typedef enum skinny_dtype {
  *   c_dtype      SKINNY_F32, SKINNY_F16 or SKINNY_BF16 (rounded to nearest even)
  *   max_m        largest m any run will pass (>= 1)
  *   n, k         output columns and reduction length (n >= 1; k >= 8, k % 8 == 0,
- *                k % 32 == 0 for Q8_0; k and lda <= 2^20 when the plan may use
- *                the GEMM, i.e. max_m > 16 or SKINNY_FORCE_GEMM)
+ *                k % 32 == 0 for Q8_0; k and lda <= 2^20, and k >= 64 for
+ *                Q8_0, when the plan may use the GEMM, i.e. max_m > 16 or
+ *                SKINNY_FORCE_GEMM)
  *   lda, ldc     row strides of A and C in elements; 0 means dense (k and n);
  *                otherwise >= the row length; lda a multiple of 8 (A rows are
  *                read 16 bytes at a time), ldc any value >= n

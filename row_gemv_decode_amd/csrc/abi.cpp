@@ -435,6 +435,9 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   // the GEMM addresses a block's rows through 32-bit buffer offsets
   const bool may_gemm = !(d.flags & SKINNY_FORCE_GEMV) && (d.max_m > kGemvMaxM || (d.flags & SKINNY_FORCE_GEMM));
   if (may_gemm && (d.k > kGemmMaxK || d.lda > kGemmMaxK)) return SKINNY_ERR_SHAPE;
+  // the GEMM fetches a k-tile's two Q8_0 scales of a row as one 4-byte word,
+  // which needs at least two scales per row (k >= 64)
+  if (may_gemm && d.w_dtype == SKINNY_Q8_0 && d.k < 64) return SKINNY_ERR_SHAPE;
   if (d.num_cus < 0) return SKINNY_ERR_INVALID_ARG;
 
   int cus = d.num_cus;

@@ -119,6 +119,12 @@ __device__ __forceinline__ u32x4 buffer_rsrc(const void* base, int64_t bytes) {
   return u32x4{(uint32_t)b, (uint32_t)(b >> 32) & 0xFFFFu, (uint32_t)bytes, (uint32_t)kBufferFlags};
 }
 
+// The kernel body is written as lambdas; each must be inlined: a lambda the
+// inliner leaves out of line becomes a call whose arguments the compiler can
+// no longer prove wave-uniform, so the scalar operands of the LDS DMA asm
+// below would not compile (and a call in the k loop would cost far more).
+#define INLINE_LAMBDA __attribute__((always_inline))
+
 // One 16-byte-per-lane load straight into LDS: lane l's bytes land at
 // lds + 16 * l.  Issued from asm so that the compiler neither counts it nor
 // orders LDS reads after it: the kernel waits for it explicitly (vmcnt and a
@@ -268,10 +274,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
     voff_s[i] = (int)((int64_t)r * (K >> 5) * 2);
   }
 
-  // k-tile kt (clamped to the last one, so every k-tile issues the same
-  // number of loads and the waits count exactly) into stage st
-  // local k-tile kt (0 .. nk - 1) into stage st
-  auto issue = [&](int st, int kt) {
+  // An odd number of scales per row (K % 64 == 32) leaves one scale in the
+  // matrix's last k-tile; the word at its usual place would run 2 bytes past
+  // the row (past the buffer for the tile's last row, which then reads as 0),
+  // so that k-tile's word is fetched 2 bytes earlier and its scale is the
+  // high half.  The other half belongs to k past K, whose products are masked.
+  const bool q8_odd = Q8 && ((K >> 5) & 1) != 0;
+  auto scale_shift = [&](int kc) INLINE_LAMBDA -> bool { return q8_odd && kc == nk_all - 1; };
+
+  // local k-tile kt (0 .. nk - 1; later ones are clamped to the last, so
+  // every k-tile issues the same number of loads and the waits count
+  // exactly) into stage st
+  auto issue = [&](int st, int kt) INLINE_LAMBDA {
     const int kc = kb + (kt < nk ? kt : nk - 1);
     const int koff = kc * kBK * 2;  // bytes of a 16-bit row
 #pragma unroll
@@ -283,7 +297,8 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
         lds_dma16(rsrc_b, lds_addr(&sB[st][(16 * (i * NW + wid_u)) * 4]), voff_b[i], kc * kBK);
 #pragma unroll
       for (int i = 0; i < S_ITERS; ++i)
-        lds_dma4(rsrc_s, lds_addr(&sS[st][64 * (i * NW + wid_u)]), voff_s[i], kc * 4);
+        lds_dma4(rsrc_s, lds_addr(&sS[st][64 * (i * NW + wid_u)]), voff_s[i],
+                 kc * 4 - (scale_shift(kc) ? 2 : 0));
     } else {
 #pragma unroll
       for (int i = 0; i < B_ITERS; ++i)
@@ -291,14 +306,16 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
     }
   };
 
-  // one B fragment: 8 weights of row `row` at k-chunk c (of 8) of a stage
-  auto read_b = [&](int st, int row, int c) -> u32x4 {
+  // one B fragment: 8 weights of row `row` at k-chunk c (of 8) of a stage;
+  // sh: the stage holds a k-tile whose scale word was fetched shifted
+  auto read_b = [&](int st, bool sh, int row, int c) INLINE_LAMBDA -> u32x4 {
     if constexpr (Q8) {
       const uint32_t* codes = reinterpret_cast<const uint32_t*>(&sB[st][0]);
       const int w = row * 16 + (((c >> 1) ^ q8_swz(row)) * 4) + (c & 1) * 2;
       const u32x2 q = *reinterpret_cast<const u32x2*>(codes + w);
       const uint32_t sc = sS[st][row];
-      return q8_dequant8(q, half_from_bits((uint16_t)((c >> 2) ? (sc >> 16) : sc)));
+      const int hi = (c >> 2) | (int)sh;
+      return q8_dequant8(q, half_from_bits((uint16_t)(hi ? (sc >> 16) : sc)));
     } else {
       return sB[st][row * kCPR + (c ^ swz(row))];
     }
@@ -319,7 +336,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
   // split-k reduce launch makes, so both launch shapes give the same bits.
   f32x16 tot[CH ? FM : 1][CH ? FN : 1];
   bool have_tot = false;
-  auto fold = [&]() {
+  auto fold = [&]() INLINE_LAMBDA {
     if constexpr (CH) {
 #pragma unroll
       for (int i = 0; i < FM; ++i)
@@ -351,7 +368,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
 
   // K % 64 != 0: the last k-tile runs outside the loop, and there the
   // fragments past K are zeroed (in both operands) before its MFMAs
-  auto mask_tail = [&](int ks, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
+  auto mask_tail = [&](int ks, u32x4 (&af)[FM], u32x4 (&bf)[FN]) INLINE_LAMBDA {
     if (k_tail && last_split && (int64_t)(kb + nk - 1) * kBK + ks * 16 + lk * 8 >= K) {
       const u32x4 zero = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -372,7 +389,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
     // multiply tile kt.
     u32x4 fa[2][kSteps][FM];
     u32x4 fb[2][kSteps][FN];
-    auto read_tile = [&](int st, u32x4 (&ta)[kSteps][FM], u32x4 (&tb)[kSteps][FN]) {
+    auto read_tile = [&](int st, bool sh, u32x4 (&ta)[kSteps][FM], u32x4 (&tb)[kSteps][FN]) INLINE_LAMBDA {
       const u32x4* a_s = sA[st];
 #pragma unroll
       for (int ks = 0; ks < kSteps; ++ks) {
@@ -380,10 +397,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < FM; ++i) ta[ks][i] = a_s[a_row[i] * kCPR + (c ^ swz(a_row[i]))];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) tb[ks][j] = read_b(st, b_row[j], c);
+        for (int j = 0; j < FN; ++j) tb[ks][j] = read_b(st, sh, b_row[j], c);
       }
     };
-    auto mma_tile = [&](u32x4 (&ta)[kSteps][FM], u32x4 (&tb)[kSteps][FN], bool last) {
+    auto mma_tile = [&](u32x4 (&ta)[kSteps][FM], u32x4 (&tb)[kSteps][FN], bool last) INLINE_LAMBDA {
 #pragma unroll
       for (int ks = 0; ks < kSteps; ++ks) {
         if (last) mask_tail(ks, ta[ks], tb[ks]);
@@ -395,25 +412,25 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
     };
     wait_vmcnt<(NS - 2) * LOADS>();  // tile 0
     barrier_only();
-    read_tile(0, fa[0], fb[0]);
+    read_tile(0, false, fa[0], fb[0]);
     int stage = 0;  // stage of tile kt
     int kt = 0;
     // one trip: tile kt's MFMAs on fragment set H while tile kt + 1 is read
     // into the other set
-    auto trip = [&](auto hc) {
+    auto trip = [&](auto hc) INLINE_LAMBDA {
       constexpr int H = decltype(hc)::value;
       wait_vmcnt<(NS - 3) * LOADS>();
       barrier_only();
       issue(stage == 0 ? NS - 1 : stage - 1, kt + NS - 1);
       stage = stage + 1 == NS ? 0 : stage + 1;
-      read_tile(stage, fa[H ^ 1], fb[H ^ 1]);
+      read_tile(stage, false, fa[H ^ 1], fb[H ^ 1]);
       mma_tile(fa[H], fb[H], false);
       ++kt;
     };
     // tiles kt .. stop - 1 (kt even on entry): trips in pairs, so the loop
     // body is one straight-line block with the fragment sets named at compile
     // time and the loop has a single exit; an odd count leaves one trip after
-    auto run_to = [&](const int stop) {
+    auto run_to = [&](const int stop) INLINE_LAMBDA {
       while (kt + 1 < stop) {
         trip(std::integral_constant<int, 0>{});
         trip(std::integral_constant<int, 1>{});
@@ -432,10 +449,15 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
     } else {
       run_to(nk - 1);
     }
-    // the last tile, read by the last trip (or the prologue)
+    // the last tile, read by the last trip (or the prologue) -- read again
+    // from its stage, which nothing refills, when its scale word was fetched
+    // shifted
+    const bool last_sh = scale_shift(kb + nk - 1);
     if ((nk - 1) & 1) {
+      if (last_sh) read_tile(stage, true, fa[1], fb[1]);
       mma_tile(fa[1], fb[1], true);
     } else {
+      if (last_sh) read_tile(stage, true, fa[0], fb[0]);
       mma_tile(fa[0], fb[0], true);
     }
     fold();
@@ -444,17 +466,18 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
     // stay in flight), barrier (every wave's part has landed, and every wave is
     // done with the stage tile kt - 1 used), refill that stage with tile
     // kt + NS - 1, then the MFMAs of tile kt
-    auto tile = [&](int kt, int st, bool last) {
+    auto tile = [&](int kt, int st, bool last) INLINE_LAMBDA {
       wait_vmcnt<(NS - 2) * LOADS>();
       barrier_only();
       issue(st == 0 ? NS - 1 : st - 1, kt + NS - 1);
       const u32x4* a_s = sA[st];
-      auto read_frags = [&](int ks, u32x4 (&af)[FM], u32x4 (&bf)[FN]) {
+      const bool sh = scale_shift(kb + kt);
+      auto read_frags = [&](int ks, u32x4 (&af)[FM], u32x4 (&bf)[FN]) INLINE_LAMBDA {
         const int c = ks * 2 + lk;
 #pragma unroll
         for (int i = 0; i < FM; ++i) af[i] = a_s[a_row[i] * kCPR + (c ^ swz(a_row[i]))];
 #pragma unroll
-        for (int j = 0; j < FN; ++j) bf[j] = read_b(st, b_row[j], c);
+        for (int j = 0; j < FN; ++j) bf[j] = read_b(st, sh, b_row[j], c);
       };
       u32x4 af[2][FM];
       u32x4 bf[2][FN];

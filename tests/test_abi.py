@@ -95,6 +95,10 @@ def test_tile_table():
     (dict(num_cus=-1), sk.ERR_INVALID_ARG),
     (dict(max_m=64, k=(1 << 20) + 8), sk.ERR_SHAPE),          # GEMM path: k <= 2^20
     (dict(max_m=16, k=(1 << 20) + 8), sk.OK),                 # GEMV only: fine
+    (dict(w_dtype=sk.Q8_0, k=32, max_m=17), sk.ERR_SHAPE),    # Q8_0 GEMM: k >= 64
+    (dict(w_dtype=sk.Q8_0, k=32, flags=sk.FORCE_GEMM), sk.ERR_SHAPE),
+    (dict(w_dtype=sk.Q8_0, k=32, max_m=16), sk.OK),           # GEMV only: fine
+    (dict(w_dtype=sk.Q8_0, k=96, max_m=17), sk.OK),           # an odd number of scales
     (dict(ldc=4870), sk.OK),                                   # any ldc >= n
     (dict(lda=904), sk.OK),
 ])

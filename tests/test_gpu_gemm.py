@@ -163,6 +163,30 @@ def test_q8_gemm_full_size_and_fused_equals_unfused():
         assert rel_err(C.float().cpu().numpy()[rows], ref) <= REL_TOL, M
 
 
+@pytest.mark.parametrize("M,N,K", [(150, 200, 544), (70, 65, 96), (40, 130, 2592)])
+def test_q8_gemm_odd_scale_count_every_tile(M, N, K):
+    """K % 64 == 32: each weight row has an odd number of scales, the last
+    k-tile holds one.  On every tile (ragged last column tiles down to one
+    row, the plan's k chunks on the narrow shapes) the fused Q8_0 GEMM gives
+    the bits of the same tile on the dequantised f16 weights, within the fp32
+    summation bound of the oracle."""
+    A = WL.gen_matrix((M, K), "f16", ("normal", 1.0), 621 + K)
+    qs, d = WL.gen_q8_0(N, K, 622 + K, 623 + K)
+    dA = to_dev(A, "f16")
+    dq = (to_dev(qs, "i8"), to_dev(d, "f16"))
+    w16 = sk.dequant_q8_0(*dq)
+    ref = oracle.mm(A, "f16", qs, "q8_0", w_scales=d)
+    bound = (K + 2) * 2.0 ** -24 * oracle.mm(A, "f16", qs, "q8_0", w_scales=d, absolute=True) + 1e-30
+    for tid in range(len(sk.gemm_tiles())):
+        print(f"q8_0 odd scales tile {tid} {sk.gemm_tiles()[tid]} M={M} N={N} K={K}", flush=True)
+        C = sk.mm(dA, dq, out_dtype=torch.float32, tile_id=tid)
+        C2 = sk.mm(dA, w16, out_dtype=torch.float32, tile_id=tid)
+        torch.cuda.synchronize()
+        got = C.cpu().numpy()
+        assert np.array_equal(got.view(np.uint32), C2.cpu().numpy().view(np.uint32)), tid
+        assert np.all(np.abs(got - ref) <= bound), tid
+
+
 @pytest.mark.parametrize("w_kind", ["f16", "q8_0"])
 def test_chunked_one_launch_equals_split_launch(w_kind):
     """A plan that cuts k into chunks gives the same bits whether each chunk
