@@ -104,8 +104,14 @@ typedef enum skinny_dtype {
 
 /* Problem description, copied into the plan.
  *   struct_size  sizeof(skinny_mm_desc), for ABI versioning
- *   a_dtype      SKINNY_F16 or SKINNY_BF16
- *   w_dtype      SKINNY_F16 / SKINNY_Q8_0 (with f16 A) or SKINNY_BF16 (with bf16 A)
+ *   a_dtype      SKINNY_F16 or SKINNY_BF16; or SKINNY_F32 with bf16 weights in
+ *                the GEMV regime (max_m <= 16, no SKINNY_FORCE_GEMM; else
+ *                SKINNY_ERR_UNSUPPORTED): fp32 rows whose values the GEMV
+ *                rounds to bf16 (nearest even) as it loads them -- the
+ *                window-row cast below fused into the GEMV, so C equals the
+ *                result for the cast rows bit for bit, in one launch
+ *   w_dtype      SKINNY_F16 / SKINNY_Q8_0 (with f16 A) or SKINNY_BF16 (with bf16
+ *                or f32 A)
  *   c_dtype      SKINNY_F32, SKINNY_F16 or SKINNY_BF16 (rounded to nearest even)
  *   max_m        largest m any run will pass (>= 1)
  *   n, k         output columns and reduction length (n >= 1; k >= 8, k % 8 == 0,
@@ -114,7 +120,7 @@ typedef enum skinny_dtype {
  *                SKINNY_FORCE_GEMM)
  *   lda, ldc     row strides of A and C in elements; 0 means dense (k and n);
  *                otherwise >= the row length; lda a multiple of 8 (A rows are
- *                read 16 bytes at a time), ldc any value >= n
+ *                read 16 bytes at a time, 32 for fp32 rows), ldc any value >= n
  *   flags        SKINNY_FORCE_* (tests and benchmarks); 0 normally
  *   tile_id      -1: the plan's tile selector; >= 0: force that GEMM tile
  *                (see skinny_gemm_tile_count)
@@ -155,7 +161,12 @@ SKINNY_API void skinny_mm_plan_destroy(skinny_plan* plan);
  *     finish the sum inside the same kernel;
  *   - a GEMM whose plan cuts k into chunks (narrow n) and runs them as one
  *     block per chunk: it holds the chunks' fp32 partial sums, which an
- *     ordered reduce launch adds.
+ *     ordered reduce launch adds;
+ *   - a plan with fp32 A whose GEMV splits k (k > 1024 for bf16 weights), at
+ *     m > 10: the fused cast measured slower there than a separate cast
+ *     launch, so the run casts the rows into the workspace (after any
+ *     partial sums) and the bf16 GEMV reads them -- the same bits as the
+ *     fused launch.
  * It must be zero-filled once before its first use; every completed run
  * leaves it ready for the next (its counters back at zero).  A run that needs
  * no workspace ignores it. */
@@ -171,7 +182,8 @@ SKINNY_API skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_
  *   stream     hipStream_t (NULL = null stream)
  * Enqueues one launch (the GEMV, whose k splits are summed inside it, or the
  * GEMM), or two when the plan's GEMM runs its k chunks as separate blocks
- * (the second adds the chunks in order).  Writes rows 0..m-1 of C, columns
+ * (the second adds the chunks in order) or its fp32 rows are cast first (see
+ * skinny_mm_workspace_size).  Writes rows 0..m-1 of C, columns
  * 0..n-1 only. */
 SKINNY_API skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
                             const void* w_scales, void* C, void* workspace,
@@ -203,7 +215,8 @@ SKINNY_API skinny_status skinny_dequant_q8_0_run(int64_t n, int64_t k, const voi
 /* The window-row cast (the Strata PR #109 page, "What": the window's fp32
  * rows are cast to bf16 in one call, the rows being contiguous):
  * out[i] = RNE_bf16(in[i]) for 0 <= i < count, round to nearest, ties to
- * even; a NaN becomes a quiet NaN.  The result feeds a bf16 plan's A.
+ * even; a NaN becomes a quiet NaN.  The result feeds a bf16 plan's A (a plan
+ * with fp32 A does the same rounding inside its one GEMV launch).
  *   1 <= count <= 2^40; in: f32 [count], out: bf16 [count]; device pointers,
  *   16-byte aligned, not overlapping (else SKINNY_ERR_INVALID_ARG). */
 SKINNY_API skinny_status skinny_cast_f32_bf16_run(int64_t count, const float* in, void* out, void* stream);

@@ -290,17 +290,15 @@ def cast_f32_bf16(x, out=None, stream=None):
 
 def gate(A, W, max_m=None, out=None, stream=None):
     """Scalar gate of fp32 window rows: sigmoid(bf16(A) . W) for A [m][k] fp32
-    and W bf16 [n][k] (n = 1 for one gate per row): the cast launch, then the
-    GEMV with the sigmoid applied as it stores."""
+    (contiguous rows) and W bf16 [n][k] (n = 1 for one gate per row), in one
+    GEMV launch that rounds A to bf16 as it loads it and applies the sigmoid
+    as it stores."""
     torch = _torch()
     m, k = A.shape
     n = W.shape[0]
-    A16 = cast_f32_bf16(A, stream=stream)
-    if stream is not None:
-        A16.record_stream(stream)  # the temporary lives until the GEMV on that stream ran
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=A.device)
-    plan = get_plan(n, k, max_m or m, BF16, _dtype_code(W.dtype, "W"), _dtype_code(out.dtype, "C"),
-                    EPILOGUE_SIGMOID)
-    plan.run(m, A16, W, out, stream=stream)
+    plan = get_plan(n, k, max_m or m, _dtype_code(A.dtype, "A"), _dtype_code(W.dtype, "W"),
+                    _dtype_code(out.dtype, "C"), EPILOGUE_SIGMOID)
+    plan.run(m, A, W, out, stream=stream)
     return out

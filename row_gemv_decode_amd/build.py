@@ -15,7 +15,8 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libskinny.so")
 ARCH = "gfx950"
-SOURCES = ["abi.cpp", "gemv.hip", "gemv_f16.hip", "gemv_bf16.hip", "gemv_q8.hip", "gemm.hip"]
+SOURCES = ["abi.cpp", "gemv.hip", "gemv_f16.hip", "gemv_bf16.hip", "gemv_bf16_a32.hip", "gemv_q8.hip",
+           "gemm.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -252,10 +252,33 @@ size_t gemm_partial_bytes(const skinny_plan* p, int64_t m) {
              : 0;
 }
 
-// bytes a run at m rows needs (the same with or without the top-k)
-size_t workspace_bytes_for(const skinny_plan* p, int64_t m) {
+// fp32 rows of A: the GEMV rounds them to bf16 as it loads them (one
+// launch).  A wave then holds twice the A bytes in flight per row, which
+// measured slower than a separate cast launch once A is not staged in LDS
+// (k split, S > 1) and m > 10 (n = 1, 256, 2048 at k = 2048..16384); there
+// the run casts the rows into the workspace and the bf16 GEMV reads them.
+// Both shapes round with the same conversion and sum identically, so the
+// choice per m changes no bit.
+constexpr int64_t kA32FusedMaxM = 10;
+
+bool a32_cast_first(const skinny_plan* p, int64_t m) {
+  return p->d.a_dtype == SKINNY_F32 && p->gemv_S > 1 && m > kA32FusedMaxM;
+}
+
+// elements of A a cast-first run converts: rows 0..m-1 at stride lda, the
+// last one only up to k
+int64_t a32_cast_count(const skinny_plan* p, int64_t m) { return (m - 1) * p->d.lda + p->d.k; }
+
+// bytes of the workspace before the cast rows: counters and partial sums
+size_t split_bytes_for(const skinny_plan* p, int64_t m) {
   const size_t part = use_gemv(p, m) ? gemv_partial_bytes(p, m) : gemm_partial_bytes(p, m);
   return part > 0 ? gemv_counter_bytes(p) + part : 0;
+}
+
+// bytes a run at m rows needs (the same with or without the top-k)
+size_t workspace_bytes_for(const skinny_plan* p, int64_t m) {
+  const size_t a16 = a32_cast_first(p, m) ? round_up((size_t)a32_cast_count(p, m) * 2) : 0;
+  return split_bytes_for(p, m) + a16;
 }
 
 skinny_status hip_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_ERR_HIP; }
@@ -263,7 +286,8 @@ skinny_status hip_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SK
 GemvArgs gemv_args(const skinny_plan* p, int64_t m, const void* A, const void* W, const void* scales,
                    void* C, int64_t ldc, void* workspace) {
   GemvArgs g;
-  g.A = (const uint16_t*)A;
+  g.A = A;
+  g.a_kind = p->d.a_dtype == SKINNY_F32 ? kAF32 : kA16;
   g.lda = p->d.lda;
   g.W = W;
   g.scales = (const uint16_t*)scales;
@@ -360,6 +384,13 @@ skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const v
     GemvArgs g = gemv_args(p, m, A, W, scales, C, ldc, workspace);
     const GemvBlock b = gemv_block(p);
     g.cg_per_block = b.ranges;
+    if (a32_cast_first(p, m)) {
+      uint16_t* a16 = (uint16_t*)((char*)workspace + split_bytes_for(p, m));
+      skinny_status st = hip_status(launch_cast_f32_bf16(a32_cast_count(p, m), (const float*)A, a16, stream));
+      if (st != SKINNY_OK) return st;
+      g.A = a16;
+      g.a_kind = kA16;
+    }
     skinny_status st = hip_status(launch_gemv(g, (int)m, p->gemv_T, p->w_kind, c_kind, b.waves, stream));
     if (st != SKINNY_OK || !want_topk) return st;
     return hip_status(launch_topk((const float*)C, (int)m, p->d.n, ldc, topk_idx, topk_val, topk, stream));
@@ -404,7 +435,13 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   if (desc->struct_size < sizeof(skinny_mm_desc)) return SKINNY_ERR_INVALID_ARG;
   skinny_mm_desc d = *desc;
 
-  if (d.a_dtype != SKINNY_F16 && d.a_dtype != SKINNY_BF16) return SKINNY_ERR_UNSUPPORTED;
+  if (d.a_dtype != SKINNY_F16 && d.a_dtype != SKINNY_BF16 && d.a_dtype != SKINNY_F32)
+    return SKINNY_ERR_UNSUPPORTED;
+  // fp32 rows are rounded to bf16 as the GEMV loads them: bf16 weights, GEMV
+  // regime only
+  if (d.a_dtype == SKINNY_F32 &&
+      (d.w_dtype != SKINNY_BF16 || d.max_m > kGemvMaxM || (d.flags & SKINNY_FORCE_GEMM)))
+    return SKINNY_ERR_UNSUPPORTED;
   if (d.a_dtype == SKINNY_F16 && d.w_dtype != SKINNY_F16 && d.w_dtype != SKINNY_Q8_0)
     return SKINNY_ERR_UNSUPPORTED;
   if (d.a_dtype == SKINNY_BF16 && d.w_dtype != SKINNY_BF16) return SKINNY_ERR_UNSUPPORTED;
@@ -545,10 +582,13 @@ skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf,
     const GemvBlock b = gemv_block(plan);
     std::snprintf(buf, len,
                   "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld x %d waves split_reduce=%s "
-                  "%sworkspace=%zu",
+                  "%s%sworkspace=%zu",
                   (long long)m, plan->gemv_T, plan->gemv_S, plan->gemv_cpw_m[m], (long long)waves,
                   (long long)gemv_blocks(plan, b, m), b.waves,
                   plan->gemv_S == 1 ? "none" : (gemv_global_split(plan) ? "global" : "in-block"),
+                  plan->d.a_dtype != SKINNY_F32 ? ""
+                  : a32_cast_first(plan, m)     ? "a=f32(cast-launch) "
+                                                : "a=f32(fused) ",
                   (plan->d.flags & SKINNY_EPILOGUE_SIGMOID) ? "epilogue=sigmoid " : "",
                   workspace_bytes_for(plan, m));
   } else {

@@ -29,6 +29,26 @@ __device__ __forceinline__ _Float16 half_from_bits(uint16_t b) {
   return __builtin_bit_cast(_Float16, b);
 }
 
+__device__ __forceinline__ float f32_from_bits(uint32_t b) { return __builtin_bit_cast(float, b); }
+
+// Eight fp32 values (two 16-byte words, in memory order) -> eight bf16 packed
+// in four dwords, each rounded to nearest even by the compiler's
+// float -> __bf16 conversion (the one the window-row cast uses), so a row
+// converted here equals the same row cast beforehand, bit for bit.
+__device__ __forceinline__ uint32_t bf16x2_rne(uint32_t lo_bits, uint32_t hi_bits) {
+  const b2_t v = {(__bf16)f32_from_bits(lo_bits), (__bf16)f32_from_bits(hi_bits)};
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ u32x4 bf16x8_rne(u32x4 lo, u32x4 hi) {
+  u32x4 out;
+  out[0] = bf16x2_rne(lo[0], lo[1]);
+  out[1] = bf16x2_rne(lo[2], lo[3]);
+  out[2] = bf16x2_rne(hi[0], hi[1]);
+  out[3] = bf16x2_rne(hi[2], hi[3]);
+  return out;
+}
+
 // ---------------------------------------------------------------------------
 // Q8_0-style dequant of eight consecutive codes of one 32-block (opus r35
 // track A, section 1: block-quantised weights become f16 through `dq_f16`).

@@ -6,8 +6,10 @@
 namespace skinny {
 
 // one translation unit per weight type (gemv_f16.hip, gemv_bf16.hip, gemv_q8.hip)
+// and one for bf16 weights fed by fp32 rows (gemv_bf16_a32.hip)
 hipError_t launch_gemv_f16(const GemvArgs&, int, int, int, int, hipStream_t);
 hipError_t launch_gemv_bf16(const GemvArgs&, int, int, int, int, hipStream_t);
+hipError_t launch_gemv_bf16_a32(const GemvArgs&, int, int, int, int, hipStream_t);
 hipError_t launch_gemv_q8(const GemvArgs&, int, int, int, int, hipStream_t);
 
 namespace {
@@ -243,6 +245,9 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const int8_t* __restr
 
 hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_kind,
                        int waves_per_block, hipStream_t stream) {
+  if (args.a_kind == kAF32)
+    return w_kind == WK_BF16 ? launch_gemv_bf16_a32(args, m, T, out_kind, waves_per_block, stream)
+                             : hipErrorInvalidValue;
   switch (w_kind) {
     case WK_F16: return launch_gemv_f16(args, m, T, out_kind, waves_per_block, stream);
     case WK_BF16: return launch_gemv_bf16(args, m, T, out_kind, waves_per_block, stream);

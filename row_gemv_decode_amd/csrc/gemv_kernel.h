@@ -235,9 +235,22 @@ __device__ __forceinline__ u32x4 w_as_halves(const WChunk<WK>& w) {
   }
 }
 
+// Chunk c (eight elements) of A row r as eight 16-bit values: loaded as
+// stored, or (AK = kAF32) two 16-byte words of fp32 rounded to bf16 on the
+// way in -- the window-row cast fused into the GEMV's A load.
+template <int AK>
+__device__ __forceinline__ u32x4 load_a8(const GemvArgs& g, int r, int c) {
+  if constexpr (AK == kAF32) {
+    const u32x4* p = (const u32x4*)((const float*)g.A + (int64_t)r * g.lda + (int64_t)c * 8);
+    return bf16x8_rne(p[0], p[1]);
+  } else {
+    return *(const u32x4*)((const uint16_t*)g.A + (int64_t)r * g.lda + (int64_t)c * 8);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // The GEMV kernel.  M rows (template), T chunk slots per lane, weight kind WK,
-// output kind CK, G columns reduced per pass.  G changes only how many
+// output kind CK, G columns reduced per pass, epilogue EPI, A kind AK.  G changes only how many
 // columns share one pass of the reduction tree, never a column's arithmetic.
 //
 // Wave -> work: with S <= kGemvBlockSplitMax k splits, a workgroup holds
@@ -252,7 +265,7 @@ __device__ __forceinline__ u32x4 w_as_halves(const WChunk<WK>& w) {
 // The range counters live in the caller's workspace, start at zero and are
 // left at zero.
 // ---------------------------------------------------------------------------
-template <int M, int T, int WK, int CK, int G, int EPI>
+template <int M, int T, int WK, int CK, int G, int EPI, int AK>
 __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(GemvArgs g) {
   using Shape = GemvShape<M, G>;
   constexpr int P = Shape::P;
@@ -299,9 +312,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
       const int e = (int)threadIdx.x + i * (int)blockDim.x;
       const int r = e / (64 * T);
       const int c = e - r * (64 * T);
-      a_share[i] = (e < M * 64 * T && c < g.nchunks)
-                       ? *(const u32x4*)(g.A + (int64_t)r * g.lda + (int64_t)c * 8)
-                       : u32x4{0u, 0u, 0u, 0u};
+      a_share[i] = (e < M * 64 * T && c < g.nchunks) ? load_a8<AK>(g, r, c) : u32x4{0u, 0u, 0u, 0u};
     }
   }
 
@@ -345,8 +356,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
     for (int t = 0; t < T; ++t) {
 #pragma unroll
       for (int r = 0; r < M; ++r) {
-        a[t][r] = valid[t] ? *(const u32x4*)(g.A + (int64_t)r * g.lda + (int64_t)chunk[t] * 8)
-                           : u32x4{0u, 0u, 0u, 0u};
+        a[t][r] = valid[t] ? load_a8<AK>(g, r, chunk[t]) : u32x4{0u, 0u, 0u, 0u};
       }
     }
   }
@@ -432,42 +442,45 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
 typedef void (*gemv_fn)(GemvArgs);
 
 // [group: 1 column, gemv_group_max(M) columns][C kind: f32, f16, bf16]
-template <int M, int T, int WK>
+template <int M, int T, int WK, int AK>
 struct GemvRow {
   static constexpr int GM = gemv_group_max(M);
   static constexpr gemv_fn out[2][3] = {
-      {gemv_rows_kernel<M, T, WK, CK_F32, 1, kEpiNone>, gemv_rows_kernel<M, T, WK, CK_F16, 1, kEpiNone>,
-       gemv_rows_kernel<M, T, WK, CK_BF16, 1, kEpiNone>},
-      {gemv_rows_kernel<M, T, WK, CK_F32, GM, kEpiNone>, gemv_rows_kernel<M, T, WK, CK_F16, GM, kEpiNone>,
-       gemv_rows_kernel<M, T, WK, CK_BF16, GM, kEpiNone>}};
+      {gemv_rows_kernel<M, T, WK, CK_F32, 1, kEpiNone, AK>, gemv_rows_kernel<M, T, WK, CK_F16, 1, kEpiNone, AK>,
+       gemv_rows_kernel<M, T, WK, CK_BF16, 1, kEpiNone, AK>},
+      {gemv_rows_kernel<M, T, WK, CK_F32, GM, kEpiNone, AK>, gemv_rows_kernel<M, T, WK, CK_F16, GM, kEpiNone, AK>,
+       gemv_rows_kernel<M, T, WK, CK_BF16, GM, kEpiNone, AK>}};
 };
 
 // the scalar gate's kernels (sigmoid epilogue; f32 or f16 gate values)
-template <int M, int T, int WK>
+template <int M, int T, int WK, int AK>
 struct GemvGateRow {
   static constexpr int GM = gemv_group_max(M);
   static constexpr gemv_fn out[2][3] = {
-      {gemv_rows_kernel<M, T, WK, CK_F32, 1, kEpiSigmoid>, gemv_rows_kernel<M, T, WK, CK_F16, 1, kEpiSigmoid>,
-       nullptr},
-      {gemv_rows_kernel<M, T, WK, CK_F32, GM, kEpiSigmoid>, gemv_rows_kernel<M, T, WK, CK_F16, GM, kEpiSigmoid>,
-       nullptr}};
+      {gemv_rows_kernel<M, T, WK, CK_F32, 1, kEpiSigmoid, AK>,
+       gemv_rows_kernel<M, T, WK, CK_F16, 1, kEpiSigmoid, AK>, nullptr},
+      {gemv_rows_kernel<M, T, WK, CK_F32, GM, kEpiSigmoid, AK>,
+       gemv_rows_kernel<M, T, WK, CK_F16, GM, kEpiSigmoid, AK>, nullptr}};
 };
 
-template <int T, int WK, int... Ms>
+template <int T, int WK, int AK, int... Ms>
 gemv_fn gemv_pick(int m, int group, int out_kind) {
-  const gemv_fn(*tbl[])[3] = {GemvRow<Ms, T, WK>::out...};
+  const gemv_fn(*tbl[])[3] = {GemvRow<Ms, T, WK, AK>::out...};
   return tbl[m - 1][group][out_kind];
 }
 
-template <int T, int WK, int... Ms>
+template <int T, int WK, int AK, int... Ms>
 gemv_fn gemv_pick_gate(int m, int group, int out_kind) {
-  const gemv_fn(*tbl[])[3] = {GemvGateRow<Ms, T, WK>::out...};
+  const gemv_fn(*tbl[])[3] = {GemvGateRow<Ms, T, WK, AK>::out...};
   return tbl[m - 1][group][out_kind];
 }
 
-template <int WK>
+// AK = kAF32 is instantiated for bf16 weights only (its own translation unit)
+template <int WK, int AK = kA16>
 hipError_t launch_gemv_kind(const GemvArgs& args, int m, int T, int out_kind, int waves_per_block,
                             hipStream_t stream) {
+  static_assert(AK == kA16 || WK == WK_BF16, "fp32 rows feed bf16 weights only");
+  if (args.a_kind != AK) return hipErrorInvalidValue;
   if (m < 1 || m > kGemvMaxM || (T != 1 && T != 2) || out_kind < 0 || out_kind > 2 ||
       waves_per_block < 1 || waves_per_block > kGemvMaxWavesPerBlock || args.cpw < 1 ||
       args.cpw > kGemvCpwMax || (args.S == 1 && waves_per_block < 4))
@@ -476,12 +489,13 @@ hipError_t launch_gemv_kind(const GemvArgs& args, int m, int T, int out_kind, in
   const int group = args.cpw < gemv_group_max(m) ? 0 : 1;
   gemv_fn fn = nullptr;
   if (args.epilogue == kEpiNone) {
-    fn = T == 1 ? gemv_pick<1, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind)
-                : gemv_pick<2, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind);
+    fn = T == 1 ? gemv_pick<1, WK, AK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind)
+                : gemv_pick<2, WK, AK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind);
   } else if constexpr (WK == WK_BF16) {  // the gate: bf16 weights only
     if (args.epilogue == kEpiSigmoid)
-      fn = T == 1 ? gemv_pick_gate<1, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind)
-                  : gemv_pick_gate<2, WK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind);
+      fn = T == 1
+               ? gemv_pick_gate<1, WK, AK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind)
+               : gemv_pick_gate<2, WK, AK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind);
   }
   if (fn == nullptr) return hipErrorInvalidValue;
   int64_t blocks;

@@ -27,7 +27,7 @@ constexpr int kGemvMaxWavesPerBlock = 8;
 constexpr int kGemvBlockSplitMax = 8;
 
 struct GemvArgs {
-  const uint16_t* A;       // [m][lda] f16/bf16 bits
+  const void* A;           // [m][lda] f16/bf16 bits, or fp32 (a_kind = kAF32)
   int64_t lda;
   const void* W;           // [n][k] f16/bf16 bits, or int8 codes for Q8_0
   const uint16_t* scales;  // Q8_0 scales [n][k/32] (f16 bits), else null
@@ -44,10 +44,16 @@ struct GemvArgs {
   uint32_t* counters;       // [waves_per_split] arrivals per column range (S > kGemvBlockSplitMax),
                             // zero between calls
   int32_t epilogue;         // kEpiNone, or kEpiSigmoid: C = 1 / (1 + e^-sum)
+  int32_t a_kind;           // kA16, or kAF32 (bf16 weights only)
 };
 
 constexpr int kEpiNone = 0;
 constexpr int kEpiSigmoid = 1;
+
+// A rows: kA16 -- the weights' own 16-bit type; kAF32 -- fp32, each value
+// rounded to bf16 (nearest even) as it is loaded
+constexpr int kA16 = 0;
+constexpr int kAF32 = 1;
 
 // out_kind: 0 f32, 1 f16, 2 bf16 (C)
 hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_kind,

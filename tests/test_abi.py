@@ -96,6 +96,12 @@ def test_tile_table():
     (dict(max_m=64, k=(1 << 20) + 8), sk.ERR_SHAPE),          # GEMM path: k <= 2^20
     (dict(max_m=16, k=(1 << 20) + 8), sk.OK),                 # GEMV only: fine
     (dict(w_dtype=sk.Q8_0, k=32, max_m=17), sk.ERR_SHAPE),    # Q8_0 GEMM: k >= 64
+    (dict(a_dtype=sk.F32, w_dtype=sk.BF16), sk.OK),           # fp32 rows, cast on load
+    (dict(a_dtype=sk.F32, w_dtype=sk.BF16, flags=sk.EPILOGUE_SIGMOID), sk.OK),  # the one-launch gate
+    (dict(a_dtype=sk.F32, w_dtype=sk.BF16, max_m=17), sk.ERR_UNSUPPORTED),      # GEMV regime only
+    (dict(a_dtype=sk.F32, w_dtype=sk.BF16, flags=sk.FORCE_GEMM), sk.ERR_UNSUPPORTED),
+    (dict(a_dtype=sk.F32, w_dtype=sk.F16), sk.ERR_UNSUPPORTED),                # bf16 weights only
+    (dict(a_dtype=sk.F32, w_dtype=sk.Q8_0), sk.ERR_UNSUPPORTED),
     (dict(w_dtype=sk.Q8_0, k=32, flags=sk.FORCE_GEMM), sk.ERR_SHAPE),
     (dict(w_dtype=sk.Q8_0, k=32, max_m=16), sk.OK),           # GEMV only: fine
     (dict(w_dtype=sk.Q8_0, k=96, max_m=17), sk.OK),           # an odd number of scales
@@ -339,6 +345,26 @@ def test_gate_plan_info():
     g = plan(n=1, k=5120, a=sk.BF16, w=sk.BF16, flags=sk.EPILOGUE_SIGMOID)
     assert " epilogue=sigmoid " in g.info(16) and "path=gemv" in g.info(16)
     assert "epilogue" not in plan(n=1, k=5120, a=sk.BF16, w=sk.BF16).info(1)
+
+
+def test_fp32_rows_shape_by_m():
+    # fp32 A: fused into the GEMV while A is staged in LDS (unsplit k) or
+    # m <= 10; above that (k split) the rows are cast into the workspace first
+    g = plan(n=1, k=5120, a=sk.F32, w=sk.BF16, flags=sk.EPILOGUE_SIGMOID)
+    assert "a=f32(fused) " in g.info(10) and "workspace=0" in g.info(10)
+    assert "a=f32(cast-launch) " in g.info(11)
+    assert f"workspace={11 * 5120 * 2}" in g.info(11)  # 112640 B, a multiple of 256
+    assert g.workspace_bytes == 16 * 5120 * 2
+    assert plan(n=1, k=5120, max_m=10, a=sk.F32, w=sk.BF16).workspace_bytes == 0
+    # lda > k: rows 0..m-2 at full stride, the last one up to k, rounded to 256 B
+    r = plan(n=256, k=5120, lda=5128, a=sk.F32, w=sk.BF16)
+    assert r.workspace_bytes == -(-(15 * 5128 + 5120) * 2 // 256) * 256
+    # k split across workgroups: the cast rows follow the counters and partials
+    q = plan(n=256, k=16384, a=sk.F32, w=sk.BF16)
+    assert q.workspace_bytes == 16 * 16 * 256 * 4 + 256 + 16 * 16384 * 2
+    # unsplit k (k <= 1024): always fused
+    u = plan(n=4864, k=896, a=sk.F32, w=sk.BF16)
+    assert "a=f32(fused) " in u.info(16) and u.workspace_bytes == 0
 
 
 @fake_pointers

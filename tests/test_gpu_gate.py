@@ -1,7 +1,8 @@
 """GPU parity of the window-row cast and the scalar gate (Strata PR #109,
 "What": the bf16 cast of the window's fp32 rows in one call; the shared
 expert's scalar gate, a multi-row GEMV followed by a sigmoid, here applied as
-the GEMV stores) against the CPU oracle.
+the GEMV stores) against the CPU oracle, and of the cast fused into the GEMV's
+A load (one launch) against the cast launch followed by the bf16 GEMV.
 
 Bars: the cast is bitwise equal to the oracle's round-to-nearest-even; the
 gate meets max|g - g_ref| / max|g_ref| <= 2e-3 and an element-wise bound (the
@@ -132,3 +133,83 @@ def test_gate_f16_output():
     torch.cuda.synchronize()
     # the f16 gate is the f32 gate rounded to nearest even
     assert np.array_equal(bits_of(out16), bits_of(out32.to(torch.float16)))
+
+
+# --- the cast fused into the GEMV's A load (plans with fp32 A) --------------
+# Every reduction shape: k = 512 unsplit (A in registers for m < 4, staged in
+# LDS for m >= 4), k = 2048 / 5120 split inside the workgroup, k = 16384 split
+# across workgroups.  The fused launch must give the bits of the cast launch
+# followed by the bf16 plan.
+
+@pytest.mark.parametrize("n,k,m", [(1, 512, 3), (1, 512, 16), (7, 2048, 5), (1, 5120, 1), (1, 5120, 16),
+                                   (3, 16384, 16)])
+def test_fused_gate_equals_cast_then_gate(n, k, m):
+    print(f"fused gate n={n} k={k} m={m}", flush=True)
+    A = WL.gen_matrix((m, k), "f32", ("normal", 1.0), 951 + k + m)
+    W = WL.gen_matrix((n, k), "bf16", ("normal", 0.02), 952 + k)
+    dA, dW = torch.from_numpy(A).cuda(), to_dev(W, "bf16")
+    fused = sk.gate(dA, dW, max_m=16)
+    two = torch.empty_like(fused)
+    plan = sk.Plan(n, k, 16, sk.BF16, sk.BF16, sk.F32, flags=sk.EPILOGUE_SIGMOID)
+    plan.run(m, sk.cast_f32_bf16(dA), dW, two)
+    torch.cuda.synchronize()
+    assert "a=f32(" in sk.get_plan(n, k, 16, sk.F32, sk.BF16, sk.F32, sk.EPILOGUE_SIGMOID).info(m)
+    assert np.array_equal(bits_of(fused), bits_of(two))
+    _check_gate(A, W, fused.cpu().numpy())
+
+
+@pytest.mark.parametrize("n,k", [(4864, 896), (256, 5120), (64, 16384)])
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+def test_fp32_rows_gemv_equals_cast_then_gemv(n, k, out):
+    odt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[out]
+    code = {"f32": sk.F32, "f16": sk.F16, "bf16": sk.BF16}[out]
+    A = WL.gen_matrix((16, k), "f32", ("normal", 1.0), 961 + k)
+    W = WL.gen_matrix((n, k), "bf16", ("normal", 0.02), 962 + k)
+    dA, dW = torch.from_numpy(A).cuda(), to_dev(W, "bf16")
+    dA16 = sk.cast_f32_bf16(dA)
+    fused_plan = sk.Plan(n, k, 16, sk.F32, sk.BF16, code)
+    plain_plan = sk.Plan(n, k, 16, sk.BF16, sk.BF16, code)
+    for m in (1, 4, 10, 11, 16):  # fused up to m = 10, cast launch above when k is split
+        print(f"fp32 rows n={n} k={k} m={m} -> {out}: {fused_plan.info(m)}", flush=True)
+        a = torch.empty((m, n), dtype=odt, device="cuda")
+        b = torch.empty((m, n), dtype=odt, device="cuda")
+        fused_plan.run(m, dA[:m], dW, a)
+        plain_plan.run(m, dA16[:m], dW, b)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(a), bits_of(b)), m
+    ref = oracle.mm(oracle.cast_bf16(A), "bf16", W, "bf16")
+    if out != "bf16":
+        assert rel_err(a.float().cpu().numpy(), ref) <= REL_TOL
+
+
+def test_router_topk_from_fp32_rows():
+    wl = WL.WORKLOADS["router_topk"]
+    W = to_dev(WL.gen_w(wl), "bf16")
+    A = WL.gen_matrix((16, wl.k), "f32", ("normal", 1.0), 971)
+    dA = torch.from_numpy(A).cuda()
+    for m in (1, 5, 16):
+        print(f"router top-k from fp32 rows m={m}", flush=True)
+        lg, idx, val = sk.gemv_topk(dA[:m], W, topk=10, max_m=16)
+        lg2, idx2, val2 = sk.gemv_topk(sk.cast_f32_bf16(dA[:m]), W, topk=10, max_m=16)
+        torch.cuda.synchronize()
+        for x, y in ((lg, lg2), (idx, idx2), (val, val2)):
+            assert np.array_equal(bits_of(x), bits_of(y)), m
+
+
+def test_fp32_rows_strided():
+    # lda > k: the fused load and the cast launch read rows at the stride
+    n, k, lda = 256, 5120, 5128
+    A = WL.gen_matrix((16, lda), "f32", ("normal", 1.0), 981)
+    W = to_dev(WL.gen_matrix((n, k), "bf16", ("normal", 0.02), 982), "bf16")
+    dA = torch.from_numpy(A).cuda()
+    dA16 = sk.cast_f32_bf16(dA[:, :k].contiguous())
+    fused_plan = sk.Plan(n, k, 16, sk.F32, sk.BF16, sk.F32, lda=lda)
+    plain_plan = sk.Plan(n, k, 16, sk.BF16, sk.BF16, sk.F32)
+    for m in (4, 16):
+        print(f"fp32 rows lda={lda} m={m}: {fused_plan.info(m)}", flush=True)
+        a = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        b = torch.empty((m, n), dtype=torch.float32, device="cuda")
+        fused_plan.run(m, dA, W, a)
+        plain_plan.run(m, dA16[:m], W, b)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(a), bits_of(b)), m

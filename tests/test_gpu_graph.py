@@ -7,7 +7,7 @@ bit for bit.  This covers the run shapes that keep state in the caller's
 workspace between calls (the arrival counters of a GEMV whose k is split across
 workgroups, which the kernels reset) and the two-launch shapes (the GEMM's
 k-chunk partials + ordered reduce, the router's GEMV + top-k, the gate's cast +
-GEMV), none of which record a memset.
+GEMV) and the gate as one launch with the cast fused; none records a memset.
 """
 import numpy as np
 import pytest
@@ -112,17 +112,23 @@ def test_gemm_chunked_graph_replays(flag):
     _replay_matches_eager(fn, outs, calls=len(ms))
 
 
-def test_gate_graph_replays():
+@pytest.mark.parametrize("shape", ["cast_then_gemv", "fused"])
+def test_gate_graph_replays(shape):
     wl = WL.WORKLOADS["scalar_gate"]
     W = to_dev(WL.gen_w(wl), "bf16")
     A = torch.from_numpy(np.ascontiguousarray(WL.gen_a(wl, 16))).cuda()
     ms = (1, 16)
     A16 = torch.empty((16, wl.k), dtype=torch.bfloat16, device="cuda")
-    plan = sk.Plan(wl.n, wl.k, 16, sk.BF16, sk.BF16, sk.F32, flags=sk.EPILOGUE_SIGMOID)
+    a_code = sk.F32 if shape == "fused" else sk.BF16
+    plan = sk.Plan(wl.n, wl.k, 16, a_code, sk.BF16, sk.F32, flags=sk.EPILOGUE_SIGMOID)
     outs = [(torch.empty((m, wl.n), dtype=torch.float32, device="cuda"),) for m in ms]
 
     def fn(i):
         m = ms[i % len(ms)]
-        sk.cast_f32_bf16(A[:m], out=A16[:m])
-        plan.run(m, A16[:m], W, outs[i % len(ms)][0])
+        if shape == "fused":
+            plan.run(m, A[:m], W, outs[i % len(ms)][0])
+        else:
+            sk.cast_f32_bf16(A[:m], out=A16[:m])
+            plan.run(m, A16[:m], W, outs[i % len(ms)][0])
+    print(f"graph gate {shape}", flush=True)
     _replay_matches_eager(fn, outs, calls=len(ms))
