@@ -142,8 +142,10 @@ const TileCost& tile_cost(int id) {
       {0.5776, 2, 0.120, 1.225},  // 64x96_w2x1
       {0.3722, 1, 0.000, 1.000},  // 32x96_w1x1
       {0.2406, 2, 0.840, 1.000},  // 32x64_w1x2
+      {0.8760, 1, 0.080, 1.000},  // 192x128_w2x2
+      {1.4250, 1, 0.000, 1.000},  // 192x256_w2x4
   };
-  static_assert(sizeof(kCost) / sizeof(kCost[0]) == 13, "one cost row per tile");
+  static_assert(sizeof(kCost) / sizeof(kCost[0]) == 15, "one cost row per tile");
   return kCost[id];
 }
 

@@ -616,11 +616,13 @@ const TileEntry* tiles() {
       make_tile<64, 96, 2, 1, 3, false>("64x96_w2x1"),
       make_tile<32, 96, 1, 1, 5, true>("32x96_w1x1"),
       make_tile<32, 64, 1, 2, 5, true>("32x64_w1x2"),
+      make_tile<192, 128, 2, 2, 3, false>("192x128_w2x2"),
+      make_tile<192, 256, 2, 4, 2, false>("192x256_w2x4"),
   };
   return table;
 }
 
-constexpr int kTileCount = 13;
+constexpr int kTileCount = 15;
 
 }  // namespace
 

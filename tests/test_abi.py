@@ -58,13 +58,13 @@ def test_abi_version_and_status_strings():
 
 def test_tile_table():
     names = sk.gemm_tiles()
-    assert len(names) == L.skinny_gemm_tile_count() == 13
+    assert len(names) == L.skinny_gemm_tile_count() == 15
     for nm in names:
         tm, rest = nm.split("x", 1)
         tn, w = rest.split("_w")
         wm, wn = w.split("x")
         assert int(tm) % (32 * int(wm)) == 0 and int(tn) % (32 * int(wn)) == 0
-    assert L.skinny_gemm_tile_name(-1) is None and L.skinny_gemm_tile_name(13) is None
+    assert L.skinny_gemm_tile_name(-1) is None and L.skinny_gemm_tile_name(15) is None
 
 
 @pytest.mark.parametrize("fields,status", [
@@ -90,7 +90,7 @@ def test_tile_table():
     (dict(flags=sk.EPILOGUE_SIGMOID | sk.FORCE_GEMM, a_dtype=sk.BF16, w_dtype=sk.BF16), sk.ERR_UNSUPPORTED),
     (dict(flags=sk.FORCE_GEMV | sk.FORCE_GEMM), sk.ERR_INVALID_ARG),
     (dict(flags=sk.FORCE_GEMV, max_m=17), sk.ERR_INVALID_ARG),
-    (dict(tile_id=13), sk.ERR_INVALID_ARG),
+    (dict(tile_id=15), sk.ERR_INVALID_ARG),
     (dict(tile_id=-2), sk.ERR_INVALID_ARG),
     (dict(num_cus=-1), sk.ERR_INVALID_ARG),
     (dict(max_m=64, k=(1 << 20) + 8), sk.ERR_SHAPE),          # GEMM path: k <= 2^20
@@ -171,8 +171,9 @@ def test_gemv_block_shape(k, S, shape, reduce):
     (7680, 2560, 150, "128x64_w2x2"),
     (7680, 2560, 306, "128x96_w4x1"),
     (7680, 2560, 448, "128x128_w2x2"),
-    (7680, 2560, 700, "256x128_w4x2"),
-    (7680, 2560, 1050, "256x256_w2x4"),
+    (7680, 2560, 520, "192x128_w2x2"),   # 3 row tiles, 8 padded rows (256 rows: 248)
+    (7680, 2560, 700, "192x128_w2x2"),
+    (7680, 2560, 1050, "192x256_w2x4"),  # 150 x 256-row blocks leave 106 CUs idle
     (7680, 2560, 2048, "256x256_w2x4"),
 ])
 def test_tile_selector_picks(n, k, m, tile):
