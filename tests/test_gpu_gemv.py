@@ -79,7 +79,7 @@ def test_router_topk_parity(m):
     assert rel_err(lg, ref) <= REL_TOL
     assert np.all(np.abs(lg - ref) <= _f32_bound(A, "bf16", W, "bf16"))
     # exact: the GPU's top-k equals the oracle's top-k of the GPU's own logits
-    oi, ov = oracle.topk(lg.astype(np.float64), 10)
+    oi, ov = oracle.topk(lg.astype(np.float64), topk)
     assert np.array_equal(idx.cpu().numpy(), oi)
     assert np.array_equal(val.cpu().numpy().view(np.uint32), ov.astype(np.float32).view(np.uint32))
 
@@ -114,7 +114,7 @@ def test_q8_gemv_parity_and_fused_equals_unfused(m):
     assert np.array_equal(bits_of(C), bits_of(C2))
 
 
-def _topk_case(m, n, k, seed, dup_cols=(), one_hot=False, max_m=16, flags=0, negative=False):
+def _topk_case(m, n, k, seed, dup_cols=(), one_hot=False, max_m=16, flags=0, negative=False, topk=10):
     """Router-style inputs; dup_cols lists (src, dst) weight rows to duplicate
     (equal logits -> ties); one_hot makes A rows one-hot so logits are exact;
     negative sets every weight's sign bit."""
@@ -129,13 +129,13 @@ def _topk_case(m, n, k, seed, dup_cols=(), one_hot=False, max_m=16, flags=0, neg
             A[r, (7 * r) % k] = 0x3F80  # bf16 1.0
     else:
         A = WL.gen_matrix((m, k), "bf16", ("normal", 1.0), seed + 1)
-    logits, idx, val = sk.gemv_topk(to_dev(A, "bf16"), to_dev(W, "bf16"), topk=10, max_m=max_m,
+    logits, idx, val = sk.gemv_topk(to_dev(A, "bf16"), to_dev(W, "bf16"), topk=topk, max_m=max_m,
                                     flags=flags)
     torch.cuda.synchronize()
     lg = logits.cpu().numpy()
     ref = oracle.mm(A, "bf16", W, "bf16")
     assert rel_err(lg, ref) <= REL_TOL
-    oi, ov = oracle.topk(lg.astype(np.float64), 10)
+    oi, ov = oracle.topk(lg.astype(np.float64), topk)
     assert np.array_equal(idx.cpu().numpy(), oi)
     assert np.array_equal(val.cpu().numpy().view(np.uint32), ov.astype(np.float32).view(np.uint32))
     return lg, idx.cpu().numpy()
@@ -166,6 +166,14 @@ def test_topk_negative_logits_every_register_width(n):
 def test_topk_rows_beyond_register_cache(n):
     # n > 1024 exercises the re-read path of the top-k; n = 10 takes every column
     _topk_case(5, n, 512, 321 + n)
+
+
+@pytest.mark.parametrize("n,topk", [(1, 1), (32, 32), (256, 32), (1100, 32), (256, 1)])
+def test_topk_sizes_at_the_limits(n, topk):
+    # one expert; topk = n; the largest topk in a register-cached row and on
+    # the re-read path; topk = 1
+    print(f"top-k n={n} topk={topk}", flush=True)
+    _topk_case(4, n, 1024, 351 + n + topk, topk=topk, dup_cols=((0, n - 1),) if n > 2 else ())
 
 
 def test_topk_on_gemm_path():
