@@ -18,6 +18,11 @@ the pages, which print none for these steps):
                  fp32 to bf16, round to nearest, ties to even
   sigmoid, gate -- Strata PR #109, "What" (the shared expert's scalar gate: a
                  multi-row GEMV, then a sigmoid): gate = 1 / (1 + e^-(a . w))
+  moe_combine -- Strata PR #109, "What" (the MoE combine, one launch over the
+                 window's tokens): each token's output row is its experts'
+                 output rows weighted by its routing weights, plus the shared
+                 expert's row times its gate.  The page does not say how the
+                 routing weights are formed, so they are an input.
 """
 import ctypes
 import os
@@ -172,3 +177,35 @@ def gate(A_f32: np.ndarray, W: np.ndarray, w_kind: str = "bf16", threads=None) -
     """The scalar gate over fp32 rows: sigmoid(cast_bf16(A) . W) in fp64,
     W stored [n][k] (n = 1 for a scalar gate)."""
     return sigmoid(mm(cast_bf16(A_f32), "bf16", W, w_kind, threads=threads))
+
+
+def _row_values(x: np.ndarray, kind: str) -> np.ndarray:
+    """fp64 values of fp32 values ("f32") or bf16 bit patterns ("bf16")."""
+    if kind == "f32":
+        return np.asarray(x, dtype=np.float32).astype(np.float64)
+    return decode(x, "bf16")
+
+
+def moe_combine(y: np.ndarray, w: np.ndarray, shared=None, gate=None, kind: str = "f32") -> np.ndarray:
+    """fp64 out[t][c] = sum over i of w[t][i] * y[t][i][c], plus gate[t] * shared[t][c]
+    when the shared expert's row is given.
+
+    y: [m][topk][d] expert output rows, w: [m][topk] fp32 routing weights,
+    shared: [m][d] or None, gate: [m] fp32 (with shared); y and shared are
+    fp32 values (kind "f32") or bf16 bit patterns (kind "bf16").  Every
+    product of two fp32 values is exact in fp64; the experts are added in
+    order i = 0 .. topk - 1, then the shared term.
+    """
+    Y = _row_values(y, kind)
+    Wt = np.asarray(w, dtype=np.float32).astype(np.float64)
+    m, topk, d = Y.shape
+    assert Wt.shape == (m, topk)
+    out = np.zeros((m, d), dtype=np.float64)
+    for i in range(topk):
+        out += Wt[:, i:i + 1] * Y[:, i, :]
+    if shared is not None:
+        S = _row_values(shared, kind)
+        G = np.asarray(gate, dtype=np.float32).astype(np.float64)
+        assert S.shape == (m, d) and G.shape == (m,)
+        out += G[:, None] * S
+    return out

@@ -377,3 +377,52 @@ def test_gate_hand_example():
     assert g.shape == (3, 1)
     assert abs(g[0, 0] - 1.0 / (1.0 + math.exp(-1.0))) < 1e-15
     assert g[1, 0] == 0.5 and g[2, 0] == 0.5
+
+
+# --- the MoE combine ---------------------------------------------------------
+
+def test_moe_combine_hand_example():
+    # 0.5 * [1, 2, 3] + 0.25 * [4, 5, 6] + 2 * [1, 1, 1]: distinct values so a
+    # transposed y (token / expert / column) or a dropped term shows
+    y = np.array([[[1, 2, 3], [4, 5, 6]]], np.float32)
+    w = np.array([[0.5, 0.25]], np.float32)
+    out = oracle.moe_combine(y, w, np.ones((1, 3), np.float32), np.array([2.0], np.float32))
+    assert out.tolist() == [[3.5, 4.25, 5.0]]
+    assert oracle.moe_combine(y, w).tolist() == [[1.5, 2.25, 3.0]]  # no shared expert
+
+
+def test_moe_combine_one_hot_weights_pick_an_expert_row():
+    y, _, sh, _ = WL.gen_combine(3, 4, 64, 4401)
+    for j in range(4):
+        w = np.zeros((3, 4), np.float32)
+        w[:, j] = 1.0
+        out = oracle.moe_combine(y, w, sh, np.zeros(3, np.float32))
+        assert np.array_equal(out, y[:, j, :].astype(np.float64))
+
+
+def test_moe_combine_brute_force_exact_rationals():
+    # dyadic inputs: every product and sum is exact in fp64, so the oracle
+    # must equal exact rational arithmetic in Python, term by term
+    rng = np.random.default_rng(4411)
+    m, topk, d = 3, 5, 7
+    y = (rng.integers(-64, 65, size=(m, topk, d)) / 16.0).astype(np.float32)
+    w = (rng.integers(0, 33, size=(m, topk)) / 32.0).astype(np.float32)
+    sh = (rng.integers(-64, 65, size=(m, d)) / 8.0).astype(np.float32)
+    g = (rng.integers(0, 17, size=m) / 16.0).astype(np.float32)
+    out = oracle.moe_combine(y, w, sh, g)
+    for t in range(m):
+        for c in range(d):
+            exact = sum(Fraction(float(w[t, i])) * Fraction(float(y[t, i, c])) for i in range(topk))
+            exact += Fraction(float(g[t])) * Fraction(float(sh[t, c]))
+            assert Fraction(out[t, c]) == exact
+
+
+def test_moe_combine_linear_in_weights_and_bf16_rows():
+    # linear in w (dyadic: exact); bf16 rows give the values of their bit patterns
+    rng = np.random.default_rng(4421)
+    y = (rng.integers(-8, 9, size=(2, 3, 16)) / 4.0).astype(np.float32)
+    w1 = (rng.integers(0, 9, size=(2, 3)) / 8.0).astype(np.float32)
+    w2 = (rng.integers(0, 9, size=(2, 3)) / 8.0).astype(np.float32)
+    assert np.array_equal(oracle.moe_combine(y, w1 + w2), oracle.moe_combine(y, w1) + oracle.moe_combine(y, w2))
+    yb = WL.to_bits(y.astype(np.float64), "bf16")  # these values are exact in bf16
+    assert np.array_equal(oracle.moe_combine(yb, w1, kind="bf16"), oracle.moe_combine(y, w1))

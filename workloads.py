@@ -22,6 +22,10 @@ The five workloads stand in for the pages' measurements:
   scalar_gate   -- Strata PR #109 ("What"): the shared expert's scalar gate over
                    the window's fp32 rows (n = 1, the router's k = 5120); the
                    rows are kept in fp32 (A ~N(0,1) stored as float32).
+  moe_combine   -- Strata PR #109 ("What"): the MoE combine over the window's
+                   tokens, each with the router's top-10 experts' output rows
+                   (d = 5120, the router's k), routing weights, the shared
+                   expert's row and its scalar gate; seed base 6 (gen_combine).
 No dataset, prompt or model from the pages exists here or is recreated.
 """
 from dataclasses import dataclass
@@ -124,3 +128,21 @@ def gen_a(wl: Workload, rows: int) -> np.ndarray:
 def gen_matrix(shape, kind: str, dist, seed: int) -> np.ndarray:
     """A free-form f16 / bf16 matrix for tests at other shapes."""
     return to_bits(draw(shape, dist, seed), kind)
+
+
+# the MoE combine's workload: top-10 experts per token, rows of the router's
+# k = 5120, the window's token counts
+COMBINE = {"index": 6, "topk": 10, "d": 5120, "ms": (1, 2, 4, 8, 16)}
+
+
+def gen_combine(m: int, topk: int, d: int, seed: int, kind: str = "f32"):
+    """Inputs of the MoE combine for m tokens: expert output rows y [m][topk][d]
+    ~N(0, 0.5), routing weights w [m][topk] ~U(0, 0.2) (fp32), the shared
+    expert's rows s [m][d] ~N(0, 0.5) and its gate g [m] ~U(0, 1) (fp32); y
+    and s stored as `kind` ("f32" values or "bf16" bits).  Seeds seed + 0..3;
+    smaller m are not prefixes (draw for the largest m and slice)."""
+    y = to_bits(draw((m, topk, d), ("normal", 0.5), seed), kind)
+    w = np.random.default_rng(seed + 1).uniform(0.0, 0.2, size=(m, topk)).astype(np.float32)
+    sh = to_bits(draw((m, d), ("normal", 0.5), seed + 2), kind)
+    g = np.random.default_rng(seed + 3).uniform(0.0, 1.0, size=m).astype(np.float32)
+    return y, w, sh, g
