@@ -221,6 +221,29 @@ SKINNY_API skinny_status skinny_dequant_q8_0_run(int64_t n, int64_t k, const voi
  *   16-byte aligned, not overlapping (else SKINNY_ERR_INVALID_ARG). */
 SKINNY_API skinny_status skinny_cast_f32_bf16_run(int64_t count, const float* in, void* out, void* stream);
 
+/* The MoE combine (the Strata PR #109 page, "What": one combine launch for
+ * the window's tokens, the token taken from the grid's y index):
+ *   out[t][c] = sum over i < topk of weights[t][i] * rows[t][i][c]
+ *               + gate[t] * shared_rows[t][c]     (when shared_rows is given)
+ * accumulated in fp32, experts in order i = 0 .. topk - 1 and the shared
+ * term last, each as one fused multiply-add, then rounded once to out_dtype
+ * (nearest even for bf16).  The page does not say how the routing weights
+ * are formed; the caller passes them.  Each token's row is computed on its
+ * own, so it does not depend on m.
+ *   m >= 1 tokens; d >= 8 with d % 8 == 0 (else SKINNY_ERR_SHAPE);
+ *   1 <= topk <= SKINNY_TOPK_MAX
+ *   rows         [m][topk][d] expert output rows, SKINNY_F32 or SKINNY_BF16
+ *                (rows_dtype); 16-byte aligned
+ *   weights      f32 [m][topk] routing weights; 4-byte aligned
+ *   shared_rows  [m][d] in rows_dtype (16-byte aligned) and gate f32 [m]
+ *                (4-byte aligned): both or neither (else SKINNY_ERR_INVALID_ARG)
+ *   out          [m][d] SKINNY_F32 or SKINNY_BF16 (out_dtype), 16-byte aligned,
+ *                overlapping no input (else SKINNY_ERR_INVALID_ARG)
+ * All device pointers.  One launch. */
+SKINNY_API skinny_status skinny_moe_combine_run(int64_t m, int64_t d, int32_t topk, const void* rows,
+                                     const float* weights, const void* shared_rows, const float* gate,
+                                     int32_t rows_dtype, void* out, int32_t out_dtype, void* stream);
+
 /* Human-readable description of what a run with this m would launch: path,
  * tile or GEMV split, grid.  Writes a NUL-terminated string (truncated to
  * len). */

@@ -44,6 +44,7 @@ EXPORTS = (
     "skinny_mm_plan", "skinny_mm_plan_destroy", "skinny_mm_workspace_size", "skinny_mm_run",
     "gemv_topk_run", "skinny_dequant_q8_0_run", "skinny_mm_plan_info", "skinny_gemm_tile_count",
     "skinny_gemm_tile_name", "skinny_status_string", "skinny_abi_version", "skinny_cast_f32_bf16_run",
+    "skinny_moe_combine_run",
 )
 
 
@@ -79,6 +80,8 @@ _lib.skinny_dequant_q8_0_run.argtypes = [_i64, _i64, _vp, _vp, _vp, _vp]
 _lib.skinny_dequant_q8_0_run.restype = ctypes.c_int
 _lib.skinny_cast_f32_bf16_run.argtypes = [_i64, _vp, _vp, _vp]
 _lib.skinny_cast_f32_bf16_run.restype = ctypes.c_int
+_lib.skinny_moe_combine_run.argtypes = [_i64, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp]
+_lib.skinny_moe_combine_run.restype = ctypes.c_int
 _lib.skinny_mm_plan_info.argtypes = [_vp, _i64, ctypes.c_char_p, _sz]
 _lib.skinny_mm_plan_info.restype = ctypes.c_int
 _lib.skinny_gemm_tile_count.argtypes = []
@@ -285,6 +288,21 @@ def cast_f32_bf16(x, out=None, stream=None):
         out = torch.empty(x.shape, dtype=torch.bfloat16, device=x.device)
     _check(_lib.skinny_cast_f32_bf16_run(x.numel(), _ptr(x), _ptr(out), _stream(stream)),
            "skinny_cast_f32_bf16_run")
+    return out
+
+
+def moe_combine(rows, weights, shared=None, gate=None, out=None, out_dtype=None, stream=None):
+    """MoE combine: out[t] = sum_i weights[t][i] * rows[t][i] (+ gate[t] * shared[t]),
+    rows [m][topk][d] float32 or bfloat16 (contiguous), weights float32 [m][topk],
+    shared [m][d] like rows and gate float32 [m] (both or neither); one launch."""
+    torch = _torch()
+    m, topk, d = rows.shape
+    if out is None:
+        out = torch.empty((m, d), dtype=out_dtype or torch.float32, device=rows.device)
+    _check(_lib.skinny_moe_combine_run(m, d, topk, _ptr(rows), _ptr(weights), _ptr(shared), _ptr(gate),
+                                       _dtype_code(rows.dtype, "rows"), _ptr(out),
+                                       _dtype_code(out.dtype, "out"), _stream(stream)),
+           "skinny_moe_combine_run")
     return out
 
 

@@ -576,6 +576,44 @@ skinny_status skinny_cast_f32_bf16_run(int64_t count, const float* in, void* out
   return hip_status(launch_cast_f32_bf16(count, in, (uint16_t*)out, (hipStream_t)stream));
 }
 
+skinny_status skinny_moe_combine_run(int64_t m, int64_t d, int32_t topk, const void* rows, const float* weights,
+                                    const void* shared_rows, const float* gate, int32_t rows_dtype, void* out,
+                                    int32_t out_dtype, void* stream) {
+  if (rows == nullptr || weights == nullptr || out == nullptr) return SKINNY_ERR_INVALID_ARG;
+  if ((shared_rows == nullptr) != (gate == nullptr)) return SKINNY_ERR_INVALID_ARG;
+  if (m < 1 || m > (1LL << 31) - 1 || d < 8 || d > (1LL << 40) || topk < 1 || topk > SKINNY_TOPK_MAX)
+    return SKINNY_ERR_INVALID_ARG;
+  if (d % 8 != 0) return SKINNY_ERR_SHAPE;
+  if ((rows_dtype != SKINNY_F32 && rows_dtype != SKINNY_BF16) || (out_dtype != SKINNY_F32 && out_dtype != SKINNY_BF16))
+    return SKINNY_ERR_UNSUPPORTED;
+  if (!aligned16(rows) || !aligned16(out) || (shared_rows != nullptr && !aligned16(shared_rows)) ||
+      (reinterpret_cast<uintptr_t>(weights) & 3u) != 0 || (reinterpret_cast<uintptr_t>(gate) & 3u) != 0)
+    return SKINNY_ERR_ALIGNMENT;
+  const uintptr_t in_elem = rows_dtype == SKINNY_F32 ? 4 : 2;
+  const uintptr_t o0 = reinterpret_cast<uintptr_t>(out);
+  const uintptr_t o1 = o0 + (uintptr_t)m * (uintptr_t)d * (out_dtype == SKINNY_F32 ? 4 : 2);
+  auto overlaps = [&](const void* p, uintptr_t bytes) {
+    const uintptr_t p0 = reinterpret_cast<uintptr_t>(p);
+    return p != nullptr && p0 < o1 && o0 < p0 + bytes;
+  };
+  if (overlaps(rows, (uintptr_t)m * (uintptr_t)topk * (uintptr_t)d * in_elem) ||
+      overlaps(shared_rows, (uintptr_t)m * (uintptr_t)d * in_elem) ||
+      overlaps(weights, (uintptr_t)m * (uintptr_t)topk * 4) || overlaps(gate, (uintptr_t)m * 4))
+    return SKINNY_ERR_INVALID_ARG;
+  CombineArgs a;
+  a.m = m;
+  a.d = d;
+  a.topk = topk;
+  a.rows = rows;
+  a.weights = weights;
+  a.shared = shared_rows;
+  a.gate = gate;
+  a.out = out;
+  const int rk = rows_dtype == SKINNY_F32 ? CK_F32 : CK_BF16;
+  const int ok = out_dtype == SKINNY_F32 ? CK_F32 : CK_BF16;
+  return hip_status(launch_moe_combine(a, rk, ok, (hipStream_t)stream));
+}
+
 skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf, size_t len) {
   if (plan == nullptr || buf == nullptr || len == 0) return SKINNY_ERR_INVALID_ARG;
   if (m < 1 || m > plan->d.max_m) return SKINNY_ERR_INVALID_ARG;

@@ -1,0 +1,110 @@
+// combine.hip -- the multi-row MoE combine for gfx950 (MI355X).
+//
+// Strata PR #109, "What": the window's MoE combine is one launch over all of
+// its tokens, the token taken from blockIdx.y.  Each token's output row is its
+// routed experts' output rows weighted by its routing weights, plus the shared
+// expert's row times the shared expert's scalar gate:
+//
+//   out[t][c] = sum over i < topk of w[t][i] * y[t][i][c]  (+ g[t] * s[t][c])
+//
+// The routing weights come in as an input (the page does not say how they are
+// formed).  One wave per workgroup covers 512 columns of one token, eight per
+// lane (one or two 16-byte loads per expert row); the sum is a chain of fp32
+// fused multiply-adds in the order i = 0 .. topk - 1, then the shared term,
+// rounded once to the output type.  Nothing depends on m, so a token's row is
+// the same bits at every m.  HBM-bound: each input byte is read once.
+#include "device_common.h"
+
+namespace skinny {
+
+namespace {
+
+constexpr int kCombineCols = 8 * 64;  // columns per workgroup
+constexpr int kCombineGroup = 8;      // expert rows in flight per lane
+
+// eight consecutive values of a row as fp32
+template <int YK>
+__device__ __forceinline__ void load8(const void* base, int64_t idx, float (&v)[8]) {
+  if constexpr (YK == CK_F32) {
+    const u32x4* p = (const u32x4*)((const float*)base + idx);
+    const u32x4 lo = p[0];
+    const u32x4 hi = p[1];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[e] = f32_from_bits(lo[e]);
+      v[4 + e] = f32_from_bits(hi[e]);
+    }
+  } else {
+    const u32x4 q = *(const u32x4*)((const uint16_t*)base + idx);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      v[2 * e] = f32_from_bits(q[e] << 16);
+      v[2 * e + 1] = f32_from_bits(q[e] & 0xffff0000u);
+    }
+  }
+}
+
+template <int YK, int OK>
+__global__ __launch_bounds__(64) void moe_combine_kernel(CombineArgs a) {
+  const int64_t c0 = ((int64_t)blockIdx.x * 64 + threadIdx.x) * 8;
+  if (c0 >= a.d) return;  // d % 8 == 0: a lane's eight columns are all in or all out
+  for (int64_t t = blockIdx.y; t < a.m; t += gridDim.y) {
+    float acc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
+    const int64_t row0 = t * a.topk;
+    for (int i0 = 0; i0 < a.topk; i0 += kCombineGroup) {
+      float v[kCombineGroup][8];
+#pragma unroll
+      for (int q = 0; q < kCombineGroup; ++q)  // the group's loads, all in flight
+        if (i0 + q < a.topk) load8<YK>(a.rows, (row0 + i0 + q) * a.d + c0, v[q]);
+#pragma unroll
+      for (int q = 0; q < kCombineGroup; ++q) {
+        if (i0 + q < a.topk) {
+          const float w = a.weights[row0 + i0 + q];
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, v[q][e], acc[e]);
+        }
+      }
+    }
+    if (a.shared != nullptr) {
+      float s[8];
+      load8<YK>(a.shared, t * a.d + c0, s);
+      const float g = a.gate[t];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(g, s[e], acc[e]);
+    }
+    if constexpr (OK == CK_F32) {
+      u32x4* o = (u32x4*)((float*)a.out + t * a.d + c0);
+      o[0] = u32x4{__builtin_bit_cast(uint32_t, acc[0]), __builtin_bit_cast(uint32_t, acc[1]),
+                   __builtin_bit_cast(uint32_t, acc[2]), __builtin_bit_cast(uint32_t, acc[3])};
+      o[1] = u32x4{__builtin_bit_cast(uint32_t, acc[4]), __builtin_bit_cast(uint32_t, acc[5]),
+                   __builtin_bit_cast(uint32_t, acc[6]), __builtin_bit_cast(uint32_t, acc[7])};
+    } else {
+      b8_t r;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) r[e] = (__bf16)acc[e];  // round to nearest even
+      *(u32x4*)((uint16_t*)a.out + t * a.d + c0) = __builtin_bit_cast(u32x4, r);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_moe_combine(const CombineArgs& args, int rows_kind, int out_kind, hipStream_t stream) {
+  typedef void (*fn_t)(CombineArgs);
+  fn_t fn = nullptr;
+  if (rows_kind == CK_F32) fn = out_kind == CK_F32 ? moe_combine_kernel<CK_F32, CK_F32> : moe_combine_kernel<CK_F32, CK_BF16>;
+  if (rows_kind == CK_BF16)
+    fn = out_kind == CK_F32 ? moe_combine_kernel<CK_BF16, CK_F32> : moe_combine_kernel<CK_BF16, CK_BF16>;
+  if (fn == nullptr || (out_kind != CK_F32 && out_kind != CK_BF16) || args.m < 1 || args.d < 8 ||
+      args.d % 8 != 0 || args.topk < 1)
+    return hipErrorInvalidValue;
+  const int64_t xb = (args.d + kCombineCols - 1) / kCombineCols;
+  const int64_t yb = args.m < 65535 ? args.m : 65535;  // more tokens: each workgroup takes every 65535th
+  if (xb > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(fn, dim3((unsigned)xb, (unsigned)yb), dim3(64), 0, stream, args);
+  return hipGetLastError();
+}
+
+}  // namespace skinny

@@ -70,6 +70,21 @@ hipError_t launch_cast_f32_bf16(int64_t count, const float* in, uint16_t* out, h
 hipError_t launch_dequant_q8_0(int64_t n, int64_t k, const int8_t* qs, const uint16_t* d,
                                uint16_t* out, hipStream_t stream);
 
+// MoE combine: out[t][c] = sum_i w[t][i] * rows[t][i][c] (+ gate[t] * shared[t][c])
+struct CombineArgs {
+  int64_t m;             // tokens
+  int64_t d;             // row length (d % 8 == 0)
+  int64_t topk;          // expert rows per token
+  const void* rows;      // [m][topk][d] fp32 or bf16
+  const float* weights;  // [m][topk]
+  const void* shared;    // [m][d] like rows, or null (then gate is not read)
+  const float* gate;     // [m]
+  void* out;             // [m][d] fp32 or bf16
+};
+
+// rows_kind / out_kind: CK_F32 or CK_BF16
+hipError_t launch_moe_combine(const CombineArgs& args, int rows_kind, int out_kind, hipStream_t stream);
+
 // ---------------------------------------------------------------------------
 // MFMA GEMM (v_mfma_f32_32x32x16_{f16,bf16} for every tile, K-tiles of 32 in
 // increasing k, so every tile gives the same bits).

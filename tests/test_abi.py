@@ -42,7 +42,7 @@ def plan_status(**fields):
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 12, names
+    assert len(names) == 13, names
     assert set(names) == set(sk.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -366,6 +366,36 @@ def test_fp32_rows_shape_by_m():
     # unsplit k (k <= 1024): always fused
     u = plan(n=4864, k=896, a=sk.F32, w=sk.BF16)
     assert "a=f32(fused) " in u.info(16) and u.workspace_bytes == 0
+
+
+@fake_pointers
+def test_moe_combine_validation():
+    # every case fails before any launch (the pointers are made up)
+    f = L.skinny_moe_combine_run
+    P16d = ctypes.c_void_p(4 << 20)
+    P4 = ctypes.c_void_p((5 << 20) + 4)  # 4-byte aligned only
+
+    def call(m=4, d=64, topk=10, rows=P16, w=P16b, sh=None, g=None, rk=sk.F32, out=P16c, ok=sk.F32):
+        return f(m, d, topk, rows, w, sh, g, rk, out, ok, None)
+    assert call(rows=None) == sk.ERR_INVALID_ARG
+    assert call(w=None) == sk.ERR_INVALID_ARG
+    assert call(out=None) == sk.ERR_INVALID_ARG
+    assert call(sh=P16d) == sk.ERR_INVALID_ARG             # shared rows without a gate
+    assert call(g=P4) == sk.ERR_INVALID_ARG                # a gate without shared rows
+    assert call(m=0) == sk.ERR_INVALID_ARG
+    assert call(d=0) == sk.ERR_INVALID_ARG
+    assert call(topk=0) == sk.ERR_INVALID_ARG
+    assert call(topk=33) == sk.ERR_INVALID_ARG
+    assert call(d=12) == sk.ERR_SHAPE                      # d % 8 != 0
+    assert call(rk=sk.F16) == sk.ERR_UNSUPPORTED
+    assert call(ok=sk.F16) == sk.ERR_UNSUPPORTED
+    assert call(rows=ODD) == sk.ERR_ALIGNMENT
+    assert call(out=ODD) == sk.ERR_ALIGNMENT
+    assert call(w=ctypes.c_void_p((2 << 20) + 2)) == sk.ERR_ALIGNMENT
+    assert call(sh=ODD, g=P4) == sk.ERR_ALIGNMENT
+    assert call(out=P16) == sk.ERR_INVALID_ARG             # out over the expert rows
+    assert call(sh=P16c, g=P4) == sk.ERR_INVALID_ARG       # out over the shared rows
+    assert call(w=ctypes.c_void_p((3 << 20) + 64)) == sk.ERR_INVALID_ARG  # out over the weights
 
 
 @fake_pointers
