@@ -378,6 +378,53 @@ def sweep(sk, torch, rounds):
     return rows
 
 
+def sweep_combine(sk, torch, rounds):
+    """The MoE combine of the window: m tokens, each with its top-10 experts'
+    fp32 output rows (d = 5120), fp32 routing weights, the shared expert's row
+    and its gate; fp32 out.  Every call reads a different copy of the inputs
+    (a pool of at least POOL_BYTES), so they come from HBM."""
+    import workloads as WL
+
+    cfg = WL.COMBINE
+    topk, d, mmax = cfg["topk"], cfg["d"], max(cfg["ms"])
+    y, w, sh, g = WL.gen_combine(mmax, topk, d, 1000 * cfg["index"])
+    per_copy = (y.nbytes + w.nbytes + sh.nbytes + g.nbytes)
+    copies = max(2, POOL_BYTES // per_copy)
+    dev = [tuple(torch.from_numpy(a).cuda() for a in (y, w, sh, g)) for _ in range(copies)]
+    rows, keep, graphs = [], [], {}
+    for m in cfg["ms"]:
+        out = torch.empty((m, d), dtype=torch.float32, device="cuda")
+        keep.append(out)
+
+        def fn(i, m=m, out=out):
+            dy, dw, ds, dg = dev[i % copies]
+            sk.moe_combine(dy[:m], dw[:m], ds[:m], dg[:m], out=out)
+        keep.append(fn)
+        L = min(copies, 256)
+        graphs[m] = (capture(torch, fn, L), L)
+    per = {m: [] for m in cfg["ms"]}
+    for _ in range(rounds):
+        for m in cfg["ms"]:
+            gr, L = graphs[m]
+            per[m].append(time_graph(torch, gr, L, 1)[0])
+    for m in cfg["ms"]:
+        ts = sorted(per[m])
+        t_min, t_med = ts[0], ts[len(ts) // 2]
+        nbytes = m * (topk + 1) * d * 4 + m * topk * 4 + m * 4 + m * d * 4  # rows, weights, gate, out
+        row = {"workload": "moe_combine", "m": m, "path": "combine",
+               "plan": f"combine topk={topk} d={d} rows=f32 out=f32 grid={(d + 511) // 512}x{m} x 1 wave",
+               "us_per_call_min": round(t_min, 3), "us_per_call_median": round(t_med, 3),
+               "us_per_row": round(t_min / m, 4), "GBps": round(nbytes / t_min / 1e3, 1),
+               "hbm_frac": round(nbytes / t_min / 1e3 / HBM_PEAK_GBS, 4)}
+        rows.append(row)
+        log(f"  moe_combine  m={m:5d} {t_min:8.3f} us (med {t_med:8.3f})  {row['GBps']:8.1f} GB/s"
+            f"  hbm {row['hbm_frac']:.3f}  [{row['plan']}]")
+    torch.cuda.synchronize()
+    del graphs, keep, dev
+    torch.cuda.empty_cache()
+    return rows
+
+
 # ---------------------------------------------------------------------------
 # CPU baseline (the oracle, as it stands) + parity on the same sample
 # ---------------------------------------------------------------------------
@@ -532,7 +579,7 @@ def main():
         del gm
     log("per m: " + ", ".join(f"m={r['m']}: {r['us_per_row']} us/row" for r in per_m))
 
-    sweep_rows = [] if args.no_sweep else sweep(sk, torch, args.rounds)
+    sweep_rows = [] if args.no_sweep else sweep(sk, torch, args.rounds) + sweep_combine(sk, torch, args.rounds)
 
     cpu = None
     parity_ok = True

@@ -9,10 +9,13 @@
 //
 // The routing weights come in as an input (the page does not say how they are
 // formed).  One wave per workgroup covers 512 columns of one token, eight per
-// lane (one or two 16-byte loads per expert row); the sum is a chain of fp32
-// fused multiply-adds in the order i = 0 .. topk - 1, then the shared term,
-// rounded once to the output type.  Nothing depends on m, so a token's row is
+// lane (one or two 16-byte loads per expert row, every row and the shared row
+// in flight together, so the combine costs one memory round trip); the sum is
+// a chain of fp32 fused multiply-adds in the order i = 0 .. topk - 1, then the
+// shared term, rounded once to the output type.  Nothing depends on m, so a token's row is
 // the same bits at every m.  HBM-bound: each input byte is read once.
+#include <utility>
+
 #include "device_common.h"
 
 namespace skinny {
@@ -20,7 +23,6 @@ namespace skinny {
 namespace {
 
 constexpr int kCombineCols = 8 * 64;  // columns per workgroup
-constexpr int kCombineGroup = 8;      // expert rows in flight per lane
 
 // eight consecutive values of a row as fp32
 template <int YK>
@@ -44,32 +46,30 @@ __device__ __forceinline__ void load8(const void* base, int64_t idx, float (&v)[
   }
 }
 
-template <int YK, int OK>
+// TK expert rows per token (a template argument, so the loops unroll with no
+// per-row branch and every row's load is in flight before the first add)
+template <int YK, int OK, int TK>
 __global__ __launch_bounds__(64) void moe_combine_kernel(CombineArgs a) {
   const int64_t c0 = ((int64_t)blockIdx.x * 64 + threadIdx.x) * 8;
   if (c0 >= a.d) return;  // d % 8 == 0: a lane's eight columns are all in or all out
+  const bool shared = a.shared != nullptr;
   for (int64_t t = blockIdx.y; t < a.m; t += gridDim.y) {
+    float v[TK][8];
+#pragma unroll
+    for (int i = 0; i < TK; ++i) load8<YK>(a.rows, (t * TK + i) * a.d + c0, v[i]);
+    float s[8];
+    if (shared) load8<YK>(a.shared, t * a.d + c0, s);
+    const float* w = a.weights + t * TK;
     float acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] = 0.0f;
-    const int64_t row0 = t * a.topk;
-    for (int i0 = 0; i0 < a.topk; i0 += kCombineGroup) {
-      float v[kCombineGroup][8];
 #pragma unroll
-      for (int q = 0; q < kCombineGroup; ++q)  // the group's loads, all in flight
-        if (i0 + q < a.topk) load8<YK>(a.rows, (row0 + i0 + q) * a.d + c0, v[q]);
+    for (int i = 0; i < TK; ++i) {
+      const float wi = w[i];
 #pragma unroll
-      for (int q = 0; q < kCombineGroup; ++q) {
-        if (i0 + q < a.topk) {
-          const float w = a.weights[row0 + i0 + q];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(w, v[q][e], acc[e]);
-        }
-      }
+      for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(wi, v[i][e], acc[e]);
     }
-    if (a.shared != nullptr) {
-      float s[8];
-      load8<YK>(a.shared, t * a.d + c0, s);
+    if (shared) {
       const float g = a.gate[t];
 #pragma unroll
       for (int e = 0; e < 8; ++e) acc[e] = __builtin_fmaf(g, s[e], acc[e]);
@@ -89,17 +89,25 @@ __global__ __launch_bounds__(64) void moe_combine_kernel(CombineArgs a) {
   }
 }
 
+typedef void (*combine_fn)(CombineArgs);
+
+// [row kind][out kind] for TK = 1 .. 32
+template <int... TKs>
+combine_fn combine_pick(int rows_kind, int out_kind, int topk, std::integer_sequence<int, TKs...>) {
+  static const combine_fn tbl[2][2][sizeof...(TKs)] = {
+      {{moe_combine_kernel<CK_F32, CK_F32, TKs + 1>...}, {moe_combine_kernel<CK_F32, CK_BF16, TKs + 1>...}},
+      {{moe_combine_kernel<CK_BF16, CK_F32, TKs + 1>...}, {moe_combine_kernel<CK_BF16, CK_BF16, TKs + 1>...}}};
+  return tbl[rows_kind == CK_F32 ? 0 : 1][out_kind == CK_F32 ? 0 : 1][topk - 1];
+}
+
 }  // namespace
 
 hipError_t launch_moe_combine(const CombineArgs& args, int rows_kind, int out_kind, hipStream_t stream) {
-  typedef void (*fn_t)(CombineArgs);
-  fn_t fn = nullptr;
-  if (rows_kind == CK_F32) fn = out_kind == CK_F32 ? moe_combine_kernel<CK_F32, CK_F32> : moe_combine_kernel<CK_F32, CK_BF16>;
-  if (rows_kind == CK_BF16)
-    fn = out_kind == CK_F32 ? moe_combine_kernel<CK_BF16, CK_F32> : moe_combine_kernel<CK_BF16, CK_BF16>;
-  if (fn == nullptr || (out_kind != CK_F32 && out_kind != CK_BF16) || args.m < 1 || args.d < 8 ||
-      args.d % 8 != 0 || args.topk < 1)
+  if ((rows_kind != CK_F32 && rows_kind != CK_BF16) || (out_kind != CK_F32 && out_kind != CK_BF16) ||
+      args.m < 1 || args.d < 8 || args.d % 8 != 0 || args.topk < 1 || args.topk > kCombineMaxTopk)
     return hipErrorInvalidValue;
+  const combine_fn fn =
+      combine_pick(rows_kind, out_kind, (int)args.topk, std::make_integer_sequence<int, kCombineMaxTopk>{});
   const int64_t xb = (args.d + kCombineCols - 1) / kCombineCols;
   const int64_t yb = args.m < 65535 ? args.m : 65535;  // more tokens: each workgroup takes every 65535th
   if (xb > 0x7fffffff) return hipErrorInvalidValue;

@@ -82,6 +82,8 @@ struct CombineArgs {
   void* out;             // [m][d] fp32 or bf16
 };
 
+constexpr int kCombineMaxTopk = 32;  // expert rows per token the combine takes
+
 // rows_kind / out_kind: CK_F32 or CK_BF16
 hipError_t launch_moe_combine(const CombineArgs& args, int rows_kind, int out_kind, hipStream_t stream);
 

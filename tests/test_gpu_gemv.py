@@ -79,7 +79,7 @@ def test_router_topk_parity(m):
     assert rel_err(lg, ref) <= REL_TOL
     assert np.all(np.abs(lg - ref) <= _f32_bound(A, "bf16", W, "bf16"))
     # exact: the GPU's top-k equals the oracle's top-k of the GPU's own logits
-    oi, ov = oracle.topk(lg.astype(np.float64), topk)
+    oi, ov = oracle.topk(lg.astype(np.float64), 10)
     assert np.array_equal(idx.cpu().numpy(), oi)
     assert np.array_equal(val.cpu().numpy().view(np.uint32), ov.astype(np.float32).view(np.uint32))
 
