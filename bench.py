@@ -130,6 +130,29 @@ def run_only(spec, steps, warmup):
         print(json.dumps({"only": spec, "bytes_read": nbytes, "bytes_written": nbytes,
                           "us_per_copy": round(us, 2)}), flush=True)
         return
+    if parts[0] == "moe_combine":
+        cfg = WL.COMBINE
+        ms = [int(x) for x in parts[1].split(",")]
+        topk, d = cfg["topk"], cfg["d"]
+        y, w, sh, g = WL.gen_combine(max(ms), topk, d, 1000 * cfg["index"])
+        copies = max(2, POOL_BYTES // (y.nbytes + w.nbytes + sh.nbytes + g.nbytes))
+        dev = [tuple(torch.from_numpy(a).cuda() for a in (y, w, sh, g)) for _ in range(copies)]
+        outs = {m: torch.empty((m, d), dtype=torch.float32, device="cuda") for m in ms}
+
+        def call_c(i):
+            m = ms[i % len(ms)]
+            dy, dw, ds, dg = dev[i % copies]
+            sk.moe_combine(dy[:m], dw[:m], ds[:m], dg[:m], out=outs[m])
+        for i in range(warmup):
+            call_c(i)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            call_c(warmup + i)
+        torch.cuda.synchronize()
+        us = (time.perf_counter() - t0) * 1e6 / steps
+        print(json.dumps({"only": spec, "calls": steps, "us_per_call_eager": round(us, 3)}), flush=True)
+        return
     wl = WL.WORKLOADS[parts[0]]
     ms = [int(x) for x in parts[1].split(",")]
     tile = int(parts[2]) if len(parts) > 2 else -1
