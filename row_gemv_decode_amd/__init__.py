@@ -220,13 +220,23 @@ def new_workspace(plan, device):
 _plan_cache = {}
 
 
+def _dense(where, **tensors):
+    """The library reads every tensor as a dense row-major block: reject views
+    with other strides instead of reading them wrongly."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_contiguous():
+            raise ValueError(f"{where}: {name} must be contiguous (pass a Plan with lda/ldc for strided rows)")
+
+
 def _weight_kind(W):
     torch = _torch()
     if isinstance(W, tuple):
         qs, d = W
         if qs.dtype != torch.int8 or d.dtype != torch.float16:
             raise TypeError("Q8_0 weight is (int8 codes [n][k], float16 scales [n][k/32])")
+        _dense("Q8_0 weight", codes=qs, scales=d)
         return Q8_0, qs, d
+    _dense("weight", W=W)
     return _dtype_code(W.dtype, "W"), W, None
 
 
@@ -248,6 +258,7 @@ def mm(A, W, out=None, out_dtype=None, flags=0, tile_id=-1, max_m=None, stream=N
     n = Wt.shape[0]
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype or torch.float32, device=A.device)
+    _dense("mm", A=A, out=out)
     plan = get_plan(n, k, max_m or m, _dtype_code(A.dtype, "A"), wk, _dtype_code(out.dtype, "C"),
                     flags, tile_id)
     plan.run(m, A, Wt, out, scales=scales, stream=stream)
@@ -263,6 +274,7 @@ def gemv_topk(A, W, topk=10, flags=0, max_m=None, stream=None):
     logits = torch.empty((m, n), dtype=torch.float32, device=A.device)
     idx = torch.empty((m, topk), dtype=torch.int32, device=A.device)
     val = torch.empty((m, topk), dtype=torch.float32, device=A.device)
+    _dense("gemv_topk", A=A)
     plan = get_plan(n, k, max_m or m, _dtype_code(A.dtype, "A"), wk, F32, flags)
     plan.run_topk(m, A, Wt, logits, idx, val, topk, scales=scales, stream=stream)
     return logits, idx, val
@@ -274,6 +286,7 @@ def dequant_q8_0(qs, d, out=None, stream=None):
     n, k = qs.shape
     if out is None:
         out = torch.empty((n, k), dtype=torch.float16, device=qs.device)
+    _dense("dequant_q8_0", qs=qs, d=d, out=out)
     _check(_lib.skinny_dequant_q8_0_run(n, k, _ptr(qs), _ptr(d), _ptr(out), _stream(stream)),
            "skinny_dequant_q8_0_run")
     return out
@@ -299,6 +312,15 @@ def moe_combine(rows, weights, shared=None, gate=None, out=None, out_dtype=None,
     m, topk, d = rows.shape
     if out is None:
         out = torch.empty((m, d), dtype=out_dtype or torch.float32, device=rows.device)
+    _dense("moe_combine", rows=rows, weights=weights, shared=shared, gate=gate, out=out)
+    if weights.dtype != torch.float32 or tuple(weights.shape) != (m, topk):
+        raise ValueError("moe_combine: weights must be float32 [m][topk]")
+    if shared is not None and (tuple(shared.shape) != (m, d) or shared.dtype != rows.dtype):
+        raise ValueError("moe_combine: shared must be [m][d] with the rows' dtype")
+    if gate is not None and (gate.dtype != torch.float32 or tuple(gate.shape) != (m,)):
+        raise ValueError("moe_combine: gate must be float32 [m]")
+    if tuple(out.shape) != (m, d):
+        raise ValueError("moe_combine: out must be [m][d]")
     _check(_lib.skinny_moe_combine_run(m, d, topk, _ptr(rows), _ptr(weights), _ptr(shared), _ptr(gate),
                                        _dtype_code(rows.dtype, "rows"), _ptr(out),
                                        _dtype_code(out.dtype, "out"), _stream(stream)),
@@ -316,6 +338,7 @@ def gate(A, W, max_m=None, out=None, stream=None):
     n = W.shape[0]
     if out is None:
         out = torch.empty((m, n), dtype=torch.float32, device=A.device)
+    _dense("gate", A=A, out=out)
     plan = get_plan(n, k, max_m or m, _dtype_code(A.dtype, "A"), _dtype_code(W.dtype, "W"),
                     _dtype_code(out.dtype, "C"), EPILOGUE_SIGMOID)
     plan.run(m, A, W, out, stream=stream)

@@ -415,3 +415,25 @@ def test_plan_info_validation():
     assert L.skinny_mm_plan_info(p.handle, 1, None, 8) == sk.ERR_INVALID_ARG
     assert L.skinny_mm_plan_info(p.handle, 1, buf, 8) == sk.OK  # truncated, NUL-terminated
     assert len(buf.value) == 7
+
+
+def test_binding_rejects_strided_views_before_any_call():
+    # CPU tensors: each check raises before a pointer reaches the library
+    torch = pytest.importorskip("torch")
+    A = torch.zeros(16, 8, dtype=torch.float16).t()  # [8][16], not contiguous
+    W = torch.zeros(4, 16, dtype=torch.float16)
+    with pytest.raises(ValueError, match="A must be contiguous"):
+        sk.mm(A, W)
+    with pytest.raises(ValueError, match="W must be contiguous"):
+        sk.mm(torch.zeros(2, 4, dtype=torch.float16), torch.zeros(4, 8, dtype=torch.float16)[:, ::2])
+    with pytest.raises(ValueError, match="A must be contiguous"):
+        sk.gemv_topk(A.to(torch.bfloat16), W.to(torch.bfloat16), topk=2)
+    with pytest.raises(ValueError, match="A must be contiguous"):
+        sk.gate(torch.zeros(16, 8).t(), torch.zeros(1, 16, dtype=torch.bfloat16))
+    y = torch.zeros(2, 3, 16)
+    with pytest.raises(ValueError, match="rows must be contiguous"):
+        sk.moe_combine(y.transpose(1, 2).contiguous().transpose(1, 2), torch.zeros(2, 3))
+    with pytest.raises(ValueError, match="weights must be float32"):
+        sk.moe_combine(y, torch.zeros(2, 4))
+    with pytest.raises(ValueError, match="shared must be"):
+        sk.moe_combine(y, torch.zeros(2, 3), torch.zeros(2, 8), torch.zeros(2))
