@@ -2,6 +2,7 @@
 // GEMV launch dispatch, for gfx950 (MI355X).  The GEMV kernel itself is in
 // gemv_kernel.h.
 #include "gemv_kernel.h"
+#include "skinny.h"
 
 namespace skinny {
 
@@ -115,30 +116,56 @@ __device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int 
       jj[u + 1] = swap ? tj : jj[u + 1];
     }
   }
-  int res_j = 0;
-  int res_k = 0;
+  // Each round: the winner is the lane whose head holds the wave maximum (a
+  // tie takes the lowest column among the tied heads); it pops its head and
+  // notes the round in a bit mask.  A lane pops in order, so its k-th win is
+  // its k-th sorted slot: after the last round every lane writes its wins to
+  // LDS by round, and lane t reads round t.  No lane index crosses to the
+  // scalar unit inside the loop: a round is the maximum's reduction plus a
+  // few selects.
+  int skey[NC];
+  int sjj[NC];
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    skey[u] = key[u];
+    sjj[u] = jj[u];
+  }
+  uint32_t rounds_won = 0;
   for (int t = 0; t < topk; ++t) {
     const int kmax = wave_max_i32(key[0]);  // the same in every lane
-    uint64_t ball = __builtin_amdgcn_ballot_w64(key[0] == kmax);
-    if (__builtin_popcountll(ball) != 1) {  // wave-uniform; a tie, rare with continuous data
-      const int wj = wave_min_i32(((ball >> lane) & 1) ? jj[0] : kNoColumn);
-      ball = __builtin_amdgcn_ballot_w64(jj[0] == wj);
+    bool mine = key[0] == kmax;
+    if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(mine)) != 1) {  // uniform; a tie, rare
+      const int wj = wave_min_i32(mine ? jj[0] : kNoColumn);
+      mine = mine && jj[0] == wj;
     }
-    const int owner = ball != 0 ? __builtin_ctzll(ball) : 0;
-    const int wj = __builtin_amdgcn_readlane(jj[0], owner);
-    res_j = lane == t ? wj : res_j;
-    res_k = lane == t ? kmax : res_k;
-    if (lane == owner) {  // the owner pops its head
+    // the winner pops its head: each slot takes the next one under an
+    // all-ones mask (one bit-field insert per slot)
+    const uint32_t pm = 0u - (uint32_t)mine;
+    rounds_won |= pm & (1u << t);
 #pragma unroll
-      for (int u = 0; u + 1 < NC; ++u) {
-        key[u] = key[u + 1];
-        jj[u] = jj[u + 1];
-      }
-      key[NC - 1] = kNoKey;
-      jj[NC - 1] = kNoColumn;
+    for (int u = 0; u + 1 < NC; ++u) {
+      key[u] = (int)((pm & (uint32_t)key[u + 1]) | (~pm & (uint32_t)key[u]));
+      jj[u] = (int)((pm & (uint32_t)jj[u + 1]) | (~pm & (uint32_t)jj[u]));
+    }
+    key[NC - 1] = (int)((pm & (uint32_t)kNoKey) | (~pm & (uint32_t)key[NC - 1]));
+    jj[NC - 1] = (int)((pm & (uint32_t)kNoColumn) | (~pm & (uint32_t)jj[NC - 1]));
+  }
+  __shared__ int won_j[SKINNY_TOPK_MAX];
+  __shared__ int won_k[SKINNY_TOPK_MAX];
+  uint32_t left = rounds_won;
+#pragma unroll
+  for (int u = 0; u < NC; ++u) {
+    if (left != 0) {
+      const int r = __builtin_ctz(left);
+      won_j[r] = sjj[u];
+      won_k[r] = skey[u];
+      left &= left - 1;
     }
   }
+  __syncthreads();  // one wave: orders the writes before the reads
   if (lane < topk) {
+    const int res_j = won_j[lane];
+    const int res_k = won_k[lane];
     out_idx[lane] = res_j;
     // the key gives the value's bits back, except that a zero may be -0
     out_val[lane] = res_k == 0 ? row[res_j] : key_value(res_k);
@@ -258,6 +285,7 @@ hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_k
 
 hipError_t launch_topk(const float* logits, int m, int64_t n, int64_t ldl, int32_t* idx, float* val,
                        int topk, hipStream_t stream) {
+  if (topk < 1 || topk > SKINNY_TOPK_MAX || topk > n) return hipErrorInvalidValue;  // the kernels' bounds
   typedef void (*topk_fn)(const float*, int64_t, int64_t, int32_t*, float*, int);
   const topk_fn fn = n <= 64    ? topk_rows_kernel<1>
                      : n <= 128 ? topk_rows_kernel<2>
