@@ -67,7 +67,9 @@ typedef enum skinny_status {
   SKINNY_ERR_INVALID_ARG = 1, /* null pointer, bad struct_size, m/n/k/topk out of range */
   SKINNY_ERR_UNSUPPORTED = 2, /* dtype combination or flag the library does not implement */
   SKINNY_ERR_ALIGNMENT = 3,   /* pointer not 16-byte aligned or lda not a multiple of 8 */
-  SKINNY_ERR_SHAPE = 4,       /* k not a multiple of 8 (32 for Q8_0), stride < row length */
+  SKINNY_ERR_SHAPE = 4,       /* k not a multiple of 8 (32 for Q8_0), stride < row length, a
+                                 size past a stated limit (a run: a GEMV of more than about
+                                 2^31 waves, k/512 x n) */
   SKINNY_ERR_HIP = 5,         /* the HIP runtime reported an error (device query or launch) */
   SKINNY_ERR_WORKSPACE = 6    /* workspace missing or smaller than skinny_mm_workspace_size */
 } skinny_status;
@@ -115,9 +117,9 @@ typedef enum skinny_dtype {
  *   c_dtype      SKINNY_F32, SKINNY_F16 or SKINNY_BF16 (rounded to nearest even)
  *   max_m        largest m any run will pass (>= 1)
  *   n, k         output columns and reduction length (n >= 1; k >= 8, k % 8 == 0,
- *                k % 32 == 0 for Q8_0; k and lda <= 2^20, and k >= 64 for
- *                Q8_0, when the plan may use the GEMM, i.e. max_m > 16 or
- *                SKINNY_FORCE_GEMM)
+ *                k % 32 == 0 for Q8_0; k and lda <= 2^20, k >= 64 for Q8_0
+ *                and max_m * n <= 2^50 when the plan may use the GEMM, i.e.
+ *                max_m > 16 or SKINNY_FORCE_GEMM)
  *   lda, ldc     row strides of A and C in elements; 0 means dense (k and n);
  *                otherwise >= the row length; lda a multiple of 8 (A rows are
  *                read 16 bytes at a time, 32 for fp32 rows), ldc any value >= n
@@ -231,7 +233,7 @@ SKINNY_API skinny_status skinny_cast_f32_bf16_run(int64_t count, const float* in
  * are formed; the caller passes them.  Each token's row is computed on its
  * own, so it does not depend on m.
  *   m >= 1 tokens; d >= 8 with d % 8 == 0 (else SKINNY_ERR_SHAPE);
- *   1 <= topk <= SKINNY_TOPK_MAX
+ *   1 <= topk <= SKINNY_TOPK_MAX; m * topk * d <= 2^56
  *   rows         [m][topk][d] expert output rows, SKINNY_F32 or SKINNY_BF16
  *                (rows_dtype); 16-byte aligned
  *   weights      f32 [m][topk] routing weights; 4-byte aligned

@@ -341,6 +341,8 @@ skinny_status check_run(const skinny_plan* p, int64_t m, const void* A, const vo
   if (q8 != (scales != nullptr)) return SKINNY_ERR_INVALID_ARG;
   if (!aligned16(A) || !aligned16(W) || !aligned16(C) || (q8 && !aligned16(scales)))
     return SKINNY_ERR_ALIGNMENT;
+  // the GEMV numbers its waves (k splits x column ranges) in 32 bits
+  if (use_gemv(p, m) && gemv_waves_per_split(p, m) * p->gemv_S > (1LL << 31) - 1024) return SKINNY_ERR_SHAPE;
   const size_t need = workspace_bytes_for(p, m);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return SKINNY_ERR_WORKSPACE;
@@ -474,6 +476,9 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   // the GEMM addresses a block's rows through 32-bit buffer offsets
   const bool may_gemm = !(d.flags & SKINNY_FORCE_GEMV) && (d.max_m > kGemvMaxM || (d.flags & SKINNY_FORCE_GEMM));
   if (may_gemm && (d.k > kGemmMaxK || d.lda > kGemmMaxK)) return SKINNY_ERR_SHAPE;
+  // the GEMM's k-chunk partials hold up to 16 x max_m x n floats: keep every
+  // index and byte count far inside 64 bits
+  if (may_gemm && d.max_m > (1LL << 50) / d.n) return SKINNY_ERR_SHAPE;
   // the GEMM fetches a k-tile's two Q8_0 scales of a row as one 4-byte word,
   // which needs at least two scales per row (k >= 64)
   if (may_gemm && d.w_dtype == SKINNY_Q8_0 && d.k < 64) return SKINNY_ERR_SHAPE;
@@ -583,6 +588,8 @@ skinny_status skinny_moe_combine_run(int64_t m, int64_t d, int32_t topk, const v
   if ((shared_rows == nullptr) != (gate == nullptr)) return SKINNY_ERR_INVALID_ARG;
   if (m < 1 || m > (1LL << 31) - 1 || d < 8 || d > (1LL << 40) || topk < 1 || topk > SKINNY_TOPK_MAX)
     return SKINNY_ERR_INVALID_ARG;
+  // every element index (and byte count) below stays far inside 64 bits
+  if (d > (1LL << 56) / (m * (int64_t)topk)) return SKINNY_ERR_INVALID_ARG;
   if (d % 8 != 0) return SKINNY_ERR_SHAPE;
   if ((rows_dtype != SKINNY_F32 && rows_dtype != SKINNY_BF16) || (out_dtype != SKINNY_F32 && out_dtype != SKINNY_BF16))
     return SKINNY_ERR_UNSUPPORTED;

@@ -96,6 +96,8 @@ def test_tile_table():
     (dict(max_m=64, k=(1 << 20) + 8), sk.ERR_SHAPE),          # GEMM path: k <= 2^20
     (dict(max_m=16, k=(1 << 20) + 8), sk.OK),                 # GEMV only: fine
     (dict(w_dtype=sk.Q8_0, k=32, max_m=17), sk.ERR_SHAPE),    # Q8_0 GEMM: k >= 64
+    (dict(max_m=(1 << 31) - 1, n=(1 << 31) - 1), sk.ERR_SHAPE),  # GEMM: max_m * n <= 2^50
+    (dict(max_m=16, n=(1 << 31) - 1), sk.OK),                # GEMV only: fine
     (dict(a_dtype=sk.F32, w_dtype=sk.BF16), sk.OK),           # fp32 rows, cast on load
     (dict(a_dtype=sk.F32, w_dtype=sk.BF16, flags=sk.EPILOGUE_SIGMOID), sk.OK),  # the one-launch gate
     (dict(a_dtype=sk.F32, w_dtype=sk.BF16, max_m=17), sk.ERR_UNSUPPORTED),      # GEMV regime only
@@ -310,6 +312,14 @@ def topk_run(p, m, logits=P16c, idx=P16, val=P16b, k=10, ws=P16, nbytes=1 << 20)
 
 
 @fake_pointers
+def test_run_rejects_a_gemv_of_more_than_2_31_waves():
+    # 2^21 k splits x 2^28 column ranges: the wave count would not fit 32 bits
+    p = plan(n=(1 << 31) - 1, k=(1 << 31) - 8, a=sk.BF16, w=sk.BF16)
+    assert "path=gemv" in p.info(1)
+    assert run(p, 1) == sk.ERR_SHAPE
+
+
+@fake_pointers
 def test_topk_validation():
     p = plan(n=256, k=5120, a=sk.BF16, w=sk.BF16)
     assert topk_run(p, 1, idx=None) == sk.ERR_INVALID_ARG
@@ -386,6 +396,7 @@ def test_moe_combine_validation():
     assert call(d=0) == sk.ERR_INVALID_ARG
     assert call(topk=0) == sk.ERR_INVALID_ARG
     assert call(topk=33) == sk.ERR_INVALID_ARG
+    assert call(m=(1 << 31) - 1, topk=32, d=1 << 40) == sk.ERR_INVALID_ARG  # m * topk * d > 2^56
     assert call(d=12) == sk.ERR_SHAPE                      # d % 8 != 0
     assert call(rk=sk.F16) == sk.ERR_UNSUPPORTED
     assert call(ok=sk.F16) == sk.ERR_UNSUPPORTED
