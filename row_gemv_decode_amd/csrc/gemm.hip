@@ -186,6 +186,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
   // XT: read the next k-tile's fragments during this one's MFMAs (small wave
   // tiles; needs a third stage and (FM + FN) * 32 fragment registers)
   constexpr bool kCrossTile = XT;
+  constexpr bool kMfmaPriority = TM == 256 && TN == 256 && NW == 8;
   static_assert(!XT || (FM + FN <= 4 && NS >= 3), "cross-tile fragment reads");
   constexpr int SA = TM * kCPR;                              // u32x4 per stage
   constexpr int SB = Q8 ? B_ITERS * 16 * NW * 4 : TN * kCPR;  // u32x4 per stage
@@ -482,6 +483,9 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
       u32x4 af[2][FM];
       u32x4 bf[2][FN];
       read_frags(0, af[0], bf[0]);
+      // the 8-wave 256 x 256 tile: a wave in its MFMA run goes first (2-3 % at
+      // M = 2048; the other tiles measured the same or slower with it)
+      if constexpr (kMfmaPriority) __builtin_amdgcn_s_setprio(1);
 #pragma unroll
       for (int ks = 0; ks < kSteps; ++ks) {
         if (ks + 1 < kSteps) read_frags(ks + 1, af[(ks + 1) & 1], bf[(ks + 1) & 1]);
@@ -491,6 +495,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
 #pragma unroll
           for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(af[ks & 1][i], bf[ks & 1][j], acc[i][j]);
       }
+      if constexpr (kMfmaPriority) __builtin_amdgcn_s_setprio(0);
     };
     int stage = 0;
     int kt = 0;
