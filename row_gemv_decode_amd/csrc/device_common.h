@@ -59,23 +59,35 @@ __device__ __forceinline__ u32x4 bf16x8_rne(u32x4 lo, u32x4 hi) {
 // fused GEMM B-loader -- calls this one function, so their weights are equal
 // bit for bit.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ h2_t q8_pair(uint32_t two_codes_lo16, _Float16 d) {
-  const int8_t q0 = (int8_t)(two_codes_lo16 & 0xff);
-  const int8_t q1 = (int8_t)((two_codes_lo16 >> 8) & 0xff);
-  h2_t q = {(_Float16)(int16_t)q0, (_Float16)(int16_t)q1};
-  h2_t s = {d, d};
-  return s * q;
+// The code reaches f16 without a conversion instruction: with u = q + 128
+// (the byte q ^ 0x80), the f16 whose bits are 0x6400 | u is 1024 + u exactly,
+// and subtracting 1152 leaves q exactly (every step is exact in f16).  Two
+// byte permutes build four such f16 from four codes, so eight codes cost one
+// xor per four, two permutes, two packed subtracts and two packed multiplies
+// per four.
+__device__ __forceinline__ void q8_quad(uint32_t four_codes, h2_t d2, uint32_t& lo, uint32_t& hi) {
+  const uint32_t u = four_codes ^ 0x80808080u;
+  const h2_t bias = {(_Float16)1152.0f, (_Float16)1152.0f};
+  // bytes (low first): lo = u0, 0x64, u1, 0x64; hi = u2, 0x64, u3, 0x64
+  const uint32_t plo = __builtin_amdgcn_perm(0x64646464u, u, 0x04010400u);
+  const uint32_t phi = __builtin_amdgcn_perm(0x64646464u, u, 0x04030402u);
+  lo = h2_bits(d2 * (as_h2(plo) - bias));
+  hi = h2_bits(d2 * (as_h2(phi) - bias));
 }
 
 // eight codes (two dwords, little-endian bytes) -> eight f16 packed in 4 dwords
 __device__ __forceinline__ u32x4 q8_dequant8(u32x2 codes, _Float16 d) {
   const uint32_t c0 = codes[0];
   const uint32_t c1 = codes[1];
+  const h2_t d2 = {d, d};
   u32x4 out;
-  out[0] = h2_bits(q8_pair(c0, d));
-  out[1] = h2_bits(q8_pair(c0 >> 16, d));
-  out[2] = h2_bits(q8_pair(c1, d));
-  out[3] = h2_bits(q8_pair(c1 >> 16, d));
+  uint32_t a, b;
+  q8_quad(c0, d2, a, b);
+  out[0] = a;
+  out[1] = b;
+  q8_quad(c1, d2, a, b);
+  out[2] = a;
+  out[3] = b;
   return out;
 }
 
