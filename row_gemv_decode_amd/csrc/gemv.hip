@@ -102,12 +102,14 @@ __device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int 
     key[u] = ok ? order_key(x[u]) : kNoKey;
     jj[u] = ok ? j : kNoColumn;
   }
-  // stable sort of the lane's slots into rank order
+  // stable sort of the lane's slots into rank order: the slots start in
+  // increasing column order and only a strictly larger key moves up, so equal
+  // keys keep increasing columns without comparing them
 #pragma unroll
   for (int round = 0; round < NC; ++round) {
 #pragma unroll
     for (int u = round & 1; u + 1 < NC; u += 2) {
-      const bool swap = after(key[u], jj[u], key[u + 1], jj[u + 1]);
+      const bool swap = key[u] < key[u + 1];
       const int tk = key[u];
       const int tj = jj[u];
       key[u] = swap ? key[u + 1] : key[u];
