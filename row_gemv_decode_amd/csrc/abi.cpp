@@ -141,7 +141,7 @@ const TileCost& tile_cost(int id) {
       {0.4583, 1, 0.340, 1.000},  // 128x96_w4x1
       {0.5776, 2, 0.120, 1.225},  // 64x96_w2x1
       {0.3722, 1, 0.000, 1.000},  // 32x96_w1x1
-      {0.2406, 2, 0.840, 1.000},  // 32x64_w1x2
+      {0.2406, 2, 0.600, 1.000},  // 32x64_w1x2
       {0.8760, 1, 0.080, 1.000},  // 192x128_w2x2
       {1.4250, 1, 0.000, 1.000},  // 192x256_w2x4
   };

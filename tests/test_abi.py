@@ -177,6 +177,8 @@ def test_gemv_block_shape(k, S, shape, reduce):
     (7680, 2560, 700, "192x128_w2x2"),
     (7680, 2560, 1050, "192x256_w2x4"),  # 150 x 256-row blocks leave 106 CUs idle
     (7680, 2560, 2048, "256x256_w2x4"),
+    (96, 2560, 1024, "64x64_w2x2"),      # narrow N: k chunks, one block per chunk
+    (96, 2560, 2048, "32x64_w1x2"),      # one launch folding the chunks
 ])
 def test_tile_selector_picks(n, k, m, tile):
     assert f"name={tile} " in plan(n=n, k=k, max_m=2048).info(m)
