@@ -4,13 +4,15 @@
  * The operation is C[m,n] = A[m,k] . W[k,n] for small-to-moderate m, the
  * product the nx_batchscale_kat page asks about ("is the matmul amortising
  * across m?"): W is read from HBM once per call for all m rows.  Around it sit
- * the two steps the Strata PR #109 page ("What", router bullet) batches over a
- * decode window -- a multi-row GEMV and a per-row top-10 -- and the f16 dequant
- * of a block-quantised weight from the opus r35 track A page (section 1,
- * `dq_f16`), fused into the weight load path.
+ * the steps the Strata PR #109 page ("What") batches over a decode window --
+ * the router's multi-row GEMV and per-row top-10, the shared expert's scalar
+ * gate, the bf16 cast of the window's rows and the MoE combine -- and the f16
+ * dequant of a block-quantised weight from the opus r35 track A page
+ * (section 1, `dq_f16`), fused into the weight load path.
  *
  * Layouts (all row-major, element strides):
- *   A  [m][lda]   f16 or bf16 rows ("tokens"); lda >= k
+ *   A  [m][lda]   f16 or bf16 rows ("tokens"), or fp32 rows that a bf16-weight
+ *                 GEMV rounds to bf16 as it loads them; lda >= k
  *   W  [n][k]     the weight stored k-contiguous: stored row j is logical
  *                 column j of W[k,n].  f16, bf16, or Q8_0 (see below)
  *   C  [m][ldc]   f32, f16 or bf16; ldc >= n
@@ -156,7 +158,7 @@ SKINNY_API void skinny_mm_plan_destroy(skinny_plan* plan);
 
 /* Bytes of device workspace a run with this plan may need (0 when none);
  * enough for every m <= max_m, for skinny_mm_run and gemv_topk_run alike.
- * Two runs need it:
+ * Three kinds of run need it:
  *   - a GEMV whose k is split into more pieces than one workgroup sums
  *     (k > 8192 for 16-bit weights): it holds the arrival counters (first)
  *     and the fp32 partial sums that let the last wave of each column range
