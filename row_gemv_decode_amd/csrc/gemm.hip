@@ -164,6 +164,41 @@ __device__ __forceinline__ void lds_dma4(const u32x4& rsrc, uint32_t lds, int vo
 // LDS, by the same function as every other path, so it equals the f16 weight.
 __device__ __forceinline__ int q8_swz(int r) { return (r >> 2) & 3; }
 
+// four adjacent outputs in one store (8 bytes of f16 / bf16, 16 of fp32),
+// each rounded exactly as store_out rounds it; idx is a multiple of 4
+template <int CK>
+__device__ __forceinline__ void store_out4(void* base, int64_t idx, const float (&v)[4]) {
+  if constexpr (CK == CK_F32) {
+    *(u32x4*)((float*)base + idx) = u32x4{__builtin_bit_cast(uint32_t, v[0]), __builtin_bit_cast(uint32_t, v[1]),
+                                          __builtin_bit_cast(uint32_t, v[2]), __builtin_bit_cast(uint32_t, v[3])};
+  } else if constexpr (CK == CK_F16) {
+    const h2_t lo = {(_Float16)v[0], (_Float16)v[1]};
+    const h2_t hi = {(_Float16)v[2], (_Float16)v[3]};
+    *(u32x2*)((uint16_t*)base + idx) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  } else {
+    const b2_t lo = {(__bf16)v[0], (__bf16)v[1]};
+    const b2_t hi = {(__bf16)v[2], (__bf16)v[3]};
+    *(u32x2*)((uint16_t*)base + idx) = u32x2{__builtin_bit_cast(uint32_t, lo), __builtin_bit_cast(uint32_t, hi)};
+  }
+}
+
+// eight adjacent f16 / bf16 outputs in one 16-byte store; idx is a multiple of 8
+template <int CK>
+__device__ __forceinline__ void store_out8(void* base, int64_t idx, const float (&lo)[4], const float (&hi)[4]) {
+  u32x4 w;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    if constexpr (CK == CK_F16) {
+      w[e] = __builtin_bit_cast(uint32_t, h2_t{(_Float16)lo[2 * e], (_Float16)lo[2 * e + 1]});
+      w[2 + e] = __builtin_bit_cast(uint32_t, h2_t{(_Float16)hi[2 * e], (_Float16)hi[2 * e + 1]});
+    } else {
+      w[e] = __builtin_bit_cast(uint32_t, b2_t{(__bf16)lo[2 * e], (__bf16)lo[2 * e + 1]});
+      w[2 + e] = __builtin_bit_cast(uint32_t, b2_t{(__bf16)hi[2 * e], (__bf16)hi[2 * e + 1]});
+    }
+  }
+  *(u32x4*)((uint16_t*)base + idx) = w;
+}
+
 template <int TM, int TN, int WM, int WN, int NS, bool XT, bool CH, int WK, int CK>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
   constexpr bool Q8 = WK == WK_Q8;
@@ -408,7 +443,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(ta[ks][i], tb[ks][j], acc[i][j]);
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(tb[ks][j], ta[ks][i], acc[i][j]);
       }
     };
     wait_vmcnt<(NS - 2) * LOADS>();  // tile 0
@@ -493,7 +528,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(af[ks & 1][i], bf[ks & 1][j], acc[i][j]);
+          for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<WK>(bf[ks & 1][j], af[ks & 1][i], acc[i][j]);
       }
       if constexpr (kMfmaPriority) __builtin_amdgcn_s_setprio(0);
     };
@@ -514,21 +549,84 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
   }
   wait_vmcnt<0>();  // the re-reads past the end land before the block exits
 
+  // The weight fragment is the MFMA's first operand, so lane l of a 32 x 32
+  // block holds output row l % 32 and, in each group q of four registers,
+  // the four adjacent columns 8 q + 4 (l / 32) .. + 3.  Stores are as wide as
+  // the row stride's alignment allows: 16 bytes per lane (fp32, or 16-bit
+  // output after the swap below), else element by element.  Where a value is
+  // stored changes no bits.
+  if (CK != CK_F32 && (CH || g.splits == 1)) {
+    // 16-bit output: lanes l and l + 32 trade halves of two groups
+    // (v_permlane32_swap), so lane l holds columns 8 q .. 8 q + 7 of its row
+    // and lane l + 32 the next eight: one 16-byte store per lane per group
+    // pair.  Every lane takes part in the swap; the stores are masked after.
+    const bool vec8 = (g.ldc & 7) == 0;
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
+    for (int i = 0; i < FM; ++i) {
+      const int64_t row = row0 + wm * WTM + i * 32 + lrow;
 #pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = col0 + wn * WTN + j * 32 + lrow;
+      for (int j = 0; j < FN; ++j) {
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = row0 + wm * WTM + i * 32 + 8 * (v >> 2) + 4 * lk + (v & 3);
-        if (row < g.M && col < g.N) {
-          if constexpr (CH) {
-            store_out<CK>(g.C, row * g.ldc + col, tot[i][j][v]);
-          } else if (g.splits > 1) {
-            g.partial[((int64_t)split * g.M + row) * g.N + col] = acc[i][j][v];
-          } else {
-            store_out<CK>(g.C, row * g.ldc + col, acc[i][j][v]);
+        for (int q = 0; q < 4; q += 2) {
+          float lo[4], hi[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float x = CH ? tot[i][j][4 * q + e] : acc[i][j][4 * q + e];
+            const float y = CH ? tot[i][j][4 * q + 4 + e] : acc[i][j][4 * q + 4 + e];
+            const auto r = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(uint32_t, x),
+                                                            __builtin_bit_cast(uint32_t, y), false, false);
+            lo[e] = __builtin_bit_cast(float, (uint32_t)r[0]);
+            hi[e] = __builtin_bit_cast(float, (uint32_t)r[1]);
+          }
+          const int64_t col = col0 + wn * WTN + j * 32 + 8 * (q + lk);
+          const int64_t rem = g.N - col;
+          if (row < g.M && rem > 0) {
+            if (vec8 && rem >= 8) {
+              store_out8<CK>(g.C, row * g.ldc + col, lo, hi);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                if (e < rem) store_out<CK>(g.C, row * g.ldc + col + e, lo[e]);
+                if (4 + e < rem) store_out<CK>(g.C, row * g.ldc + col + 4 + e, hi[e]);
+              }
+            }
+          }
+        }
+      }
+    }
+  } else {
+    const bool vec_c = (g.ldc & 3) == 0;
+    const bool vec_p = (g.N & 3) == 0;
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      const int64_t row = row0 + wm * WTM + i * 32 + lrow;
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int64_t col = col0 + wn * WTN + j * 32 + 8 * q + 4 * lk;
+          const int64_t rem = g.N - col;
+          float v4[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v4[e] = CH ? tot[i][j][4 * q + e] : acc[i][j][4 * q + e];
+          if (row < g.M && rem > 0) {
+            if (!CH && g.splits > 1) {
+              float* dst = g.partial + ((int64_t)split * g.M + row) * g.N + col;
+              if (vec_p && rem >= 4) {
+                *(u32x4*)dst = u32x4{__builtin_bit_cast(uint32_t, v4[0]), __builtin_bit_cast(uint32_t, v4[1]),
+                                     __builtin_bit_cast(uint32_t, v4[2]), __builtin_bit_cast(uint32_t, v4[3])};
+              } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                  if (e < rem) dst[e] = v4[e];
+              }
+            } else if (vec_c && rem >= 4) {
+              store_out4<CK>(g.C, row * g.ldc + col, v4);
+            } else {
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (e < rem) store_out<CK>(g.C, row * g.ldc + col + e, v4[e]);
+            }
           }
         }
       }
