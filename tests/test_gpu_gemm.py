@@ -82,6 +82,31 @@ def test_gemm_strided_a():
     assert rel_err(C.cpu().numpy(), oracle.mm(A, "f16", W, "f16")) <= REL_TOL
 
 
+@pytest.mark.parametrize("N,flags", [(99, sk.GEMM_SPLIT_LAUNCH), (99, sk.GEMM_ONE_LAUNCH), (4003, 0)])
+@pytest.mark.parametrize("ldc", [4104, 4108, 4105])
+@pytest.mark.parametrize("out", ["f32", "f16", "bf16"])
+def test_gemm_strided_c(N, flags, ldc, out):
+    # C is a column slice of a wider buffer (ldc > N; N % 8 = 3, so a row's
+    # last group of columns is partial; ldc a multiple of 8, of 4 only, and
+    # odd): the stored values are the dense run's bits and the padding
+    # columns keep their bytes.  N = 99 runs k in chunks (partial sums + a
+    # reduce, or one launch folding them), N = 4003 whole.
+    M, K = 150, 520
+    A, W = _inputs(M, N, K, 231)
+    dA, dW = to_dev(A, "f16"), to_dev(W, "f16")
+    ck = {"f32": sk.F32, "f16": sk.F16, "bf16": sk.BF16}[out]
+    dense = torch.empty((M, N), dtype=OUT[out], device="cuda")
+    sk.Plan(N, K, M, sk.F16, sk.F16, ck, flags=flags).run(M, dA, dW, dense)
+    full = torch.full((M, ldc), 7.0, dtype=OUT[out], device="cuda")
+    plan = sk.Plan(N, K, M, sk.F16, sk.F16, ck, ldc=ldc, flags=flags)
+    print(f"strided C N={N} ldc={ldc} out={out}: {plan.info(M)}", flush=True)
+    plan.run(M, dA, dW, full)
+    torch.cuda.synchronize()
+    assert np.array_equal(bits_of(full[:, :N].contiguous()), bits_of(dense))
+    assert torch.all(full[:, N:] == 7.0).item()
+    assert rel_err(dense.float().cpu().numpy(), oracle.mm(A, "f16", W, "f16")) <= (REL_TOL if out == "f32" else 8e-3)
+
+
 @pytest.mark.parametrize("M,N,K", [(150, 200, 512), (150, 200, 520), (300, 2048, 520)])
 def test_gemm_every_tile_bitwise_equal(M, N, K):
     """Every tile gives the same bits: N = 200 with k cut into chunks (the
