@@ -147,7 +147,8 @@ def _stream(stream):
 
 
 class Plan:
-    """A skinny_mm_plan: host-only, immutable, reusable across streams."""
+    """A skinny_mm_plan: host-only, immutable, reusable across streams (the
+    workspaces it hands out are kept per device and stream)."""
 
     def __init__(self, n, k, max_m, a_dtype=F16, w_dtype=F16, c_dtype=F32, lda=0, ldc=0,
                  flags=0, tile_id=-1, num_cus=0):
@@ -173,30 +174,46 @@ class Plan:
         _check(_lib.skinny_mm_plan_info(self._h, m, buf, 256), "skinny_mm_plan_info")
         return buf.value.decode()
 
-    def workspace(self, device):
-        """This plan's own zero-initialised device workspace (None when none is
-        needed).  Each plan keeps its own: the counters of one plan's layout
-        must not be overwritten by another plan's partial sums."""
+    def workspace(self, device, stream=None):
+        """A zero-initialised device workspace of this plan for one (device,
+        stream) pair (None when none is needed).  Runs on one stream are
+        ordered, so they may share it; runs on different streams may be in
+        flight at once and must not (the workspace holds arrival counters and
+        partial sums), so every stream gets its own.  It is allocated and
+        zero-filled on that stream, so the fill precedes the stream's first
+        run.  Each plan keeps its own: one plan's counters must not be
+        overwritten by another plan's partial sums."""
         if self.workspace_bytes == 0:
             return None
-        key = str(device)
+        torch = _torch()
+        dev = torch.device(device)
+        if stream is None:
+            stream = torch.cuda.current_stream(dev)
+        key = (str(dev), int(stream.cuda_stream))
         ws = self._ws.get(key)
         if ws is None:
-            ws = _torch().zeros(self.workspace_bytes, dtype=_torch().uint8, device=device)
+            with torch.cuda.stream(stream):
+                ws = torch.zeros(self.workspace_bytes, dtype=torch.uint8, device=dev)
             self._ws[key] = ws
         return ws
 
-    def run(self, m, A, W, C, scales=None, workspace=None, stream=None):
-        ws = workspace if workspace is not None else self.workspace(A.device)
+    def _resolve(self, A, workspace, stream):
+        torch = _torch()
+        if stream is None:
+            stream = torch.cuda.current_stream(A.device)
+        ws = workspace if workspace is not None else self.workspace(A.device, stream)
         nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        return ws, nbytes, ctypes.c_void_p(stream.cuda_stream)
+
+    def run(self, m, A, W, C, scales=None, workspace=None, stream=None):
+        ws, nbytes, st = self._resolve(A, workspace, stream)
         _check(_lib.skinny_mm_run(self._h, m, _ptr(A), _ptr(W), _ptr(scales), _ptr(C), _ptr(ws),
-                                  nbytes, _stream(stream)), "skinny_mm_run")
+                                  nbytes, st), "skinny_mm_run")
 
     def run_topk(self, m, A, W, logits, idx, val, topk, scales=None, workspace=None, stream=None):
-        ws = workspace if workspace is not None else self.workspace(A.device)
-        nbytes = 0 if ws is None else ws.numel() * ws.element_size()
+        ws, nbytes, st = self._resolve(A, workspace, stream)
         _check(_lib.gemv_topk_run(self._h, m, _ptr(A), _ptr(W), _ptr(scales), _ptr(logits),
-                                  _ptr(idx), _ptr(val), topk, _ptr(ws), nbytes, _stream(stream)),
+                                  _ptr(idx), _ptr(val), topk, _ptr(ws), nbytes, st),
                "gemv_topk_run")
 
     def __del__(self):

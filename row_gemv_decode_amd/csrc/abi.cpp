@@ -271,22 +271,44 @@ bool a32_cast_first(const skinny_plan* p, int64_t m) {
 // last one only up to k
 int64_t a32_cast_count(const skinny_plan* p, int64_t m) { return (m - 1) * p->d.lda + p->d.k; }
 
-// bytes of the workspace before the cast rows: counters and partial sums
-size_t split_bytes_for(const skinny_plan* p, int64_t m) {
-  const size_t part = use_gemv(p, m) ? gemv_partial_bytes(p, m) : gemm_partial_bytes(p, m);
-  return part > 0 ? gemv_counter_bytes(p) + part : 0;
+// A run's scratch is two regions: the arrival counters (zero between runs;
+// every run leaves them at zero) and the data region, which needs no initial
+// value: the partial sums (the GEMV's S x m x n, or the GEMM's chunks x m x n)
+// and after them the cast rows of a cast-first run.
+struct Scratch {
+  uint32_t* counters;
+  char* data;
+};
+
+// bytes of the data region before the cast rows: partial sums
+size_t partial_bytes_for(const skinny_plan* p, int64_t m) {
+  return use_gemv(p, m) ? gemv_partial_bytes(p, m) : gemm_partial_bytes(p, m);
 }
 
-// bytes a run at m rows needs (the same with or without the top-k)
-size_t workspace_bytes_for(const skinny_plan* p, int64_t m) {
+// bytes of the data region a run at m rows needs (with or without the top-k)
+size_t data_bytes_for(const skinny_plan* p, int64_t m) {
   const size_t a16 = a32_cast_first(p, m) ? round_up((size_t)a32_cast_count(p, m) * 2) : 0;
-  return split_bytes_for(p, m) + a16;
+  return partial_bytes_for(p, m) + a16;
+}
+
+// bytes of a caller's workspace a run at m rows needs: [counters][data], or
+// nothing when the run needs no data region (counters exist only beside
+// partial sums)
+size_t workspace_bytes_for(const skinny_plan* p, int64_t m) {
+  const size_t data = data_bytes_for(p, m);
+  return data > 0 ? gemv_counter_bytes(p) + data : 0;
+}
+
+// the two regions inside a caller's workspace
+Scratch caller_scratch(const skinny_plan* p, void* workspace) {
+  char* ws = (char*)workspace;
+  return Scratch{(uint32_t*)ws, ws != nullptr ? ws + gemv_counter_bytes(p) : nullptr};
 }
 
 skinny_status hip_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_ERR_HIP; }
 
 GemvArgs gemv_args(const skinny_plan* p, int64_t m, const void* A, const void* W, const void* scales,
-                   void* C, int64_t ldc, void* workspace) {
+                   void* C, int64_t ldc, const Scratch& sc) {
   GemvArgs g;
   g.A = A;
   g.a_kind = p->d.a_dtype == SKINNY_F32 ? kAF32 : kA16;
@@ -303,15 +325,13 @@ GemvArgs gemv_args(const skinny_plan* p, int64_t m, const void* A, const void* W
   g.C = C;
   g.ldc = ldc;
   g.epilogue = (p->d.flags & SKINNY_EPILOGUE_SIGMOID) ? kEpiSigmoid : kEpiNone;
-  const int64_t mm = p->d.max_m < kGemvMaxM ? p->d.max_m : kGemvMaxM;
-  char* ws = (char*)workspace;
-  g.counters = (ws != nullptr && gemv_global_split(p)) ? (uint32_t*)ws : nullptr;
-  g.partial = (ws != nullptr && gemv_global_split(p)) ? (float*)(ws + gemv_counter_bytes(p)) : nullptr;
+  g.counters = gemv_global_split(p) ? sc.counters : nullptr;
+  g.partial = gemv_global_split(p) ? (float*)sc.data : nullptr;
   return g;
 }
 
 GemmArgs gemm_args(const skinny_plan* p, int64_t m, const void* A, const void* W,
-                   const void* scales, void* C, int64_t ldc, void* workspace) {
+                   const void* scales, void* C, int64_t ldc, const Scratch& sc) {
   GemmArgs g;
   g.A = (const uint16_t*)A;
   g.lda = p->d.lda;
@@ -324,16 +344,13 @@ GemmArgs gemm_args(const skinny_plan* p, int64_t m, const void* A, const void* W
   g.ldc = ldc;
   g.splits = 1;
   g.kt_per_split = p->gemm_kps;
-  g.partial = (workspace != nullptr && p->gemm_splits > 1)
-                  ? (float*)((char*)workspace + gemv_counter_bytes(p))
-                  : nullptr;
+  g.partial = p->gemm_splits > 1 ? (float*)sc.data : nullptr;
   return g;
 }
 
-// checks shared by skinny_mm_run and gemv_topk_run
-skinny_status check_run(const skinny_plan* p, int64_t m, const void* A, const void* W,
-                        const void* scales, const void* C, const void* workspace,
-                        size_t workspace_bytes) {
+// checks shared by the run calls (everything but the workspace)
+skinny_status check_run_args(const skinny_plan* p, int64_t m, const void* A, const void* W,
+                             const void* scales, const void* C) {
   if (p == nullptr) return SKINNY_ERR_INVALID_ARG;
   if (m < 1 || m > p->d.max_m) return SKINNY_ERR_INVALID_ARG;
   if (A == nullptr || W == nullptr || C == nullptr) return SKINNY_ERR_INVALID_ARG;
@@ -343,6 +360,15 @@ skinny_status check_run(const skinny_plan* p, int64_t m, const void* A, const vo
     return SKINNY_ERR_ALIGNMENT;
   // the GEMV numbers its waves (k splits x column ranges) in 32 bits
   if (use_gemv(p, m) && gemv_waves_per_split(p, m) * p->gemv_S > (1LL << 31) - 1024) return SKINNY_ERR_SHAPE;
+  return SKINNY_OK;
+}
+
+// the argument checks plus the caller's workspace
+skinny_status check_run(const skinny_plan* p, int64_t m, const void* A, const void* W,
+                        const void* scales, const void* C, const void* workspace,
+                        size_t workspace_bytes) {
+  const skinny_status st = check_run_args(p, m, A, W, scales, C);
+  if (st != SKINNY_OK) return st;
   const size_t need = workspace_bytes_for(p, m);
   if (need > 0) {
     if (workspace == nullptr || workspace_bytes < need) return SKINNY_ERR_WORKSPACE;
@@ -381,15 +407,15 @@ int64_t gemv_blocks(const skinny_plan* p, const GemvBlock& b, int64_t m) {
 // over the rows of C (Strata PR #109, "What": one multi-row GEMV launch and
 // one multi-row top-10 launch per window)
 skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const void* W,
-                         const void* scales, void* C, int64_t ldc, int c_kind, void* workspace,
+                         const void* scales, void* C, int64_t ldc, int c_kind, const Scratch& sc,
                          int32_t* topk_idx, float* topk_val, int32_t topk, hipStream_t stream) {
   const bool want_topk = topk_idx != nullptr;
   if (use_gemv(p, m)) {
-    GemvArgs g = gemv_args(p, m, A, W, scales, C, ldc, workspace);
+    GemvArgs g = gemv_args(p, m, A, W, scales, C, ldc, sc);
     const GemvBlock b = gemv_block(p);
     g.cg_per_block = b.ranges;
     if (a32_cast_first(p, m)) {
-      uint16_t* a16 = (uint16_t*)((char*)workspace + split_bytes_for(p, m));
+      uint16_t* a16 = (uint16_t*)(sc.data + partial_bytes_for(p, m));
       skinny_status st = hip_status(launch_cast_f32_bf16(a32_cast_count(p, m), (const float*)A, a16, stream));
       if (st != SKINNY_OK) return st;
       g.A = a16;
@@ -399,7 +425,7 @@ skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const v
     if (st != SKINNY_OK || !want_topk) return st;
     return hip_status(launch_topk((const float*)C, (int)m, p->d.n, ldc, topk_idx, topk_val, topk, stream));
   }
-  GemmArgs g = gemm_args(p, m, A, W, scales, C, ldc, workspace);
+  GemmArgs g = gemm_args(p, m, A, W, scales, C, ldc, sc);
   const GemmChoice gc = choose_gemm(p, m);
   if (gc.split) g.splits = p->gemm_splits;
   skinny_status st = hip_status(launch_gemm(gc.tile, g, p->w_kind, c_kind, gc.chunked, stream));
@@ -545,8 +571,8 @@ skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const void* A, c
                             size_t workspace_bytes, void* stream) {
   skinny_status st = check_run(plan, m, A, W, w_scales, C, workspace, workspace_bytes);
   if (st != SKINNY_OK) return st;
-  return enqueue_mm(plan, m, A, W, w_scales, C, plan->d.ldc, plan->c_kind, workspace, nullptr, nullptr,
-                    0, (hipStream_t)stream);
+  return enqueue_mm(plan, m, A, W, w_scales, C, plan->d.ldc, plan->c_kind, caller_scratch(plan, workspace),
+                    nullptr, nullptr, 0, (hipStream_t)stream);
 }
 
 skinny_status gemv_topk_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
@@ -559,8 +585,8 @@ skinny_status gemv_topk_run(const skinny_plan* plan, int64_t m, const void* A, c
   if (topk_idx == nullptr || topk_val == nullptr) return SKINNY_ERR_INVALID_ARG;
   if (topk < 1 || topk > SKINNY_TOPK_MAX || topk > plan->d.n) return SKINNY_ERR_INVALID_ARG;
   if (!aligned16(topk_idx) || !aligned16(topk_val)) return SKINNY_ERR_ALIGNMENT;
-  return enqueue_mm(plan, m, A, W, w_scales, logits, plan->d.ldc, CK_F32, workspace, topk_idx, topk_val,
-                    topk, (hipStream_t)stream);
+  return enqueue_mm(plan, m, A, W, w_scales, logits, plan->d.ldc, CK_F32, caller_scratch(plan, workspace),
+                    topk_idx, topk_val, topk, (hipStream_t)stream);
 }
 
 skinny_status skinny_dequant_q8_0_run(int64_t n, int64_t k, const void* qs, const void* d,

@@ -665,10 +665,10 @@ struct TileEntry {
   gemm_fn fn_ch[3][3];  // one launch over k chunks (null where the tile cannot hold two sums)
 };
 
-// 16-bit weights run the multi-stage kernel with NS k-tiles in LDS (XT: the
-// next k-tile's fragments are read during this one's MFMAs); Q8_0 weights the
-// register-staged kernel (they are dequantised on their way into LDS).  Both
-// issue the same MFMA sequence for every output.
+// Every weight kind runs the same multi-stage kernel with NS k-tiles in LDS
+// (XT: the next k-tile's fragments are read during this one's MFMAs); Q8_0
+// codes and scales enter LDS as stored and each B fragment is dequantised as
+// it is read.  All kinds issue the same MFMA sequence for every output.
 template <int TM, int TN, int WM, int WN, int NS, bool XT, bool CH>
 void fill_kinds(gemm_fn (&f)[3][3]) {
   f[WK_F16][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_F16, CK_F32>;

@@ -260,3 +260,136 @@ def test_topk_with_split_shapes(m, k):
     # (k = 16384) workgroups
     print(f"topk split m={m} k={k}", flush=True)
     _topk_case(m, 300, k, 411 + k + m)
+
+
+@pytest.mark.parametrize("name", ["router_topk", "q8_0_n512"])
+def test_row_invariance_at_the_workload_shape(name):
+    """Row r of every output at m = 2, 4, 8, 16 equals the m = 1 call on that
+    row, bit for bit (the Strata PR #109 page, "What": the batched window's
+    outputs are bit-identical to the per-token calls) -- at the router's
+    own shape (256 x 5120 bf16, k split in five inside a workgroup; logits,
+    top-10 indices and values) and at the Q8_0 GEMV's (512 x 2560, codes
+    dequantised in the load, f16 out)."""
+    wl = WL.WORKLOADS[name]
+    A = WL.gen_a(wl, 16)
+    W = WL.gen_w(wl)
+    dA = to_dev(A, wl.a_kind)
+    if wl.w_kind == "q8_0":
+        dW, dS = to_dev(W[0], "i8"), to_dev(W[1], "f16")
+        plan = sk.Plan(wl.n, wl.k, 16, sk.F16, sk.Q8_0, sk.F16)
+    else:
+        dW, dS = to_dev(W, wl.w_kind), None
+        plan = sk.Plan(wl.n, wl.k, 16, sk.BF16, sk.BF16, sk.F32)
+    cdt = torch.float16 if wl.w_kind == "q8_0" else torch.float32
+
+    def call(m, rows):
+        C = torch.empty((m, wl.n), dtype=cdt, device="cuda")
+        if wl.topk:
+            idx = torch.empty((m, wl.topk), dtype=torch.int32, device="cuda")
+            val = torch.empty((m, wl.topk), dtype=torch.float32, device="cuda")
+            plan.run_topk(m, rows, dW, C, idx, val, wl.topk)
+            return C, idx, val
+        plan.run(m, rows, dW, C, scales=dS)
+        return (C,)
+
+    print(f"row invariance {name}: {plan.info(1)} | {plan.info(16)}", flush=True)
+    singles = [call(1, dA[r:r + 1]) for r in range(16)]
+    torch.cuda.synchronize()
+    ref = [torch.cat([s[i] for s in singles]).contiguous() for i in range(len(singles[0]))]
+    ref = [t.view(torch.int16 if t.dtype == torch.float16 else torch.int32).cpu().numpy() for t in ref]
+    for m in (2, 4, 8, 16):
+        outs = call(m, dA[:m])
+        torch.cuda.synchronize()
+        for i, t in enumerate(outs):
+            got = t.contiguous().view(torch.int16 if t.dtype == torch.float16 else torch.int32).cpu().numpy()
+            assert np.array_equal(got, ref[i][:m]), (name, m, i)
+
+
+def _check_topk_against_fp64(ref, bound, gpu_idx, topk):
+    """The bounded check of the top-k against fp64 logits.  Each GPU logit is
+    within E (the row's largest fp32 summation bound) of its fp64 value, so
+    the GPU's t-th pick has an fp64 value within 2E of the t-th largest fp64
+    value, and where that value stands more than 2E away from both of its
+    neighbours in fp64 order the pick is exactly its index."""
+    m, n = ref.shape
+    for r in range(m):
+        E = float(np.max(bound[r]))
+        order = np.lexsort((np.arange(n), -ref[r]))  # value desc, index asc
+        s = ref[r][order]
+        for t in range(topk):
+            prev_gap = s[t - 1] - s[t] if t > 0 else np.inf
+            next_gap = s[t] - s[t + 1] if t + 1 < n else np.inf
+            g = int(gpu_idx[r, t])
+            if min(prev_gap, next_gap) > 2 * E:
+                assert g == int(order[t]), (r, t, g, int(order[t]))
+            else:
+                assert abs(ref[r][g] - s[t]) <= 2 * E, (r, t, g)
+
+
+@pytest.mark.parametrize("m", [1, 5, 16])
+def test_router_topk_against_fp64_logits(m):
+    """Top-10 of the router workload against the oracle's fp64 logits (not
+    the GPU's own): indices agree except among fp64 values closer than the
+    rigorous fp32 summation bound."""
+    wl = WL.WORKLOADS["router_topk"]
+    W = WL.gen_w(wl)
+    A = WL.gen_a(wl, 16)[:m]
+    _, idx, _ = sk.gemv_topk(to_dev(A, "bf16"), to_dev(W, "bf16"), topk=10, max_m=16)
+    torch.cuda.synchronize()
+    ref = oracle.mm(A, "bf16", W, "bf16")
+    _check_topk_against_fp64(ref, _f32_bound(A, "bf16", W, "bf16"), idx.cpu().numpy(), 10)
+
+
+def test_topk_against_fp64_with_near_ties():
+    """Near-ties in fp64 (weight rows that differ in one low bit) may come out
+    in either order but must stay within the bound; exact duplicates keep
+    the lower index first."""
+    n, k, m = 256, 5120, 8
+    W = WL.gen_matrix((n, k), "bf16", ("normal", 0.02), 361)
+    for src, dst in ((3, 200), (50, 51), (77, 12)):
+        W[dst] = W[src]
+        W[dst, 0] ^= np.uint16(1)  # one ulp of one weight: a near-tie
+    W[90] = W[91]                  # an exact tie
+    A = WL.gen_matrix((m, k), "bf16", ("normal", 1.0), 362)
+    _, idx, _ = sk.gemv_topk(to_dev(A, "bf16"), to_dev(W, "bf16"), topk=10, max_m=16)
+    torch.cuda.synchronize()
+    ref = oracle.mm(A, "bf16", W, "bf16")
+    _check_topk_against_fp64(ref, _f32_bound(A, "bf16", W, "bf16"), idx.cpu().numpy(), 10)
+
+
+@pytest.mark.parametrize("kind", ["gemv_global_split", "gemm_split_launch"])
+def test_two_streams_at_once_use_their_own_workspaces(kind):
+    """The binding's Plan hands each (device, stream) its own workspace, so
+    runs of one plan on two streams in flight at once do not share arrival
+    counters or partial sums: each stream's results equal the serial calls'
+    bits, and every workspace's counters are back at zero afterwards."""
+    if kind == "gemv_global_split":
+        n, k, m, flags, cdt = 256, 16384, 16, 0, torch.float32
+    else:
+        n, k, m, flags, cdt = 96, 2560, 300, sk.GEMM_SPLIT_LAUNCH, torch.float16
+    W = to_dev(WL.gen_matrix((n, k), "f16", ("normal", 0.02), 811), "f16")
+    As = [to_dev(WL.gen_matrix((m, k), "f16", ("normal", 1.0), 812 + i), "f16") for i in range(2)]
+    plan = sk.Plan(n, k, m, sk.F16, sk.F16, sk.F32 if cdt == torch.float32 else sk.F16, flags=flags)
+    print(f"two streams {kind}: {plan.info(m)}", flush=True)
+    serial = []
+    for A in As:
+        C = torch.empty((m, n), dtype=cdt, device="cuda")
+        plan.run(m, A, W, C)
+        serial.append(C)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.empty((m, n), dtype=cdt, device="cuda") for _ in range(6)] for _ in range(2)]
+    for rep in range(6):  # interleaved enqueues: both streams have work in flight together
+        for i in range(2):
+            plan.run(m, As[i], W, outs[i][rep], stream=streams[i])
+    torch.cuda.synchronize()
+    ibits = torch.int32 if cdt == torch.float32 else torch.int16
+    for i in range(2):
+        ref = serial[i].view(ibits).cpu().numpy()
+        for rep in range(6):
+            assert np.array_equal(outs[i][rep].view(ibits).cpu().numpy(), ref), (i, rep)
+        ws = plan.workspace(As[i].device, streams[i])
+        assert ws is not None and ws.data_ptr() != plan.workspace(As[i].device, streams[1 - i]).data_ptr()
+        if kind == "gemv_global_split":
+            head = ws[:256].cpu().numpy()  # the arrival counters
+            assert not np.any(head), head[np.nonzero(head)][:8]
