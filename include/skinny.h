@@ -73,7 +73,9 @@ typedef enum skinny_status {
                                  size past a stated limit (a run: a GEMV of more than about
                                  2^31 waves, k/512 x n) */
   SKINNY_ERR_HIP = 5,         /* the HIP runtime reported an error (device query or launch) */
-  SKINNY_ERR_WORKSPACE = 6    /* workspace missing or smaller than skinny_mm_workspace_size */
+  SKINNY_ERR_WORKSPACE = 6,   /* workspace missing or smaller than skinny_mm_workspace_size */
+  SKINNY_ERR_SCRATCH = 7      /* skinny_mm_run_static: the run needs more scratch than the
+                                 library's static array holds (SKINNY_STATIC_*_BYTES) */
 } skinny_status;
 
 typedef enum skinny_dtype {
@@ -192,6 +194,33 @@ SKINNY_API skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_
 SKINNY_API skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,
                             const void* w_scales, void* C, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* skinny_mm_run without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc.  It computes what skinny_mm_run computes,
+ * with the same kernels, bit for bit, but a run that needs scratch (the
+ * cases listed under skinny_mm_workspace_size) uses the library's own static
+ * device array instead of a caller's workspace.  It allocates nothing and
+ * calls no allocating routine.
+ *   The array is SKINNY_STATIC_SCRATCH_BYTES per GPU, held by every GPU the
+ *   library runs on until the process ends: SKINNY_STATIC_COUNTER_BYTES of
+ *   arrival counters, the rest for partial sums and cast rows.  A run that
+ *   needs more (its skinny_mm_workspace_size counters beyond the first
+ *   region, or its partial sums and cast rows beyond the second) returns
+ *   SKINNY_ERR_SCRATCH before any HIP call; so does nothing else.
+ *   The current device's copy is used: `stream` must belong to the current
+ *   device (else SKINNY_ERR_HIP).  The first call on a device looks up the
+ *   array's device address and enqueues a zero fill of its counter region on
+ *   `stream` before the run; every run leaves the counters at zero again.
+ *   Every call on one GPU shares that GPU's array, which keeps the last
+ *   call's contents: two calls in flight at once on one GPU (on different
+ *   streams, or from different threads without ordering) race and may give
+ *   wrong results; calls ordered on one stream do not.
+ * Other arguments, ownership and errors as skinny_mm_run. */
+#define SKINNY_STATIC_SCRATCH_BYTES (32u << 20)
+#define SKINNY_STATIC_COUNTER_BYTES (1u << 20)
+SKINNY_API skinny_status skinny_mm_run_static(const skinny_plan* plan, int64_t m, const void* A,
+                                              const void* W, const void* w_scales, void* C, void* stream);
 
 /* Router step (Strata PR #109, "What": one multi-row router GEMV launch into
  * fp32 logits, then one multi-row top-k launch with a wavefront per row).

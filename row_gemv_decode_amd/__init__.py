@@ -33,7 +33,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 
 # --- C ABI mirror -----------------------------------------------------------
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_SHAPE, ERR_HIP, ERR_WORKSPACE = range(7)
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_SHAPE, ERR_HIP, ERR_WORKSPACE, ERR_SCRATCH = range(8)
 F16, BF16, F32, Q8_0 = 1, 2, 3, 4
 FORCE_GEMV, FORCE_GEMM, GEMM_SPLIT_LAUNCH, GEMM_ONE_LAUNCH = 0x1, 0x2, 0x4, 0x8
 EPILOGUE_SIGMOID = 0x10
@@ -44,8 +44,10 @@ EXPORTS = (
     "skinny_mm_plan", "skinny_mm_plan_destroy", "skinny_mm_workspace_size", "skinny_mm_run",
     "gemv_topk_run", "skinny_dequant_q8_0_run", "skinny_mm_plan_info", "skinny_gemm_tile_count",
     "skinny_gemm_tile_name", "skinny_status_string", "skinny_abi_version", "skinny_cast_f32_bf16_run",
-    "skinny_moe_combine_run",
+    "skinny_moe_combine_run", "skinny_mm_run_static",
 )
+STATIC_SCRATCH_BYTES = 32 << 20
+STATIC_COUNTER_BYTES = 1 << 20
 
 
 class MMDesc(ctypes.Structure):
@@ -74,6 +76,8 @@ _lib.skinny_mm_workspace_size.argtypes = [_vp, ctypes.POINTER(_sz)]
 _lib.skinny_mm_workspace_size.restype = ctypes.c_int
 _lib.skinny_mm_run.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _sz, _vp]
 _lib.skinny_mm_run.restype = ctypes.c_int
+_lib.skinny_mm_run_static.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp]
+_lib.skinny_mm_run_static.restype = ctypes.c_int
 _lib.gemv_topk_run.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _vp, _sz, _vp]
 _lib.gemv_topk_run.restype = ctypes.c_int
 _lib.skinny_dequant_q8_0_run.argtypes = [_i64, _i64, _vp, _vp, _vp, _vp]
@@ -215,6 +219,15 @@ class Plan:
         _check(_lib.gemv_topk_run(self._h, m, _ptr(A), _ptr(W), _ptr(scales), _ptr(logits),
                                   _ptr(idx), _ptr(val), topk, _ptr(ws), nbytes, st),
                "gemv_topk_run")
+
+    def run_static(self, m, A, W, C, scales=None, stream=None):
+        """skinny_mm_run_static: the run without a workspace argument (the
+        library's own static scratch; calls in flight at once on one GPU race)."""
+        torch = _torch()
+        if stream is None:
+            stream = torch.cuda.current_stream(A.device)
+        _check(_lib.skinny_mm_run_static(self._h, m, _ptr(A), _ptr(W), _ptr(scales), _ptr(C),
+                                         ctypes.c_void_p(stream.cuda_stream)), "skinny_mm_run_static")
 
     def __del__(self):
         h = getattr(self, "_h", None)

@@ -16,7 +16,7 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libskinny.so")
 ARCH = "gfx950"
 SOURCES = ["abi.cpp", "gemv.hip", "gemv_f16.hip", "gemv_bf16.hip", "gemv_bf16_a32.hip", "gemv_q8.hip",
-           "gemm.hip", "combine.hip"]
+           "gemm.hip", "combine.hip", "static_scratch.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [

@@ -13,6 +13,9 @@
 
 using namespace skinny;
 
+static_assert(SKINNY_STATIC_SCRATCH_BYTES == kStaticScratchBytes, "static scratch size");
+static_assert(SKINNY_STATIC_COUNTER_BYTES == kStaticCounterBytes, "static counter region");
+
 struct skinny_plan {
   skinny_mm_desc d;   // normalised copy (lda/ldc filled in)
   int num_cus;
@@ -449,6 +452,7 @@ const char* skinny_status_string(skinny_status s) {
     case SKINNY_ERR_SHAPE: return "unsupported shape";
     case SKINNY_ERR_HIP: return "HIP runtime error";
     case SKINNY_ERR_WORKSPACE: return "workspace missing or too small";
+    case SKINNY_ERR_SCRATCH: return "run needs more scratch than the library's static array holds";
   }
   return "unknown status";
 }
@@ -573,6 +577,26 @@ skinny_status skinny_mm_run(const skinny_plan* plan, int64_t m, const void* A, c
   if (st != SKINNY_OK) return st;
   return enqueue_mm(plan, m, A, W, w_scales, C, plan->d.ldc, plan->c_kind, caller_scratch(plan, workspace),
                     nullptr, nullptr, 0, (hipStream_t)stream);
+}
+
+skinny_status skinny_mm_run_static(const skinny_plan* plan, int64_t m, const void* A, const void* W,
+                                   const void* w_scales, void* C, void* stream) {
+  skinny_status st = check_run_args(plan, m, A, W, w_scales, C);
+  if (st != SKINNY_OK) return st;
+  // sizes first, before any HIP call: the counters must fit their region and
+  // the partial sums and cast rows the data region
+  const size_t data = data_bytes_for(plan, m);
+  if (data > 0 && (gemv_counter_bytes(plan) > kStaticCounterBytes || data > kStaticDataBytes))
+    return SKINNY_ERR_SCRATCH;
+  Scratch sc{nullptr, nullptr};
+  if (data > 0) {
+    char* base = nullptr;
+    st = hip_status(static_scratch((hipStream_t)stream, &base));
+    if (st != SKINNY_OK) return st;
+    sc = Scratch{(uint32_t*)base, base + kStaticCounterBytes};
+  }
+  return enqueue_mm(plan, m, A, W, w_scales, C, plan->d.ldc, plan->c_kind, sc, nullptr, nullptr, 0,
+                    (hipStream_t)stream);
 }
 
 skinny_status gemv_topk_run(const skinny_plan* plan, int64_t m, const void* A, const void* W,

@@ -128,4 +128,17 @@ bool gemm_tile_chunkable(int tile_id);
 // to the output kind
 hipError_t launch_splitk_reduce(const GemmArgs& args, int c_kind, hipStream_t stream);
 
+// ---------------------------------------------------------------------------
+// The library's own scratch for skinny_mm_run_static: one file-scope device
+// array per GPU (static_scratch.hip), [counters: kStaticCounterBytes]
+// [data: the rest].  static_scratch() returns the current device's address of
+// it; on its first call on a device it looks the address up and enqueues a
+// zero fill of the counter region on `stream`.
+// ---------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = size_t(32) << 20;
+constexpr size_t kStaticCounterBytes = size_t(1) << 20;
+constexpr size_t kStaticDataBytes = kStaticScratchBytes - kStaticCounterBytes;
+
+hipError_t static_scratch(hipStream_t stream, char** base);
+
 }  // namespace skinny

@@ -42,7 +42,7 @@ def plan_status(**fields):
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 13, names
+    assert len(names) == 14, names
     assert set(names) == set(sk.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -50,7 +50,7 @@ def test_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert sk.abi_version() == 1
-    for st in range(7):
+    for st in range(8):
         assert L.skinny_status_string(st)
     assert L.skinny_status_string(99) == b"unknown status"
     assert ctypes.sizeof(sk.MMDesc) == 72  # layout shared with the C header
