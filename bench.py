@@ -453,7 +453,7 @@ def sweep_combine(sk, torch, rounds):
 # ---------------------------------------------------------------------------
 COUNTERS = os.path.join(ROOT, "profiles", "router_gemv_topk_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "row_gemv_decode_amd", "csrc", f)
-                  for f in ("gemv_kernel.h", "gemv_bf16.hip", "device_common.h", "internal.h")]
+                  for f in ("gemv_kernel.h", "gemv_inst.hip", "device_common.h", "internal.h")]
 
 
 def kernel_source_hash():

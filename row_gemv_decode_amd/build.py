@@ -15,8 +15,14 @@ CSRC = os.path.join(PKG, "csrc")
 OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libskinny.so")
 ARCH = "gfx950"
-SOURCES = ["abi.cpp", "gemv.hip", "gemv_f16.hip", "gemv_bf16.hip", "gemv_bf16_a32.hip", "gemv_q8.hip",
-           "gemm.hip", "combine.hip", "static_scratch.hip"]
+SOURCES = ["abi.cpp", "gemv.hip", "gemm.hip", "combine.hip", "static_scratch.hip"]
+# gemv_inst.hip once per (weight kind, A kind, chunk slots T): object name -> defines
+GEMV_INSTANCES = {
+    f"gemv_{w}{'_a32' if a == 'kAF32' else ''}_t{t}": (wk, a, t)
+    for w, wk, a in (("f16", "WK_F16", "kA16"), ("bf16", "WK_BF16", "kA16"), ("q8", "WK_Q8", "kA16"),
+                     ("bf16", "WK_BF16", "kAF32"))
+    for t in (1, 2)
+}
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [
@@ -27,10 +33,11 @@ COMMON = [
 ]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(OUT_DIR, os.path.splitext(src)[0] + ".o")
+def _compile(job, verbose: bool) -> str:
+    src, name, defines = job
+    obj = os.path.join(OUT_DIR, name + ".o")
     lang = ["-x", "hip"] if src.endswith(".cpp") else []
-    cmd = [HIPCC, *COMMON, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *COMMON, *defines, *lang, "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -45,8 +52,12 @@ def _compile(src: str, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
+    jobs = [("gemv_inst.hip", name, [f"-DGEMV_WK={wk}", f"-DGEMV_AK={a}", f"-DGEMV_T={t}",
+                                     f"-DGEMV_LAUNCHER=launch_{name}"])
+            for name, (wk, a, t) in GEMV_INSTANCES.items()]
+    jobs += [(src, os.path.splitext(src)[0], []) for src in SOURCES]
+    with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(lambda j: _compile(j, verbose), jobs))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -73,13 +73,14 @@ void gemv_split(int64_t k, int* T_out, int* S_out) {
 }
 
 // columns per wave: enough for about `waves_per_cu` waves per CU, but at
-// most kGemvCpwMax columns so the wave's weight loads all fit in registers
+// most kGemvCpwMax columns so the wave's weight loads all fit in registers;
+// a power of two (the kernels are compiled for 1, 2, 4 and 8)
 int gemv_cols_per_wave(int64_t n, int S, int num_cus, int waves_per_cu) {
   const int64_t target_waves = (int64_t)waves_per_cu * num_cus;
-  int64_t cpw = (n * S) / (target_waves > 0 ? target_waves : 1);
-  if (cpw < 1) cpw = 1;
-  if (cpw > kGemvCpwMax) cpw = kGemvCpwMax;
-  return (int)cpw;
+  const int64_t want = (n * S) / (target_waves > 0 ? target_waves : 1);
+  int cpw = 1;
+  while (cpw * 2 <= want && cpw * 2 <= kGemvCpwMax) cpw *= 2;
+  return cpw;
 }
 
 // GEMM k split: narrow N leaves most CUs idle at moderate M, so the plan

@@ -6,12 +6,13 @@
 
 namespace skinny {
 
-// one translation unit per weight type (gemv_f16.hip, gemv_bf16.hip, gemv_q8.hip)
-// and one for bf16 weights fed by fp32 rows (gemv_bf16_a32.hip)
-hipError_t launch_gemv_f16(const GemvArgs&, int, int, int, int, hipStream_t);
-hipError_t launch_gemv_bf16(const GemvArgs&, int, int, int, int, hipStream_t);
-hipError_t launch_gemv_bf16_a32(const GemvArgs&, int, int, int, int, hipStream_t);
-hipError_t launch_gemv_q8(const GemvArgs&, int, int, int, int, hipStream_t);
+// the launchers of gemv_inst.hip, one object per (weight kind, A kind, T)
+#define SKINNY_GEMV_LAUNCHERS(X) \
+  X(launch_gemv_f16_t1) X(launch_gemv_f16_t2) X(launch_gemv_bf16_t1) X(launch_gemv_bf16_t2) \
+  X(launch_gemv_q8_t1) X(launch_gemv_q8_t2) X(launch_gemv_bf16_a32_t1) X(launch_gemv_bf16_a32_t2)
+#define SKINNY_DECLARE_LAUNCHER(name) hipError_t name(const GemvArgs&, int, int, int, hipStream_t);
+SKINNY_GEMV_LAUNCHERS(SKINNY_DECLARE_LAUNCHER)
+#undef SKINNY_DECLARE_LAUNCHER
 
 namespace {
 
@@ -274,13 +275,23 @@ __global__ __launch_bounds__(256) void dequant_q8_0_kernel(const int8_t* __restr
 
 hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_kind,
                        int waves_per_block, hipStream_t stream) {
-  if (args.a_kind == kAF32)
-    return w_kind == WK_BF16 ? launch_gemv_bf16_a32(args, m, T, out_kind, waves_per_block, stream)
-                             : hipErrorInvalidValue;
+  if (T != 1 && T != 2) return hipErrorInvalidValue;
+  const bool t1 = T == 1;
+  if (args.a_kind == kAF32) {
+    if (w_kind != WK_BF16) return hipErrorInvalidValue;
+    return t1 ? launch_gemv_bf16_a32_t1(args, m, out_kind, waves_per_block, stream)
+              : launch_gemv_bf16_a32_t2(args, m, out_kind, waves_per_block, stream);
+  }
   switch (w_kind) {
-    case WK_F16: return launch_gemv_f16(args, m, T, out_kind, waves_per_block, stream);
-    case WK_BF16: return launch_gemv_bf16(args, m, T, out_kind, waves_per_block, stream);
-    case WK_Q8: return launch_gemv_q8(args, m, T, out_kind, waves_per_block, stream);
+    case WK_F16:
+      return t1 ? launch_gemv_f16_t1(args, m, out_kind, waves_per_block, stream)
+                : launch_gemv_f16_t2(args, m, out_kind, waves_per_block, stream);
+    case WK_BF16:
+      return t1 ? launch_gemv_bf16_t1(args, m, out_kind, waves_per_block, stream)
+                : launch_gemv_bf16_t2(args, m, out_kind, waves_per_block, stream);
+    case WK_Q8:
+      return t1 ? launch_gemv_q8_t1(args, m, out_kind, waves_per_block, stream)
+                : launch_gemv_q8_t2(args, m, out_kind, waves_per_block, stream);
   }
   return hipErrorInvalidValue;
 }

@@ -1,6 +1,7 @@
 // gemv_kernel.h -- the multi-row GEMV kernel for gfx950 (MI355X), included by
-// one translation unit per weight type (gemv_f16.hip, gemv_bf16.hip,
-// gemv_q8.hip) and by gemv.hip for the shared wave helpers.
+// gemv_inst.hip (compiled once per weight kind, A kind and T, so the
+// instantiations build in parallel) and by gemv.hip for the shared wave
+// helpers.
 //
 // What is computed (the pages print no code for any of it):
 //   C[r][j] = sum_kk A[r][kk] * W[j][kk] for r < m <= 16, W stored [n][k]
@@ -250,99 +251,128 @@ __device__ __forceinline__ u32x4 load_a8(const GemvArgs& g, int r, int c) {
 
 // ---------------------------------------------------------------------------
 // The GEMV kernel.  M rows (template), T chunk slots per lane, weight kind WK,
-// output kind CK, G columns reduced per pass, epilogue EPI, A kind AK.  G changes only how many
-// columns share one pass of the reduction tree, never a column's arithmetic.
+// output kind CK, CPW columns per wave, epilogue EPI, A kind AK, and the
+// split class SPLIT of the plan's k split S.  The columns of a wave are
+// reduced G = min(CPW, gemv_group_max(M)) per pass of the tree; neither CPW
+// nor G changes a column's arithmetic.  SPLIT only selects which code the
+// kernel carries (each class its own staging and reduction, so no kernel
+// reserves registers or LDS for another's).  Every count a loop runs to is a
+// constant, and the only runtime conditions around loads are wave-uniform
+// (the last column range may hold fewer columns), so the wave issues its
+// whole weight stream without per-lane branches.
 //
-// Wave -> work: with S <= kGemvBlockSplitMax k splits, a workgroup holds
-// cg_per_block column ranges and S waves per range (wave w: split w % S,
-// range w / S).  Each wave reduces its sums over its 64 lanes, parks them in
-// LDS, and after one barrier the block adds the S splits in the fixed order
-// s = 0..S-1 and writes C.  With more splits the waves of one range sit in
-// different workgroups: each writes its sums to partial[s][r][j], makes them
-// visible device-wide and counts itself in on its range; the wave that arrives
-// last adds the S partials in the same fixed order.  No wave ever waits for
-// another workgroup.  Either way row r sees the same arithmetic at every m.
-// The range counters live in the caller's workspace, start at zero and are
-// left at zero.
+// Wave -> work:
+//   kSplitNone (S = 1): each wave owns a run of columns over all of k and
+//     stores its sums directly; with M >= 4 the block first stages its A
+//     slice in LDS (every wave needs the same slice).
+//   kSplitBlock (1 < S <= kGemvBlockSplitMax): a workgroup holds cg_per_block
+//     column ranges and S waves per range (wave w: split w % S, range w / S).
+//     Each wave reduces its sums over its 64 lanes and parks them in LDS;
+//     after one barrier wave q adds the S splits of range q in the fixed
+//     order s = 0..S-1 and writes C.
+//   kSplitGlobal (S > kGemvBlockSplitMax): the waves of one range sit in
+//     different workgroups: each writes its sums to partial[s][r][j], makes
+//     them visible device-wide and counts itself in on its range; the wave
+//     that arrives last adds the S partials in the same fixed order.  No
+//     wave ever waits for another workgroup.  The range counters live in the
+//     caller's workspace, start at zero and are left at zero.
+// Either way row r sees the same arithmetic at every m.
 // ---------------------------------------------------------------------------
-template <int M, int T, int WK, int CK, int G, int EPI, int AK>
+constexpr int kSplitNone = 0;
+constexpr int kSplitBlock = 1;
+constexpr int kSplitGlobal = 2;
+
+template <int M, int T, int WK, int CK, int CPW, int EPI, int AK, int SPLIT>
 __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(GemvArgs g) {
+  static_assert(CPW >= 1 && CPW <= kGemvCpwMax, "columns per wave");
+  constexpr int G = CPW < gemv_group_max(M) ? CPW : gemv_group_max(M);
   using Shape = GemvShape<M, G>;
   constexpr int P = Shape::P;
   constexpr int P2 = Shape::P2;
   constexpr int LV = Shape::LV;
   static_assert(LV <= 6, "at most 64 values per lane");
 
-  // sums of one block's waves: [wave][column of the wave][row]
-  __shared__ float red[kGemvMaxWavesPerBlock * kGemvCpwMax * M];
+  // sums of one block's waves (in-block split): [wave][column of the wave][row]
+  __shared__ float red[SPLIT == kSplitBlock ? kGemvMaxWavesPerBlock * CPW * M : 1];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int wpb = blockDim.x >> 6;
-  const bool in_block = g.S <= kGemvBlockSplitMax;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   int s, wc;
   bool active;
-  if (in_block) {
-    const int cg = wave / g.S;
-    s = wave - cg * g.S;
-    wc = blockIdx.x * g.cg_per_block + cg;
-    active = cg < g.cg_per_block && wc < g.waves_per_split;
-  } else {
-    const int gw = blockIdx.x * wpb + wave;
+  if constexpr (SPLIT == kSplitGlobal) {
+    const int gw = blockIdx.x * (int)(blockDim.x >> 6) + wave;
     s = gw / g.waves_per_split;
     active = s < g.S;  // trailing waves of the last block have no columns
     wc = active ? gw - s * g.waves_per_split : 0;
+  } else {
+    // in-block ranges (an unsplit k is the case S = 1)
+    const int S = SPLIT == kSplitNone ? 1 : g.S;
+    const int cg = wave / S;
+    s = wave - cg * S;
+    wc = blockIdx.x * g.cg_per_block + cg;
+    active = cg < g.cg_per_block && wc < g.waves_per_split;
   }
   if (!active) wc = 0;
-  const int64_t j0 = (int64_t)wc * g.cpw;
-  const int ncol = active ? (int)min((int64_t)g.cpw, g.n - j0) : 0;
+  const int64_t j0 = (int64_t)wc * CPW;
+  const int ncol = active ? (int)min((int64_t)CPW, g.n - j0) : 0;
 
-  // Unsplit k (S = 1) with four or more rows: every wave of the block needs
-  // the same A slice (chunks 0 .. 64 T - 1 of every row), so the block loads
-  // it once into LDS and each wave reads its chunks from there, instead of
-  // every wave fetching all of A through its own load path.
-  constexpr bool kStageA = M >= 4;
+  // Unsplit k with four or more rows: every wave of the block needs the same
+  // A slice (chunks 0 .. 64 T - 1 of every row), so the block loads it once
+  // into LDS and each wave reads its chunks from there, instead of every wave
+  // fetching all of A through its own load path.
+  constexpr bool kStageA = SPLIT == kSplitNone && M >= 4;
+  constexpr int kStageIters = kStageA ? (M * 64 * T + 255) / 256 : 0;
   __shared__ u32x4 sAr[kStageA ? M * 64 * T : 1];
-  const bool stage_a = kStageA && g.S == 1;
-  u32x4 a_share[kStageA ? (M * 64 * T + 255) / 256 : 1];
-  if (stage_a) {
+  u32x4 a_share[kStageA ? kStageIters : 1];
+  if constexpr (kStageA) {
     // issued before the weight loads, so their latencies overlap
 #pragma unroll
-    for (int i = 0; i < (kStageA ? (M * 64 * T + 255) / 256 : 0); ++i) {
+    for (int i = 0; i < kStageIters; ++i) {
+      // slots past the slice (e >= M * 64 T, the last iteration) load row
+      // M - 1 and are never stored; chunks past k load chunk 0 (left out of
+      // the sums below)
       const int e = (int)threadIdx.x + i * (int)blockDim.x;
       const int r = e / (64 * T);
       const int c = e - r * (64 * T);
-      a_share[i] = (e < M * 64 * T && c < g.nchunks) ? load_a8<AK>(g, r, c) : u32x4{0u, 0u, 0u, 0u};
+      a_share[i] = load_a8<AK>(g, r < M ? r : M - 1, c < g.nchunks ? c : 0);
     }
   }
 
+  // Chunks past k (the last split's tail lanes) load chunk 0 of the row
+  // instead, and their products are left out of the sum (a select after each
+  // dot product).  So no load sits behind a per-lane branch, and no value is
+  // touched between its load and its use: a select on loaded data would make
+  // the wave wait for its weight loads before it issues its A loads.
   int chunk[T];
+  int lchunk[T];
   bool valid[T];
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     chunk[t] = s * 64 * T + t * 64 + lane;
-    valid[t] = active && chunk[t] < g.nchunks;
+    valid[t] = chunk[t] < g.nchunks;
+    lchunk[t] = valid[t] ? chunk[t] : 0;
   }
 
   // every weight load of the wave, issued before anything else waits
-  WChunk<WK> w[kGemvCpwMax][T];
+  WChunk<WK> w[CPW][T];
 #pragma unroll
-  for (int c = 0; c < kGemvCpwMax; ++c) {
+  for (int c = 0; c < CPW; ++c) {
 #pragma unroll
     for (int t = 0; t < T; ++t) {
-      if (c < ncol && valid[t]) {
-        load_w<WK>(w[c][t], g, j0 + c, chunk[t]);
+      if (c < ncol) {  // wave-uniform
+        load_w<WK>(w[c][t], g, j0 + c, lchunk[t]);
       } else {
         zero_w<WK>(w[c][t]);
       }
     }
   }
 
+
   // the wave's A slice, kept in registers for all its columns
   u32x4 a[T][M];
-  if (stage_a) {
+  if constexpr (kStageA) {
 #pragma unroll
-    for (int i = 0; i < (kStageA ? (M * 64 * T + 255) / 256 : 0); ++i) {
+    for (int i = 0; i < kStageIters; ++i) {
       const int e = (int)threadIdx.x + i * (int)blockDim.x;
       if (e < M * 64 * T) sAr[e] = a_share[i];
     }
@@ -352,34 +382,46 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
 #pragma unroll
       for (int r = 0; r < M; ++r) a[t][r] = sAr[(r * T + t) * 64 + lane];
   } else {
+    if (active) {  // wave-uniform
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
+      for (int t = 0; t < T; ++t)
 #pragma unroll
-      for (int r = 0; r < M; ++r) {
-        a[t][r] = valid[t] ? load_a8<AK>(g, r, chunk[t]) : u32x4{0u, 0u, 0u, 0u};
-      }
+        for (int r = 0; r < M; ++r) a[t][r] = load_a8<AK>(g, r, lchunk[t]);
+    } else {
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+#pragma unroll
+        for (int r = 0; r < M; ++r) a[t][r] = u32x4{0u, 0u, 0u, 0u};
     }
   }
 
-  if (active) {
+  // every load above is issued before the first product: without this fence
+  // the scheduler interleaves loads with the products that use them, to save
+  // registers, and the loads then wait for one another
+  __builtin_amdgcn_sched_barrier(0);
 
+  if (active) {
     constexpr int plain_mask = plain_lane_mask<LV>();
     const bool writer_lane = (lane & plain_mask) == 0;
 
 #pragma unroll
-    for (int c0 = 0; c0 < kGemvCpwMax; c0 += G) {
+    for (int c0 = 0; c0 < CPW; c0 += G) {
       if (c0 >= ncol) break;
       float v[P2];
 #pragma unroll
       for (int gi = 0; gi < G; ++gi) {
         u32x4 wh[T];
 #pragma unroll
-        for (int t = 0; t < T; ++t) wh[t] = w_as_halves<WK>(w[(c0 + gi) < kGemvCpwMax ? (c0 + gi) : 0][t]);
+        for (int t = 0; t < T; ++t) wh[t] = w_as_halves<WK>(w[c0 + gi][t]);
 #pragma unroll
         for (int r = 0; r < M; ++r) {
+          // chunk by chunk in increasing k; a chunk past k adds nothing
           float acc = 0.0f;
 #pragma unroll
-          for (int t = 0; t < T; ++t) acc = dot8<WK>(a[t][r], wh[t], acc);
+          for (int t = 0; t < T; ++t) {
+            const float next = dot8<WK>(a[t][r], wh[t], acc);
+            acc = valid[t] ? next : acc;
+          }
           v[gi * M + r] = acc;
         }
       }
@@ -392,17 +434,17 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
       const int r = idx - gi * M;
       if (writer_lane && idx < P && c0 + gi < ncol) {
         const int64_t j = j0 + c0 + gi;
-        if (g.S == 1) {
+        if constexpr (SPLIT == kSplitNone) {
           store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish<EPI>(sum));
-        } else if (in_block) {
-          red[(wave * kGemvCpwMax + c0 + gi) * M + r] = sum;
+        } else if constexpr (SPLIT == kSplitBlock) {
+          red[(wave * CPW + c0 + gi) * M + r] = sum;
         } else {
           st_dev(g.partial + ((int64_t)s * M + r) * g.n + j, sum);
         }
       }
     }
 
-    if (!in_block) {
+    if constexpr (SPLIT == kSplitGlobal) {
       wait_mem();  // this wave's partials have reached the device-coherent level
       uint32_t old = 0;
       if (lane == 0) old = atomicAdd(&g.counters[wc], 1u);
@@ -421,19 +463,23 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
     }
   }
 
-  if (in_block && g.S > 1) {
+  if constexpr (SPLIT == kSplitBlock) {
     __syncthreads();  // every wave's sums are in LDS
-    const int per_range = g.cpw * M;
-    for (int e = threadIdx.x; e < g.cg_per_block * per_range; e += blockDim.x) {
-      const int cg = e / per_range;
-      const int c = (e - cg * per_range) / M;
-      const int r = e - cg * per_range - c * M;
-      const int64_t j = (int64_t)(blockIdx.x * g.cg_per_block + cg) * g.cpw + c;
-      if (j >= g.n) continue;  // past the last column (or the last range)
-      const int w0 = cg * g.S;
-      float acc = red[(w0 * kGemvCpwMax + c) * M + r];
-      for (int q = 1; q < g.S; ++q) acc += red[((w0 + q) * kGemvCpwMax + c) * M + r];
-      store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish<EPI>(acc));
+    // wave q adds the S splits of range q (its first split is wave q * S)
+    if (wave < g.cg_per_block) {
+      const int64_t rbase = (int64_t)(blockIdx.x * g.cg_per_block + wave) * CPW;
+      const int w0 = wave * g.S;
+#pragma unroll
+      for (int e0 = 0; e0 < CPW * M; e0 += 64) {
+        const int e = e0 + lane;
+        const int c = e / M;  // M is a constant: no division instruction
+        const int r = e - c * M;
+        const int64_t j = rbase + c;
+        if (e >= CPW * M || j >= g.n) break;  // past the last column
+        float acc = red[(w0 * CPW + c) * M + r];
+        for (int q = 1; q < g.S; ++q) acc += red[((w0 + q) * CPW + c) * M + r];
+        store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish<EPI>(acc));
+      }
     }
   }
 }
@@ -441,62 +487,78 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
 // --- kernel table and launcher (instantiated once per weight type) ---------
 typedef void (*gemv_fn)(GemvArgs);
 
-// [group: 1 column, gemv_group_max(M) columns][C kind: f32, f16, bf16]
-template <int M, int T, int WK, int AK>
+// [columns per wave: 1, 2, 4, 8][C kind: f32, f16, bf16]
+template <int M, int T, int WK, int AK, int SPLIT>
 struct GemvRow {
-  static constexpr int GM = gemv_group_max(M);
-  static constexpr gemv_fn out[2][3] = {
-      {gemv_rows_kernel<M, T, WK, CK_F32, 1, kEpiNone, AK>, gemv_rows_kernel<M, T, WK, CK_F16, 1, kEpiNone, AK>,
-       gemv_rows_kernel<M, T, WK, CK_BF16, 1, kEpiNone, AK>},
-      {gemv_rows_kernel<M, T, WK, CK_F32, GM, kEpiNone, AK>, gemv_rows_kernel<M, T, WK, CK_F16, GM, kEpiNone, AK>,
-       gemv_rows_kernel<M, T, WK, CK_BF16, GM, kEpiNone, AK>}};
+  template <int CPW>
+  static constexpr gemv_fn fn(int ck) {
+    return ck == CK_F32 ? gemv_rows_kernel<M, T, WK, CK_F32, CPW, kEpiNone, AK, SPLIT>
+         : ck == CK_F16 ? gemv_rows_kernel<M, T, WK, CK_F16, CPW, kEpiNone, AK, SPLIT>
+                        : gemv_rows_kernel<M, T, WK, CK_BF16, CPW, kEpiNone, AK, SPLIT>;
+  }
+  static constexpr gemv_fn out[4][3] = {{fn<1>(0), fn<1>(1), fn<1>(2)}, {fn<2>(0), fn<2>(1), fn<2>(2)},
+                                        {fn<4>(0), fn<4>(1), fn<4>(2)}, {fn<8>(0), fn<8>(1), fn<8>(2)}};
 };
 
 // the scalar gate's kernels (sigmoid epilogue; f32 or f16 gate values)
-template <int M, int T, int WK, int AK>
+template <int M, int T, int WK, int AK, int SPLIT>
 struct GemvGateRow {
-  static constexpr int GM = gemv_group_max(M);
-  static constexpr gemv_fn out[2][3] = {
-      {gemv_rows_kernel<M, T, WK, CK_F32, 1, kEpiSigmoid, AK>,
-       gemv_rows_kernel<M, T, WK, CK_F16, 1, kEpiSigmoid, AK>, nullptr},
-      {gemv_rows_kernel<M, T, WK, CK_F32, GM, kEpiSigmoid, AK>,
-       gemv_rows_kernel<M, T, WK, CK_F16, GM, kEpiSigmoid, AK>, nullptr}};
+  template <int CPW>
+  static constexpr gemv_fn fn(int ck) {
+    return ck == CK_F32 ? gemv_rows_kernel<M, T, WK, CK_F32, CPW, kEpiSigmoid, AK, SPLIT>
+         : ck == CK_F16 ? gemv_rows_kernel<M, T, WK, CK_F16, CPW, kEpiSigmoid, AK, SPLIT>
+                        : nullptr;
+  }
+  static constexpr gemv_fn out[4][3] = {{fn<1>(0), fn<1>(1), nullptr}, {fn<2>(0), fn<2>(1), nullptr},
+                                        {fn<4>(0), fn<4>(1), nullptr}, {fn<8>(0), fn<8>(1), nullptr}};
 };
 
-template <int T, int WK, int AK, int... Ms>
-gemv_fn gemv_pick(int m, int group, int out_kind) {
-  const gemv_fn(*tbl[])[3] = {GemvRow<Ms, T, WK, AK>::out...};
-  return tbl[m - 1][group][out_kind];
+template <int T, int WK, int AK, int SPLIT, int... Ms>
+gemv_fn gemv_pick(int m, int cpw_log2, int out_kind) {
+  const gemv_fn(*tbl[])[3] = {GemvRow<Ms, T, WK, AK, SPLIT>::out...};
+  return tbl[m - 1][cpw_log2][out_kind];
 }
 
-template <int T, int WK, int AK, int... Ms>
-gemv_fn gemv_pick_gate(int m, int group, int out_kind) {
-  const gemv_fn(*tbl[])[3] = {GemvGateRow<Ms, T, WK, AK>::out...};
-  return tbl[m - 1][group][out_kind];
+template <int T, int WK, int AK, int SPLIT, int... Ms>
+gemv_fn gemv_pick_gate(int m, int cpw_log2, int out_kind) {
+  const gemv_fn(*tbl[])[3] = {GemvGateRow<Ms, T, WK, AK, SPLIT>::out...};
+  return tbl[m - 1][cpw_log2][out_kind];
 }
 
-// AK = kAF32 is instantiated for bf16 weights only (its own translation unit)
-template <int WK, int AK = kA16>
-hipError_t launch_gemv_kind(const GemvArgs& args, int m, int T, int out_kind, int waves_per_block,
-                            hipStream_t stream) {
-  static_assert(AK == kA16 || WK == WK_BF16, "fp32 rows feed bf16 weights only");
-  if (args.a_kind != AK) return hipErrorInvalidValue;
-  if (m < 1 || m > kGemvMaxM || (T != 1 && T != 2) || out_kind < 0 || out_kind > 2 ||
-      waves_per_block < 1 || waves_per_block > kGemvMaxWavesPerBlock || args.cpw < 1 ||
-      args.cpw > kGemvCpwMax || (args.S == 1 && waves_per_block < 4))
-    return hipErrorInvalidValue;  // (unsplit blocks stage A with at least 256 threads)
-  // one column per pass when the wave owns fewer columns than a full group
-  const int group = args.cpw < gemv_group_max(m) ? 0 : 1;
-  gemv_fn fn = nullptr;
-  if (args.epilogue == kEpiNone) {
-    fn = T == 1 ? gemv_pick<1, WK, AK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind)
-                : gemv_pick<2, WK, AK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind);
-  } else if constexpr (WK == WK_BF16) {  // the gate: bf16 weights only
-    if (args.epilogue == kEpiSigmoid)
-      fn = T == 1
-               ? gemv_pick_gate<1, WK, AK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind)
-               : gemv_pick_gate<2, WK, AK, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, group, out_kind);
+template <int T, int WK, int AK, int SPLIT>
+gemv_fn gemv_pick_any(bool gate, int m, int cpw_log2, int out_kind) {
+  if (!gate)
+    return gemv_pick<T, WK, AK, SPLIT, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, cpw_log2, out_kind);
+  if constexpr (WK == WK_BF16) {  // the gate: bf16 weights only
+    return gemv_pick_gate<T, WK, AK, SPLIT, 1, 2, 3, 4, 5, 6, 7, 8, 9, 10, 11, 12, 13, 14, 15, 16>(m, cpw_log2,
+                                                                                                out_kind);
   }
+  return nullptr;
+}
+
+template <int T, int WK, int AK>
+gemv_fn gemv_pick_split(int split, bool gate, int m, int cpw_log2, int out_kind) {
+  switch (split) {
+    case kSplitNone: return gemv_pick_any<T, WK, AK, kSplitNone>(gate, m, cpw_log2, out_kind);
+    case kSplitBlock: return gemv_pick_any<T, WK, AK, kSplitBlock>(gate, m, cpw_log2, out_kind);
+    default: return gemv_pick_any<T, WK, AK, kSplitGlobal>(gate, m, cpw_log2, out_kind);
+  }
+}
+
+// AK = kAF32 is instantiated for bf16 weights only
+template <int WK, int AK, int T>
+hipError_t launch_gemv_kind(const GemvArgs& args, int m, int out_kind, int waves_per_block, hipStream_t stream) {
+  static_assert(AK == kA16 || WK == WK_BF16, "fp32 rows feed bf16 weights only");
+  static_assert(T == 1 || T == 2, "chunk slots per lane");
+  if (args.a_kind != AK) return hipErrorInvalidValue;
+  if (m < 1 || m > kGemvMaxM || out_kind < 0 || out_kind > 2 || waves_per_block < 1 ||
+      waves_per_block > kGemvMaxWavesPerBlock || (args.S == 1 && waves_per_block < 4))
+    return hipErrorInvalidValue;  // (unsplit blocks stage A with at least 256 threads)
+  const int cpw_log2 = args.cpw == 1 ? 0 : args.cpw == 2 ? 1 : args.cpw == 4 ? 2 : args.cpw == 8 ? 3 : -1;
+  if (cpw_log2 < 0) return hipErrorInvalidValue;  // columns per wave: 1, 2, 4 or 8
+  const int split = args.S == 1 ? kSplitNone : args.S <= kGemvBlockSplitMax ? kSplitBlock : kSplitGlobal;
+  if (args.epilogue != kEpiNone && args.epilogue != kEpiSigmoid) return hipErrorInvalidValue;
+  const gemv_fn fn = gemv_pick_split<T, WK, AK>(split, args.epilogue == kEpiSigmoid, m, cpw_log2, out_kind);
   if (fn == nullptr) return hipErrorInvalidValue;
   int64_t blocks;
   if (args.S <= kGemvBlockSplitMax) {
