@@ -61,6 +61,8 @@ def parse():
     p.add_argument("--no-sweep", action="store_true")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
+    p.add_argument("--oracle-seconds", type=float, default=0.25,
+                   help="CPU-oracle budget per sweep row (a sample of rows, scaled to the call)")
     p.add_argument("--tiles", default=None, metavar="WORKLOAD",
                    help="time every GEMM tile at every m > 16 of WORKLOAD (cold weights, "
                         "HIP-graph replay, min of 5) and print one JSON line per m; the "
@@ -198,7 +200,14 @@ def run_only(spec, steps, warmup):
 # inputs
 # ---------------------------------------------------------------------------
 class Inputs:
-    """Device copies of one workload: a pool of weight copies and one A."""
+    """Device copies of one workload: a rotating pool of (weight, A) copies.
+
+    Every call of a timed loop takes the next copy, so neither operand is
+    cache-warm: the pool (A at the largest m plus the weight, times the copy
+    count) is larger than the 256 MiB Infinity Cache.  For the GEMV
+    workloads A is tiny and the pool is nearly all weight; for the narrow-N
+    and Q8_0 GEMMs at large M, A is most of the bytes and rotates with W.
+    A is copy 0 of the rows (the headline step uses it)."""
 
     def __init__(self, wl, torch, max_rows, pool_bytes=POOL_BYTES):
         import numpy as np
@@ -218,7 +227,9 @@ class Inputs:
             self.A = torch.from_numpy(np.ascontiguousarray(A, dtype=np.float32)).cuda()
         else:
             self.A = dev16(A, wl.a_kind)
-        copies = max(2, int(pool_bytes // max(1, wl.w_bytes)))
+        a_bytes = self.A.numel() * self.A.element_size()
+        copies = max(2, int(pool_bytes // max(1, wl.w_bytes + a_bytes)))
+        self.As = [self.A] + [self.A.clone() for _ in range(copies - 1)]
         if wl.w_kind == "q8_0":
             qs, d = W
             q0 = torch.from_numpy(qs).cuda()
@@ -334,7 +345,34 @@ class RouterStep:
 # ---------------------------------------------------------------------------
 # sweep over every workload and m
 # ---------------------------------------------------------------------------
-def sweep(sk, torch, rounds):
+def oracle_call_time(wl, m, inp, budget_s):
+    """The CPU oracle's time for one call of this workload at m rows, on this
+    host's cores, beside the GPU's: the oracle (fp64, plain C) runs on the
+    first r <= m rows of the same inputs, r chosen so the sample costs about
+    budget_s, and its time is scaled by m / r (every row is the same work).
+    The top-k (router) and the sigmoid (gate) are part of the timed call."""
+    import oracle
+
+    threads = oracle.default_threads()
+    flops_per_row = 2.0 * wl.n * wl.k
+    rows = max(1, min(m, int(budget_s * 2.0e9 * threads / flops_per_row)))
+    A = inp.A_bits[:rows]
+    t0 = time.perf_counter()
+    if wl.a_kind == "f32":
+        oracle.gate(A, inp.W_bits, threads=threads)
+    elif wl.w_kind == "q8_0":
+        qs, d = inp.W_bits
+        oracle.mm(A, "f16", qs, "q8_0", w_scales=d, threads=threads)
+    else:
+        ref = oracle.mm(A, wl.a_kind, inp.W_bits, wl.w_kind, threads=threads)
+        if wl.topk:
+            oracle.topk(ref, wl.topk)
+    dt = time.perf_counter() - t0
+    return {"us_per_call": round(dt * 1e6 * m / rows, 1), "rows_timed": rows, "cores": threads,
+            "kind": "oracle", "gpu_speedup": None}
+
+
+def sweep(sk, torch, rounds, oracle_s=0.0):
     import workloads as WL
 
     rows = []
@@ -350,24 +388,25 @@ def sweep(sk, torch, rounds):
         for m in wl.ms:
             C = torch.empty((m, wl.n), dtype=cdt, device="cuda")
             keep.append(C)
-            Am = inp.A[:m]
             L = min(len(inp.W), 256)
+            nA = len(inp.As)
 
             if wl.w_kind == "q8_0":
-                def fn(i, m=m, C=C, Am=Am):
+                def fn(i, m=m, C=C):
                     qs, d = inp.W[i % len(inp.W)]
-                    plan.run(m, Am, qs, C, scales=d, workspace=ws)
+                    plan.run(m, inp.As[i % nA][:m], qs, C, scales=d, workspace=ws)
             elif wl.topk:
                 lg = C
                 idx = torch.empty((m, wl.topk), dtype=torch.int32, device="cuda")
                 val = torch.empty((m, wl.topk), dtype=torch.float32, device="cuda")
                 keep += [idx, val]
 
-                def fn(i, m=m, Am=Am, lg=lg, idx=idx, val=val):
-                    plan.run_topk(m, Am, inp.W[i % len(inp.W)], lg, idx, val, wl.topk, workspace=ws)
+                def fn(i, m=m, lg=lg, idx=idx, val=val):
+                    plan.run_topk(m, inp.As[i % nA][:m], inp.W[i % len(inp.W)], lg, idx, val, wl.topk,
+                                  workspace=ws)
             else:
-                def fn(i, m=m, C=C, Am=Am):
-                    plan.run(m, Am, inp.W[i % len(inp.W)], C, workspace=ws)
+                def fn(i, m=m, C=C):
+                    plan.run(m, inp.As[i % nA][:m], inp.W[i % len(inp.W)], C, workspace=ws)
             keep.append(fn)
             graphs[m] = (capture(torch, fn, L), L)
         # interleave rounds across m (the min over interleaved rounds)
@@ -390,6 +429,9 @@ def sweep(sk, torch, rounds):
                 "TFLOPs": round(flops / t_min / 1e6, 2),
                 "mfma_frac": round(flops / t_min / 1e6 / MFMA_F16_PEAK_TFLOPS, 4),
             }
+            if oracle_s > 0:
+                row["oracle"] = oracle_call_time(wl, m, inp, oracle_s)
+                row["oracle"]["gpu_speedup"] = round(row["oracle"]["us_per_call"] / t_min, 1)
             rows.append(row)
             log(f"  {name:12s} m={m:5d} {t_min:8.3f} us (med {t_med:8.3f})  us/row {t_min / m:8.4f}"
                 f"  W {row['weight_GBps']:8.1f} GB/s  hbm {row['hbm_frac']:.3f}  "
@@ -401,7 +443,7 @@ def sweep(sk, torch, rounds):
     return rows
 
 
-def sweep_combine(sk, torch, rounds):
+def sweep_combine(sk, torch, rounds, oracle_s=0.0):
     """The MoE combine of the window: m tokens, each with its top-10 experts'
     fp32 output rows (d = 5120), fp32 routing weights, the shared expert's row
     and its gate; fp32 out.  Every call reads a different copy of the inputs
@@ -439,6 +481,14 @@ def sweep_combine(sk, torch, rounds):
                "us_per_call_min": round(t_min, 3), "us_per_call_median": round(t_med, 3),
                "us_per_row": round(t_min / m, 4), "GBps": round(nbytes / t_min / 1e3, 1),
                "hbm_frac": round(nbytes / t_min / 1e3 / HBM_PEAK_GBS, 4)}
+        if oracle_s > 0:
+            import oracle
+
+            t0 = time.perf_counter()
+            oracle.moe_combine(y[:m], w[:m], sh[:m], g[:m])
+            dt = time.perf_counter() - t0
+            row["oracle"] = {"us_per_call": round(dt * 1e6, 1), "rows_timed": m, "cores": 1, "kind": "oracle",
+                             "gpu_speedup": round(dt * 1e6 / t_min, 1)}
         rows.append(row)
         log(f"  moe_combine  m={m:5d} {t_min:8.3f} us (med {t_med:8.3f})  {row['GBps']:8.1f} GB/s"
             f"  hbm {row['hbm_frac']:.3f}  [{row['plan']}]")
@@ -485,6 +535,18 @@ def measured_traffic():
         return None
 
 
+def cpu_model():
+    """The host CPU's model name (from /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(torch, step, budget_s):
     import numpy as np
 
@@ -520,6 +582,7 @@ def cpu_baseline(torch, step, budget_s):
     gbps = step.weight_bytes_per_step() * done_steps / dt / 1e9
     return {
         "value": round(gbps, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+        "cpu_model": cpu_model(),
         "sample": f"{done_steps} headline steps (router m=1,2,4,8,16 + top-10), fp64 oracle, "
                   f"{dt:.1f} s wall",
     }, ok
@@ -602,7 +665,9 @@ def main():
         del gm
     log("per m: " + ", ".join(f"m={r['m']}: {r['us_per_row']} us/row" for r in per_m))
 
-    sweep_rows = [] if args.no_sweep else sweep(sk, torch, args.rounds) + sweep_combine(sk, torch, args.rounds)
+    osec = 0.0 if args.no_cpu else args.oracle_seconds
+    sweep_rows = [] if args.no_sweep else (sweep(sk, torch, args.rounds, osec) +
+                                           sweep_combine(sk, torch, args.rounds, osec))
 
     cpu = None
     parity_ok = True

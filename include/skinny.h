@@ -95,6 +95,13 @@ typedef enum skinny_dtype {
  * tile that cannot hold two accumulator sets falls back to the first. */
 #define SKINNY_GEMM_SPLIT_LAUNCH 0x4u
 #define SKINNY_GEMM_ONE_LAUNCH 0x8u
+/* A third shape, one launch with one block per (tile, chunk) in which the
+ * last block of each tile to finish adds the tile's chunk sums in chunk order
+ * (the same bits again; no reduce launch, arrival counters in the
+ * workspace).  It measured slower than the other two on MI355X, so a plan
+ * runs it only when this flag asks for it; tiles that cannot run it use the
+ * split launch.  At most one of the three shape flags may be set. */
+#define SKINNY_GEMM_FOLD_LAUNCH 0x20u
 /* C = sigmoid(A . W) elementwise, sigmoid(x) = 1 / (1 + e^-x) in fp32 (the
  * Strata PR #109 page, "What": the shared expert's scalar gate is a
  * multi-row GEMV followed by a sigmoid; here the sigmoid is applied as the
@@ -167,7 +174,8 @@ SKINNY_API void skinny_mm_plan_destroy(skinny_plan* plan);
  *     finish the sum inside the same kernel;
  *   - a GEMM whose plan cuts k into chunks (narrow n) and runs them as one
  *     block per chunk: it holds the chunks' fp32 partial sums, which an
- *     ordered reduce launch adds;
+ *     ordered reduce launch adds (or, with SKINNY_GEMM_FOLD_LAUNCH, the
+ *     arrival counters per tile and the chunk sums the last block adds);
  *   - a plan with fp32 A whose GEMV splits k (k > 1024 for bf16 weights), at
  *     m > 10: the fused cast measured slower there than a separate cast
  *     launch, so the run casts the rows into the workspace (after any

@@ -37,6 +37,7 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_SHAPE, ERR_HIP, ERR_WOR
 F16, BF16, F32, Q8_0 = 1, 2, 3, 4
 FORCE_GEMV, FORCE_GEMM, GEMM_SPLIT_LAUNCH, GEMM_ONE_LAUNCH = 0x1, 0x2, 0x4, 0x8
 EPILOGUE_SIGMOID = 0x10
+GEMM_FOLD_LAUNCH = 0x20
 GEMV_MAX_M = 16
 TOPK_MAX = 32
 

@@ -187,15 +187,23 @@ double reduce_estimate(const skinny_plan* p, int64_t m) {
 
 struct GemmChoice {
   int tile;
-  bool split;  // splits > 1: one block per chunk + the reduce launch
-  bool chunked;  // splits > 1 plan run as one chunk-folding launch
+  int shape;   // kGemmPlain, kGemmChunked (in-block chunk fold) or kGemmFold (last block folds)
+  bool split;  // one block per (tile, chunk): the plain shape + the reduce launch, or the fold shape
   double est;
 };
 
+// The fold launch (one block per (tile, chunk); the last block of a tile to
+// finish adds the tile's chunk sums in order) gives the split launch's bits
+// without the reduce launch, but measured slower than split + reduce on every
+// MI355X shape tried (N = 96 and 512, K = 2560, M = 306 .. 2048: e.g. 13.6
+// against 7.5 us at N = 96, M = 512 on 64 x 64 tiles): one block per tile
+// reads all of the tile's chunk sums after a device-scope handoff, where
+// the reduce launch spreads them over every CU.  So a plan takes it only
+// when SKINNY_GEMM_FOLD_LAUNCH asks for it.
 GemmChoice choose_gemm(const skinny_plan* p, int64_t m) {
   const int64_t nk = (p->d.k + 63) / 64;
   const int C = p->gemm_splits;
-  GemmChoice best{0, false, false, 0.0};
+  GemmChoice best{0, kGemmPlain, false, 0.0};
   bool have = false;
   const int first = p->d.tile_id >= 0 ? p->d.tile_id : 0;
   const int last = p->d.tile_id >= 0 ? p->d.tile_id + 1 : gemm_tile_count();
@@ -203,14 +211,18 @@ GemmChoice choose_gemm(const skinny_plan* p, int64_t m) {
     GemmChoice c[2];
     int n = 0;
     if (C == 1) {
-      c[n++] = GemmChoice{id, false, false, tile_estimate(p, id, m, 1, nk)};
+      c[n++] = GemmChoice{id, kGemmPlain, false, tile_estimate(p, id, m, 1, nk)};
+    } else if ((p->d.flags & SKINNY_GEMM_FOLD_LAUNCH) && gemm_tile_foldable(id)) {
+      c[n++] = GemmChoice{id, kGemmFold, true, tile_estimate(p, id, m, C, p->gemm_kps)};
     } else {
-      const bool one_ok = gemm_tile_chunkable(id) && !(p->d.flags & SKINNY_GEMM_SPLIT_LAUNCH);
-      const bool split_ok = !(p->d.flags & SKINNY_GEMM_ONE_LAUNCH) || !gemm_tile_chunkable(id);
+      const bool force_one = (p->d.flags & SKINNY_GEMM_ONE_LAUNCH) != 0;
+      const bool force_split = (p->d.flags & (SKINNY_GEMM_SPLIT_LAUNCH | SKINNY_GEMM_FOLD_LAUNCH)) != 0;
+      const bool one_ok = gemm_tile_chunkable(id) && !force_split;
+      const bool split_ok = !force_one || !gemm_tile_chunkable(id);
       if (split_ok)
-        c[n++] = GemmChoice{id, true, false,
+        c[n++] = GemmChoice{id, kGemmPlain, true,
                             tile_estimate(p, id, m, C, p->gemm_kps) + reduce_estimate(p, m)};
-      if (one_ok) c[n++] = GemmChoice{id, false, true, tile_estimate(p, id, m, 1, nk)};
+      if (one_ok) c[n++] = GemmChoice{id, kGemmChunked, false, tile_estimate(p, id, m, 1, nk)};
     }
     for (int i = 0; i < n; ++i) {
       if (!have || c[i].est < best.est * (1.0 - 1e-9)) {
@@ -246,6 +258,44 @@ size_t gemv_counter_bytes(const skinny_plan* p) {
              : 0;
 }
 
+bool plan_may_gemm(const skinny_plan* p) {
+  return !(p->d.flags & SKINNY_FORCE_GEMV) && (p->d.max_m > kGemvMaxM || (p->d.flags & SKINNY_FORCE_GEMM));
+}
+
+bool plan_may_fold(const skinny_plan* p) {
+  return plan_may_gemm(p) && p->gemm_splits > 1 && (p->d.flags & SKINNY_GEMM_FOLD_LAUNCH);
+}
+
+int64_t tile_count(int id, int64_t m, int64_t n) {
+  const GemmTileInfo& t = gemm_tile(id);
+  return ((m + t.tm - 1) / t.tm) * ((n + t.tn - 1) / t.tn);
+}
+
+// the fold launch's largest tile count (one arrival counter each) and chunk
+// sums (TM x TN fp32 per tile and chunk) over the tiles it may run, at max_m
+size_t fold_counter_bytes_max(const skinny_plan* p) {
+  if (!plan_may_fold(p)) return 0;
+  int64_t most = 0;
+  for (int id = 0; id < gemm_tile_count(); ++id)
+    if (gemm_tile_foldable(id) && (p->d.tile_id < 0 || p->d.tile_id == id)) {
+      const int64_t t = tile_count(id, p->d.max_m, p->d.n);
+      most = t > most ? t : most;
+    }
+  return round_up((size_t)most * sizeof(uint32_t));
+}
+
+size_t fold_slot_bytes(int id, int64_t m, const skinny_plan* p) {
+  const GemmTileInfo& t = gemm_tile(id);
+  return round_up((size_t)tile_count(id, m, p->d.n) * (size_t)p->gemm_splits * (size_t)t.tm * (size_t)t.tn *
+                  sizeof(float));
+}
+
+// the counter region: the GEMV's arrival counters or the fold launch's
+size_t counter_bytes(const skinny_plan* p) {
+  const size_t a = gemv_counter_bytes(p), b = fold_counter_bytes_max(p);
+  return a > b ? a : b;
+}
+
 size_t gemv_partial_bytes(const skinny_plan* p, int64_t m) {
   return gemv_global_split(p)
              ? round_up((size_t)p->gemv_S * (size_t)m * (size_t)p->d.n * sizeof(float))
@@ -253,9 +303,10 @@ size_t gemv_partial_bytes(const skinny_plan* p, int64_t m) {
 }
 
 size_t gemm_partial_bytes(const skinny_plan* p, int64_t m) {
-  return choose_gemm(p, m).split
-             ? round_up((size_t)p->gemm_splits * (size_t)m * (size_t)p->d.n * sizeof(float))
-             : 0;
+  const GemmChoice gc = choose_gemm(p, m);
+  if (!gc.split) return 0;
+  if (gc.shape == kGemmFold) return fold_slot_bytes(gc.tile, m, p);
+  return round_up((size_t)p->gemm_splits * (size_t)m * (size_t)p->d.n * sizeof(float));
 }
 
 // fp32 rows of A: the GEMV rounds them to bf16 as it loads them (one
@@ -300,13 +351,13 @@ size_t data_bytes_for(const skinny_plan* p, int64_t m) {
 // partial sums)
 size_t workspace_bytes_for(const skinny_plan* p, int64_t m) {
   const size_t data = data_bytes_for(p, m);
-  return data > 0 ? gemv_counter_bytes(p) + data : 0;
+  return data > 0 ? counter_bytes(p) + data : 0;
 }
 
 // the two regions inside a caller's workspace
 Scratch caller_scratch(const skinny_plan* p, void* workspace) {
   char* ws = (char*)workspace;
-  return Scratch{(uint32_t*)ws, ws != nullptr ? ws + gemv_counter_bytes(p) : nullptr};
+  return Scratch{(uint32_t*)ws, ws != nullptr ? ws + counter_bytes(p) : nullptr};
 }
 
 skinny_status hip_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_ERR_HIP; }
@@ -349,6 +400,7 @@ GemmArgs gemm_args(const skinny_plan* p, int64_t m, const void* A, const void* W
   g.splits = 1;
   g.kt_per_split = p->gemm_kps;
   g.partial = p->gemm_splits > 1 ? (float*)sc.data : nullptr;
+  g.counters = sc.counters;
   return g;
 }
 
@@ -432,8 +484,9 @@ skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const v
   GemmArgs g = gemm_args(p, m, A, W, scales, C, ldc, sc);
   const GemmChoice gc = choose_gemm(p, m);
   if (gc.split) g.splits = p->gemm_splits;
-  skinny_status st = hip_status(launch_gemm(gc.tile, g, p->w_kind, c_kind, gc.chunked, stream));
-  if (st == SKINNY_OK && g.splits > 1) st = hip_status(launch_splitk_reduce(g, c_kind, stream));
+  skinny_status st = hip_status(launch_gemm(gc.tile, g, p->w_kind, c_kind, gc.shape, stream));
+  if (st == SKINNY_OK && gc.split && gc.shape == kGemmPlain)
+    st = hip_status(launch_splitk_reduce(g, c_kind, stream));
   if (st != SKINNY_OK || !want_topk) return st;
   return hip_status(launch_topk((const float*)C, (int)m, p->d.n, ldc, topk_idx, topk_val, topk, stream));
 }
@@ -492,7 +545,7 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   if (d.lda < d.k || d.ldc < d.n) return SKINNY_ERR_SHAPE;
   if (d.lda % 8 != 0) return SKINNY_ERR_ALIGNMENT;  // A rows are read 16 bytes at a time
   if (d.flags & ~(SKINNY_FORCE_GEMV | SKINNY_FORCE_GEMM | SKINNY_GEMM_SPLIT_LAUNCH | SKINNY_GEMM_ONE_LAUNCH |
-                  SKINNY_EPILOGUE_SIGMOID))
+                  SKINNY_GEMM_FOLD_LAUNCH | SKINNY_EPILOGUE_SIGMOID))
     return SKINNY_ERR_UNSUPPORTED;
   // the gate's sigmoid is applied by the GEMV only, for bf16 weights and an
   // f32 or f16 gate
@@ -500,7 +553,10 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
       (d.max_m > kGemvMaxM || (d.flags & SKINNY_FORCE_GEMM) || d.w_dtype != SKINNY_BF16 ||
        d.c_dtype == SKINNY_BF16))
     return SKINNY_ERR_UNSUPPORTED;
-  if ((d.flags & SKINNY_GEMM_SPLIT_LAUNCH) && (d.flags & SKINNY_GEMM_ONE_LAUNCH)) return SKINNY_ERR_INVALID_ARG;
+  {
+    const uint32_t shapes = d.flags & (SKINNY_GEMM_SPLIT_LAUNCH | SKINNY_GEMM_ONE_LAUNCH | SKINNY_GEMM_FOLD_LAUNCH);
+    if (shapes & (shapes - 1)) return SKINNY_ERR_INVALID_ARG;  // at most one launch shape forced
+  }
   if ((d.flags & SKINNY_FORCE_GEMV) && (d.flags & SKINNY_FORCE_GEMM)) return SKINNY_ERR_INVALID_ARG;
   if ((d.flags & SKINNY_FORCE_GEMV) && d.max_m > kGemvMaxM) return SKINNY_ERR_INVALID_ARG;
   if (d.tile_id < -1 || d.tile_id >= gemm_tile_count()) return SKINNY_ERR_INVALID_ARG;
@@ -559,12 +615,18 @@ skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_t* bytes) {
   // max_m (each needs the workspace only when it splits k across workgroups)
   // (a GEMM that cuts k into chunks may use the split launch at any m, so
   // its partials are sized for max_m)
+  // (the fold launch's chunk sums are TM x TN per tile and chunk: the
+  // largest of its tiles at max_m bounds every m)
   size_t need = workspace_bytes_for(plan, plan->d.max_m < kGemvMaxM ? plan->d.max_m : kGemvMaxM);
-  const bool may_gemm = !(plan->d.flags & SKINNY_FORCE_GEMV) &&
-                        (plan->d.max_m > kGemvMaxM || (plan->d.flags & SKINNY_FORCE_GEMM));
-  if (may_gemm && plan->gemm_splits > 1) {
-    const size_t g = gemv_counter_bytes(plan) + round_up((size_t)plan->gemm_splits * (size_t)plan->d.max_m *
-                                                         (size_t)plan->d.n * sizeof(float));
+  if (plan_may_gemm(plan) && plan->gemm_splits > 1) {
+    size_t data = round_up((size_t)plan->gemm_splits * (size_t)plan->d.max_m * (size_t)plan->d.n * sizeof(float));
+    if (plan_may_fold(plan))
+      for (int id = 0; id < gemm_tile_count(); ++id)
+        if (gemm_tile_foldable(id) && (plan->d.tile_id < 0 || plan->d.tile_id == id)) {
+          const size_t f = fold_slot_bytes(id, plan->d.max_m, plan);
+          data = f > data ? f : data;
+        }
+    const size_t g = counter_bytes(plan) + data;
     need = g > need ? g : need;
   }
   *bytes = need;
@@ -587,7 +649,7 @@ skinny_status skinny_mm_run_static(const skinny_plan* plan, int64_t m, const voi
   // sizes first, before any HIP call: the counters must fit their region and
   // the partial sums and cast rows the data region
   const size_t data = data_bytes_for(plan, m);
-  if (data > 0 && (gemv_counter_bytes(plan) > kStaticCounterBytes || data > kStaticDataBytes))
+  if (data > 0 && (counter_bytes(plan) > kStaticCounterBytes || data > kStaticDataBytes))
     return SKINNY_ERR_SCRATCH;
   Scratch sc{nullptr, nullptr};
   if (data > 0) {
@@ -698,7 +760,8 @@ skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf,
                   "path=gemm m=%lld tile=%d name=%s chunks=%d launch=%s blocks=%lld threads=%d "
                   "est_us=%.1f workspace=%zu",
                   (long long)m, gc.tile, t.name, plan->gemm_splits,
-                  gc.split ? "split" : (gc.chunked ? "one" : "plain"), (long long)blocks,
+                  gc.shape == kGemmFold ? "fold" : gc.split ? "split" : (gc.shape == kGemmChunked ? "one" : "plain"),
+                  (long long)blocks,
                   64 * t.wm * t.wn, gc.est, workspace_bytes_for(plan, m));
   }
   return SKINNY_OK;

@@ -199,8 +199,9 @@ __device__ __forceinline__ void store_out8(void* base, int64_t idx, const float 
   *(u32x4*)((uint16_t*)base + idx) = w;
 }
 
-template <int TM, int TN, int WM, int WN, int NS, bool XT, bool CH, int WK, int CK>
+template <int TM, int TN, int WM, int WN, int NS, bool XT, bool CH, int WK, int CK, bool FD = false>
 __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
+  static_assert(!(CH && FD), "a launch folds chunk sums in-block or across blocks, not both");
   constexpr bool Q8 = WK == WK_Q8;
   constexpr int NW = WM * WN;
   constexpr int WTM = TM / WM;
@@ -549,13 +550,61 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
   }
   wait_vmcnt<0>();  // the re-reads past the end land before the block exits
 
+  // FD (one block per (tile, chunk), folded in this launch): every block
+  // parks its chunk sum in the workspace slot of its (tile, chunk), in
+  // register order (each lane's own values, so the stores and the loads
+  // below are 256-byte rows per wave instruction), with device-coherent
+  // stores; waits for them; and counts itself in on its tile.  The block
+  // that arrives last adds the tile's chunk sums in chunk order -- the first
+  // copied, each later one added -- exactly the additions of the reduce
+  // launch and of the in-block chunk fold, so every launch shape gives the
+  // same bits -- and writes C below.  The others are done.  No block waits
+  // for another; the counter is left at zero.
+  if constexpr (FD) {
+    constexpr int64_t kSlot = (int64_t)TM * TN;
+    const int64_t tile_id = bm * tiles_n + bn;
+    float* slots = g.partial + tile_id * g.splits * kSlot;
+    auto at = [&](int c, int i, int j, int v) INLINE_LAMBDA -> float* {
+      return slots + c * kSlot + (((wid * FM + i) * FN + j) * 16 + v) * 64 + lane;
+    };
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) st_dev(at(split, i, j, v), acc[i][j][v]);
+    wait_mem();
+    __shared__ uint32_t s_last;
+    __syncthreads();  // every wave's chunk sum has reached the device-coherent level
+    if (tid == 0) s_last = atomicAdd(&g.counters[tile_id], 1u) == (uint32_t)(g.splits - 1) ? 1u : 0u;
+    __syncthreads();
+    if (s_last == 0u) return;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        f32x16 tot;
+        f32x16 p;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) tot[v] = split == 0 ? acc[i][j][v] : ld_dev(at(0, i, j, v));
+        for (int c = 1; c < g.splits; ++c) {
+#pragma unroll
+          for (int v = 0; v < 16; ++v) p[v] = c == split ? acc[i][j][v] : ld_dev(at(c, i, j, v));
+#pragma unroll
+          for (int v = 0; v < 16; ++v) tot[v] = tot[v] + p[v];
+        }
+        acc[i][j] = tot;
+      }
+    if (tid == 0) g.counters[tile_id] = 0u;  // every block of the tile has counted in
+  }
+
   // The weight fragment is the MFMA's first operand, so lane l of a 32 x 32
   // block holds output row l % 32 and, in each group q of four registers,
   // the four adjacent columns 8 q + 4 (l / 32) .. + 3.  Stores are as wide as
   // the row stride's alignment allows: 16 bytes per lane (fp32, or 16-bit
   // output after the swap below), else element by element.  Where a value is
   // stored changes no bits.
-  if (CK != CK_F32 && (CH || g.splits == 1)) {
+  if (CK != CK_F32 && (CH || FD || g.splits == 1)) {
     // 16-bit output: lanes l and l + 32 trade halves of two groups
     // (v_permlane32_swap), so lane l holds columns 8 q .. 8 q + 7 of its row
     // and lane l + 32 the next eight: one 16-byte store per lane per group
@@ -610,7 +659,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) v4[e] = CH ? tot[i][j][4 * q + e] : acc[i][j][4 * q + e];
           if (row < g.M && rem > 0) {
-            if (!CH && g.splits > 1) {
+            if (!CH && !FD && g.splits > 1) {
               float* dst = g.partial + ((int64_t)split * g.M + row) * g.N + col;
               if (vec_p && rem >= 4) {
                 *(u32x4*)dst = u32x4{__builtin_bit_cast(uint32_t, v4[0]), __builtin_bit_cast(uint32_t, v4[1]),
@@ -663,23 +712,24 @@ struct TileEntry {
   GemmTileInfo info;
   gemm_fn fn[3][3];     // [w_kind][c_kind]
   gemm_fn fn_ch[3][3];  // one launch over k chunks (null where the tile cannot hold two sums)
+  gemm_fn fn_fd[3][3];  // one block per (tile, chunk), folded by the last (null: not built)
 };
 
 // Every weight kind runs the same multi-stage kernel with NS k-tiles in LDS
 // (XT: the next k-tile's fragments are read during this one's MFMAs); Q8_0
 // codes and scales enter LDS as stored and each B fragment is dequantised as
 // it is read.  All kinds issue the same MFMA sequence for every output.
-template <int TM, int TN, int WM, int WN, int NS, bool XT, bool CH>
+template <int TM, int TN, int WM, int WN, int NS, bool XT, bool CH, bool FD = false>
 void fill_kinds(gemm_fn (&f)[3][3]) {
-  f[WK_F16][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_F16, CK_F32>;
-  f[WK_F16][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_F16, CK_F16>;
-  f[WK_F16][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_F16, CK_BF16>;
-  f[WK_BF16][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_BF16, CK_F32>;
-  f[WK_BF16][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_BF16, CK_F16>;
-  f[WK_BF16][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_BF16, CK_BF16>;
-  f[WK_Q8][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_Q8, CK_F32>;
-  f[WK_Q8][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_Q8, CK_F16>;
-  f[WK_Q8][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_Q8, CK_BF16>;
+  f[WK_F16][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_F16, CK_F32, FD>;
+  f[WK_F16][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_F16, CK_F16, FD>;
+  f[WK_F16][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_F16, CK_BF16, FD>;
+  f[WK_BF16][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_BF16, CK_F32, FD>;
+  f[WK_BF16][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_BF16, CK_F16, FD>;
+  f[WK_BF16][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_BF16, CK_BF16, FD>;
+  f[WK_Q8][CK_F32] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_Q8, CK_F32, FD>;
+  f[WK_Q8][CK_F16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_Q8, CK_F16, FD>;
+  f[WK_Q8][CK_BF16] = gemm_lds_kernel<TM, TN, WM, WN, NS, XT, CH, WK_Q8, CK_BF16, FD>;
 }
 
 // the chunked one-launch variant keeps a second set of accumulators, so only
@@ -692,10 +742,15 @@ TileEntry make_tile(const char* name) {
   TileEntry e;
   e.info = GemmTileInfo{TM, TN, WM, WN, name};
   fill_kinds<TM, TN, WM, WN, NS, XT, false>(e.fn);
+  // the chunk-cut launches serve narrow n, where the small tiles run: the
+  // fold launch is built for the tiles that can also fold in-block
   if constexpr (kChunkable<TM, TN, WM, WN>) {
     fill_kinds<TM, TN, WM, WN, NS, XT, true>(e.fn_ch);
+    fill_kinds<TM, TN, WM, WN, NS, XT, false, true>(e.fn_fd);
   } else {
     for (auto& row : e.fn_ch)
+      for (auto& f : row) f = nullptr;
+    for (auto& row : e.fn_fd)
       for (auto& f : row) f = nullptr;
   }
   return e;
@@ -735,9 +790,10 @@ const GemmTileInfo& gemm_tile(int id) { return tiles()[id].info; }
 
 bool gemm_tile_chunkable(int id) { return tiles()[id].fn_ch[0][0] != nullptr; }
 
-hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind, bool chunked,
+hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind, int shape,
                        hipStream_t stream) {
-  if (tile_id < 0 || tile_id >= kTileCount || w_kind < 0 || w_kind > 2 || c_kind < 0 || c_kind > 2)
+  if (tile_id < 0 || tile_id >= kTileCount || w_kind < 0 || w_kind > 2 || c_kind < 0 || c_kind > 2 ||
+      shape < kGemmPlain || shape > kGemmFold)
     return hipErrorInvalidValue;
   const TileEntry& e = tiles()[tile_id];
   const int64_t nk = (args.K + kBK - 1) / kBK;
@@ -748,14 +804,23 @@ hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind
   const int64_t blocks =
       ((args.M + e.info.tm - 1) / e.info.tm) * ((args.N + e.info.tn - 1) / e.info.tn) * args.splits;
   if (blocks > 0x7fffffff) return hipErrorInvalidValue;
-  // a chunked launch folds between pairs of k-tiles: chunks of even length
-  if (chunked && (args.splits != 1 || e.fn_ch[w_kind][c_kind] == nullptr ||
-                  (args.kt_per_split % 2 != 0 && args.kt_per_split < nk)))
-    return hipErrorInvalidValue;
-  hipLaunchKernelGGL(chunked ? e.fn_ch[w_kind][c_kind] : e.fn[w_kind][c_kind], dim3((unsigned)blocks),
-                     dim3(64 * e.info.wm * e.info.wn), 0, stream, args);
+  gemm_fn fn = e.fn[w_kind][c_kind];
+  if (shape == kGemmChunked) {
+    // a chunked launch folds between pairs of k-tiles: chunks of even length
+    if (args.splits != 1 || e.fn_ch[w_kind][c_kind] == nullptr ||
+        (args.kt_per_split % 2 != 0 && args.kt_per_split < nk))
+      return hipErrorInvalidValue;
+    fn = e.fn_ch[w_kind][c_kind];
+  } else if (shape == kGemmFold) {
+    if (args.splits < 2 || e.fn_fd[w_kind][c_kind] == nullptr || args.counters == nullptr)
+      return hipErrorInvalidValue;
+    fn = e.fn_fd[w_kind][c_kind];
+  }
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * e.info.wm * e.info.wn), 0, stream, args);
   return hipGetLastError();
 }
+
+bool gemm_tile_foldable(int id) { return tiles()[id].fn_fd[0][0] != nullptr; }
 
 hipError_t launch_splitk_reduce(const GemmArgs& args, int c_kind, hipStream_t stream) {
   if (args.splits < 2 || args.splits > kMaxSplits || args.partial == nullptr || c_kind < 0 || c_kind > 2)

@@ -57,25 +57,6 @@ struct GemvShape {
 __device__ __forceinline__ float fbits(uint32_t u) { return __builtin_bit_cast(float, u); }
 __device__ __forceinline__ uint32_t ubits(float f) { return __builtin_bit_cast(uint32_t, f); }
 
-// Device-coherent accesses for data handed from one workgroup to another in
-// the same launch.  Relaxed agent-scope atomic stores/loads compile to plain
-// global stores/loads with the sc1 (device scope) bit: they are coherent
-// across the XCDs' L2 caches without the whole-L2 write-back and invalidate
-// that an agent-scope fence costs.  A writer waits for its stores to complete
-// (s_waitcnt) before it counts itself in with an atomic; the reader issues its
-// loads only after its atomic returned the final count.
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float ld_dev(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void wait_mem() {
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  __builtin_amdgcn_s_waitcnt(0);  // every outstanding load and store of this wave completed
-  __atomic_signal_fence(__ATOMIC_SEQ_CST);
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp_mov(float x) {
   return fbits(__builtin_amdgcn_update_dpp(0u, ubits(x), CTRL, 0xF, 0xF, false));

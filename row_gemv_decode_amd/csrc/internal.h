@@ -107,7 +107,9 @@ struct GemmArgs {
   int64_t ldc;
   int32_t splits;          // blocks per tile: k split into this many ranges of
   int32_t kt_per_split;    // kt_per_split k-tiles (also the chunk of a chunked launch)
-  float* partial;          // [splits][M][N] fp32 partial sums (splits > 1)
+  float* partial;          // splits > 1: [splits][M][N] fp32 partial sums (split launch), or
+                           // [tile][split][TM * TN] chunk sums in register order (fold launch)
+  uint32_t* counters;      // fold launch: arrivals per tile, zero between calls
 };
 
 struct GemmTileInfo {
@@ -118,11 +120,22 @@ struct GemmTileInfo {
 int gemm_tile_count();
 const GemmTileInfo& gemm_tile(int id);
 
-// chunked: one launch over a k cut into chunks of kt_per_split k-tiles
-// (splits == 1), folding the chunk sums in order; needs a chunkable tile
-hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind, bool chunked,
+// Launch shapes of a plan whose k is cut into chunks (args.splits > 1 for the
+// split and fold shapes; 1 for the chunked shape, which walks all chunks):
+//   kGemmPlain    one block per tile over all of k (unchunked plans), or one
+//                 block per (tile, chunk) writing partial sums for the
+//                 reduce launch (splits > 1);
+//   kGemmChunked  one block per tile folding its chunk sums in order
+//                 (needs a chunkable tile);
+//   kGemmFold     one block per (tile, chunk); the last block of a tile to
+//                 finish folds the tile's chunk sums in order and writes C.
+constexpr int kGemmPlain = 0;
+constexpr int kGemmChunked = 1;
+constexpr int kGemmFold = 2;
+hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind, int shape,
                        hipStream_t stream);
 bool gemm_tile_chunkable(int tile_id);
+bool gemm_tile_foldable(int tile_id);
 
 // C = sum over s = 0..splits-1, in that order, of partial[s] (fp32), rounded
 // to the output kind

@@ -82,7 +82,10 @@ def test_tile_table():
     (dict(lda=800), sk.ERR_SHAPE),
     (dict(lda=900), sk.ERR_ALIGNMENT),
     (dict(ldc=100), sk.ERR_SHAPE),
-    (dict(flags=0x20), sk.ERR_UNSUPPORTED),
+    (dict(flags=0x40), sk.ERR_UNSUPPORTED),                           # an unknown flag
+    (dict(flags=sk.GEMM_FOLD_LAUNCH), sk.OK),
+    (dict(flags=sk.GEMM_FOLD_LAUNCH | sk.GEMM_SPLIT_LAUNCH), sk.ERR_INVALID_ARG),  # two shapes forced
+    (dict(flags=sk.GEMM_FOLD_LAUNCH | sk.GEMM_ONE_LAUNCH), sk.ERR_INVALID_ARG),
     (dict(flags=sk.EPILOGUE_SIGMOID, a_dtype=sk.BF16, w_dtype=sk.BF16), sk.OK),  # the gate
     (dict(flags=sk.EPILOGUE_SIGMOID), sk.ERR_UNSUPPORTED),            # f16 weights: no gate
     (dict(flags=sk.EPILOGUE_SIGMOID, a_dtype=sk.BF16, w_dtype=sk.BF16, c_dtype=sk.BF16), sk.ERR_UNSUPPORTED),
@@ -450,3 +453,25 @@ def test_binding_rejects_strided_views_before_any_call():
         sk.moe_combine(y, torch.zeros(2, 4))
     with pytest.raises(ValueError, match="shared must be"):
         sk.moe_combine(y, torch.zeros(2, 3), torch.zeros(2, 8), torch.zeros(2))
+
+
+def test_fold_launch_plan_and_workspace():
+    # the fold launch runs only when asked for; its workspace holds one arrival
+    # counter per tile (before the chunk sums) and TM x TN fp32 per tile and chunk
+    n, k, max_m = 96, 2560, 2048
+    base = plan(n=n, k=k, max_m=max_m)
+    fold = plan(n=n, k=k, max_m=max_m, flags=sk.GEMM_FOLD_LAUNCH)
+    for m in (17, 512, 2048):
+        assert "launch=fold" not in base.info(m)
+        info = fold.info(m)
+        assert "launch=fold" in info, info
+        tile = info.split(" name=")[1].split()[0]
+        tm, tn = (int(x) for x in tile.split("_")[0].split("x"))
+        tiles = -(-m // tm) * -(-n // tn)
+        ws = int(info.split("workspace=")[1].split()[0])
+        # counters for the most tiles any foldable tile has at max_m (32 x 64: 64 x 2)
+        assert ws >= 64 * 2 * 4 + tiles * 10 * tm * tn * 4
+        assert fold.workspace_bytes >= ws
+    # a tile that cannot fold (two accumulator sets do not fit) takes the split launch
+    big = plan(n=n, k=k, max_m=max_m, flags=sk.GEMM_FOLD_LAUNCH, tile_id=0)
+    assert "launch=split" in big.info(512)

@@ -237,8 +237,9 @@ def test_q8_gemm_odd_scale_count_every_tile(M, N, K):
 @pytest.mark.parametrize("w_kind", ["f16", "q8_0"])
 def test_chunked_one_launch_equals_split_launch(w_kind):
     """A plan that cuts k into chunks gives the same bits whether each chunk
-    runs in its own block (partials + ordered reduce) or one block folds the
-    chunk sums in the same order; K = 2600 leaves a short last chunk."""
+    runs in its own block (partials + ordered reduce), one block folds the
+    chunk sums in the same order, or the last block of each tile to finish
+    folds them (one launch); K = 2600 leaves a short last chunk."""
     N, K = 256, 2560 if w_kind == "q8_0" else 2600
     A = WL.gen_matrix((300, K), "f16", ("normal", 1.0), 601)
     if w_kind == "q8_0":
@@ -251,7 +252,7 @@ def test_chunked_one_launch_equals_split_launch(w_kind):
         ref_all = oracle.mm(A, "f16", W, "f16")
     dA = to_dev(A, "f16")
     outs = {}
-    for flag in (sk.GEMM_SPLIT_LAUNCH, sk.GEMM_ONE_LAUNCH):
+    for flag in (sk.GEMM_SPLIT_LAUNCH, sk.GEMM_ONE_LAUNCH, sk.GEMM_FOLD_LAUNCH):
         plan = sk.Plan(N, K, 300, sk.F16, wk, sk.F32, flags=flag)
         ws = plan.workspace(dA.device)
         for M in (17, 64, 300):
@@ -263,5 +264,41 @@ def test_chunked_one_launch_equals_split_launch(w_kind):
     for M in (17, 64, 300):
         a, b = outs[(sk.GEMM_SPLIT_LAUNCH, M)], outs[(sk.GEMM_ONE_LAUNCH, M)]
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), M
+        f = outs[(sk.GEMM_FOLD_LAUNCH, M)]
+        assert np.array_equal(a.view(np.uint32), f.view(np.uint32)), ("fold", M)
         assert np.array_equal(a.view(np.uint32), outs[(sk.GEMM_SPLIT_LAUNCH, 300)][:M].view(np.uint32)), M
         assert rel_err(a, ref_all[:M]) <= REL_TOL
+
+
+@pytest.mark.parametrize("w_kind", ["f16", "q8_0"])
+def test_fold_launch_every_tile_and_repeated_calls(w_kind):
+    """The fold launch on every tile that runs it (ragged row and column
+    tiles, the workload's own k chunks) gives the split launch's bits, call
+    after call on one workspace (its arrival counters are back at zero after
+    each call: the next call's last block would be wrong otherwise)."""
+    N, K, M = (96, 2560, 150) if w_kind == "f16" else (512, 2560, 306)
+    A = WL.gen_matrix((M, K), "f16", ("normal", 1.0), 631)
+    if w_kind == "q8_0":
+        qs, d = WL.gen_q8_0(N, K, 632, 633)
+        dW, scales, wk = to_dev(qs, "i8"), to_dev(d, "f16"), sk.Q8_0
+    else:
+        dW, scales, wk = to_dev(WL.gen_matrix((N, K), "f16", ("normal", 0.02), 632), "f16"), None, sk.F16
+    dA = to_dev(A, "f16")
+    ref = sk.Plan(N, K, M, sk.F16, wk, sk.F16, flags=sk.GEMM_SPLIT_LAUNCH)
+    C0 = torch.empty((M, N), dtype=torch.float16, device="cuda")
+    ref.run(M, dA, dW, C0, scales=scales)
+    torch.cuda.synchronize()
+    want = bits_of(C0)
+    for tid, name in enumerate(sk.gemm_tiles()):
+        plan = sk.Plan(N, K, M, sk.F16, wk, sk.F16, flags=sk.GEMM_FOLD_LAUNCH, tile_id=tid)
+        if "launch=fold" not in plan.info(M):
+            continue
+        print(f"fold {w_kind} tile {name}: {plan.info(M)}", flush=True)
+        ws = sk.new_workspace(plan, dA.device)
+        for rep in range(3):
+            for m in (M, 17):
+                C = torch.empty((m, N), dtype=torch.float16, device="cuda")
+                plan.run(m, dA[:m], dW, C, scales=scales, workspace=ws)
+                torch.cuda.synchronize()
+                if m == M:
+                    assert np.array_equal(bits_of(C), want), (name, rep)

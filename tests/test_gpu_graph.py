@@ -92,13 +92,13 @@ def test_router_topk_graph_replays():
     _replay_matches_eager(fn, outs, calls=len(ms))
 
 
-@pytest.mark.parametrize("flag", ["split", "one"])
+@pytest.mark.parametrize("flag", ["split", "one", "fold"])
 def test_gemm_chunked_graph_replays(flag):
     # narrow N: k cut into chunks, as partials + reduce launch or one launch
     N, K = 96, 2560
     W = to_dev(WL.gen_matrix((N, K), "f16", ("normal", 0.02), 711), "f16")
     A = to_dev(WL.gen_matrix((600, K), "f16", ("normal", 1.0), 712), "f16")
-    flags = sk.GEMM_SPLIT_LAUNCH if flag == "split" else sk.GEMM_ONE_LAUNCH
+    flags = {"split": sk.GEMM_SPLIT_LAUNCH, "one": sk.GEMM_ONE_LAUNCH, "fold": sk.GEMM_FOLD_LAUNCH}[flag]
     plan = sk.Plan(N, K, 600, sk.F16, sk.F16, sk.F16, flags=flags)
     ws = plan.workspace(A.device)
     ms = (17, 300, 600)

@@ -5,7 +5,8 @@ On the GPU (through the C ABI): on two calls in a row, the second with a
 smaller input, it gives skinny_mm_run's bits on every kind of run that needs
 scratch -- a GEMV whose k splits are summed across workgroups (arrival
 counters + partial sums), a GEMM whose k chunks run as separate blocks
-(partial sums + the ordered reduce), fp32 rows cast before the GEMV (cast
+(partial sums + the ordered reduce, or chunk sums folded by the last block
+of each tile, with arrival counters), fp32 rows cast before the GEMV (cast
 rows) -- and on a run that needs none; the results also meet the oracle's
 bar.  The second GEMV call is right only if the first left its arrival
 counters at zero.  On the host: sizes beyond the array are rejected before
@@ -56,6 +57,8 @@ def _cases():
                                    flags=sk.GEMM_SPLIT_LAUNCH), "f16", (700, 130)),
         ("gemm_split_q8", dict(n=512, k=2560, a=sk.F16, w=sk.Q8_0, c=sk.F16,
                                flags=sk.GEMM_SPLIT_LAUNCH), "f16", (306, 40)),
+        ("gemm_fold_launch", dict(n=96, k=2560, a=sk.F16, w=sk.F16, c=sk.F16,
+                                  flags=sk.GEMM_FOLD_LAUNCH), "f16", (700, 130)),
         ("fp32_rows_cast_first", dict(n=256, k=5120, a=sk.F32, w=sk.BF16, c=sk.F32), "f32", (16, 11)),
         ("no_scratch_gemm", dict(n=384, k=512, a=sk.F16, w=sk.F16, c=sk.F32), "f16", (150, 33)),
     ]
