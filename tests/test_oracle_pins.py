@@ -426,3 +426,85 @@ def test_moe_combine_linear_in_weights_and_bf16_rows():
     assert np.array_equal(oracle.moe_combine(y, w1 + w2), oracle.moe_combine(y, w1) + oracle.moe_combine(y, w2))
     yb = WL.to_bits(y.astype(np.float64), "bf16")  # these values are exact in bf16
     assert np.array_equal(oracle.moe_combine(yb, w1, kind="bf16"), oracle.moe_combine(y, w1))
+
+
+# ---------------------------------------------------------------------------
+# Q4_0-style dequant (4-bit codes, two per byte)
+# ---------------------------------------------------------------------------
+
+def _q4_block(element, q, rows=1):
+    """One 32-weight block whose codes are all 8 (weight 0) but `element`'s."""
+    codes = np.full((rows, 32), 8, np.uint8)
+    codes[:, element] = q
+    return (codes[:, 0::2] | (codes[:, 1::2] << 4)).astype(np.uint8)
+
+
+def test_dequant_q4_0_golden_values():
+    rows = [line.split() for line in golden_lines("dequant_q4_0_rne.txt")]
+    for d_hex, q, element, exp_hex in rows:
+        e = int(element)
+        out = oracle.dequant_q4_0(_q4_block(e, int(q)), np.array([[int(d_hex, 16)]], np.uint16))
+        assert out[0, e] == int(exp_hex, 16), (d_hex, q, e, hex(out[0, e]), exp_hex)
+        # every other element holds code 8: a zero weight with d's sign
+        others = np.delete(out[0], e)
+        assert np.all(others == (0x8000 if int(d_hex, 16) & 0x8000 else 0)), (d_hex, q, e)
+
+
+def test_dequant_q4_0_nibble_order():
+    # element 2i in the low nibble of byte i, element 2i + 1 in the high nibble
+    codes = np.arange(32, dtype=np.uint8) % 16          # element kk has code kk % 16
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)[None, :]
+    assert packed[0, 0] == 0x10 and packed[0, 1] == 0x32   # elements 0,1 and 2,3
+    out = np_f16(oracle.dequant_q4_0(packed, WL.to_f16_bits(np.array([[1.0]]))))
+    assert np.array_equal(out[0], (codes.astype(np.float64) - 8.0))
+
+
+def test_dequant_q4_0_exhaustive_every_finite_scale_every_code():
+    """All 63488 finite f16 scales x all 16 codes (in both nibble positions)
+    against numpy's correctly rounded float64 -> float16 cast of the exact
+    product d * (q - 8)."""
+    d_all = F16_ALL[((F16_ALL >> 10) & 0x1F) != 0x1F]
+    codes = np.concatenate([np.arange(16), np.arange(16)[::-1]]).astype(np.uint8)  # 32 = one block
+    n = d_all.size
+    packed = np.broadcast_to((codes[0::2] | (codes[1::2] << 4)).astype(np.uint8), (n, 16)).copy()
+    d = d_all[:, None].copy()
+    got = oracle.dequant_q4_0(packed, d)
+    exact = np_f16(d_all)[:, None] * (codes.astype(np.float64) - 8.0)[None, :]
+    with np.errstate(over="ignore"):
+        ref = exact.astype(np.float16).view(np.uint16)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, bad[:5]
+
+
+def test_dequant_q4_0_uses_the_scale_of_each_32_block():
+    k = 128
+    packed = np.full((2, k // 2), 0x99, np.uint8)         # every code 9: weight = d
+    d = WL.to_f16_bits(np.array([[1.0, 2.0, 4.0, 8.0], [0.5, 0.25, 0.125, 16.0]]))
+    out = np_f16(oracle.dequant_q4_0(packed, d))
+    assert np.array_equal(out, np.repeat(np_f16(d), 32, axis=1))
+
+
+def test_brute_force_exact_rationals_q4_0():
+    m, n, k = 3, 5, 64
+    A = WL.gen_matrix((m, k), "f16", ("normal", 1.0), 31)
+    qs, d = WL.gen_q4_0(n, k, 32, 33)
+    got = oracle.mm(A, "f16", qs, "q4_0", w_scales=d)
+    a = np_f16(A)
+    # unpack the nibbles and dequant by numpy's correctly rounded cast
+    q = np.empty((n, k), np.float64)
+    q[:, 0::2] = qs & 0x0F
+    q[:, 1::2] = qs >> 4
+    w = (np.repeat(np_f16(d), 32, axis=1) * (q - 8.0)).astype(np.float16).astype(np.float64)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(Fraction(a[i, t]) * Fraction(w[j, t]) for t in range(k))
+            abs_sum = float(sum(abs(Fraction(a[i, t]) * Fraction(w[j, t])) for t in range(k)))
+            assert float(abs(Fraction(got[i, j]) - exact)) <= rounding_bound(k, abs_sum)
+
+
+def test_q4_0_generator_codes_and_scales():
+    qs, d = WL.gen_q4_0(8, 64, 41, 42)
+    assert qs.shape == (8, 32) and qs.dtype == np.uint8 and d.shape == (8, 2)
+    q = np.concatenate([qs & 0x0F, qs >> 4])
+    assert q.min() == 0 and q.max() == 15
+    assert np.all((np_f16(d) >= 1e-3 - 1e-6) & (np_f16(d) <= 2e-3 + 1e-6))

@@ -22,6 +22,10 @@ The five workloads stand in for the pages' measurements:
   scalar_gate   -- Strata PR #109 ("What"): the shared expert's scalar gate over
                    the window's fp32 rows (n = 1, the router's k = 5120); the
                    rows are kept in fp32 (A ~N(0,1) stored as float32).
+  q4_0_n512     -- the q8_0_n512 shape with a 4-bit Q4_0-style weight (the
+                   4-bit block formats the Strata PR #109 page names, "Measured",
+                   without a definition; the format is fixed by the oracle);
+                   seed base 7.
   moe_combine   -- Strata PR #109 ("What"): the MoE combine over the window's
                    tokens, each with the router's top-10 experts' output rows
                    (d = 5120, the router's k), routing weights, the shared
@@ -41,16 +45,18 @@ class Workload:
     n: int              # output columns (rows of the stored [n][k] weight)
     k: int              # reduction length
     a_kind: str         # "f16" | "bf16" | "f32"
-    w_kind: str         # "f16" | "bf16" | "q8_0"
+    w_kind: str         # "f16" | "bf16" | "q8_0" | "q4_0"
     c_kind: str         # "f32" | "f16"
     ms: Tuple[int, ...]  # row counts swept
-    w_dist: Tuple       # ("uniform", lo, hi) | ("normal", sd) | ("q8_0", dlo, dhi)
+    w_dist: Tuple       # ("uniform", lo, hi) | ("normal", sd) | ("q8_0" or "q4_0", dlo, dhi)
     topk: Optional[int] = None
 
     @property
     def w_bytes(self) -> int:
         if self.w_kind == "q8_0":
             return self.n * self.k + self.n * (self.k // 32) * 2
+        if self.w_kind == "q4_0":
+            return self.n * self.k // 2 + self.n * (self.k // 32) * 2
         return self.n * self.k * 2
 
 
@@ -110,12 +116,25 @@ def gen_q8_0(n: int, k: int, seed_q: int, seed_d: int, dlo=1e-3, dhi=2e-3):
     return qs, d
 
 
+def gen_q4_0(n: int, k: int, seed_q: int, seed_d: int, dlo=1e-3, dhi=2e-3):
+    """Q4_0-style weight: 4-bit codes ~U{0..15} packed two per byte (element kk
+    of a row in byte kk // 2, the low nibble for even kk) [n][k/2] uint8, and
+    f16 scales ~U(dlo, dhi) [n][k/32]."""
+    assert k % 32 == 0
+    q = np.random.default_rng(seed_q).integers(0, 16, size=(n, k), dtype=np.uint8)
+    qs = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    d = to_f16_bits(np.random.default_rng(seed_d).uniform(dlo, dhi, size=(n, k // 32)))
+    return qs, d
+
+
 def gen_w(wl: Workload, n: Optional[int] = None):
-    """The workload's stored weight [n][k]: uint16 bits, or (qs, d) for q8_0."""
+    """The workload's stored weight [n][k]: uint16 bits, or (qs, d) for q8_0 and q4_0."""
     n = wl.n if n is None else n
     c = wl.index
     if wl.w_kind == "q8_0":
         return gen_q8_0(n, wl.k, 1000 * c + 0, 1000 * c + 2, wl.w_dist[1], wl.w_dist[2])
+    if wl.w_kind == "q4_0":
+        return gen_q4_0(n, wl.k, 1000 * c + 0, 1000 * c + 2, wl.w_dist[1], wl.w_dist[2])
     return to_bits(draw((n, wl.k), wl.w_dist, 1000 * c + 0), wl.w_kind)
 
 
