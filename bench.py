@@ -95,7 +95,7 @@ def run_tiles(name):
 
             def fn(i, plan=plan):
                 W = inp.W[i % len(inp.W)]
-                if wl.w_kind == "q8_0":
+                if wl.w_kind in ("q8_0", "q4_0"):
                     plan.run(m, inp.A[:m], W[0], C, scales=W[1])
                 else:
                     plan.run(m, inp.A[:m], W, C)
@@ -173,7 +173,7 @@ def run_only(spec, steps, warmup):
         m = ms[i % len(ms)]
         C, idx, val = outs[m]
         W = inp.W[i % len(inp.W)]
-        if wl.w_kind == "q8_0":
+        if wl.w_kind in ("q8_0", "q4_0"):
             plan.run(m, inp.A[:m], W[0], C, scales=W[1], workspace=ws)
         elif wl.topk:
             plan.run_topk(m, inp.A[:m], W, C, idx, val, TOPK, workspace=ws)
@@ -230,7 +230,7 @@ class Inputs:
         a_bytes = self.A.numel() * self.A.element_size()
         copies = max(2, int(pool_bytes // max(1, wl.w_bytes + a_bytes)))
         self.As = [self.A] + [self.A.clone() for _ in range(copies - 1)]
-        if wl.w_kind == "q8_0":
+        if wl.w_kind in ("q8_0", "q4_0"):
             qs, d = W
             q0 = torch.from_numpy(qs).cuda()
             d0 = dev16(d, "f16")
@@ -244,7 +244,7 @@ class Inputs:
 def dtype_codes(sk, wl):
     # fp32 rows (the gate) are rounded to bf16 by the GEMV as it loads them
     a = {"bf16": sk.BF16, "f32": sk.F32}.get(wl.a_kind, sk.F16)
-    w = {"f16": sk.F16, "bf16": sk.BF16, "q8_0": sk.Q8_0}[wl.w_kind]
+    w = {"f16": sk.F16, "bf16": sk.BF16, "q8_0": sk.Q8_0, "q4_0": sk.Q4_0}[wl.w_kind]
     c = sk.F32 if wl.c_kind == "f32" else sk.F16
     return a, w, c
 
@@ -360,9 +360,9 @@ def oracle_call_time(wl, m, inp, budget_s):
     t0 = time.perf_counter()
     if wl.a_kind == "f32":
         oracle.gate(A, inp.W_bits, threads=threads)
-    elif wl.w_kind == "q8_0":
+    elif wl.w_kind in ("q8_0", "q4_0"):
         qs, d = inp.W_bits
-        oracle.mm(A, "f16", qs, "q8_0", w_scales=d, threads=threads)
+        oracle.mm(A, "f16", qs, wl.w_kind, w_scales=d, threads=threads)
     else:
         ref = oracle.mm(A, wl.a_kind, inp.W_bits, wl.w_kind, threads=threads)
         if wl.topk:
@@ -391,7 +391,7 @@ def sweep(sk, torch, rounds, oracle_s=0.0):
             L = min(len(inp.W), 256)
             nA = len(inp.As)
 
-            if wl.w_kind == "q8_0":
+            if wl.w_kind in ("q8_0", "q4_0"):
                 def fn(i, m=m, C=C):
                     qs, d = inp.W[i % len(inp.W)]
                     plan.run(m, inp.As[i % nA][:m], qs, C, scales=d, workspace=ws)

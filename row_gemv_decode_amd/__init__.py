@@ -34,7 +34,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 # --- C ABI mirror -----------------------------------------------------------
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_SHAPE, ERR_HIP, ERR_WORKSPACE, ERR_SCRATCH = range(8)
-F16, BF16, F32, Q8_0 = 1, 2, 3, 4
+F16, BF16, F32, Q8_0, Q4_0 = 1, 2, 3, 4, 5
 FORCE_GEMV, FORCE_GEMM, GEMM_SPLIT_LAUNCH, GEMM_ONE_LAUNCH = 0x1, 0x2, 0x4, 0x8
 EPILOGUE_SIGMOID = 0x10
 GEMM_FOLD_LAUNCH = 0x20
@@ -43,7 +43,8 @@ TOPK_MAX = 32
 
 EXPORTS = (
     "skinny_mm_plan", "skinny_mm_plan_destroy", "skinny_mm_workspace_size", "skinny_mm_run",
-    "gemv_topk_run", "skinny_dequant_q8_0_run", "skinny_mm_plan_info", "skinny_gemm_tile_count",
+    "gemv_topk_run", "skinny_dequant_q8_0_run", "skinny_dequant_q4_0_run", "skinny_mm_plan_info",
+    "skinny_gemm_tile_count",
     "skinny_gemm_tile_name", "skinny_status_string", "skinny_abi_version", "skinny_cast_f32_bf16_run",
     "skinny_moe_combine_run", "skinny_mm_run_static",
 )
@@ -83,6 +84,8 @@ _lib.gemv_topk_run.argtypes = [_vp, _i64, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _v
 _lib.gemv_topk_run.restype = ctypes.c_int
 _lib.skinny_dequant_q8_0_run.argtypes = [_i64, _i64, _vp, _vp, _vp, _vp]
 _lib.skinny_dequant_q8_0_run.restype = ctypes.c_int
+_lib.skinny_dequant_q4_0_run.argtypes = [_i64, _i64, _vp, _vp, _vp, _vp]
+_lib.skinny_dequant_q4_0_run.restype = ctypes.c_int
 _lib.skinny_cast_f32_bf16_run.argtypes = [_i64, _vp, _vp, _vp]
 _lib.skinny_cast_f32_bf16_run.restype = ctypes.c_int
 _lib.skinny_moe_combine_run.argtypes = [_i64, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp]
@@ -263,10 +266,11 @@ def _weight_kind(W):
     torch = _torch()
     if isinstance(W, tuple):
         qs, d = W
-        if qs.dtype != torch.int8 or d.dtype != torch.float16:
-            raise TypeError("Q8_0 weight is (int8 codes [n][k], float16 scales [n][k/32])")
-        _dense("Q8_0 weight", codes=qs, scales=d)
-        return Q8_0, qs, d
+        if qs.dtype not in (torch.int8, torch.uint8) or d.dtype != torch.float16:
+            raise TypeError("a block-quantised weight is (int8 codes [n][k] (Q8_0) or uint8 packed "
+                            "4-bit codes [n][k/2] (Q4_0), float16 scales [n][k/32])")
+        _dense("block-quantised weight", codes=qs, scales=d)
+        return (Q8_0 if qs.dtype == torch.int8 else Q4_0), qs, d
     _dense("weight", W=W)
     return _dtype_code(W.dtype, "W"), W, None
 
@@ -282,7 +286,8 @@ def get_plan(n, k, max_m, a_dtype, w_dtype, c_dtype, flags=0, tile_id=-1) -> Pla
 
 def mm(A, W, out=None, out_dtype=None, flags=0, tile_id=-1, max_m=None, stream=None):
     """C = A . W^T_storage for A [m][k] (f16/bf16, contiguous rows) and W [n][k]
-    (same dtype), or W = (qs int8 [n][k], d f16 [n][k/32]) for Q8_0."""
+    (same dtype), or W = (qs int8 [n][k], d f16 [n][k/32]) for Q8_0, or
+    W = (qs uint8 [n][k/2] packed 4-bit codes, d f16 [n][k/32]) for Q4_0."""
     torch = _torch()
     wk, Wt, scales = _weight_kind(W)
     m, k = A.shape
@@ -309,6 +314,18 @@ def gemv_topk(A, W, topk=10, flags=0, max_m=None, stream=None):
     plan = get_plan(n, k, max_m or m, _dtype_code(A.dtype, "A"), wk, F32, flags)
     plan.run_topk(m, A, Wt, logits, idx, val, topk, scales=scales, stream=stream)
     return logits, idx, val
+
+
+def dequant_q4_0(qs, d, out=None, stream=None):
+    """f16 [n][k] weight of a Q4_0-style (packed codes uint8 [n][k/2], scales) pair."""
+    torch = _torch()
+    n, kh = qs.shape
+    if out is None:
+        out = torch.empty((n, 2 * kh), dtype=torch.float16, device=qs.device)
+    _dense("dequant_q4_0", qs=qs, d=d, out=out)
+    _check(_lib.skinny_dequant_q4_0_run(n, 2 * kh, _ptr(qs), _ptr(d), _ptr(out), _stream(stream)),
+           "skinny_dequant_q4_0_run")
+    return out
 
 
 def dequant_q8_0(qs, d, out=None, stream=None):

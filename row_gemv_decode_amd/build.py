@@ -16,13 +16,24 @@ OUT_DIR = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libskinny.so")
 ARCH = "gfx950"
 SOURCES = ["abi.cpp", "gemv.hip", "gemm.hip", "combine.hip", "static_scratch.hip"]
-# gemv_inst.hip once per (weight kind, A kind, chunk slots T): object name -> defines
-GEMV_INSTANCES = {
-    f"gemv_{w}{'_a32' if a == 'kAF32' else ''}_t{t}": (wk, a, t)
+# sources compiled once per kernel family member: (source, object name, defines)
+INSTANCES = [
+    ("gemv_inst.hip", f"gemv_{w}{'_a32' if a == 'kAF32' else ''}_t{t}",
+     [f"-DGEMV_WK={wk}", f"-DGEMV_AK={a}", f"-DGEMV_T={t}",
+      f"-DGEMV_LAUNCHER=launch_gemv_{w}{'_a32' if a == 'kAF32' else ''}_t{t}"])
     for w, wk, a in (("f16", "WK_F16", "kA16"), ("bf16", "WK_BF16", "kA16"), ("q8", "WK_Q8", "kA16"),
-                     ("bf16", "WK_BF16", "kAF32"))
+                     ("q4", "WK_Q4", "kA16"), ("bf16", "WK_BF16", "kAF32"))
     for t in (1, 2)
-}
+] + [
+    ("gemm_inst.hip", f"gemm_{w}", [f"-DGEMM_WK={wk}", f"-DGEMM_LAUNCHER=launch_gemm_{w}"])
+    for w, wk in (("f16", "WK_F16"), ("bf16", "WK_BF16"), ("q8", "WK_Q8"), ("q4", "WK_Q4"))
+]
+
+
+def jobs():
+    """Every object of the library: (source, object name, extra defines)."""
+    return list(INSTANCES) + [(src, os.path.splitext(src)[0], []) for src in SOURCES]
+
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 COMMON = [
@@ -52,12 +63,9 @@ def _compile(job, verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(OUT_DIR, exist_ok=True)
-    jobs = [("gemv_inst.hip", name, [f"-DGEMV_WK={wk}", f"-DGEMV_AK={a}", f"-DGEMV_T={t}",
-                                     f"-DGEMV_LAUNCHER=launch_{name}"])
-            for name, (wk, a, t) in GEMV_INSTANCES.items()]
-    jobs += [(src, os.path.splitext(src)[0], []) for src in SOURCES]
-    with cf.ThreadPoolExecutor(max_workers=len(jobs)) as ex:
-        objs = list(ex.map(lambda j: _compile(j, verbose), jobs))
+    todo = jobs()
+    with cf.ThreadPoolExecutor(max_workers=len(todo)) as ex:
+        objs = list(ex.map(lambda j: _compile(j, verbose), todo))
     tmp = LIB + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     if verbose:

@@ -91,6 +91,35 @@ __device__ __forceinline__ u32x4 q8_dequant8(u32x2 codes, _Float16 d) {
   return out;
 }
 
+// ---------------------------------------------------------------------------
+// Q4_0-style dequant of eight consecutive 4-bit codes of one 32-block.  The
+// pages name 4-bit block formats (the Strata PR #109 page, "Measured")
+// without defining one; the format here: unsigned codes q in 0..15, two per
+// byte (element 2i in the low nibble of byte i, 2i + 1 in the high nibble),
+// one f16 scale d per 32-block, weight RNE_f16(d * (q - 8)).  As for Q8_0,
+// the code reaches f16 exactly (bits 0x6400 | q are 1024 + q; subtracting
+// 1032 leaves q - 8 exactly) and one IEEE f16 multiply rounds the exact
+// product once.  Every path (standalone, fused GEMV, fused GEMM) calls this.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 q4_dequant8(uint32_t codes, _Float16 d) {
+  const uint32_t lo = codes & 0x0F0F0F0Fu;         // elements 0, 2, 4, 6 (one per byte)
+  const uint32_t hi = (codes >> 4) & 0x0F0F0F0Fu;  // elements 1, 3, 5, 7
+  const h2_t d2 = {d, d};
+  const h2_t bias = {(_Float16)1032.0f, (_Float16)1032.0f};
+  // pair i = (element 2i, element 2i + 1): byte i of lo in the low half, byte
+  // i of hi in the high half (selector 0x0c gives a zero byte)
+  const uint32_t p0 = __builtin_amdgcn_perm(hi, lo, 0x0C040C00u) | 0x64006400u;
+  const uint32_t p1 = __builtin_amdgcn_perm(hi, lo, 0x0C050C01u) | 0x64006400u;
+  const uint32_t p2 = __builtin_amdgcn_perm(hi, lo, 0x0C060C02u) | 0x64006400u;
+  const uint32_t p3 = __builtin_amdgcn_perm(hi, lo, 0x0C070C03u) | 0x64006400u;
+  u32x4 out;
+  out[0] = h2_bits(d2 * (as_h2(p0) - bias));
+  out[1] = h2_bits(d2 * (as_h2(p1) - bias));
+  out[2] = h2_bits(d2 * (as_h2(p2) - bias));
+  out[3] = h2_bits(d2 * (as_h2(p3) - bias));
+  return out;
+}
+
 // Device-coherent accesses for data handed from one workgroup to another in
 // the same launch.  Relaxed agent-scope atomic stores/loads compile to plain
 // global stores/loads with the sc1 (device scope) bit: they are coherent

@@ -174,8 +174,8 @@ __device__ __forceinline__ float dot8(const u32x4& a, const u32x4& w, float acc)
   return acc;
 }
 
-// Raw weight registers of one (column, chunk): 16 bytes of f16/bf16, or 8
-// bytes of codes plus the block's scale for Q8_0.
+// Raw weight registers of one (column, chunk): 16 bytes of f16/bf16, or the
+// codes (8 bytes for Q8_0, 4 for Q4_0) plus the block's scale.
 template <int WK>
 struct WChunk {
   u32x4 v;
@@ -185,12 +185,21 @@ struct WChunk<WK_Q8> {
   u32x2 codes;
   uint16_t scale;
 };
+template <>
+struct WChunk<WK_Q4> {
+  uint32_t codes;  // eight 4-bit codes
+  uint16_t scale;
+};
 
 template <int WK>
 __device__ __forceinline__ void load_w(WChunk<WK>& dst, const GemvArgs& g, int64_t j, int chunk) {
   if constexpr (WK == WK_Q8) {
     const int8_t* wq = (const int8_t*)g.W;
     dst.codes = *(const u32x2*)(wq + j * g.k + (int64_t)chunk * 8);
+    dst.scale = g.scales[j * (g.k >> 5) + (chunk >> 2)];
+  } else if constexpr (WK == WK_Q4) {
+    const uint8_t* wq = (const uint8_t*)g.W;
+    dst.codes = *(const uint32_t*)(wq + j * (g.k >> 1) + (int64_t)chunk * 4);
     dst.scale = g.scales[j * (g.k >> 5) + (chunk >> 2)];
   } else {
     const uint16_t* w16 = (const uint16_t*)g.W;
@@ -203,6 +212,9 @@ __device__ __forceinline__ void zero_w(WChunk<WK>& dst) {
   if constexpr (WK == WK_Q8) {
     dst.codes = u32x2{0u, 0u};
     dst.scale = 0;
+  } else if constexpr (WK == WK_Q4) {
+    dst.codes = 0u;
+    dst.scale = 0;
   } else {
     dst.v = u32x4{0u, 0u, 0u, 0u};
   }
@@ -212,6 +224,8 @@ template <int WK>
 __device__ __forceinline__ u32x4 w_as_halves(const WChunk<WK>& w) {
   if constexpr (WK == WK_Q8) {
     return q8_dequant8(w.codes, half_from_bits(w.scale));
+  } else if constexpr (WK == WK_Q4) {
+    return q4_dequant8(w.codes, half_from_bits(w.scale));
   } else {
     return w.v;
   }

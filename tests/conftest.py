@@ -33,12 +33,15 @@ def gpu_available():
 
 
 def to_dev(bits, kind):
-    """numpy f16/bf16 bit patterns (uint16) or int8 codes -> a device tensor."""
+    """numpy f16/bf16 bit patterns (uint16), int8 codes ("i8") or packed 4-bit
+    codes ("u8") -> a device tensor."""
     import numpy as np
     import torch
 
     if kind == "i8":
         return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.int8)).cuda()
+    if kind == "u8":
+        return torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint8)).cuda()
     t = torch.from_numpy(np.ascontiguousarray(bits, dtype=np.uint16).view(np.int16))
     return t.view(torch.bfloat16 if kind == "bf16" else torch.float16).cuda()
 

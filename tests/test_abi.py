@@ -42,7 +42,7 @@ def plan_status(**fields):
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 14, names
+    assert len(names) == 15, names
     assert set(names) == set(sk.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -415,13 +415,32 @@ def test_moe_combine_validation():
 
 
 @fake_pointers
-def test_dequant_validation():
-    f = L.skinny_dequant_q8_0_run
+@pytest.mark.parametrize("f", [L.skinny_dequant_q8_0_run, L.skinny_dequant_q4_0_run])
+def test_dequant_validation(f):
     assert f(0, 64, P16, P16b, P16c, None) == sk.ERR_INVALID_ARG
     assert f(4, 16, P16, P16b, P16c, None) == sk.ERR_INVALID_ARG
     assert f(4, 80, P16, P16b, P16c, None) == sk.ERR_SHAPE
     assert f(4, 64, None, P16b, P16c, None) == sk.ERR_INVALID_ARG
     assert f(4, 64, ODD, P16b, P16c, None) == sk.ERR_ALIGNMENT
+
+
+@pytest.mark.parametrize("fields,status", [
+    (dict(w_dtype=sk.Q4_0, n=512, k=2560, c_dtype=sk.F16), sk.OK),
+    (dict(w_dtype=sk.Q4_0, k=2568), sk.ERR_SHAPE),                     # k % 32 != 0
+    (dict(w_dtype=sk.Q4_0, a_dtype=sk.BF16), sk.ERR_UNSUPPORTED),      # f16 rows only
+    (dict(w_dtype=sk.Q4_0, k=32, max_m=17), sk.ERR_SHAPE),             # the GEMM needs k >= 64
+    (dict(w_dtype=sk.Q4_0, k=32, max_m=16), sk.OK),                    # the GEMV does not
+    (dict(w_dtype=6), sk.ERR_UNSUPPORTED),
+])
+def test_q4_0_plan_validation(fields, status):
+    assert plan_status(**fields) == status
+
+
+@fake_pointers
+def test_q4_0_run_needs_scales():
+    q = plan(n=512, k=2560, w=sk.Q4_0, c=sk.F16)
+    assert run(q, 1) == sk.ERR_INVALID_ARG                 # Q4_0 needs scales
+    assert run(q, 1, S=ODD) == sk.ERR_ALIGNMENT
 
 
 def test_plan_info_validation():

@@ -42,11 +42,13 @@ def test_call_bytes_count_each_operand_once():
     assert bench.call_bytes(gate, 2) == 5120 * 2 + 2 * 5120 * 4 + 2 * 4
     q8 = WL.WORKLOADS["q8_0_n512"]  # one code byte per weight + one f16 scale per 32
     assert bench.call_bytes(q8, 4) == 512 * 2560 + 512 * 80 * 2 + 4 * 2560 * 2 + 4 * 512 * 2
+    q4 = WL.WORKLOADS["q4_0_n512"]  # half a code byte per weight + one f16 scale per 32
+    assert bench.call_bytes(q4, 4) == 512 * 2560 // 2 + 512 * 80 * 2 + 4 * 2560 * 2 + 4 * 512 * 2
 
 
 def test_dtype_codes_follow_the_workload_kinds():
     class Codes:
-        F16, BF16, F32, Q8_0 = "f16", "bf16", "f32", "q8_0"
+        F16, BF16, F32, Q8_0, Q4_0 = "f16", "bf16", "f32", "q8_0", "q4_0"
     for wl in WL.WORKLOADS.values():
         a, w, c = bench.dtype_codes(Codes, wl)
         assert (a, w, c) == (wl.a_kind, wl.w_kind, wl.c_kind), wl.name

@@ -32,17 +32,20 @@ CASES = [
     (191, 96, 3000, "f16", "f32"), (255, 300, 512, "bf16", "f16"), (257, 2050, 520, "f16", "f32"),
     (300, 7680, 200, "f16", "f16"), (33, 512, 2560, "q8_0", "f16"), (200, 96, 1024, "q8_0", "f32"),
     (130, 2000, 544, "q8_0", "bf16"),
+    (4, 8, 32, "q4_0", "f16"), (6, 100, 1056, "q4_0", "f32"), (16, 513, 2080, "q4_0", "f16"),
+    (1, 2, 9216, "q4_0", "f32"), (33, 512, 2560, "q4_0", "f16"), (200, 96, 1024, "q4_0", "f32"),
+    (130, 2000, 544, "q4_0", "bf16"), (257, 70, 96, "q4_0", "f16"),
 ]
 
 
 def _case(m, n, k, wk, ck, seed):
     a_kind = "bf16" if wk == "bf16" else "f16"
     A = WL.gen_matrix((m, k), a_kind, ("normal", 1.0), seed)
-    if wk == "q8_0":
-        qs, d = WL.gen_q8_0(n, k, seed + 1, seed + 2)
-        dW = (to_dev(qs, "i8"), to_dev(d, "f16"))
-        ref = oracle.mm(A, "f16", qs, "q8_0", w_scales=d)
-        absum = oracle.mm(A, "f16", qs, "q8_0", w_scales=d, absolute=True)
+    if wk in ("q8_0", "q4_0"):
+        qs, d = (WL.gen_q8_0 if wk == "q8_0" else WL.gen_q4_0)(n, k, seed + 1, seed + 2)
+        dW = (to_dev(qs, "i8" if wk == "q8_0" else "u8"), to_dev(d, "f16"))
+        ref = oracle.mm(A, "f16", qs, wk, w_scales=d)
+        absum = oracle.mm(A, "f16", qs, wk, w_scales=d, absolute=True)
     else:
         W = WL.gen_matrix((n, k), wk, ("normal", 0.05), seed + 1)
         dW = to_dev(W, wk)
@@ -56,7 +59,7 @@ def _case(m, n, k, wk, ck, seed):
 @pytest.mark.parametrize("m,n,k,wk,ck", CASES)
 def test_shape_parity(m, n, k, wk, ck):
     plan = sk.get_plan(n, k, m, sk.BF16 if wk == "bf16" else sk.F16,
-                       {"f16": sk.F16, "bf16": sk.BF16, "q8_0": sk.Q8_0}[wk], {"f32": sk.F32, "f16": sk.F16,
+                       {"f16": sk.F16, "bf16": sk.BF16, "q8_0": sk.Q8_0, "q4_0": sk.Q4_0}[wk], {"f32": sk.F32, "f16": sk.F16,
                                                                               "bf16": sk.BF16}[ck])
     print(f"m={m} n={n} k={k} {wk}->{ck}: {plan.info(m)}", flush=True)
     got, ref, absum = _case(m, n, k, wk, ck, 1000 + 7 * m + n)

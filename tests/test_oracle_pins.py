@@ -192,6 +192,7 @@ def _exact_int64(a_f64, w_f64):
     ("narrow_n96", 64, None),
     ("wide_n7680", 6, None),
     ("q8_0_n512", 16, None),
+    ("q4_0_n512", 16, None),
 ])
 def test_exact_int64_at_workload_shapes(name, rows, cols):
     wl = WL.WORKLOADS[name]
@@ -201,6 +202,12 @@ def test_exact_int64_at_workload_shapes(name, rows, cols):
         qs, d = W
         got = oracle.mm(A, "f16", qs, "q8_0", w_scales=d)
         w = (np.repeat(np_f16(d), 32, axis=1) * qs.astype(np.float64)).astype(np.float16).astype(np.float64)
+    elif wl.w_kind == "q4_0":
+        qs, d = W
+        got = oracle.mm(A, "f16", qs, "q4_0", w_scales=d)
+        q = np.empty((wl.n, wl.k), np.float64)
+        q[:, 0::2], q[:, 1::2] = qs & 0x0F, qs >> 4
+        w = (np.repeat(np_f16(d), 32, axis=1) * (q - 8.0)).astype(np.float16).astype(np.float64)
     else:
         got = oracle.mm(A, wl.a_kind, W, wl.w_kind)
         w = np_f16(W)

@@ -75,6 +75,8 @@ WORKLOADS = {
                  ("q8_0", 1e-3, 2e-3)),
         Workload("scalar_gate", 5, 1, 5120, "f32", "bf16", "f32", (1, 2, 4, 8, 16),
                  ("normal", 0.02)),
+        Workload("q4_0_n512", 7, 512, 2560, "f16", "q4_0", "f16", (1, 4, 16, 306, 2048),
+                 ("q4_0", 1e-3, 2e-3)),
     )
 }
 
