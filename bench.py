@@ -59,6 +59,8 @@ def parse():
     p.add_argument("--warmup", type=int, default=20)
     p.add_argument("--rounds", type=int, default=9)
     p.add_argument("--no-sweep", action="store_true")
+    p.add_argument("--sweep-only", default=None, metavar="NAME[,NAME...]",
+                   help="sweep only these workloads ('moe_combine' names the combine rows)")
     p.add_argument("--no-cpu", action="store_true")
     p.add_argument("--cpu-seconds", type=float, default=10.0)
     p.add_argument("--oracle-seconds", type=float, default=0.25,
@@ -372,11 +374,13 @@ def oracle_call_time(wl, m, inp, budget_s):
             "kind": "oracle", "gpu_speedup": None}
 
 
-def sweep(sk, torch, rounds, oracle_s=0.0):
+def sweep(sk, torch, rounds, oracle_s=0.0, names=None):
     import workloads as WL
 
     rows = []
     for name, wl in WL.WORKLOADS.items():
+        if names is not None and name not in names:
+            continue
         inp = Inputs(wl, torch, max(wl.ms))
         a, w, c = dtype_codes(sk, wl)
         gate = wl.a_kind == "f32"  # the scalar gate: one GEMV, cast on load, sigmoid on store
@@ -666,8 +670,12 @@ def main():
     log("per m: " + ", ".join(f"m={r['m']}: {r['us_per_row']} us/row" for r in per_m))
 
     osec = 0.0 if args.no_cpu else args.oracle_seconds
-    sweep_rows = [] if args.no_sweep else (sweep(sk, torch, args.rounds, osec) +
-                                           sweep_combine(sk, torch, args.rounds, osec))
+    names = None if args.sweep_only is None else set(args.sweep_only.split(","))
+    sweep_rows = []
+    if not args.no_sweep:
+        sweep_rows = sweep(sk, torch, args.rounds, osec, names)
+        if names is None or "moe_combine" in names:
+            sweep_rows += sweep_combine(sk, torch, args.rounds, osec)
 
     cpu = None
     parity_ok = True

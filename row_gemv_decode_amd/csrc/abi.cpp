@@ -591,15 +591,23 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   p->w_kind = to_wkind(d.w_dtype);
   p->c_kind = to_ckind(d.c_dtype);
   gemv_split(d.k, &p->gemv_T, &p->gemv_S);
-  // about four waves per CU as the base; a k split inside the workgroup runs
-  // about eight per CU, which hides more latency (measured on MI355X at
-  // n x k = 4864 x 896, 2048 x 2048, 8192 x 1024, 1024 x 4096, 14336 x 4096),
-  // except that an unsplit k at m > 8 keeps the base: there each workgroup
-  // stages all m rows of A in LDS, and fewer, wider workgroups load less of it
+  // Columns per wave by m (a column's arithmetic does not depend on it).
+  // The base is about four waves per CU (it also lays out the arrival
+  // counters of a k split across workgroups).  A k split inside the
+  // workgroup runs about eight waves per CU.  An unsplit k runs about
+  // sixteen waves per CU up to m = 8 and eight above: measured on MI355X at
+  // n x k = 4864 x 896 (graph replay, cold weights), one column per wave
+  // took 3.64 / 4.12 / 4.69 us at m = 1 / 4 / 8 against 3.72 / 4.39 / 5.17
+  // for two, and at m = 16 two columns took 7.00 us against 7.92 for four
+  // (more waves hide more of the load and reduction latency).
   p->gemv_cpw = gemv_cols_per_wave(d.n, p->gemv_S, cus, 4);
   for (int m = 0; m <= kGemvMaxM; ++m) {
-    const bool base = p->gemv_S > kGemvBlockSplitMax || (p->gemv_S == 1 && m > 8);
-    p->gemv_cpw_m[m] = base ? p->gemv_cpw : gemv_cols_per_wave(d.n, p->gemv_S, cus, 8);
+    if (p->gemv_S == 1)
+      p->gemv_cpw_m[m] = gemv_cols_per_wave(d.n, 1, cus, m <= 8 ? 16 : 8);
+    else if (p->gemv_S <= kGemvBlockSplitMax)
+      p->gemv_cpw_m[m] = gemv_cols_per_wave(d.n, p->gemv_S, cus, 8);
+    else
+      p->gemv_cpw_m[m] = p->gemv_cpw;
   }
   gemm_split(d.n, d.k, cus, &p->gemm_splits, &p->gemm_kps);
   if (log_enabled()) {
