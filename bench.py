@@ -66,9 +66,10 @@ def parse():
     p.add_argument("--oracle-seconds", type=float, default=0.25,
                    help="CPU-oracle budget per sweep row (a sample of rows, scaled to the call)")
     p.add_argument("--tiles", default=None, metavar="WORKLOAD",
-                   help="time every GEMM tile at every m > 16 of WORKLOAD (cold weights, "
-                        "HIP-graph replay, min of 5) and print one JSON line per m; the "
-                        "measurements behind the tile selector's cost table")
+                   help="time every GEMM tile (and, for a plan that cuts k into chunks, both "
+                        "the split and the one-launch shape) at every m > 16 of WORKLOAD (cold "
+                        "weights and A, HIP-graph replay, min of 5) and print one JSON line per "
+                        "m; the measurements behind the tile selector's cost table")
     p.add_argument("--only", default=None, metavar="WORKLOAD:M[,M...][:TILE]",
                    help="profiling mode: run one workload at the given m values (cycled; "
                         "optionally a forced GEMM tile id) --steps times eagerly, print the "
@@ -88,22 +89,30 @@ def run_tiles(name):
     inp = Inputs(wl, torch, max(wl.ms), pool_bytes=512 << 20)
     a, w, c = dtype_codes(sk, wl)
     cdt = torch.float32 if wl.c_kind == "f32" else torch.float16
+    chunked = "chunks=1 " not in sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c).info(max(wl.ms))
+    shapes = ((sk.GEMM_SPLIT_LAUNCH, "split"), (sk.GEMM_ONE_LAUNCH, "one")) if chunked else ((0, "plain"),)
+    nA = len(inp.As)
     for m in [x for x in wl.ms if x > 16]:
         C = torch.empty((m, wl.n), dtype=cdt, device="cuda")
         row = {"workload": name, "m": m, "us": {}}
         for tid, tname in enumerate(sk.gemm_tiles()):
-            plan = sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c, tile_id=tid)
-            L = min(len(inp.W), 64)
+            for flag, sname in shapes:
+                plan = sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c, tile_id=tid, flags=flag)
+                if f"launch={sname}" not in plan.info(m):
+                    continue  # the tile has no such launch shape
+                ws = plan.workspace(inp.A.device)
+                L = min(len(inp.W), 64)
 
-            def fn(i, plan=plan):
-                W = inp.W[i % len(inp.W)]
-                if wl.w_kind in ("q8_0", "q4_0"):
-                    plan.run(m, inp.A[:m], W[0], C, scales=W[1])
-                else:
-                    plan.run(m, inp.A[:m], W, C)
-            g = capture(torch, fn, L)
-            row["us"][tname] = round(time_graph(torch, g, L, 5)[0], 2)
-            del g
+                def fn(i, plan=plan, ws=ws):
+                    W = inp.W[i % len(inp.W)]
+                    A = inp.As[i % nA]
+                    if wl.w_kind in ("q8_0", "q4_0"):
+                        plan.run(m, A[:m], W[0], C, scales=W[1], workspace=ws)
+                    else:
+                        plan.run(m, A[:m], W, C, workspace=ws)
+                g = capture(torch, fn, L)
+                row["us"][f"{tname}/{sname}"] = round(time_graph(torch, g, L, 5)[0], 2)
+                del g
         row["selector"] = sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c).info(m)
         print(json.dumps(row), flush=True)
         del C
@@ -111,8 +120,10 @@ def run_tiles(name):
 
 def run_only(spec, steps, warmup):
     """Profiling mode: `steps` eager calls of one workload (m values cycled,
-    each call on the next cold weight copy), for rocprofv3 kernel traces and
-    counter passes; or a plain copy of a known size for calibration."""
+    each call on the next cold copy of the weight and of A), for rocprofv3
+    kernel traces and counter passes; or a plain copy of a known size for
+    calibration.  NAME_f16_twin runs a block-quantised workload on the f16
+    dequantisation of its weight."""
     import torch
 
     import row_gemv_decode_amd as sk
@@ -157,10 +168,17 @@ def run_only(spec, steps, warmup):
         us = (time.perf_counter() - t0) * 1e6 / steps
         print(json.dumps({"only": spec, "calls": steps, "us_per_call_eager": round(us, 3)}), flush=True)
         return
-    wl = WL.WORKLOADS[parts[0]]
+    twin = parts[0].endswith("_f16_twin")  # a block-quantised workload on its f16 dequantisation
+    wl = WL.WORKLOADS[parts[0][:-len("_f16_twin")] if twin else parts[0]]
     ms = [int(x) for x in parts[1].split(",")]
     tile = int(parts[2]) if len(parts) > 2 else -1
     inp = Inputs(wl, torch, max(ms))
+    if twin:
+        import dataclasses
+
+        deq = sk.dequant_q8_0 if wl.w_kind == "q8_0" else sk.dequant_q4_0
+        inp.W = [deq(qs, d) for qs, d in inp.W]
+        wl = dataclasses.replace(wl, w_kind="f16")
     a, w, c = dtype_codes(sk, wl)
     gate = wl.a_kind == "f32"  # the scalar gate: one GEMV, cast on load, sigmoid on store
     plan = sk.Plan(wl.n, wl.k, max(max(ms), max(wl.ms)), a, w, c, tile_id=tile,
@@ -175,12 +193,13 @@ def run_only(spec, steps, warmup):
         m = ms[i % len(ms)]
         C, idx, val = outs[m]
         W = inp.W[i % len(inp.W)]
+        A = inp.As[i % len(inp.As)]
         if wl.w_kind in ("q8_0", "q4_0"):
-            plan.run(m, inp.A[:m], W[0], C, scales=W[1], workspace=ws)
+            plan.run(m, A[:m], W[0], C, scales=W[1], workspace=ws)
         elif wl.topk:
-            plan.run_topk(m, inp.A[:m], W, C, idx, val, TOPK, workspace=ws)
+            plan.run_topk(m, A[:m], W, C, idx, val, TOPK, workspace=ws)
         else:
-            plan.run(m, inp.A[:m], W, C, workspace=ws)
+            plan.run(m, A[:m], W, C, workspace=ws)
 
     for i in range(warmup):
         call(i)
@@ -375,6 +394,8 @@ def oracle_call_time(wl, m, inp, budget_s):
 
 
 def sweep(sk, torch, rounds, oracle_s=0.0, names=None):
+    import dataclasses
+
     import workloads as WL
 
     rows = []
@@ -382,68 +403,89 @@ def sweep(sk, torch, rounds, oracle_s=0.0, names=None):
         if names is not None and name not in names:
             continue
         inp = Inputs(wl, torch, max(wl.ms))
-        a, w, c = dtype_codes(sk, wl)
-        gate = wl.a_kind == "f32"  # the scalar gate: one GEMV, cast on load, sigmoid on store
-        plan = sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c, flags=sk.EPILOGUE_SIGMOID if gate else 0)
-        ws = plan.workspace(inp.A.device)
-        cdt = torch.float32 if wl.c_kind == "f32" else torch.float16
-        graphs = {}
-        keep = []  # every tensor a captured graph touches, alive until the graphs go
-        for m in wl.ms:
-            C = torch.empty((m, wl.n), dtype=cdt, device="cuda")
-            keep.append(C)
-            L = min(len(inp.W), 256)
-            nA = len(inp.As)
-
-            if wl.w_kind in ("q8_0", "q4_0"):
-                def fn(i, m=m, C=C):
-                    qs, d = inp.W[i % len(inp.W)]
-                    plan.run(m, inp.As[i % nA][:m], qs, C, scales=d, workspace=ws)
-            elif wl.topk:
-                lg = C
-                idx = torch.empty((m, wl.topk), dtype=torch.int32, device="cuda")
-                val = torch.empty((m, wl.topk), dtype=torch.float32, device="cuda")
-                keep += [idx, val]
-
-                def fn(i, m=m, lg=lg, idx=idx, val=val):
-                    plan.run_topk(m, inp.As[i % nA][:m], inp.W[i % len(inp.W)], lg, idx, val, wl.topk,
-                                  workspace=ws)
-            else:
-                def fn(i, m=m, C=C):
-                    plan.run(m, inp.As[i % nA][:m], inp.W[i % len(inp.W)], C, workspace=ws)
-            keep.append(fn)
-            graphs[m] = (capture(torch, fn, L), L)
-        # interleave rounds across m (the min over interleaved rounds)
-        per = {m: [] for m in wl.ms}
-        for _ in range(rounds):
-            for m in wl.ms:
-                g, L = graphs[m]
-                per[m].append(time_graph(torch, g, L, 1)[0])
-        for m in wl.ms:
-            ts = sorted(per[m])
-            t_min, t_med = ts[0], ts[len(ts) // 2]
-            nbytes = call_bytes(wl, m, bool(wl.topk))
-            flops = 2.0 * m * wl.n * wl.k
-            row = {
-                "workload": name, "m": m, "path": plan.info(m).split()[0].split("=")[1],
-                "plan": plan.info(m), "us_per_call_min": round(t_min, 3),
-                "us_per_call_median": round(t_med, 3), "us_per_row": round(t_min / m, 4),
-                "weight_GBps": round(wl.w_bytes / t_min / 1e3, 1),
-                "hbm_frac": round(nbytes / t_min / 1e3 / HBM_PEAK_GBS, 4),
-                "TFLOPs": round(flops / t_min / 1e6, 2),
-                "mfma_frac": round(flops / t_min / 1e6 / MFMA_F16_PEAK_TFLOPS, 4),
-            }
-            if oracle_s > 0:
-                row["oracle"] = oracle_call_time(wl, m, inp, oracle_s)
-                row["oracle"]["gpu_speedup"] = round(row["oracle"]["us_per_call"] / t_min, 1)
-            rows.append(row)
-            log(f"  {name:12s} m={m:5d} {t_min:8.3f} us (med {t_med:8.3f})  us/row {t_min / m:8.4f}"
-                f"  W {row['weight_GBps']:8.1f} GB/s  hbm {row['hbm_frac']:.3f}  "
-                f"{row['TFLOPs']:8.1f} TF/s  mfma {row['mfma_frac']:.3f}  [{row['plan']}]")
-        torch.cuda.synchronize()
-        del graphs
-        del keep, inp
+        rows += sweep_workload(sk, torch, name, wl, inp, rounds, oracle_s)
+        if wl.w_kind in ("q8_0", "q4_0"):
+            # the f16 twin: the same shape on the library's own dequantisation of
+            # each pool copy (the fused path's cost over a plain f16 weight)
+            deq = sk.dequant_q8_0 if wl.w_kind == "q8_0" else sk.dequant_q4_0
+            inp.W = [deq(qs, d) for qs, d in inp.W]
+            twin = dataclasses.replace(wl, w_kind="f16")
+            trows = sweep_workload(sk, torch, name + "_f16_twin", twin, inp, rounds, 0.0)
+            by_m = {r["m"]: r for r in trows}
+            for r in rows:
+                if r["workload"] == name and r["m"] in by_m:
+                    r["vs_f16_twin"] = round(r["us_per_call_min"] / by_m[r["m"]]["us_per_call_min"], 3)
+            rows += trows
+        del inp
         torch.cuda.empty_cache()
+    return rows
+
+
+def sweep_workload(sk, torch, name, wl, inp, rounds, oracle_s):
+    """Sweep rows of one workload: each m captured as one HIP graph of L
+    cold-weight calls, rounds interleaved across m, min and median kept."""
+    rows = []
+    a, w, c = dtype_codes(sk, wl)
+    gate = wl.a_kind == "f32"  # the scalar gate: one GEMV, cast on load, sigmoid on store
+    plan = sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c, flags=sk.EPILOGUE_SIGMOID if gate else 0)
+    ws = plan.workspace(inp.A.device)
+    cdt = torch.float32 if wl.c_kind == "f32" else torch.float16
+    graphs = {}
+    keep = []  # every tensor a captured graph touches, alive until the graphs go
+    for m in wl.ms:
+        C = torch.empty((m, wl.n), dtype=cdt, device="cuda")
+        keep.append(C)
+        L = min(len(inp.W), 256)
+        nA = len(inp.As)
+
+        if wl.w_kind in ("q8_0", "q4_0"):
+            def fn(i, m=m, C=C):
+                qs, d = inp.W[i % len(inp.W)]
+                plan.run(m, inp.As[i % nA][:m], qs, C, scales=d, workspace=ws)
+        elif wl.topk:
+            lg = C
+            idx = torch.empty((m, wl.topk), dtype=torch.int32, device="cuda")
+            val = torch.empty((m, wl.topk), dtype=torch.float32, device="cuda")
+            keep += [idx, val]
+
+            def fn(i, m=m, lg=lg, idx=idx, val=val):
+                plan.run_topk(m, inp.As[i % nA][:m], inp.W[i % len(inp.W)], lg, idx, val, wl.topk,
+                              workspace=ws)
+        else:
+            def fn(i, m=m, C=C):
+                plan.run(m, inp.As[i % nA][:m], inp.W[i % len(inp.W)], C, workspace=ws)
+        keep.append(fn)
+        graphs[m] = (capture(torch, fn, L), L)
+    # interleave rounds across m (the min over interleaved rounds)
+    per = {m: [] for m in wl.ms}
+    for _ in range(rounds):
+        for m in wl.ms:
+            g, L = graphs[m]
+            per[m].append(time_graph(torch, g, L, 1)[0])
+    for m in wl.ms:
+        ts = sorted(per[m])
+        t_min, t_med = ts[0], ts[len(ts) // 2]
+        nbytes = call_bytes(wl, m, bool(wl.topk))
+        flops = 2.0 * m * wl.n * wl.k
+        row = {
+            "workload": name, "m": m, "path": plan.info(m).split()[0].split("=")[1],
+            "plan": plan.info(m), "us_per_call_min": round(t_min, 3),
+            "us_per_call_median": round(t_med, 3), "us_per_row": round(t_min / m, 4),
+            "weight_GBps": round(wl.w_bytes / t_min / 1e3, 1),
+            "hbm_frac": round(nbytes / t_min / 1e3 / HBM_PEAK_GBS, 4),
+            "TFLOPs": round(flops / t_min / 1e6, 2),
+            "mfma_frac": round(flops / t_min / 1e6 / MFMA_F16_PEAK_TFLOPS, 4),
+        }
+        if oracle_s > 0:
+            row["oracle"] = oracle_call_time(wl, m, inp, oracle_s)
+            row["oracle"]["gpu_speedup"] = round(row["oracle"]["us_per_call"] / t_min, 1)
+        rows.append(row)
+        log(f"  {name:12s} m={m:5d} {t_min:8.3f} us (med {t_med:8.3f})  us/row {t_min / m:8.4f}"
+            f"  W {row['weight_GBps']:8.1f} GB/s  hbm {row['hbm_frac']:.3f}  "
+            f"{row['TFLOPs']:8.1f} TF/s  mfma {row['mfma_frac']:.3f}  [{row['plan']}]")
+    torch.cuda.synchronize()
+    del graphs
+    del keep
     return rows
 
 
@@ -689,6 +731,9 @@ def main():
         u = {r["m"]: r["us_per_row"] for r in rows0}
         if 1 in u and 8 in u:
             derived["gemv_k896_us_per_row_ratio_m1_over_m8"] = round(u[1] / u[8], 3)
+    for r in sweep_rows:
+        if "vs_f16_twin" in r and r["m"] > 16:
+            derived[f"{r['workload']}_over_f16_twin_M{r['m']}"] = r["vs_f16_twin"]
     g2048 = [r for r in sweep_rows if r["workload"] == "wide_n7680" and r["m"] == 2048]
     if g2048:
         derived["f16_gemm_TFLOPs_M2048"] = g2048[0]["TFLOPs"]
