@@ -376,6 +376,28 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int r = 0; r < M; ++r) a[t][r] = sAr[(r * T + t) * 64 + lane];
+  } else if constexpr (AK == kAF32) {
+    // fp32 rows: every raw load first, then the rounding to bf16 -- a
+    // conversion between the loads makes the compiler wait for each pair
+    // before it issues the next
+    u32x4 raw[T][M][2];
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < M; ++r) {
+        if (active) {  // wave-uniform
+          const u32x4* p = (const u32x4*)((const float*)g.A + (int64_t)r * g.lda + (int64_t)lchunk[t] * 8);
+          raw[t][r][0] = p[0];
+          raw[t][r][1] = p[1];
+        } else {
+          raw[t][r][0] = raw[t][r][1] = u32x4{0u, 0u, 0u, 0u};
+        }
+      }
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+#pragma unroll
+      for (int r = 0; r < M; ++r) a[t][r] = bf16x8_rne(raw[t][r][0], raw[t][r][1]);
   } else {
     if (active) {  // wave-uniform
 #pragma unroll
