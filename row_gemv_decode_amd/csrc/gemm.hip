@@ -43,7 +43,7 @@ const GemmTileInfo* tile_infos() {
   return table;
 }
 
-constexpr int kTileCount = 15;
+constexpr int kTileCount = 16;
 
 }  // namespace
 
