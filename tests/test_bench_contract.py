@@ -7,6 +7,7 @@ import os
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 
 import workloads as WL
@@ -75,3 +76,12 @@ def test_committed_counters_match_the_router_kernel():
     wl = WL.WORKLOADS["router_topk"]
     alg = sum(bench.call_bytes(wl, m) for m in bench.HEADLINE_MS) / len(bench.HEADLINE_MS)
     assert alg <= t <= 1.6 * alg
+
+
+def test_shard_workload_is_the_first_rows_of_the_full_weight():
+    # one GPU's share of an 8-way column shard is the first n / 8 output rows
+    # of the full weight, drawn from the same seed
+    full, part = WL.WORKLOADS["gemv_k896"], WL.WORKLOADS["gemv_k896_shard8"]
+    assert part.n * 8 == full.n and part.k == full.k
+    assert np.array_equal(WL.gen_w(part), WL.gen_w(full)[:part.n])
+    assert np.array_equal(WL.gen_a(part, 16), WL.gen_a(full, 16))

@@ -10,9 +10,11 @@ float64 and is rounded once to the storage format (numpy's f16 cast, torch's
 bf16 cast; both round to nearest even).  Seeds: W = 1000*c + 0,
 A = 1000*c + 1, Q8_0 scales = 1000*c + 2, with c the workload's index.
 
-The five workloads stand in for the pages' measurements:
+The workloads stand in for the pages' measurements:
   gemv_k896     -- the nx_batchscale_kat page: synthetic W at the FFN inner
                    dimension k = 896, m swept to see whether W is amortised.
+  gemv_k896_shard8 -- one GPU's share of it under an 8-way column shard
+                   (n = 608, W = the first 608 rows of gemv_k896's W).
   router_topk   -- Strata PR #109 ("What"): the bf16 router GEMV (a 2.6 MB
                    weight) with a per-token top-10, rows = window tokens.
   narrow_n96    -- opus r35 track A, section 2, the N = 96, K = 2560 table.
@@ -64,6 +66,10 @@ WORKLOADS = {
     w.name: w
     for w in (
         Workload("gemv_k896", 0, 4864, 896, "f16", "f16", "f32", (1, 2, 4, 8, 16),
+                 ("uniform", -0.05, 0.05)),
+        # one GPU's share of gemv_k896 sharded by output columns over eight
+        # GPUs: the same seed, so W is the first 608 rows of gemv_k896's W
+        Workload("gemv_k896_shard8", 0, 608, 896, "f16", "f16", "f32", (1, 2, 4, 8, 16),
                  ("uniform", -0.05, 0.05)),
         Workload("router_topk", 1, 256, 5120, "bf16", "bf16", "f32", (1, 2, 4, 8, 16),
                  ("normal", 0.02), topk=10),
