@@ -153,8 +153,9 @@ const TileCost& tile_cost(int id) {
       {0.8760, 1, 0.080, 1.000},  // 192x128_w2x2
       {1.4250, 1, 0.000, 1.000},  // 192x256_w2x4
       {1.1030, 1, 0.145, 1.000},  // 192x192_w3x2
+      {0.2700, 2, 0.000, 2.000},  // 32x32_w1x1
   };
-  static_assert(sizeof(kCost) / sizeof(kCost[0]) == 16, "one cost row per tile");
+  static_assert(sizeof(kCost) / sizeof(kCost[0]) == 17, "one cost row per tile");
   return kCost[id];
 }
 

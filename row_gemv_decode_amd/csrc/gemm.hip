@@ -43,7 +43,7 @@ const GemmTileInfo* tile_infos() {
   return table;
 }
 
-constexpr int kTileCount = 16;
+constexpr int kTileCount = 17;
 
 }  // namespace
 

@@ -728,7 +728,8 @@ typedef void (*gemm_fn)(GemmArgs);
   X(32, 64, 1, 2, 5, true, "32x64_w1x2")          \
   X(192, 128, 2, 2, 3, false, "192x128_w2x2")     \
   X(192, 256, 2, 4, 2, false, "192x256_w2x4")     \
-  X(192, 192, 3, 2, 3, false, "192x192_w3x2")
+  X(192, 192, 3, 2, 3, false, "192x192_w3x2")     \
+  X(32, 32, 1, 1, 6, true, "32x32_w1x1")
 
 // the chunked one-launch variant keeps a second set of accumulators, so only
 // tiles with at most four 32 x 32 blocks per wave get it; the fold launch
