@@ -134,6 +134,8 @@ struct TileCost {
   double sigma;
 };
 
+constexpr int kCostRows = 17;  // must equal gemm_tile_count(); the plan checks it
+
 const TileCost& tile_cost(int id) {
   // indexed like the tile table in gemm.hip
   static const TileCost kCost[] = {
@@ -155,7 +157,7 @@ const TileCost& tile_cost(int id) {
       {1.1030, 1, 0.145, 1.000},  // 192x192_w3x2
       {0.2700, 2, 0.000, 2.000},  // 32x32_w1x1
   };
-  static_assert(sizeof(kCost) / sizeof(kCost[0]) == 17, "one cost row per tile");
+  static_assert(sizeof(kCost) / sizeof(kCost[0]) == kCostRows, "one cost row per tile");
   return kCost[id];
 }
 
@@ -565,6 +567,7 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   }
   if ((d.flags & SKINNY_FORCE_GEMV) && (d.flags & SKINNY_FORCE_GEMM)) return SKINNY_ERR_INVALID_ARG;
   if ((d.flags & SKINNY_FORCE_GEMV) && d.max_m > kGemvMaxM) return SKINNY_ERR_INVALID_ARG;
+  if (gemm_tile_count() != kCostRows) return SKINNY_ERR_UNSUPPORTED;  // a build whose tables disagree
   if (d.tile_id < -1 || d.tile_id >= gemm_tile_count()) return SKINNY_ERR_INVALID_ARG;
   // the GEMM addresses a block's rows through 32-bit buffer offsets
   const bool may_gemm = !(d.flags & SKINNY_FORCE_GEMV) && (d.max_m > kGemvMaxM || (d.flags & SKINNY_FORCE_GEMM));

@@ -36,14 +36,13 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(GemmArgs g) {
   }
 }
 
-const GemmTileInfo* tile_infos() {
 #define SKINNY_GEMM_INFO(TM, TN, WM, WN, NS, XT, NAME) GemmTileInfo{TM, TN, WM, WN, NAME},
-  static const GemmTileInfo table[] = {SKINNY_GEMM_TILE_LIST(SKINNY_GEMM_INFO)};
+const GemmTileInfo kTileTable[] = {SKINNY_GEMM_TILE_LIST(SKINNY_GEMM_INFO)};
 #undef SKINNY_GEMM_INFO
-  return table;
-}
 
-constexpr int kTileCount = 17;
+const GemmTileInfo* tile_infos() { return kTileTable; }
+
+constexpr int kTileCount = (int)(sizeof(kTileTable) / sizeof(kTileTable[0]));
 
 }  // namespace
 
