@@ -106,7 +106,7 @@ def run_tiles(name):
                 def fn(i, plan=plan, ws=ws):
                     W = inp.W[i % len(inp.W)]
                     A = inp.As[i % nA]
-                    if wl.w_kind in ("q8_0", "q4_0"):
+                    if wl.w_kind in BLOCK_KINDS:
                         plan.run(m, A[:m], W[0], C, scales=W[1], workspace=ws)
                     else:
                         plan.run(m, A[:m], W, C, workspace=ws)
@@ -176,7 +176,7 @@ def run_only(spec, steps, warmup):
     if twin:
         import dataclasses
 
-        deq = sk.dequant_q8_0 if wl.w_kind == "q8_0" else sk.dequant_q4_0
+        deq = block_dequant(sk, wl.w_kind)
         inp.W = [deq(qs, d) for qs, d in inp.W]
         wl = dataclasses.replace(wl, w_kind="f16")
     a, w, c = dtype_codes(sk, wl)
@@ -194,7 +194,7 @@ def run_only(spec, steps, warmup):
         C, idx, val = outs[m]
         W = inp.W[i % len(inp.W)]
         A = inp.As[i % len(inp.As)]
-        if wl.w_kind in ("q8_0", "q4_0"):
+        if wl.w_kind in BLOCK_KINDS:
             plan.run(m, A[:m], W[0], C, scales=W[1], workspace=ws)
         elif wl.topk:
             plan.run_topk(m, A[:m], W, C, idx, val, TOPK, workspace=ws)
@@ -251,7 +251,7 @@ class Inputs:
         a_bytes = self.A.numel() * self.A.element_size()
         copies = max(2, int(pool_bytes // max(1, wl.w_bytes + a_bytes)))
         self.As = [self.A] + [self.A.clone() for _ in range(copies - 1)]
-        if wl.w_kind in ("q8_0", "q4_0"):
+        if wl.w_kind in BLOCK_KINDS:
             qs, d = W
             q0 = torch.from_numpy(qs).cuda()
             d0 = dev16(d, "f16")
@@ -262,10 +262,19 @@ class Inputs:
         self.scales = None
 
 
+# block-quantised weight kinds: (codes, scales) pairs with a fused path and a
+# standalone dequant to f16
+BLOCK_KINDS = ("q8_0", "q4_0", "q2_0")
+
+
+def block_dequant(sk, kind):
+    return {"q8_0": sk.dequant_q8_0, "q4_0": sk.dequant_q4_0, "q2_0": sk.dequant_q2_0}[kind]
+
+
 def dtype_codes(sk, wl):
     # fp32 rows (the gate) are rounded to bf16 by the GEMV as it loads them
     a = {"bf16": sk.BF16, "f32": sk.F32}.get(wl.a_kind, sk.F16)
-    w = {"f16": sk.F16, "bf16": sk.BF16, "q8_0": sk.Q8_0, "q4_0": sk.Q4_0}[wl.w_kind]
+    w = {"f16": sk.F16, "bf16": sk.BF16, "q8_0": sk.Q8_0, "q4_0": sk.Q4_0, "q2_0": sk.Q2_0}[wl.w_kind]
     c = sk.F32 if wl.c_kind == "f32" else sk.F16
     return a, w, c
 
@@ -381,7 +390,7 @@ def oracle_call_time(wl, m, inp, budget_s):
     t0 = time.perf_counter()
     if wl.a_kind == "f32":
         oracle.gate(A, inp.W_bits, threads=threads)
-    elif wl.w_kind in ("q8_0", "q4_0"):
+    elif wl.w_kind in BLOCK_KINDS:
         qs, d = inp.W_bits
         oracle.mm(A, "f16", qs, wl.w_kind, w_scales=d, threads=threads)
     else:
@@ -404,10 +413,10 @@ def sweep(sk, torch, rounds, oracle_s=0.0, names=None):
             continue
         inp = Inputs(wl, torch, max(wl.ms))
         rows += sweep_workload(sk, torch, name, wl, inp, rounds, oracle_s)
-        if wl.w_kind in ("q8_0", "q4_0"):
+        if wl.w_kind in BLOCK_KINDS:
             # the f16 twin: the same shape on the library's own dequantisation of
             # each pool copy (the fused path's cost over a plain f16 weight)
-            deq = sk.dequant_q8_0 if wl.w_kind == "q8_0" else sk.dequant_q4_0
+            deq = block_dequant(sk, wl.w_kind)
             inp.W = [deq(qs, d) for qs, d in inp.W]
             twin = dataclasses.replace(wl, w_kind="f16")
             trows = sweep_workload(sk, torch, name + "_f16_twin", twin, inp, rounds, 0.0)
@@ -438,7 +447,7 @@ def sweep_workload(sk, torch, name, wl, inp, rounds, oracle_s):
         L = min(len(inp.W), 256)
         nA = len(inp.As)
 
-        if wl.w_kind in ("q8_0", "q4_0"):
+        if wl.w_kind in BLOCK_KINDS:
             def fn(i, m=m, C=C):
                 qs, d = inp.W[i % len(inp.W)]
                 plan.run(m, inp.As[i % nA][:m], qs, C, scales=d, workspace=ws)

@@ -16,6 +16,10 @@ the pages, which print none for these steps):
                  ("Measured": IQ3_S, Q2_0) but does not define, fixed here as
                  Q4_0-style: blocks of 32 along k, one f16 scale d, 4-bit
                  codes q two per byte (even k low nibble), w = RNE_f16(d*(q-8))
+  dequant_q2_0 -- the 2-bit block format the same page names (Q2_0 runs) but
+                 does not define, fixed here as the 2-bit counterpart: blocks
+                 of 32 along k, one f16 scale d, 2-bit codes q four per byte
+                 (element kk at bits 2*(kk%4)), w = RNE_f16(d*(q-2))
   topk        -- Strata PR #109, "What" (router top-10 per token), ties to the
                  lower index
   cast_bf16   -- Strata PR #109, "What" (the bf16 cast of the window's rows):
@@ -35,8 +39,10 @@ import numpy as np
 
 from . import build as _build
 
-F16, BF16, Q8_0, Q4_0 = 1, 2, 4, 5
-_KINDS = {"f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0}
+F16, BF16, Q8_0, Q4_0, Q2_0 = 1, 2, 4, 5, 6
+_KINDS = {"f16": F16, "bf16": BF16, "q8_0": Q8_0, "q4_0": Q4_0, "q2_0": Q2_0}
+# stored codes per byte of the packed block formats
+_CODES_PER_BYTE = {"q8_0": 1, "q4_0": 2, "q2_0": 4}
 
 _lib = None
 
@@ -59,6 +65,8 @@ def _load():
     lib.oracle_dequant_q8_0.restype = ctypes.c_int
     lib.oracle_dequant_q4_0.argtypes = [i64, i64, vp, vp, vp]
     lib.oracle_dequant_q4_0.restype = ctypes.c_int
+    lib.oracle_dequant_q2_0.argtypes = [i64, i64, vp, vp, vp]
+    lib.oracle_dequant_q2_0.restype = ctypes.c_int
     lib.oracle_mm.argtypes = [i64, i64, i64, ctypes.c_int, vp, i64, ctypes.c_int, vp, vp, vp,
                               i64, ctypes.c_int, ctypes.c_int]
     lib.oracle_mm.restype = ctypes.c_int
@@ -134,18 +142,34 @@ def dequant_q4_0(qs: np.ndarray, d: np.ndarray) -> np.ndarray:
     return out
 
 
+def dequant_q2_0(qs: np.ndarray, d: np.ndarray) -> np.ndarray:
+    """f16 bits [n][k] of RNE_f16(d[j][kk/32] * (q - 2)), q the 2-bit code of
+    element kk: bits 2*(kk%4) and 2*(kk%4)+1 of qs[j][kk/4]."""
+    qs = np.ascontiguousarray(qs, dtype=np.uint8)
+    d = np.ascontiguousarray(d, dtype=np.uint16)
+    n, kq = qs.shape
+    k = 4 * kq
+    assert d.shape == (n, k // 32), (d.shape, qs.shape)
+    out = np.empty((n, k), dtype=np.uint16)
+    rc = _load().oracle_dequant_q2_0(n, k, _ptr(qs), _ptr(d), _ptr(out))
+    if rc != 0:
+        raise ValueError(f"oracle_dequant_q2_0 failed ({rc})")
+    return out
+
+
 def mm(A: np.ndarray, a_kind: str, W: np.ndarray, w_kind: str, w_scales=None,
        threads=None, absolute=False) -> np.ndarray:
     """fp64 C[m][n] = sum_kk A[i][kk] * W[j][kk] (W stored [n][k]).
 
     A: uint16 bits [m][k]; W: uint16 bits [n][k], or int8 codes [n][k] for
-    q8_0, or packed 4-bit codes uint8 [n][k/2] for q4_0, each with w_scales
-    uint16 bits [n][k/32].  absolute=True returns
-    sum |A| * |W| instead (the fp32 rounding-error yardstick).
+    q8_0, packed 4-bit codes uint8 [n][k/2] for q4_0 or packed 2-bit codes
+    uint8 [n][k/4] for q2_0, each with w_scales uint16 bits [n][k/32].
+    absolute=True returns sum |A| * |W| instead (the fp32 rounding-error
+    yardstick).
     """
     A = np.ascontiguousarray(A, dtype=np.uint16)
     m, k = A.shape
-    if w_kind in ("q8_0", "q4_0"):
+    if w_kind in _CODES_PER_BYTE:
         W = np.ascontiguousarray(W, dtype=np.int8 if w_kind == "q8_0" else np.uint8)
         w_scales = np.ascontiguousarray(w_scales, dtype=np.uint16)
         sp = _ptr(w_scales)
@@ -153,8 +177,7 @@ def mm(A: np.ndarray, a_kind: str, W: np.ndarray, w_kind: str, w_scales=None,
         W = np.ascontiguousarray(W, dtype=np.uint16)
         sp = None
     n, k2 = W.shape
-    if w_kind == "q4_0":
-        k2 *= 2  # two codes per byte
+    k2 *= _CODES_PER_BYTE.get(w_kind, 1)
     assert k2 == k, (A.shape, W.shape)
     C = np.zeros((m, n), dtype=np.float64)
     t = default_threads() if threads is None else int(threads)

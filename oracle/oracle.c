@@ -1,7 +1,8 @@
 /*
  * oracle.c -- plain, slow, obviously correct CPU oracle for the weight-streaming
- * skinny matmul C[m,n] = A[m,k] . W[k,n] and the steps around it (Q8_0- and
- * Q4_0-style block dequant, per-row top-k, the window-row cast, the gate).
+ * skinny matmul C[m,n] = A[m,k] . W[k,n] and the steps around it (Q8_0-,
+ * Q4_0- and Q2_0-style block dequant, per-row top-k, the window-row cast, the
+ * gate).
  *
  * TEST INFRASTRUCTURE ONLY.  The test suite, the smoke check and the bench's
  * CPU-baseline leg call this code; the library's product path never does, and
@@ -44,7 +45,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_Q8_0 = 4, ORACLE_Q4_0 = 5 };
+enum { ORACLE_F16 = 1, ORACLE_BF16 = 2, ORACLE_Q8_0 = 4, ORACLE_Q4_0 = 5, ORACLE_Q2_0 = 6 };
 
 /* ---------------------------------------------------------------------------
  * Scalar conversions, written from the format definitions.
@@ -233,6 +234,37 @@ int oracle_dequant_q4_0(int64_t n, int64_t k, const uint8_t* qs, const uint16_t*
 }
 
 /* ---------------------------------------------------------------------------
+ * Dequant of the Q2_0-style block format (2-bit codes).  The Strata PR #109
+ * page names a 2-bit block format ("Measured": Q2_0 runs) without defining
+ * it, so this format is fixed here as the 2-bit counterpart of the Q4_0-style
+ * one above:
+ *   blocks of 32 consecutive k, one f16 scale d per block, unsigned 2-bit
+ *   codes q in 0..3 stored four per byte, element kk of a row in byte kk / 4
+ *   at bits 2 * (kk % 4) and 2 * (kk % 4) + 1 (the first element of a byte in
+ *   its lowest two bits); the weight is d * (q - 2), rounded once to f16
+ *   (round to nearest, ties to even).
+ *   qs: uint8 [n][k/4], d: f16 bits [n][k/32], out: f16 bits [n][k]
+ * The product is exact in fp64 (q - 2 is -2, -1, 0 or 1); the rounding only
+ * matters where 2 * |d| passes the largest f16.  Returns 0, or -1 when k is
+ * not a multiple of 32.
+ * ------------------------------------------------------------------------- */
+int oracle_dequant_q2_0(int64_t n, int64_t k, const uint8_t* qs, const uint16_t* d,
+                        uint16_t* out) {
+  if (k % 32 != 0) return -1;
+  int64_t nb = k / 32;
+  for (int64_t j = 0; j < n; ++j) {
+    for (int64_t kk = 0; kk < k; ++kk) {
+      uint8_t byte = qs[j * (k / 4) + kk / 4];
+      int q = (byte >> (2 * (kk % 4))) & 0x3;
+      double scale = oracle_f16_to_f64(d[j * nb + kk / 32]);
+      double w = scale * (double)(q - 2);
+      out[j * k + kk] = oracle_f64_to_f16_rne(w);
+    }
+  }
+  return 0;
+}
+
+/* ---------------------------------------------------------------------------
  * The matmul.  Inputs are decoded to fp64 once, then every C[i][j] is one
  * sequential fp64 sum over kk = 0..k-1.  Threads split the (i, j) pairs into
  * contiguous column blocks per row; no dot product is ever split.
@@ -277,7 +309,8 @@ static double decode16(int kind, uint16_t v) {
 }
 
 /* A: bits [m][lda] (f16 or bf16, a_kind).  W: for F16/BF16 bits [n][k]; for
- * Q8_0 int8 codes [n][k], for Q4_0 packed codes uint8 [n][k/2], each with
+ * Q8_0 int8 codes [n][k], for Q4_0 packed codes uint8 [n][k/2], for Q2_0
+ * packed codes uint8 [n][k/4], each with
  * w_scales f16 bits [n][k/32].  C: fp64 [m][ldc].
  * threads <= 0 means 1.  Returns 0, -1 on a bad argument, -2 on no memory. */
 int oracle_mm(int64_t m, int64_t n, int64_t k, int a_kind, const uint16_t* A, int64_t lda,
@@ -285,9 +318,9 @@ int oracle_mm(int64_t m, int64_t n, int64_t k, int a_kind, const uint16_t* A, in
               int threads, int absolute) {
   if (m < 0 || n < 0 || k < 0 || lda < k || ldc < n) return -1;
   if (a_kind != ORACLE_F16 && a_kind != ORACLE_BF16) return -1;
-  if (w_kind != ORACLE_F16 && w_kind != ORACLE_BF16 && w_kind != ORACLE_Q8_0 && w_kind != ORACLE_Q4_0)
-    return -1;
-  if ((w_kind == ORACLE_Q8_0 || w_kind == ORACLE_Q4_0) && (k % 32 != 0 || w_scales == NULL)) return -1;
+  const int blockq = w_kind == ORACLE_Q8_0 || w_kind == ORACLE_Q4_0 || w_kind == ORACLE_Q2_0;
+  if (w_kind != ORACLE_F16 && w_kind != ORACLE_BF16 && !blockq) return -1;
+  if (blockq && (k % 32 != 0 || w_scales == NULL)) return -1;
   if (m == 0 || n == 0) return 0;
 
   double* a = (double*)malloc(sizeof(double) * (size_t)(m * k + 1));
@@ -301,7 +334,7 @@ int oracle_mm(int64_t m, int64_t n, int64_t k, int a_kind, const uint16_t* A, in
   for (int64_t i = 0; i < m; ++i)
     for (int64_t kk = 0; kk < k; ++kk) a[i * k + kk] = decode16(a_kind, A[i * lda + kk]);
 
-  if (w_kind == ORACLE_Q8_0 || w_kind == ORACLE_Q4_0) {
+  if (blockq) {
     deq = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)(n * k + 1));
     if (!deq) {
       free(a);
@@ -310,8 +343,10 @@ int oracle_mm(int64_t m, int64_t n, int64_t k, int a_kind, const uint16_t* A, in
     }
     if (w_kind == ORACLE_Q8_0)
       oracle_dequant_q8_0(n, k, (const int8_t*)W, w_scales, deq);
-    else
+    else if (w_kind == ORACLE_Q4_0)
       oracle_dequant_q4_0(n, k, (const uint8_t*)W, w_scales, deq);
+    else
+      oracle_dequant_q2_0(n, k, (const uint8_t*)W, w_scales, deq);
     for (int64_t idx = 0; idx < n * k; ++idx) w[idx] = oracle_f16_to_f64(deq[idx]);
     free(deq);
   } else {

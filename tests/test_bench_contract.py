@@ -49,7 +49,7 @@ def test_call_bytes_count_each_operand_once():
 
 def test_dtype_codes_follow_the_workload_kinds():
     class Codes:
-        F16, BF16, F32, Q8_0, Q4_0 = "f16", "bf16", "f32", "q8_0", "q4_0"
+        F16, BF16, F32, Q8_0, Q4_0, Q2_0 = "f16", "bf16", "f32", "q8_0", "q4_0", "q2_0"
     for wl in WL.WORKLOADS.values():
         a, w, c = bench.dtype_codes(Codes, wl)
         assert (a, w, c) == (wl.a_kind, wl.w_kind, wl.c_kind), wl.name

@@ -193,6 +193,7 @@ def _exact_int64(a_f64, w_f64):
     ("wide_n7680", 6, None),
     ("q8_0_n512", 16, None),
     ("q4_0_n512", 16, None),
+    ("q2_0_n512", 16, None),
 ])
 def test_exact_int64_at_workload_shapes(name, rows, cols):
     wl = WL.WORKLOADS[name]
@@ -208,6 +209,10 @@ def test_exact_int64_at_workload_shapes(name, rows, cols):
         q = np.empty((wl.n, wl.k), np.float64)
         q[:, 0::2], q[:, 1::2] = qs & 0x0F, qs >> 4
         w = (np.repeat(np_f16(d), 32, axis=1) * (q - 8.0)).astype(np.float16).astype(np.float64)
+    elif wl.w_kind == "q2_0":
+        qs, d = W
+        got = oracle.mm(A, "f16", qs, "q2_0", w_scales=d)
+        w = (np.repeat(np_f16(d), 32, axis=1) * (_unpack_q2(qs) - 2.0)).astype(np.float16).astype(np.float64)
     else:
         got = oracle.mm(A, wl.a_kind, W, wl.w_kind)
         w = np_f16(W)
@@ -514,4 +519,99 @@ def test_q4_0_generator_codes_and_scales():
     assert qs.shape == (8, 32) and qs.dtype == np.uint8 and d.shape == (8, 2)
     q = np.concatenate([qs & 0x0F, qs >> 4])
     assert q.min() == 0 and q.max() == 15
+    assert np.all((np_f16(d) >= 1e-3 - 1e-6) & (np_f16(d) <= 2e-3 + 1e-6))
+
+
+# ---------------------------------------------------------------------------
+# Q2_0-style dequant (2-bit codes, four per byte)
+# ---------------------------------------------------------------------------
+
+def _unpack_q2(qs):
+    """fp64 codes [rows][4 * bytes]: element kk from bits 2*(kk%4) of byte kk//4."""
+    q = np.empty((qs.shape[0], 4 * qs.shape[1]), np.float64)
+    for p in range(4):
+        q[:, p::4] = (qs >> (2 * p)) & 0x3
+    return q
+
+
+def _q2_block(element, q, rows=1):
+    """One 32-weight block whose codes are all 2 (weight 0) but `element`'s,
+    packed byte by byte."""
+    packed = np.full((rows, 8), 0xAA, np.uint8)            # 0b10101010: four codes 2
+    b, p = divmod(element, 4)
+    packed[:, b] = (0xAA & ~(0x3 << (2 * p)) | (q << (2 * p))) & 0xFF
+    return packed
+
+
+def test_dequant_q2_0_golden_values():
+    rows = [line.split() for line in golden_lines("dequant_q2_0_rne.txt")]
+    assert len(rows) == 17
+    for d_hex, q, element, exp_hex in rows:
+        e = int(element)
+        with np.errstate(over="ignore"):
+            out = oracle.dequant_q2_0(_q2_block(e, int(q)), np.array([[int(d_hex, 16)]], np.uint16))
+        assert out[0, e] == int(exp_hex, 16), (d_hex, q, e, hex(out[0, e]), exp_hex)
+        # every other element holds code 2: a zero weight with d's sign
+        others = np.delete(out[0], e)
+        assert np.all(others == (0x8000 if int(d_hex, 16) & 0x8000 else 0)), (d_hex, q, e)
+
+
+def test_dequant_q2_0_bit_order():
+    ones = WL.to_f16_bits(np.array([[1.0]]))
+    # byte 0x1b = 0b00_01_10_11: element 0 (lowest bits) code 3, element 1 code 2,
+    # element 2 code 1, element 3 (highest bits) code 0
+    out = np_f16(oracle.dequant_q2_0(np.full((1, 8), 0x1B, np.uint8), ones))
+    assert np.array_equal(out[0, :8], [1.0, 0.0, -1.0, -2.0, 1.0, 0.0, -1.0, -2.0])
+    # byte 0xe4 = 0b11_10_01_00: element kk has code kk % 4
+    out = np_f16(oracle.dequant_q2_0(np.full((1, 8), 0xE4, np.uint8), ones))
+    assert np.array_equal(out[0], np.arange(32) % 4 - 2.0)
+
+
+def test_dequant_q2_0_exhaustive_every_finite_scale_every_code():
+    """All 63488 finite f16 scales x all 4 codes in each of the four bit
+    positions of a byte, against numpy's correctly rounded float64 -> float16
+    cast of the exact product d * (q - 2) (overflow to inf included)."""
+    d_all = F16_ALL[((F16_ALL >> 10) & 0x1F) != 0x1F]
+    codes = np.array([(kk % 4 + kk // 4) % 4 for kk in range(32)], np.uint8)  # byte b holds codes b..b+3 rotated
+    byte = [int(codes[4 * b] | (codes[4 * b + 1] << 2) | (codes[4 * b + 2] << 4) | (codes[4 * b + 3] << 6))
+            for b in range(8)]
+    assert byte[:4] == [0xE4, 0x39, 0x4E, 0x93]
+    n = d_all.size
+    packed = np.broadcast_to(np.array(byte, np.uint8), (n, 8)).copy()
+    d = d_all[:, None].copy()
+    got = oracle.dequant_q2_0(packed, d)
+    exact = np_f16(d_all)[:, None] * (codes.astype(np.float64) - 2.0)[None, :]
+    with np.errstate(over="ignore"):
+        ref = exact.astype(np.float16).view(np.uint16)
+    bad = np.argwhere(got != ref)
+    assert bad.size == 0, bad[:5]
+
+
+def test_dequant_q2_0_uses_the_scale_of_each_32_block():
+    k = 128
+    packed = np.full((2, k // 4), 0xFF, np.uint8)         # every code 3: weight = d
+    d = WL.to_f16_bits(np.array([[1.0, 2.0, 4.0, 8.0], [0.5, 0.25, 0.125, 16.0]]))
+    out = np_f16(oracle.dequant_q2_0(packed, d))
+    assert np.array_equal(out, np.repeat(np_f16(d), 32, axis=1))
+
+
+def test_brute_force_exact_rationals_q2_0():
+    m, n, k = 3, 5, 64
+    A = WL.gen_matrix((m, k), "f16", ("normal", 1.0), 34)
+    qs, d = WL.gen_q2_0(n, k, 35, 36)
+    got = oracle.mm(A, "f16", qs, "q2_0", w_scales=d)
+    a = np_f16(A)
+    w = (np.repeat(np_f16(d), 32, axis=1) * (_unpack_q2(qs) - 2.0)).astype(np.float16).astype(np.float64)
+    for i in range(m):
+        for j in range(n):
+            exact = sum(Fraction(a[i, t]) * Fraction(w[j, t]) for t in range(k))
+            abs_sum = float(sum(abs(Fraction(a[i, t]) * Fraction(w[j, t])) for t in range(k)))
+            assert float(abs(Fraction(got[i, j]) - exact)) <= rounding_bound(k, abs_sum)
+
+
+def test_q2_0_generator_codes_and_scales():
+    qs, d = WL.gen_q2_0(8, 64, 43, 44)
+    assert qs.shape == (8, 16) and qs.dtype == np.uint8 and d.shape == (8, 2)
+    q = _unpack_q2(qs)
+    assert q.min() == 0 and q.max() == 3
     assert np.all((np_f16(d) >= 1e-3 - 1e-6) & (np_f16(d) <= 2e-3 + 1e-6))

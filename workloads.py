@@ -28,6 +28,9 @@ The workloads stand in for the pages' measurements:
                    4-bit block formats the Strata PR #109 page names, "Measured",
                    without a definition; the format is fixed by the oracle);
                    seed base 7.
+  q2_0_n512     -- the q8_0_n512 shape with a 2-bit Q2_0-style weight (the
+                   Strata PR #109 page, "Measured", names Q2_0 runs without a
+                   definition; the format is fixed by the oracle); seed base 8.
   moe_combine   -- Strata PR #109 ("What"): the MoE combine over the window's
                    tokens, each with the router's top-10 experts' output rows
                    (d = 5120, the router's k), routing weights, the shared
@@ -47,10 +50,10 @@ class Workload:
     n: int              # output columns (rows of the stored [n][k] weight)
     k: int              # reduction length
     a_kind: str         # "f16" | "bf16" | "f32"
-    w_kind: str         # "f16" | "bf16" | "q8_0" | "q4_0"
+    w_kind: str         # "f16" | "bf16" | "q8_0" | "q4_0" | "q2_0"
     c_kind: str         # "f32" | "f16"
     ms: Tuple[int, ...]  # row counts swept
-    w_dist: Tuple       # ("uniform", lo, hi) | ("normal", sd) | ("q8_0" or "q4_0", dlo, dhi)
+    w_dist: Tuple       # ("uniform", lo, hi) | ("normal", sd) | (block format, dlo, dhi)
     topk: Optional[int] = None
 
     @property
@@ -59,6 +62,8 @@ class Workload:
             return self.n * self.k + self.n * (self.k // 32) * 2
         if self.w_kind == "q4_0":
             return self.n * self.k // 2 + self.n * (self.k // 32) * 2
+        if self.w_kind == "q2_0":
+            return self.n * self.k // 4 + self.n * (self.k // 32) * 2
         return self.n * self.k * 2
 
 
@@ -83,6 +88,8 @@ WORKLOADS = {
                  ("normal", 0.02)),
         Workload("q4_0_n512", 7, 512, 2560, "f16", "q4_0", "f16", (1, 4, 16, 306, 2048),
                  ("q4_0", 1e-3, 2e-3)),
+        Workload("q2_0_n512", 8, 512, 2560, "f16", "q2_0", "f16", (1, 4, 16, 306, 2048),
+                 ("q2_0", 1e-3, 2e-3)),
     )
 }
 
@@ -135,14 +142,27 @@ def gen_q4_0(n: int, k: int, seed_q: int, seed_d: int, dlo=1e-3, dhi=2e-3):
     return qs, d
 
 
+def gen_q2_0(n: int, k: int, seed_q: int, seed_d: int, dlo=1e-3, dhi=2e-3):
+    """Q2_0-style weight: 2-bit codes ~U{0..3} packed four per byte (element kk
+    of a row in byte kk // 4 at bits 2 * (kk % 4)) [n][k/4] uint8, and f16
+    scales ~U(dlo, dhi) [n][k/32]."""
+    assert k % 32 == 0
+    q = np.random.default_rng(seed_q).integers(0, 4, size=(n, k), dtype=np.uint8)
+    qs = (q[:, 0::4] | (q[:, 1::4] << 2) | (q[:, 2::4] << 4) | (q[:, 3::4] << 6)).astype(np.uint8)
+    d = to_f16_bits(np.random.default_rng(seed_d).uniform(dlo, dhi, size=(n, k // 32)))
+    return qs, d
+
+
 def gen_w(wl: Workload, n: Optional[int] = None):
-    """The workload's stored weight [n][k]: uint16 bits, or (qs, d) for q8_0 and q4_0."""
+    """The workload's stored weight [n][k]: uint16 bits, or (qs, d) for the block formats."""
     n = wl.n if n is None else n
     c = wl.index
     if wl.w_kind == "q8_0":
         return gen_q8_0(n, wl.k, 1000 * c + 0, 1000 * c + 2, wl.w_dist[1], wl.w_dist[2])
     if wl.w_kind == "q4_0":
         return gen_q4_0(n, wl.k, 1000 * c + 0, 1000 * c + 2, wl.w_dist[1], wl.w_dist[2])
+    if wl.w_kind == "q2_0":
+        return gen_q2_0(n, wl.k, 1000 * c + 0, 1000 * c + 2, wl.w_dist[1], wl.w_dist[2])
     return to_bits(draw((n, wl.k), wl.w_dist, 1000 * c + 0), wl.w_kind)
 
 
