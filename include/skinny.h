@@ -14,7 +14,7 @@
  *   A  [m][lda]   f16 or bf16 rows ("tokens"), or fp32 rows that a bf16-weight
  *                 GEMV rounds to bf16 as it loads them; lda >= k
  *   W  [n][k]     the weight stored k-contiguous: stored row j is logical
- *                 column j of W[k,n].  f16, bf16, Q8_0 or Q4_0 (see below)
+ *                 column j of W[k,n].  f16, bf16, Q8_0, Q4_0 or Q2_0 (see below)
  *   C  [m][ldc]   f32, f16 or bf16; ldc >= n
  * Q8_0-style weights are two arrays: codes int8 [n][k] and scales f16
  * [n][k/32]; weight (j, kk) is RNE_f16(scale[j][kk/32] * code[j][kk]).
@@ -24,6 +24,11 @@
  * byte, element kk in byte kk/2, the low nibble for even kk and the high
  * nibble for odd kk -- and scales f16 [n][k/32]; weight (j, kk) is
  * RNE_f16(scale[j][kk/32] * (q - 8)).
+ * Q2_0-style weights (the 2-bit format the same page names, Q2_0 runs, also
+ * without a definition; fixed here as the 2-bit counterpart of Q4_0) are
+ * codes uint8 [n][k/4] -- four unsigned 2-bit codes q per byte, element kk
+ * in byte kk/4 at bits 2*(kk%4) and 2*(kk%4)+1 -- and scales f16 [n][k/32];
+ * weight (j, kk) is RNE_f16(scale[j][kk/32] * (q - 2)).
  *
  * Paths: m <= 16 runs a multi-row GEMV (every W byte read once for all rows);
  * m >= 17 runs an f16/bf16 MFMA GEMM with a tile chosen by the plan.
@@ -34,9 +39,9 @@
  *   - tile invariance and M invariance in the GEMM regime: every tile, and
  *     every m >= 17, gives the same bits for the same A row (opus r35 track A,
  *     section 2 and "verification": all tiles memcmp-equal);
- *   - the fused Q8_0 (Q4_0) path equals skinny_dequant_q8_0_run
- *     (skinny_dequant_q4_0_run) followed by the f16 path on the dequantised
- *     weight.
+ *   - the fused Q8_0 (Q4_0, Q2_0) path equals skinny_dequant_q8_0_run
+ *     (skinny_dequant_q4_0_run, skinny_dequant_q2_0_run) followed by the f16
+ *     path on the dequantised weight.
  * Across the two regimes results agree to rounding only.
  *
  * Memory and threading:
@@ -76,7 +81,7 @@ typedef enum skinny_status {
   SKINNY_ERR_INVALID_ARG = 1, /* null pointer, bad struct_size, m/n/k/topk out of range */
   SKINNY_ERR_UNSUPPORTED = 2, /* dtype combination or flag the library does not implement */
   SKINNY_ERR_ALIGNMENT = 3,   /* pointer not 16-byte aligned or lda not a multiple of 8 */
-  SKINNY_ERR_SHAPE = 4,       /* k not a multiple of 8 (32 for Q8_0, Q4_0), stride < row length, a
+  SKINNY_ERR_SHAPE = 4,       /* k not a multiple of 8 (32 for the block formats), stride < row length, a
                                  size past a stated limit (a run: a GEMV of more than about
                                  2^31 waves, k/512 x n) */
   SKINNY_ERR_HIP = 5,         /* the HIP runtime reported an error (device query or launch) */
@@ -90,7 +95,8 @@ typedef enum skinny_dtype {
   SKINNY_BF16 = 2,
   SKINNY_F32 = 3,
   SKINNY_Q8_0 = 4,
-  SKINNY_Q4_0 = 5
+  SKINNY_Q4_0 = 5,
+  SKINNY_Q2_0 = 6
 } skinny_dtype;
 
 /* desc.flags */
@@ -131,13 +137,13 @@ typedef enum skinny_dtype {
  *                rounds to bf16 (nearest even) as it loads them -- the
  *                window-row cast below fused into the GEMV, so C equals the
  *                result for the cast rows bit for bit, in one launch
- *   w_dtype      SKINNY_F16 / SKINNY_Q8_0 / SKINNY_Q4_0 (with f16 A) or SKINNY_BF16 (with bf16
- *                or f32 A)
+ *   w_dtype      SKINNY_F16 / SKINNY_Q8_0 / SKINNY_Q4_0 / SKINNY_Q2_0 (with f16 A) or
+ *                SKINNY_BF16 (with bf16 or f32 A)
  *   c_dtype      SKINNY_F32, SKINNY_F16 or SKINNY_BF16 (rounded to nearest even)
  *   max_m        largest m any run will pass (>= 1)
  *   n, k         output columns and reduction length (n >= 1; k >= 8, k % 8 == 0,
- *                k % 32 == 0 for Q8_0 and Q4_0; k and lda <= 2^20, k >= 64 for
- *                Q8_0 and Q4_0
+ *                k % 32 == 0 for Q8_0, Q4_0 and Q2_0; k and lda <= 2^20, k >= 64
+ *                for those three
  *                and max_m * n <= 2^50 when the plan may use the GEMM, i.e.
  *                max_m > 16 or SKINNY_FORCE_GEMM)
  *   lda, ldc     row strides of A and C in elements; 0 means dense (k and n);
@@ -198,7 +204,7 @@ SKINNY_API skinny_status skinny_mm_workspace_size(const skinny_plan* plan, size_
 /* C[0:m, 0:n] = A[0:m, :] . W  (nx_batchscale_kat: the product with fp32
  * accumulation; Strata PR #109 "What": every W byte read once for the window).
  *   m          1 <= m <= max_m
- *   A, W, C    device pointers (16-byte aligned); w_scales: Q8_0 / Q4_0 scales
+ *   A, W, C    device pointers (16-byte aligned); w_scales: Q8_0 / Q4_0 / Q2_0 scales
  *              f16 [n][k/32] (16-byte aligned), else must be NULL
  *   workspace  zero-initialised device scratch of >= skinny_mm_workspace_size
  *              bytes (may be NULL when that size is 0)
@@ -253,6 +259,15 @@ SKINNY_API skinny_status gemv_topk_run(const skinny_plan* plan, int64_t m, const
                             const void* w_scales, float* logits, int32_t* topk_idx,
                             float* topk_val, int32_t topk, void* workspace,
                             size_t workspace_bytes, void* stream);
+
+/* Standalone Q2_0-style dequant, the 2-bit format above:
+ * out[j][kk] = RNE_f16(f32(d[j][kk/32]) * (q - 2)), q the 2-bit code of
+ * element kk (bits 2*(kk%4) and 2*(kk%4)+1 of qs[j][kk/4]); the same
+ * arithmetic the fused paths use.
+ *   n >= 1, k >= 32 and k % 32 == 0; qs uint8 [n][k/4], d f16 [n][k/32],
+ *   out f16 [n][k]; all device pointers, 16-byte aligned. */
+SKINNY_API skinny_status skinny_dequant_q2_0_run(int64_t n, int64_t k, const void* qs, const void* d,
+                                      void* out, void* stream);
 
 /* Standalone Q4_0-style dequant, the 4-bit format above:
  * out[j][kk] = RNE_f16(f32(d[j][kk/32]) * (q - 8)), q the 4-bit code of

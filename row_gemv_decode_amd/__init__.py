@@ -7,6 +7,7 @@ fallback -- importing this package fails loudly when the library is missing.
 
     C = mm(A, W)                       # f16/bf16 rows x [n][k] weight
     C = mm(A, (qs, d))                 # Q8_0-style weight: int8 codes, f16 scales
+                                       # (Q4_0 / Q2_0: packed uint8 codes)
     logits, idx, val = gemv_topk(A, W, topk=10)
     w16 = dequant_q8_0(qs, d)
 
@@ -34,7 +35,9 @@ _lib = ctypes.CDLL(LIB_PATH)
 
 # --- C ABI mirror -----------------------------------------------------------
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_ALIGNMENT, ERR_SHAPE, ERR_HIP, ERR_WORKSPACE, ERR_SCRATCH = range(8)
-F16, BF16, F32, Q8_0, Q4_0 = 1, 2, 3, 4, 5
+F16, BF16, F32, Q8_0, Q4_0, Q2_0 = 1, 2, 3, 4, 5, 6
+# stored codes per byte of the block-quantised weight kinds
+CODES_PER_BYTE = {Q8_0: 1, Q4_0: 2, Q2_0: 4}
 FORCE_GEMV, FORCE_GEMM, GEMM_SPLIT_LAUNCH, GEMM_ONE_LAUNCH = 0x1, 0x2, 0x4, 0x8
 EPILOGUE_SIGMOID = 0x10
 GEMM_FOLD_LAUNCH = 0x20
@@ -43,7 +46,8 @@ TOPK_MAX = 32
 
 EXPORTS = (
     "skinny_mm_plan", "skinny_mm_plan_destroy", "skinny_mm_workspace_size", "skinny_mm_run",
-    "gemv_topk_run", "skinny_dequant_q8_0_run", "skinny_dequant_q4_0_run", "skinny_mm_plan_info",
+    "gemv_topk_run", "skinny_dequant_q8_0_run", "skinny_dequant_q4_0_run", "skinny_dequant_q2_0_run",
+    "skinny_mm_plan_info",
     "skinny_gemm_tile_count",
     "skinny_gemm_tile_name", "skinny_status_string", "skinny_abi_version", "skinny_cast_f32_bf16_run",
     "skinny_moe_combine_run", "skinny_mm_run_static",
@@ -86,6 +90,8 @@ _lib.skinny_dequant_q8_0_run.argtypes = [_i64, _i64, _vp, _vp, _vp, _vp]
 _lib.skinny_dequant_q8_0_run.restype = ctypes.c_int
 _lib.skinny_dequant_q4_0_run.argtypes = [_i64, _i64, _vp, _vp, _vp, _vp]
 _lib.skinny_dequant_q4_0_run.restype = ctypes.c_int
+_lib.skinny_dequant_q2_0_run.argtypes = [_i64, _i64, _vp, _vp, _vp, _vp]
+_lib.skinny_dequant_q2_0_run.restype = ctypes.c_int
 _lib.skinny_cast_f32_bf16_run.argtypes = [_i64, _vp, _vp, _vp]
 _lib.skinny_cast_f32_bf16_run.restype = ctypes.c_int
 _lib.skinny_moe_combine_run.argtypes = [_i64, _i64, _i32, _vp, _vp, _vp, _vp, _i32, _vp, _i32, _vp]
@@ -262,15 +268,26 @@ def _dense(where, **tensors):
             raise ValueError(f"{where}: {name} must be contiguous (pass a Plan with lda/ldc for strided rows)")
 
 
-def _weight_kind(W):
+def _weight_kind(W, k):
+    """(dtype code, weight or codes, scales or None) of a weight for reduction
+    length k.  Packed uint8 codes are Q4_0 when a row holds k/2 bytes and
+    Q2_0 when it holds k/4."""
     torch = _torch()
     if isinstance(W, tuple):
         qs, d = W
-        if qs.dtype not in (torch.int8, torch.uint8) or d.dtype != torch.float16:
-            raise TypeError("a block-quantised weight is (int8 codes [n][k] (Q8_0) or uint8 packed "
-                            "4-bit codes [n][k/2] (Q4_0), float16 scales [n][k/32])")
+        if qs.dtype not in (torch.int8, torch.uint8) or d.dtype != torch.float16 or qs.dim() != 2:
+            raise TypeError("a block-quantised weight is (int8 codes [n][k] (Q8_0), or uint8 packed "
+                            "4-bit codes [n][k/2] (Q4_0) or 2-bit codes [n][k/4] (Q2_0), float16 "
+                            "scales [n][k/32])")
+        if qs.dtype == torch.int8:
+            kind = Q8_0
+        else:
+            kind = Q4_0 if 2 * qs.shape[1] == k else Q2_0
+        if qs.shape[1] * CODES_PER_BYTE[kind] != k or tuple(d.shape) != (qs.shape[0], k // 32):
+            raise ValueError(f"block-quantised weight: codes {tuple(qs.shape)} and scales {tuple(d.shape)} "
+                             f"do not fit k = {k}")
         _dense("block-quantised weight", codes=qs, scales=d)
-        return (Q8_0 if qs.dtype == torch.int8 else Q4_0), qs, d
+        return kind, qs, d
     _dense("weight", W=W)
     return _dtype_code(W.dtype, "W"), W, None
 
@@ -287,10 +304,11 @@ def get_plan(n, k, max_m, a_dtype, w_dtype, c_dtype, flags=0, tile_id=-1) -> Pla
 def mm(A, W, out=None, out_dtype=None, flags=0, tile_id=-1, max_m=None, stream=None):
     """C = A . W^T_storage for A [m][k] (f16/bf16, contiguous rows) and W [n][k]
     (same dtype), or W = (qs int8 [n][k], d f16 [n][k/32]) for Q8_0, or
-    W = (qs uint8 [n][k/2] packed 4-bit codes, d f16 [n][k/32]) for Q4_0."""
+    W = (qs uint8 [n][k/2] packed 4-bit codes, d f16 [n][k/32]) for Q4_0, or
+    W = (qs uint8 [n][k/4] packed 2-bit codes, d f16 [n][k/32]) for Q2_0."""
     torch = _torch()
-    wk, Wt, scales = _weight_kind(W)
     m, k = A.shape
+    wk, Wt, scales = _weight_kind(W, k)
     n = Wt.shape[0]
     if out is None:
         out = torch.empty((m, n), dtype=out_dtype or torch.float32, device=A.device)
@@ -304,8 +322,8 @@ def mm(A, W, out=None, out_dtype=None, flags=0, tile_id=-1, max_m=None, stream=N
 def gemv_topk(A, W, topk=10, flags=0, max_m=None, stream=None):
     """(logits f32 [m][n], idx int32 [m][topk], val f32 [m][topk]) of the router step."""
     torch = _torch()
-    wk, Wt, scales = _weight_kind(W)
     m, k = A.shape
+    wk, Wt, scales = _weight_kind(W, k)
     n = Wt.shape[0]
     logits = torch.empty((m, n), dtype=torch.float32, device=A.device)
     idx = torch.empty((m, topk), dtype=torch.int32, device=A.device)
@@ -314,6 +332,18 @@ def gemv_topk(A, W, topk=10, flags=0, max_m=None, stream=None):
     plan = get_plan(n, k, max_m or m, _dtype_code(A.dtype, "A"), wk, F32, flags)
     plan.run_topk(m, A, Wt, logits, idx, val, topk, scales=scales, stream=stream)
     return logits, idx, val
+
+
+def dequant_q2_0(qs, d, out=None, stream=None):
+    """f16 [n][k] weight of a Q2_0-style (packed codes uint8 [n][k/4], scales) pair."""
+    torch = _torch()
+    n, kq = qs.shape
+    if out is None:
+        out = torch.empty((n, 4 * kq), dtype=torch.float16, device=qs.device)
+    _dense("dequant_q2_0", qs=qs, d=d, out=out)
+    _check(_lib.skinny_dequant_q2_0_run(n, 4 * kq, _ptr(qs), _ptr(d), _ptr(out), _stream(stream)),
+           "skinny_dequant_q2_0_run")
+    return out
 
 
 def dequant_q4_0(qs, d, out=None, stream=None):

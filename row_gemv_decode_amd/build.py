@@ -22,11 +22,11 @@ INSTANCES = [
      [f"-DGEMV_WK={wk}", f"-DGEMV_AK={a}", f"-DGEMV_T={t}",
       f"-DGEMV_LAUNCHER=launch_gemv_{w}{'_a32' if a == 'kAF32' else ''}_t{t}"])
     for w, wk, a in (("f16", "WK_F16", "kA16"), ("bf16", "WK_BF16", "kA16"), ("q8", "WK_Q8", "kA16"),
-                     ("q4", "WK_Q4", "kA16"), ("bf16", "WK_BF16", "kAF32"))
+                     ("q4", "WK_Q4", "kA16"), ("q2", "WK_Q2", "kA16"), ("bf16", "WK_BF16", "kAF32"))
     for t in (1, 2)
 ] + [
     ("gemm_inst.hip", f"gemm_{w}", [f"-DGEMM_WK={wk}", f"-DGEMM_LAUNCHER=launch_gemm_{w}"])
-    for w, wk in (("f16", "WK_F16"), ("bf16", "WK_BF16"), ("q8", "WK_Q8"), ("q4", "WK_Q4"))
+    for w, wk in (("f16", "WK_F16"), ("bf16", "WK_BF16"), ("q8", "WK_Q8"), ("q4", "WK_Q4"), ("q2", "WK_Q2"))
 ]
 
 

@@ -49,10 +49,14 @@ bool log_enabled() {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 int to_wkind(int dt) {
-  return dt == SKINNY_F16 ? WK_F16 : dt == SKINNY_BF16 ? WK_BF16 : dt == SKINNY_Q8_0 ? WK_Q8 : WK_Q4;
+  return dt == SKINNY_F16    ? WK_F16
+         : dt == SKINNY_BF16  ? WK_BF16
+         : dt == SKINNY_Q8_0  ? WK_Q8
+         : dt == SKINNY_Q4_0  ? WK_Q4
+                              : WK_Q2;
 }
 
-bool block_quantised(int dt) { return dt == SKINNY_Q8_0 || dt == SKINNY_Q4_0; }
+bool block_quantised(int dt) { return dt == SKINNY_Q8_0 || dt == SKINNY_Q4_0 || dt == SKINNY_Q2_0; }
 int to_ckind(int dt) { return dt == SKINNY_F32 ? CK_F32 : dt == SKINNY_F16 ? CK_F16 : CK_BF16; }
 
 // k split of the GEMV: each wave covers 64*T chunks of eight elements; T in
@@ -180,8 +184,9 @@ double tile_estimate(const skinny_plan* p, int id, int64_t m, int64_t copies, in
     rounds += (busiest >= 2 ? sigma : 1.0) * (1.0 + tc.a * (double)nb / (double)slots);
   }
   // block-quantised weights are dequantised per fragment: about 1.65x the
-  // f16 time per k-tile on MI355X (measured for Q8_0; Q4_0 taken the same)
-  const double kind = (p->w_kind == WK_Q8 || p->w_kind == WK_Q4) ? 1.65 : 1.0;
+  // f16 time per k-tile on MI355X (measured for Q8_0; Q4_0 and Q2_0 taken
+  // the same)
+  const double kind = (p->w_kind == WK_Q8 || p->w_kind == WK_Q4 || p->w_kind == WK_Q2) ? 1.65 : 1.0;
   return (double)ktiles * tc.t * kind * rounds;
 }
 
@@ -538,7 +543,7 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   if (d.a_dtype == SKINNY_F32 &&
       (d.w_dtype != SKINNY_BF16 || d.max_m > kGemvMaxM || (d.flags & SKINNY_FORCE_GEMM)))
     return SKINNY_ERR_UNSUPPORTED;
-  if (d.a_dtype == SKINNY_F16 && d.w_dtype != SKINNY_F16 && d.w_dtype != SKINNY_Q8_0 && d.w_dtype != SKINNY_Q4_0)
+  if (d.a_dtype == SKINNY_F16 && d.w_dtype != SKINNY_F16 && !block_quantised(d.w_dtype))
     return SKINNY_ERR_UNSUPPORTED;
   if (d.a_dtype == SKINNY_BF16 && d.w_dtype != SKINNY_BF16) return SKINNY_ERR_UNSUPPORTED;
   if (d.c_dtype != SKINNY_F32 && d.c_dtype != SKINNY_F16 && d.c_dtype != SKINNY_BF16)
@@ -575,7 +580,7 @@ skinny_status skinny_mm_plan(const skinny_mm_desc* desc, skinny_plan** out_plan)
   // the GEMM's k-chunk partials hold up to 16 x max_m x n floats: keep every
   // index and byte count far inside 64 bits
   if (may_gemm && d.max_m > (1LL << 50) / d.n) return SKINNY_ERR_SHAPE;
-  // the GEMM fetches a k-tile's two Q8_0 scales of a row as one 4-byte word,
+  // the GEMM fetches a k-tile's two block scales of a row as one 4-byte word,
   // which needs at least two scales per row (k >= 64)
   if (may_gemm && block_quantised(d.w_dtype) && d.k < 64) return SKINNY_ERR_SHAPE;
   if (d.num_cus < 0) return SKINNY_ERR_INVALID_ARG;
@@ -691,6 +696,16 @@ skinny_status gemv_topk_run(const skinny_plan* plan, int64_t m, const void* A, c
   if (!aligned16(topk_idx) || !aligned16(topk_val)) return SKINNY_ERR_ALIGNMENT;
   return enqueue_mm(plan, m, A, W, w_scales, logits, plan->d.ldc, CK_F32, caller_scratch(plan, workspace),
                     topk_idx, topk_val, topk, (hipStream_t)stream);
+}
+
+skinny_status skinny_dequant_q2_0_run(int64_t n, int64_t k, const void* qs, const void* d,
+                                      void* out, void* stream) {
+  if (qs == nullptr || d == nullptr || out == nullptr) return SKINNY_ERR_INVALID_ARG;
+  if (n < 1 || k < 32 || n > (1LL << 31) - 1 || k > (1LL << 31) - 1) return SKINNY_ERR_INVALID_ARG;
+  if (k % 32 != 0) return SKINNY_ERR_SHAPE;
+  if (!aligned16(qs) || !aligned16(d) || !aligned16(out)) return SKINNY_ERR_ALIGNMENT;
+  return hip_status(launch_dequant_q2_0(n, k, (const uint8_t*)qs, (const uint16_t*)d, (uint16_t*)out,
+                                        (hipStream_t)stream));
 }
 
 skinny_status skinny_dequant_q4_0_run(int64_t n, int64_t k, const void* qs, const void* d,

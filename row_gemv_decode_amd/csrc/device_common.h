@@ -120,6 +120,34 @@ __device__ __forceinline__ u32x4 q4_dequant8(uint32_t codes, _Float16 d) {
   return out;
 }
 
+// ---------------------------------------------------------------------------
+// Q2_0-style dequant of eight consecutive 2-bit codes of one 32-block, given
+// as the low 16 bits of `codes` (code i at bits 2i and 2i + 1).  The pages
+// name a 2-bit block format (the Strata PR #109 page, "Measured": Q2_0 runs)
+// without defining one; the format here: unsigned codes q in 0..3, four per
+// byte (element 4b + i at bits 2i of byte b), one f16 scale d per 32-block,
+// weight RNE_f16(d * (q - 2)).  As for Q4_0, a code reaches f16 exactly in
+// the low bits of 0x6400 (1024 + q), subtracting 1026 leaves q - 2 exactly,
+// and one IEEE f16 multiply rounds the exact product once.  With
+// s = codes | codes << 14, bits 4p .. 4p + 1 of s hold code 2p and bits
+// 4p + 16 .. 4p + 17 hold code 2p + 1, so one shift and one and-or place
+// each pair of codes in the two halves of a dword.  Every path (standalone,
+// fused GEMV, fused GEMM) calls this.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ u32x4 q2_dequant8(uint32_t codes, _Float16 d) {
+  const uint32_t c = codes & 0xFFFFu;
+  const uint32_t s = c | (c << 14);
+  const h2_t d2 = {d, d};
+  const h2_t bias = {(_Float16)1026.0f, (_Float16)1026.0f};
+  u32x4 out;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const uint32_t pair = ((s >> (4 * p)) & 0x00030003u) | 0x64006400u;
+    out[p] = h2_bits(d2 * (as_h2(pair) - bias));
+  }
+  return out;
+}
+
 // Device-coherent accesses for data handed from one workgroup to another in
 // the same launch.  Relaxed agent-scope atomic stores/loads compile to plain
 // global stores/loads with the sc1 (device scope) bit: they are coherent

@@ -10,6 +10,7 @@ hipError_t launch_gemm_f16(int, const GemmArgs&, int, int, int64_t, int, hipStre
 hipError_t launch_gemm_bf16(int, const GemmArgs&, int, int, int64_t, int, hipStream_t);
 hipError_t launch_gemm_q8(int, const GemmArgs&, int, int, int64_t, int, hipStream_t);
 hipError_t launch_gemm_q4(int, const GemmArgs&, int, int, int64_t, int, hipStream_t);
+hipError_t launch_gemm_q2(int, const GemmArgs&, int, int, int64_t, int, hipStream_t);
 
 namespace {
 
@@ -57,7 +58,7 @@ bool gemm_tile_chunkable(int id) {
 
 hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind, int shape,
                        hipStream_t stream) {
-  if (tile_id < 0 || tile_id >= kTileCount || w_kind < 0 || w_kind > 3 || c_kind < 0 || c_kind > 2 ||
+  if (tile_id < 0 || tile_id >= kTileCount || w_kind < WK_F16 || w_kind > WK_Q2 || c_kind < 0 || c_kind > 2 ||
       shape < kGemmPlain || shape > kGemmFold)
     return hipErrorInvalidValue;
   const GemmTileInfo& t = tile_infos()[tile_id];
@@ -81,6 +82,7 @@ hipError_t launch_gemm(int tile_id, const GemmArgs& args, int w_kind, int c_kind
     case WK_BF16: return launch_gemm_bf16(tile_id, args, c_kind, shape, blocks, threads, stream);
     case WK_Q8: return launch_gemm_q8(tile_id, args, c_kind, shape, blocks, threads, stream);
     case WK_Q4: return launch_gemm_q4(tile_id, args, c_kind, shape, blocks, threads, stream);
+    case WK_Q2: return launch_gemm_q2(tile_id, args, c_kind, shape, blocks, threads, stream);
   }
   return hipErrorInvalidValue;
 }

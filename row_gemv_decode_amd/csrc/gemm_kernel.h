@@ -173,6 +173,10 @@ __device__ __forceinline__ int q8_swz(int r) { return (r >> 2) & 3; }
 // same two scales per row as Q8_0.
 __device__ __forceinline__ int q4_swz(int r) { return (r >> 3) & 1; }
 
+// Q2_0 weights: a row's k-tile is 64 codes in one 16-byte slot (chunk c in
+// bits 16 (c & 1) .. 16 (c & 1) + 15 of its dword c >> 1) plus the same two
+// scales per row; one load instruction of a wave fills 64 rows.
+
 // four adjacent outputs in one store (8 bytes of f16 / bf16, 16 of fp32),
 // each rounded exactly as store_out rounds it; idx is a multiple of 4
 template <int CK>
@@ -213,10 +217,11 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
   static_assert(!(CH && FD), "a launch folds chunk sums in-block or across blocks, not both");
   constexpr bool Q8 = WK == WK_Q8;
   constexpr bool Q4 = WK == WK_Q4;
-  constexpr bool QB = Q8 || Q4;  // block-quantised: codes + per-32 scales
+  constexpr bool Q2 = WK == WK_Q2;
+  constexpr bool QB = Q8 || Q4 || Q2;  // block-quantised: codes + per-32 scales
   // block-quantised code rows: bytes per row per k-tile, lanes per row in one
   // 16-byte-per-lane load, rows per load instruction
-  constexpr int kBpr = Q4 ? 32 : 64;
+  constexpr int kBpr = Q2 ? 16 : Q4 ? 32 : 64;
   constexpr int kLpr = kBpr / 16;
   constexpr int kRpl = 64 / kLpr;
   constexpr int NW = WM * WN;
@@ -226,9 +231,10 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
   constexpr int FN = WTN / 32;
   static_assert(WTM % 32 == 0 && WTN % 32 == 0, "wave tile must be whole 32x32 blocks");
   // one load instruction of one wave fills 8 rows of 16-bit data (64 lanes x
-  // 16 bytes), 16 rows of Q8_0 codes, or the scale words of 64 rows; a Q8_0
-  // stage rounds its code and scale rows up to whole instructions (rows past
-  // the tile are loaded and never read)
+  // 16 bytes), 16 rows of Q8_0 codes (32 of Q4_0, 64 of Q2_0), or the scale
+  // words of 64 rows; a block-quantised stage rounds its code and scale rows
+  // up to whole instructions (rows past the tile lie outside the weight's
+  // buffer resource, read as 0 and are never used)
   static_assert(TM % (8 * NW) == 0 && (QB || TN % (8 * NW) == 0), "tile rows must split evenly over the waves");
   constexpr int A_ITERS = TM / (8 * NW);
   constexpr int B_ITERS = QB ? (TN + kRpl * NW - 1) / (kRpl * NW) : TN / (8 * NW);
@@ -315,7 +321,7 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
   for (int i = 0; i < B_ITERS; ++i) {
     if constexpr (QB) {
       const int r = kRpl * (i * NW + wid) + lane / kLpr;
-      const int slot = (lane % kLpr) ^ (Q4 ? q4_swz(r) : q8_swz(r));
+      const int slot = Q2 ? 0 : (lane % kLpr) ^ (Q4 ? q4_swz(r) : q8_swz(r));
       voff_b[i] = (int)((int64_t)r * wrow + slot * 16);
     } else {
       const int r = 8 * (i * NW + wid) + lr;
@@ -376,6 +382,12 @@ __global__ __launch_bounds__(64 * WM * WN) void gemm_lds_kernel(GemmArgs g) {
       const uint32_t sc = sS[st][row];
       const int hi = (c >> 2) | (int)sh;
       return q4_dequant8(q, half_from_bits((uint16_t)(hi ? (sc >> 16) : sc)));
+    } else if constexpr (Q2) {
+      const uint32_t* codes = reinterpret_cast<const uint32_t*>(&sB[st][0]);
+      const uint32_t w = codes[row * 4 + (c >> 1)];
+      const uint32_t sc = sS[st][row];
+      const int hi = (c >> 2) | (int)sh;
+      return q2_dequant8((c & 1) ? (w >> 16) : w, half_from_bits((uint16_t)(hi ? (sc >> 16) : sc)));
     } else {
       return sB[st][row * kCPR + (c ^ swz(row))];
     }

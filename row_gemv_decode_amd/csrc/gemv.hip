@@ -1,4 +1,4 @@
-// gemv.hip -- the per-row top-k launch, the standalone Q8_0 dequant and the
+// gemv.hip -- the per-row top-k launch, the standalone block dequants and the
 // GEMV launch dispatch, for gfx950 (MI355X).  The GEMV kernel itself is in
 // gemv_kernel.h.
 #include "gemv_kernel.h"
@@ -10,7 +10,7 @@ namespace skinny {
 #define SKINNY_GEMV_LAUNCHERS(X) \
   X(launch_gemv_f16_t1) X(launch_gemv_f16_t2) X(launch_gemv_bf16_t1) X(launch_gemv_bf16_t2) \
   X(launch_gemv_q8_t1) X(launch_gemv_q8_t2) X(launch_gemv_q4_t1) X(launch_gemv_q4_t2) \
-  X(launch_gemv_bf16_a32_t1) X(launch_gemv_bf16_a32_t2)
+  X(launch_gemv_q2_t1) X(launch_gemv_q2_t2) X(launch_gemv_bf16_a32_t1) X(launch_gemv_bf16_a32_t2)
 #define SKINNY_DECLARE_LAUNCHER(name) hipError_t name(const GemvArgs&, int, int, int, hipStream_t);
 SKINNY_GEMV_LAUNCHERS(SKINNY_DECLARE_LAUNCHER)
 #undef SKINNY_DECLARE_LAUNCHER
@@ -289,6 +289,23 @@ __global__ __launch_bounds__(256) void dequant_q4_0_kernel(const uint8_t* __rest
   }
 }
 
+// eight weights per thread and step: two bytes of packed codes
+__global__ __launch_bounds__(256) void dequant_q2_0_kernel(const uint8_t* __restrict__ qs,
+                                                           const uint16_t* __restrict__ d,
+                                                           uint16_t* __restrict__ out, int64_t n,
+                                                           int64_t k) {
+  const int64_t chunks_per_row = k >> 3;
+  const int64_t total = n * chunks_per_row;
+  for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < total;
+       e += (int64_t)gridDim.x * 256) {
+    const int64_t j = e / chunks_per_row;
+    const int64_t c = e - j * chunks_per_row;
+    const uint32_t codes = *(const uint16_t*)(qs + j * (k >> 2) + c * 2);
+    const _Float16 scale = half_from_bits(d[j * (k >> 5) + (c >> 2)]);
+    *(u32x4*)(out + j * k + c * 8) = q2_dequant8(codes, scale);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_kind,
@@ -313,6 +330,9 @@ hipError_t launch_gemv(const GemvArgs& args, int m, int T, int w_kind, int out_k
     case WK_Q4:
       return t1 ? launch_gemv_q4_t1(args, m, out_kind, waves_per_block, stream)
                 : launch_gemv_q4_t2(args, m, out_kind, waves_per_block, stream);
+    case WK_Q2:
+      return t1 ? launch_gemv_q2_t1(args, m, out_kind, waves_per_block, stream)
+                : launch_gemv_q2_t2(args, m, out_kind, waves_per_block, stream);
   }
   return hipErrorInvalidValue;
 }
@@ -346,6 +366,16 @@ hipError_t launch_dequant_q4_0(int64_t n, int64_t k, const uint8_t* qs, const ui
   int64_t blocks = (total + 255) / 256;
   if (blocks > 65536) blocks = 65536;
   hipLaunchKernelGGL(dequant_q4_0_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, qs, d, out,
+                     n, k);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_q2_0(int64_t n, int64_t k, const uint8_t* qs, const uint16_t* d,
+                               uint16_t* out, hipStream_t stream) {
+  const int64_t total = n * (k >> 3);
+  int64_t blocks = (total + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(dequant_q2_0_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, qs, d, out,
                      n, k);
   return hipGetLastError();
 }

@@ -175,7 +175,7 @@ __device__ __forceinline__ float dot8(const u32x4& a, const u32x4& w, float acc)
 }
 
 // Raw weight registers of one (column, chunk): 16 bytes of f16/bf16, or the
-// codes (8 bytes for Q8_0, 4 for Q4_0) plus the block's scale.
+// codes (8 bytes for Q8_0, 4 for Q4_0, 2 for Q2_0) plus the block's scale.
 template <int WK>
 struct WChunk {
   u32x4 v;
@@ -188,6 +188,11 @@ struct WChunk<WK_Q8> {
 template <>
 struct WChunk<WK_Q4> {
   uint32_t codes;  // eight 4-bit codes
+  uint16_t scale;
+};
+template <>
+struct WChunk<WK_Q2> {
+  uint16_t codes;  // eight 2-bit codes
   uint16_t scale;
 };
 
@@ -215,6 +220,10 @@ __device__ __forceinline__ void load_w(WChunk<WK>& dst, const GemvArgs& g, int64
     const uint8_t* wq = (const uint8_t*)g.W;
     dst.codes = load_stream<NT>((const uint32_t*)(wq + j * (g.k >> 1) + (int64_t)chunk * 4));
     dst.scale = load_stream<NT>(g.scales + j * (g.k >> 5) + (chunk >> 2));
+  } else if constexpr (WK == WK_Q2) {
+    const uint8_t* wq = (const uint8_t*)g.W;
+    dst.codes = load_stream<NT>((const uint16_t*)(wq + j * (g.k >> 2) + (int64_t)chunk * 2));
+    dst.scale = load_stream<NT>(g.scales + j * (g.k >> 5) + (chunk >> 2));
   } else {
     const uint16_t* w16 = (const uint16_t*)g.W;
     dst.v = load_stream<NT>((const u32x4*)(w16 + j * g.k + (int64_t)chunk * 8));
@@ -226,7 +235,7 @@ __device__ __forceinline__ void zero_w(WChunk<WK>& dst) {
   if constexpr (WK == WK_Q8) {
     dst.codes = u32x2{0u, 0u};
     dst.scale = 0;
-  } else if constexpr (WK == WK_Q4) {
+  } else if constexpr (WK == WK_Q4 || WK == WK_Q2) {
     dst.codes = 0u;
     dst.scale = 0;
   } else {
@@ -240,6 +249,8 @@ __device__ __forceinline__ u32x4 w_as_halves(const WChunk<WK>& w) {
     return q8_dequant8(w.codes, half_from_bits(w.scale));
   } else if constexpr (WK == WK_Q4) {
     return q4_dequant8(w.codes, half_from_bits(w.scale));
+  } else if constexpr (WK == WK_Q2) {
+    return q2_dequant8(w.codes, half_from_bits(w.scale));
   } else {
     return w.v;
   }

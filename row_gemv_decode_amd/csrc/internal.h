@@ -9,7 +9,7 @@
 namespace skinny {
 
 // weight storage kinds and output kinds (kernel template parameters)
-enum WKind : int { WK_F16 = 0, WK_BF16 = 1, WK_Q8 = 2, WK_Q4 = 3 };
+enum WKind : int { WK_F16 = 0, WK_BF16 = 1, WK_Q8 = 2, WK_Q4 = 3, WK_Q2 = 4 };
 enum CKind : int { CK_F32 = 0, CK_F16 = 1, CK_BF16 = 2 };
 
 // ---------------------------------------------------------------------------
@@ -29,8 +29,9 @@ constexpr int kGemvBlockSplitMax = 8;
 struct GemvArgs {
   const void* A;           // [m][lda] f16/bf16 bits, or fp32 (a_kind = kAF32)
   int64_t lda;
-  const void* W;           // [n][k] f16/bf16 bits, int8 codes (Q8_0) or packed 4-bit codes [n][k/2] (Q4_0)
-  const uint16_t* scales;  // Q8_0 / Q4_0 scales [n][k/32] (f16 bits), else null
+  const void* W;           // [n][k] f16/bf16 bits, int8 codes (Q8_0), or packed 4-bit codes
+                           // [n][k/2] (Q4_0) or 2-bit codes [n][k/4] (Q2_0)
+  const uint16_t* scales;  // block formats: scales [n][k/32] (f16 bits), else null
   int64_t n;
   int64_t k;
   int32_t nchunks;          // k / 8
@@ -71,6 +72,8 @@ hipError_t launch_dequant_q8_0(int64_t n, int64_t k, const int8_t* qs, const uin
                                uint16_t* out, hipStream_t stream);
 hipError_t launch_dequant_q4_0(int64_t n, int64_t k, const uint8_t* qs, const uint16_t* d,
                                uint16_t* out, hipStream_t stream);
+hipError_t launch_dequant_q2_0(int64_t n, int64_t k, const uint8_t* qs, const uint16_t* d,
+                               uint16_t* out, hipStream_t stream);
 
 // MoE combine: out[t][c] = sum_i w[t][i] * rows[t][i][c] (+ gate[t] * shared[t][c])
 struct CombineArgs {
@@ -100,8 +103,9 @@ constexpr int64_t kGemmMaxK = 1 << 20;
 struct GemmArgs {
   const uint16_t* A;       // [M][lda]
   int64_t lda;
-  const void* W;           // [N][K] (f16/bf16 bits, int8 codes, or packed 4-bit codes [N][K/2])
-  const uint16_t* scales;  // Q8_0 / Q4_0 scales [N][K/32]
+  const void* W;           // [N][K] (f16/bf16 bits, int8 codes, or packed 4-bit codes [N][K/2]
+                           // or 2-bit codes [N][K/4])
+  const uint16_t* scales;  // block formats: scales [N][K/32]
   int64_t M;
   int64_t N;
   int64_t K;

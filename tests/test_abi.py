@@ -42,7 +42,7 @@ def plan_status(**fields):
 
 def test_exports_every_declared_symbol():
     names = declared_functions()
-    assert len(names) == 15, names
+    assert len(names) == 16, names
     assert set(names) == set(sk.EXPORTS)
     for n in names:
         assert hasattr(L, n), n
@@ -416,7 +416,8 @@ def test_moe_combine_validation():
 
 
 @fake_pointers
-@pytest.mark.parametrize("f", [L.skinny_dequant_q8_0_run, L.skinny_dequant_q4_0_run])
+@pytest.mark.parametrize("f", [L.skinny_dequant_q8_0_run, L.skinny_dequant_q4_0_run,
+                               L.skinny_dequant_q2_0_run])
 def test_dequant_validation(f):
     assert f(0, 64, P16, P16b, P16c, None) == sk.ERR_INVALID_ARG
     assert f(4, 16, P16, P16b, P16c, None) == sk.ERR_INVALID_ARG
@@ -425,22 +426,27 @@ def test_dequant_validation(f):
     assert f(4, 64, ODD, P16b, P16c, None) == sk.ERR_ALIGNMENT
 
 
+@pytest.mark.parametrize("w", [sk.Q4_0, sk.Q2_0])
 @pytest.mark.parametrize("fields,status", [
-    (dict(w_dtype=sk.Q4_0, n=512, k=2560, c_dtype=sk.F16), sk.OK),
-    (dict(w_dtype=sk.Q4_0, k=2568), sk.ERR_SHAPE),                     # k % 32 != 0
-    (dict(w_dtype=sk.Q4_0, a_dtype=sk.BF16), sk.ERR_UNSUPPORTED),      # f16 rows only
-    (dict(w_dtype=sk.Q4_0, k=32, max_m=17), sk.ERR_SHAPE),             # the GEMM needs k >= 64
-    (dict(w_dtype=sk.Q4_0, k=32, max_m=16), sk.OK),                    # the GEMV does not
-    (dict(w_dtype=6), sk.ERR_UNSUPPORTED),
+    (dict(n=512, k=2560, c_dtype=sk.F16), sk.OK),
+    (dict(k=2568), sk.ERR_SHAPE),                     # k % 32 != 0
+    (dict(a_dtype=sk.BF16), sk.ERR_UNSUPPORTED),      # f16 rows only
+    (dict(k=32, max_m=17), sk.ERR_SHAPE),             # the GEMM needs k >= 64
+    (dict(k=32, max_m=16), sk.OK),                    # the GEMV does not
 ])
-def test_q4_0_plan_validation(fields, status):
-    assert plan_status(**fields) == status
+def test_packed_block_plan_validation(w, fields, status):
+    assert plan_status(w_dtype=w, **fields) == status
+
+
+def test_unknown_weight_dtype():
+    assert plan_status(w_dtype=7) == sk.ERR_UNSUPPORTED
 
 
 @fake_pointers
-def test_q4_0_run_needs_scales():
-    q = plan(n=512, k=2560, w=sk.Q4_0, c=sk.F16)
-    assert run(q, 1) == sk.ERR_INVALID_ARG                 # Q4_0 needs scales
+@pytest.mark.parametrize("w", [sk.Q4_0, sk.Q2_0])
+def test_packed_block_run_needs_scales(w):
+    q = plan(n=512, k=2560, w=w, c=sk.F16)
+    assert run(q, 1) == sk.ERR_INVALID_ARG                 # block formats need scales
     assert run(q, 1, S=ODD) == sk.ERR_ALIGNMENT
 
 
