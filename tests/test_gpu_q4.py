@@ -159,3 +159,21 @@ def test_q4_gemm_launch_shapes_and_m_invariance():
         for flag in (sk.GEMM_ONE_LAUNCH, sk.GEMM_FOLD_LAUNCH):
             assert np.array_equal(outs[(sk.GEMM_SPLIT_LAUNCH, M)], outs[(flag, M)]), (flag, M)
         assert np.array_equal(outs[(sk.GEMM_SPLIT_LAUNCH, M)], outs[(sk.GEMM_SPLIT_LAUNCH, 306)][:M]), M
+
+
+@pytest.mark.parametrize("n,k", [(1, 32), (5, 32), (33, 64), (3, 2080)])
+@pytest.mark.parametrize("m", [1, 3, 16])
+def test_q4_gemv_small_and_ragged_shapes(n, k, m):
+    """The smallest block count (k = 32: one scale per row, four chunks), a
+    single column, a ragged column count and an odd scale count, against the
+    oracle and bitwise against the f16 path on the dequantised weight."""
+    A, qs, d = _inputs(m, n, k, 1301 + 7 * n + k + m)
+    dq = (to_dev(qs, "u8"), to_dev(d, "f16"))
+    print(f"q4_0 gemv n={n} k={k} m={m}", flush=True)
+    C = sk.mm(to_dev(A, "f16"), dq, out_dtype=torch.float32, max_m=16)
+    C2 = sk.mm(to_dev(A, "f16"), sk.dequant_q4_0(*dq), out_dtype=torch.float32, max_m=16)
+    torch.cuda.synchronize()
+    got = C.cpu().numpy()
+    assert np.array_equal(got.view(np.uint32), C2.cpu().numpy().view(np.uint32))
+    ref = oracle.mm(A, "f16", qs, "q4_0", w_scales=d)
+    assert np.all(np.abs(got - ref) <= _bound(A, qs, d))
