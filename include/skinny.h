@@ -192,10 +192,11 @@ SKINNY_API void skinny_mm_plan_destroy(skinny_plan* plan);
  *     ordered reduce launch adds (or, with SKINNY_GEMM_FOLD_LAUNCH, the
  *     arrival counters per tile and the chunk sums the last block adds);
  *   - a plan with fp32 A whose GEMV splits k (k > 1024 for bf16 weights), at
- *     m > 10: the fused cast measured slower there than a separate cast
- *     launch, so the run casts the rows into the workspace (after any
- *     partial sums) and the bf16 GEMV reads them -- the same bits as the
- *     fused launch.
+ *     m > 10, unless its one-row launch fills at most half the CUs m times
+ *     over (then each row runs as its own workgroup row, fused): the fused
+ *     cast measured slower there than a separate cast launch, so the run
+ *     casts the rows into the workspace (after any partial sums) and the
+ *     bf16 GEMV reads them -- the same bits as the fused launch.
  * It must be zero-filled once before its first use; every completed run
  * leaves it ready for the next (its counters back at zero).  A run that needs
  * no workspace ignores it. */

@@ -331,8 +331,10 @@ size_t gemm_partial_bytes(const skinny_plan* p, int64_t m) {
 // choice per m changes no bit.
 constexpr int64_t kA32FusedMaxM = 10;
 
+int64_t gemv_row_groups(const skinny_plan* p, int64_t m);
+
 bool a32_cast_first(const skinny_plan* p, int64_t m) {
-  return p->d.a_dtype == SKINNY_F32 && p->gemv_S > 1 && m > kA32FusedMaxM;
+  return p->d.a_dtype == SKINNY_F32 && p->gemv_S > 1 && m > kA32FusedMaxM && gemv_row_groups(p, m) == 1;
 }
 
 // elements of A a cast-first run converts: rows 0..m-1 at stride lda, the
@@ -375,9 +377,15 @@ Scratch caller_scratch(const skinny_plan* p, void* workspace) {
 
 skinny_status hip_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SKINNY_ERR_HIP; }
 
-GemvArgs gemv_args(const skinny_plan* p, int64_t m, const void* A, const void* W, const void* scales,
+// the GEMV launch for m rows runs the kernel for gemv_kernel_rows(p, m) rows
+// in gemv_row_groups(p, m) workgroup rows
+int64_t gemv_kernel_rows(const skinny_plan* p, int64_t m) { return gemv_row_groups(p, m) > 1 ? 1 : m; }
+
+GemvArgs gemv_args(const skinny_plan* p, int64_t m_rows, const void* A, const void* W, const void* scales,
                    void* C, int64_t ldc, const Scratch& sc) {
+  const int64_t m = gemv_kernel_rows(p, m_rows);
   GemvArgs g;
+  g.row_groups = (int32_t)gemv_row_groups(p, m_rows);
   g.A = A;
   g.a_kind = p->d.a_dtype == SKINNY_F32 ? kAF32 : kA16;
   g.lda = p->d.lda;
@@ -472,6 +480,18 @@ int64_t gemv_blocks(const skinny_plan* p, const GemvBlock& b, int64_t m) {
   return (wps * p->gemv_S + b.waves - 1) / b.waves;
 }
 
+// Row groups.  When the columns fill only a few workgroups (the scalar gate:
+// n = 1, one workgroup of five waves), the launch for m rows gives each row
+// its own workgroup row (blockIdx.y) running the one-row kernel, so the m
+// rows spread over m times the CUs.  Rows are independent and each one sees
+// the m = 1 call's arithmetic, so this changes no bit.  It needs the one-row
+// grid times m to stay within half the CUs (the weight is then small and
+// each workgroup row reads it from L2), and k not split across workgroups.
+int64_t gemv_row_groups(const skinny_plan* p, int64_t m) {
+  if (m <= 1 || gemv_global_split(p)) return 1;
+  return gemv_blocks(p, gemv_block(p), 1) * m <= p->num_cus / 2 ? m : 1;
+}
+
 // enqueue C = A . W for m rows, then (when idx/val are given) the top-k launch
 // over the rows of C (Strata PR #109, "What": one multi-row GEMV launch and
 // one multi-row top-10 launch per window)
@@ -481,6 +501,7 @@ skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const v
   const bool want_topk = topk_idx != nullptr;
   if (use_gemv(p, m)) {
     GemvArgs g = gemv_args(p, m, A, W, scales, C, ldc, sc);
+    const int64_t mk = gemv_kernel_rows(p, m);
     const GemvBlock b = gemv_block(p);
     g.cg_per_block = b.ranges;
     if (a32_cast_first(p, m)) {
@@ -490,7 +511,7 @@ skinny_status enqueue_mm(const skinny_plan* p, int64_t m, const void* A, const v
       g.A = a16;
       g.a_kind = kA16;
     }
-    skinny_status st = hip_status(launch_gemv(g, (int)m, p->gemv_T, p->w_kind, c_kind, b.waves, stream));
+    skinny_status st = hip_status(launch_gemv(g, (int)mk, p->gemv_T, p->w_kind, c_kind, b.waves, stream));
     if (st != SKINNY_OK || !want_topk) return st;
     return hip_status(launch_topk((const float*)C, (int)m, p->d.n, ldc, topk_idx, topk_val, topk, stream));
   }
@@ -780,13 +801,18 @@ skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf,
   if (plan == nullptr || buf == nullptr || len == 0) return SKINNY_ERR_INVALID_ARG;
   if (m < 1 || m > plan->d.max_m) return SKINNY_ERR_INVALID_ARG;
   if (use_gemv(plan, m)) {
-    const int64_t waves = gemv_waves_per_split(plan, m) * plan->gemv_S;
+    // the launch: the kernel for mk rows, in `groups` workgroup rows
+    const int64_t mk = gemv_kernel_rows(plan, m);
+    const int64_t groups = gemv_row_groups(plan, m);
+    const int64_t waves = gemv_waves_per_split(plan, mk) * plan->gemv_S * groups;
     const GemvBlock b = gemv_block(plan);
+    char rows_token[40] = "";
+    if (groups > 1) std::snprintf(rows_token, sizeof(rows_token), "row_groups=%lld ", (long long)groups);
     std::snprintf(buf, len,
-                  "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld x %d waves split_reduce=%s "
+                  "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld x %d waves %ssplit_reduce=%s "
                   "%s%sworkspace=%zu",
-                  (long long)m, plan->gemv_T, plan->gemv_S, plan->gemv_cpw_m[m], (long long)waves,
-                  (long long)gemv_blocks(plan, b, m), b.waves,
+                  (long long)m, plan->gemv_T, plan->gemv_S, plan->gemv_cpw_m[mk], (long long)waves,
+                  (long long)(gemv_blocks(plan, b, mk) * groups), b.waves, rows_token,
                   plan->gemv_S == 1 ? "none" : (gemv_global_split(plan) ? "global" : "in-block"),
                   plan->d.a_dtype != SKINNY_F32 ? ""
                   : a32_cast_first(plan, m)     ? "a=f32(cast-launch) "

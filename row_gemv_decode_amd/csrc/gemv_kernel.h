@@ -315,6 +315,14 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
   // sums of one block's waves (in-block split): [wave][column of the wave][row]
   __shared__ float red[SPLIT == kSplitBlock ? kGemvMaxWavesPerBlock * CPW * M : 1];
 
+  // row groups: the one-row kernel may run with one workgroup row per row of
+  // A (blockIdx.y); each takes its own row of A and of C
+  if constexpr (M == 1) {
+    const int64_t r0 = blockIdx.y;
+    g.A = (const char*)g.A + r0 * g.lda * (AK == kAF32 ? 4 : 2);
+    g.C = (char*)g.C + r0 * g.ldc * (CK == CK_F32 ? 4 : 2);
+  }
+
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
   int s, wc;
@@ -600,6 +608,11 @@ hipError_t launch_gemv_kind(const GemvArgs& args, int m, int out_kind, int waves
   if (cpw_log2 < 0) return hipErrorInvalidValue;  // columns per wave: 1, 2, 4 or 8
   const int split = args.S == 1 ? kSplitNone : args.S <= kGemvBlockSplitMax ? kSplitBlock : kSplitGlobal;
   if (args.epilogue != kEpiNone && args.epilogue != kEpiSigmoid) return hipErrorInvalidValue;
+  // row groups: the one-row kernel only, and not with a k split across
+  // workgroups (its arrival counters are per column range)
+  if (args.row_groups < 1 || args.row_groups > kGemvMaxM ||
+      (args.row_groups > 1 && (m != 1 || split == kSplitGlobal)))
+    return hipErrorInvalidValue;
   const gemv_fn fn = gemv_pick_split<T, WK, AK>(split, args.epilogue == kEpiSigmoid, m, cpw_log2, out_kind);
   if (fn == nullptr) return hipErrorInvalidValue;
   int64_t blocks;
@@ -610,7 +623,8 @@ hipError_t launch_gemv_kind(const GemvArgs& args, int m, int out_kind, int waves
     const int64_t waves = (int64_t)args.S * args.waves_per_split;
     blocks = (waves + waves_per_block - 1) / waves_per_block;
   }
-  hipLaunchKernelGGL(fn, dim3((unsigned)blocks), dim3(64 * waves_per_block), 0, stream, args);
+  hipLaunchKernelGGL(fn, dim3((unsigned)blocks, (unsigned)args.row_groups), dim3(64 * waves_per_block), 0, stream,
+                     args);
   return hipGetLastError();
 }
 

@@ -358,6 +358,24 @@ def test_cast_validation():
     assert f(64, ctypes.c_void_p(base + 96), ctypes.c_void_p(base), None) == sk.ERR_INVALID_ARG
 
 
+def test_row_groups_for_a_few_workgroups():
+    # the gate (n = 1: one workgroup of five waves at m = 1) runs the one-row
+    # kernel in m workgroup rows: fused fp32 rows at every m, no workspace
+    g = plan(n=1, k=5120, a=sk.F32, w=sk.BF16, flags=sk.EPILOGUE_SIGMOID)
+    assert "row_groups" not in g.info(1)
+    for m in (2, 11, 16):
+        info = g.info(m)
+        assert f"row_groups={m} " in info and f"blocks={m} x 5 waves" in info, info
+        assert "a=f32(fused) " in info and "workspace=0" in info, info
+    assert g.workspace_bytes == 0
+    # up to half the CUs: 64 columns at k = 5120 make 64 one-row workgroups
+    assert "row_groups=2 " in plan(n=64, k=5120, a=sk.BF16, w=sk.BF16).info(2)
+    assert "row_groups" not in plan(n=64, k=5120, a=sk.BF16, w=sk.BF16).info(3)
+    # never with a k split across workgroups, nor for wide grids
+    assert "row_groups" not in plan(n=2, k=16384, a=sk.BF16, w=sk.BF16).info(4)
+    assert "row_groups" not in plan(n=256, k=5120, a=sk.BF16, w=sk.BF16).info(2)
+
+
 def test_gate_plan_info():
     g = plan(n=1, k=5120, a=sk.BF16, w=sk.BF16, flags=sk.EPILOGUE_SIGMOID)
     assert " epilogue=sigmoid " in g.info(16) and "path=gemv" in g.info(16)
@@ -367,12 +385,12 @@ def test_gate_plan_info():
 def test_fp32_rows_shape_by_m():
     # fp32 A: fused into the GEMV while A is staged in LDS (unsplit k) or
     # m <= 10; above that (k split) the rows are cast into the workspace first
-    g = plan(n=1, k=5120, a=sk.F32, w=sk.BF16, flags=sk.EPILOGUE_SIGMOID)
+    g = plan(n=256, k=5120, a=sk.F32, w=sk.BF16)
     assert "a=f32(fused) " in g.info(10) and "workspace=0" in g.info(10)
     assert "a=f32(cast-launch) " in g.info(11)
     assert f"workspace={11 * 5120 * 2}" in g.info(11)  # 112640 B, a multiple of 256
     assert g.workspace_bytes == 16 * 5120 * 2
-    assert plan(n=1, k=5120, max_m=10, a=sk.F32, w=sk.BF16).workspace_bytes == 0
+    assert plan(n=256, k=5120, max_m=10, a=sk.F32, w=sk.BF16).workspace_bytes == 0
     # lda > k: rows 0..m-2 at full stride, the last one up to k, rounded to 256 B
     r = plan(n=256, k=5120, lda=5128, a=sk.F32, w=sk.BF16)
     assert r.workspace_bytes == -(-(15 * 5128 + 5120) * 2 // 256) * 256

@@ -393,3 +393,55 @@ def test_two_streams_at_once_use_their_own_workspaces(kind):
         if kind == "gemv_global_split":
             head = ws[:256].cpu().numpy()  # the arrival counters
             assert not np.any(head), head[np.nonzero(head)][:8]
+
+
+_CODES = {"f16": sk.F16, "bf16": sk.BF16, "f32": sk.F32, "q2_0": sk.Q2_0}
+_TORCH = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}
+
+
+@pytest.mark.parametrize("akind,wkind,ckind,k", [
+    ("bf16", "bf16", "f32", 5120),   # k split inside the workgroup (S = 5)
+    ("f16", "f16", "f16", 512),      # unsplit k
+    ("f32", "bf16", "bf16", 2048),   # fp32 rows rounded to bf16 as they load
+    ("f16", "q2_0", "f16", 2560),    # a block-quantised weight
+])
+def test_row_groups_equal_single_row_calls(akind, wkind, ckind, k):
+    """Eight columns fill a single workgroup, so the plan runs m rows as m
+    workgroup rows of the one-row kernel.  A and C are strided (lda and ldc
+    past the row), so each group's offsets are checked; every row must be
+    its own m = 1 call bit for bit, and the oracle's product within 2e-3."""
+    n, lda, ldc = 8, k + 24, 16   # every row pointer stays 16-byte aligned
+    seed = 1400 + k
+    if akind == "f32":
+        A = WL.gen_matrix((16, k), "f32", ("normal", 1.0), seed)
+        dA = torch.zeros((16, lda), dtype=torch.float32, device="cuda")
+        dA[:, :k] = torch.from_numpy(A).cuda()
+    else:
+        A = WL.gen_matrix((16, k), akind, ("normal", 1.0), seed)
+        dA = torch.zeros((16, lda), dtype=_TORCH[akind], device="cuda")
+        dA[:, :k] = to_dev(A, akind)
+    if wkind == "q2_0":
+        qs, d = WL.gen_q2_0(n, k, seed + 1, seed + 2)
+        dW, ds = to_dev(qs, "u8"), to_dev(d, "f16")
+    else:
+        W = WL.gen_matrix((n, k), wkind, ("normal", 0.02), seed + 1)
+        dW, ds = to_dev(W, wkind), None
+    plan = sk.Plan(n, k, 16, _CODES[akind], _CODES[wkind], {"f32": sk.F32, "f16": sk.F16, "bf16": sk.BF16}[ckind],
+                   lda=lda, ldc=ldc)
+    singles = torch.zeros((16, ldc), dtype=_TORCH[ckind], device="cuda")
+    for r in range(16):
+        plan.run(1, dA[r:r + 1], dW, singles[r:r + 1], scales=ds)
+    for m in (2, 5, 16):
+        info = plan.info(m)
+        print(f"row groups {akind}/{wkind}/{ckind} k={k} m={m}: {info}", flush=True)
+        assert f"row_groups={m} " in info, info
+        C = torch.full((m, ldc), 7.0, dtype=_TORCH[ckind], device="cuda")
+        plan.run(m, dA[:m], dW, C, scales=ds)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(C[:, :n]), bits_of(singles[:m, :n])), m
+        assert np.all(C[:, n:].float().cpu().numpy() == 7.0), m   # nothing past column n
+    if akind != "f32":
+        got = singles[:, :n].float().cpu().numpy()
+        ref = (oracle.mm(A, akind, qs, "q2_0", w_scales=d) if wkind == "q2_0"
+               else oracle.mm(A, akind, W, wkind))
+        assert rel_err(got, ref) <= REL_TOL
