@@ -379,7 +379,7 @@ skinny_status hip_status(hipError_t e) { return e == hipSuccess ? SKINNY_OK : SK
 
 // the GEMV launch for m rows runs the kernel for gemv_kernel_rows(p, m) rows
 // in gemv_row_groups(p, m) workgroup rows
-int64_t gemv_kernel_rows(const skinny_plan* p, int64_t m) { return gemv_row_groups(p, m) > 1 ? 1 : m; }
+int64_t gemv_kernel_rows(const skinny_plan* p, int64_t m) { return m / gemv_row_groups(p, m); }
 
 GemvArgs gemv_args(const skinny_plan* p, int64_t m_rows, const void* A, const void* W, const void* scales,
                    void* C, int64_t ldc, const Scratch& sc) {
@@ -480,16 +480,29 @@ int64_t gemv_blocks(const skinny_plan* p, const GemvBlock& b, int64_t m) {
   return (wps * p->gemv_S + b.waves - 1) / b.waves;
 }
 
-// Row groups.  When the columns fill only a few workgroups (the scalar gate:
-// n = 1, one workgroup of five waves), the launch for m rows gives each row
-// its own workgroup row (blockIdx.y) running the one-row kernel, so the m
-// rows spread over m times the CUs.  Rows are independent and each one sees
-// the m = 1 call's arithmetic, so this changes no bit.  It needs the one-row
-// grid times m to stay within half the CUs (the weight is then small and
-// each workgroup row reads it from L2), and k not split across workgroups.
+// Row groups.  The launch for m rows may run the kernel for r rows (r
+// divides m) in m / r workgroup rows (blockIdx.y), row group y taking rows
+// y r .. y r + r - 1 of A and C.  Rows are independent and a row's
+// arithmetic does not depend on how many rows its kernel holds, so this
+// changes no bit; it trades re-reads of the weight (from L2 or the
+// last-level cache) for more workgroups and fewer rows per wave.  Never with
+// k split across workgroups.  Two cases, measured on MI355X (graph replay,
+// cold weights):
+//   - a few workgroups: when the one-row grid times m fits in half the CUs
+//     (the scalar gate: n = 1, one workgroup), r = 1 -- 2.19 / 3.88 / 6.12
+//     -> 2.23 / 2.60 / 2.60 us at m = 1 / 8 / 16;
+//   - unsplit k: the smallest power-of-two r whose m / r groups keep the
+//     launch within about ten waves per CU -- n x k = 608 x 896: 2.59 /
+//     3.10 / 3.86 -> 2.35 / 2.66 / 3.31 us at m = 4 / 8 / 16 (r = 1 / 2 / 4);
+//     at 4864 x 896 no r fits, and every r measured slower there.
 int64_t gemv_row_groups(const skinny_plan* p, int64_t m) {
   if (m <= 1 || gemv_global_split(p)) return 1;
-  return gemv_blocks(p, gemv_block(p), 1) * m <= p->num_cus / 2 ? m : 1;
+  if (gemv_blocks(p, gemv_block(p), 1) * m <= p->num_cus / 2) return m;
+  if (p->gemv_S == 1) {
+    for (int64_t r = 1; r < m; r *= 2)
+      if (m % r == 0 && gemv_waves_per_split(p, r) * (m / r) <= 10 * (int64_t)p->num_cus) return m / r;
+  }
+  return 1;
 }
 
 // enqueue C = A . W for m rows, then (when idx/val are given) the top-k launch
@@ -809,11 +822,11 @@ skinny_status skinny_mm_plan_info(const skinny_plan* plan, int64_t m, char* buf,
     char rows_token[40] = "";
     if (groups > 1) std::snprintf(rows_token, sizeof(rows_token), "row_groups=%lld ", (long long)groups);
     std::snprintf(buf, len,
-                  "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld x %d waves %ssplit_reduce=%s "
-                  "%s%sworkspace=%zu",
+                  "path=gemv m=%lld T=%d S=%d cpw=%d waves=%lld blocks=%lld x %d waves split_reduce=%s "
+                  "%s%s%sworkspace=%zu",
                   (long long)m, plan->gemv_T, plan->gemv_S, plan->gemv_cpw_m[mk], (long long)waves,
-                  (long long)(gemv_blocks(plan, b, mk) * groups), b.waves, rows_token,
-                  plan->gemv_S == 1 ? "none" : (gemv_global_split(plan) ? "global" : "in-block"),
+                  (long long)(gemv_blocks(plan, b, mk) * groups), b.waves,
+                  plan->gemv_S == 1 ? "none" : (gemv_global_split(plan) ? "global" : "in-block"), rows_token,
                   plan->d.a_dtype != SKINNY_F32 ? ""
                   : a32_cast_first(plan, m)     ? "a=f32(cast-launch) "
                                                 : "a=f32(fused) ",

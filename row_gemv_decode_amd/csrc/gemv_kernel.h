@@ -315,10 +315,10 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
   // sums of one block's waves (in-block split): [wave][column of the wave][row]
   __shared__ float red[SPLIT == kSplitBlock ? kGemvMaxWavesPerBlock * CPW * M : 1];
 
-  // row groups: the one-row kernel may run with one workgroup row per row of
-  // A (blockIdx.y); each takes its own row of A and of C
-  if constexpr (M == 1) {
-    const int64_t r0 = blockIdx.y;
+  // row groups: workgroup row y of the grid (blockIdx.y) takes rows y M ..
+  // y M + M - 1 of A and of C
+  {
+    const int64_t r0 = (int64_t)blockIdx.y * M;
     g.A = (const char*)g.A + r0 * g.lda * (AK == kAF32 ? 4 : 2);
     g.C = (char*)g.C + r0 * g.ldc * (CK == CK_F32 ? 4 : 2);
   }
@@ -608,10 +608,10 @@ hipError_t launch_gemv_kind(const GemvArgs& args, int m, int out_kind, int waves
   if (cpw_log2 < 0) return hipErrorInvalidValue;  // columns per wave: 1, 2, 4 or 8
   const int split = args.S == 1 ? kSplitNone : args.S <= kGemvBlockSplitMax ? kSplitBlock : kSplitGlobal;
   if (args.epilogue != kEpiNone && args.epilogue != kEpiSigmoid) return hipErrorInvalidValue;
-  // row groups: the one-row kernel only, and not with a k split across
-  // workgroups (its arrival counters are per column range)
-  if (args.row_groups < 1 || args.row_groups > kGemvMaxM ||
-      (args.row_groups > 1 && (m != 1 || split == kSplitGlobal)))
+  // row groups: not with a k split across workgroups (its arrival counters
+  // are per column range)
+  if (args.row_groups < 1 || args.row_groups * m > kGemvMaxM ||
+      (args.row_groups > 1 && split == kSplitGlobal))
     return hipErrorInvalidValue;
   const gemv_fn fn = gemv_pick_split<T, WK, AK>(split, args.epilogue == kEpiSigmoid, m, cpw_log2, out_kind);
   if (fn == nullptr) return hipErrorInvalidValue;

@@ -47,7 +47,7 @@ struct GemvArgs {
   int32_t epilogue;         // kEpiNone, or kEpiSigmoid: C = 1 / (1 + e^-sum)
   int32_t a_kind;           // kA16, or kAF32 (bf16 weights only)
   int32_t row_groups;       // workgroup rows of the grid: row y of the grid takes rows y*m ..
-                            // y*m + m - 1 of A and C (more than one only for m = 1, S <= 8)
+                            // y*m + m - 1 of A and C (more than one only for S <= 8)
 };
 
 constexpr int kEpiNone = 0;

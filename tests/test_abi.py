@@ -371,6 +371,14 @@ def test_row_groups_for_a_few_workgroups():
     # up to half the CUs: 64 columns at k = 5120 make 64 one-row workgroups
     assert "row_groups=2 " in plan(n=64, k=5120, a=sk.BF16, w=sk.BF16).info(2)
     assert "row_groups" not in plan(n=64, k=5120, a=sk.BF16, w=sk.BF16).info(3)
+    # unsplit k: the smallest power-of-two rows per group whose groups keep
+    # the launch within ten waves per CU (608 one-row waves at 608 x 896)
+    shard = plan(n=608, k=896)
+    for m, groups in ((2, 2), (3, 3), (4, 4), (6, 3), (8, 4), (16, 4)):
+        assert f"row_groups={groups} " in shard.info(m), (m, shard.info(m))
+    for m in (1, 5, 13):
+        assert "row_groups" not in shard.info(m), m   # no power of two divides into few enough groups
+    assert "row_groups" not in plan(n=4864, k=896).info(16)
     # never with a k split across workgroups, nor for wide grids
     assert "row_groups" not in plan(n=2, k=16384, a=sk.BF16, w=sk.BF16).info(4)
     assert "row_groups" not in plan(n=256, k=5120, a=sk.BF16, w=sk.BF16).info(2)

@@ -445,3 +445,33 @@ def test_row_groups_equal_single_row_calls(akind, wkind, ckind, k):
         ref = (oracle.mm(A, akind, qs, "q2_0", w_scales=d) if wkind == "q2_0"
                else oracle.mm(A, akind, W, wkind))
         assert rel_err(got, ref) <= REL_TOL
+
+
+def test_row_groups_at_the_shard_shape_equal_single_row_calls():
+    """608 x 896 (one GPU's share of the k = 896 weight under an 8-way column
+    shard): the plan runs m rows as groups of 1, 2 or 4 rows (m = 2 .. 16;
+    the 4-row kernel stages A in LDS).  A and C strided; every row at every
+    m must be its own m = 1 call bit for bit."""
+    wl = WL.WORKLOADS["gemv_k896_shard8"]
+    n, k, lda, ldc = wl.n, wl.k, wl.k + 8, wl.n + 8
+    A = WL.gen_a(wl, 16)
+    dA = torch.zeros((16, lda), dtype=torch.float16, device="cuda")
+    dA[:, :k] = to_dev(A, "f16")
+    dW = to_dev(WL.gen_w(wl), "f16")
+    plan = sk.Plan(n, k, 16, sk.F16, sk.F16, sk.F32, lda=lda, ldc=ldc)
+    singles = torch.zeros((16, ldc), dtype=torch.float32, device="cuda")
+    for r in range(16):
+        plan.run(1, dA[r:r + 1], dW, singles[r:r + 1])
+    grouped = 0
+    for m in range(2, 17):
+        info = plan.info(m)
+        grouped += "row_groups=" in info
+        print(f"shard m={m}: {info}", flush=True)
+        C = torch.full((m, ldc), 7.0, dtype=torch.float32, device="cuda")
+        plan.run(m, dA[:m], dW, C)
+        torch.cuda.synchronize()
+        assert np.array_equal(bits_of(C[:, :n]), bits_of(singles[:m, :n])), m
+        assert np.all(C[:, n:].cpu().numpy() == 7.0), m
+    assert grouped >= 6
+    ref = oracle.mm(A, "f16", WL.gen_w(wl), "f16")
+    assert rel_err(singles[:, :n].cpu().numpy(), ref) <= REL_TOL
