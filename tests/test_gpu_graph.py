@@ -6,8 +6,9 @@ synchronisations in between; every replay must reproduce the eager results
 bit for bit.  This covers the run shapes that keep state in the caller's
 workspace between calls (the arrival counters of a GEMV whose k is split across
 workgroups, which the kernels reset) and the two-launch shapes (the GEMM's
-k-chunk partials + ordered reduce, the router's GEMV + top-k, the gate's cast +
-GEMV) and the gate as one launch with the cast fused; none records a memset.
+k-chunk partials + ordered reduce, the router's GEMV + top-k, fp32 rows cast
+into the workspace + the bf16 GEMV), the row-grouped launches and the gate as
+one launch with the cast fused; none records a memset.
 """
 import numpy as np
 import pytest
@@ -58,7 +59,9 @@ def _replay_matches_eager(fn, outs, calls=3, replays=3):
 
 @pytest.mark.parametrize("n,k,ms", [(256, 5120, (1, 8, 16)),    # k split in the workgroup
                                      (256, 16384, (1, 5, 16)),  # k split across workgroups (counters)
-                                     (4864, 896, (2, 16))])     # unsplit, A staged in LDS
+                                     (4864, 896, (2, 16)),      # unsplit, A staged in LDS
+                                     (608, 896, (4, 8, 16)),    # unsplit, row groups of 1, 2, 4 rows
+                                     (8, 5120, (2, 16))])       # one workgroup: a row group per row
 def test_gemv_graph_replays(n, k, ms):
     print(f"graph gemv n={n} k={k}", flush=True)
     W = to_dev(WL.gen_matrix((n, k), "bf16", ("normal", 0.02), 701), "bf16")
@@ -131,4 +134,25 @@ def test_gate_graph_replays(shape):
             sk.cast_f32_bf16(A[:m], out=A16[:m])
             plan.run(m, A16[:m], W, outs[i % len(ms)][0])
     print(f"graph gate {shape}", flush=True)
+    _replay_matches_eager(fn, outs, calls=len(ms))
+
+
+def test_fp32_rows_cast_first_graph_replays():
+    """fp32 rows, k split inside the workgroup, 256 columns: m = 11 and 16 run
+    the cast into the workspace and the bf16 GEMV (two launches of one run),
+    m = 1 the fused launch."""
+    n, k = 256, 5120
+    W = to_dev(WL.gen_matrix((n, k), "bf16", ("normal", 0.02), 721), "bf16")
+    A = torch.from_numpy(np.ascontiguousarray(WL.gen_matrix((16, k), "f32", ("normal", 1.0), 722))).cuda()
+    plan = sk.Plan(n, k, 16, sk.F32, sk.BF16, sk.F32)
+    ws = plan.workspace(A.device)
+    ms = (1, 11, 16)
+    for m in ms:
+        print(f"graph fp32 rows m={m}: {plan.info(m)}", flush=True)
+    assert "a=f32(cast-launch) " in plan.info(16)
+    outs = [(torch.empty((m, n), dtype=torch.float32, device="cuda"),) for m in ms]
+
+    def fn(i):
+        m = ms[i % len(ms)]
+        plan.run(m, A[:m], W, outs[i % len(ms)][0], workspace=ws)
     _replay_matches_eager(fn, outs, calls=len(ms))
