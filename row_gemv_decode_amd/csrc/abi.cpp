@@ -435,8 +435,10 @@ skinny_status check_run_args(const skinny_plan* p, int64_t m, const void* A, con
   if (qb != (scales != nullptr)) return SKINNY_ERR_INVALID_ARG;
   if (!aligned16(A) || !aligned16(W) || !aligned16(C) || (qb && !aligned16(scales)))
     return SKINNY_ERR_ALIGNMENT;
-  // the GEMV numbers its waves (k splits x column ranges) in 32 bits
-  if (use_gemv(p, m) && gemv_waves_per_split(p, m) * p->gemv_S > (1LL << 31) - 1024) return SKINNY_ERR_SHAPE;
+  // the GEMV numbers its waves (k splits x column ranges of one row group) in
+  // 32 bits
+  if (use_gemv(p, m) && gemv_waves_per_split(p, gemv_kernel_rows(p, m)) * p->gemv_S > (1LL << 31) - 1024)
+    return SKINNY_ERR_SHAPE;
   return SKINNY_OK;
 }
 
