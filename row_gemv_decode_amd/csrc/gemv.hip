@@ -134,18 +134,10 @@ __device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int 
     skey[u] = key[u];
     sjj[u] = jj[u];
   }
-  uint32_t rounds_won = 0;
-  for (int t = 0; t < topk; ++t) {
-    const int kmax = wave_max_i32(key[0]);  // the same in every lane
-    bool mine = key[0] == kmax;
-    if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(mine)) != 1) {  // uniform; a tie, rare
-      const int wj = wave_min_i32(mine ? jj[0] : kNoColumn);
-      mine = mine && jj[0] == wj;
-    }
-    // the winner pops its head: each slot takes the next one under an
-    // all-ones mask (one bit-field insert per slot)
+  // the winner pops its head: each slot takes the next one under an all-ones
+  // mask (one bit-field insert per slot)
+  auto pop = [&](bool mine) __attribute__((always_inline)) {
     const uint32_t pm = 0u - (uint32_t)mine;
-    rounds_won |= pm & (1u << t);
 #pragma unroll
     for (int u = 0; u + 1 < NC; ++u) {
       key[u] = (int)((pm & (uint32_t)key[u + 1]) | (~pm & (uint32_t)key[u]));
@@ -153,6 +145,39 @@ __device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int 
     }
     key[NC - 1] = (int)((pm & (uint32_t)kNoKey) | (~pm & (uint32_t)key[NC - 1]));
     jj[NC - 1] = (int)((pm & (uint32_t)kNoColumn) | (~pm & (uint32_t)jj[NC - 1]));
+  };
+  // Fast pass: every lane whose head equals the maximum pops, and the
+  // ballots only record whether any round had two such lanes (a tie), off
+  // the rounds' critical path.  A tie makes the pass wrong from that round
+  // on, so then the rounds are redone from the sorted slots with the tie
+  // rule (the lowest column among the tied heads wins).
+  uint32_t rounds_won = 0;
+  uint64_t ties = 0;
+  for (int t = 0; t < topk; ++t) {
+    const int kmax = wave_max_i32(key[0]);  // the same in every lane
+    const bool mine = key[0] == kmax;
+    const uint64_t b = __builtin_amdgcn_ballot_w64(mine);
+    ties |= b & (b - 1);  // non-zero when two or more lanes hold the maximum
+    rounds_won |= (0u - (uint32_t)mine) & (1u << t);
+    pop(mine);
+  }
+  if (ties != 0) {  // uniform; equal logits among the leaders, rare
+#pragma unroll
+    for (int u = 0; u < NC; ++u) {
+      key[u] = skey[u];
+      jj[u] = sjj[u];
+    }
+    rounds_won = 0;
+    for (int t = 0; t < topk; ++t) {
+      const int kmax = wave_max_i32(key[0]);
+      bool mine = key[0] == kmax;
+      if (__builtin_popcountll(__builtin_amdgcn_ballot_w64(mine)) != 1) {  // uniform
+        const int wj = wave_min_i32(mine ? jj[0] : kNoColumn);
+        mine = mine && jj[0] == wj;
+      }
+      rounds_won |= (0u - (uint32_t)mine) & (1u << t);
+      pop(mine);
+    }
   }
   __shared__ int won_j[SKINNY_TOPK_MAX];
   __shared__ int won_k[SKINNY_TOPK_MAX];
