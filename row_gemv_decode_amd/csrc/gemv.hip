@@ -86,8 +86,9 @@ __device__ __forceinline__ float key_value(int key) {
   return fbits((uint32_t)key ^ ((uint32_t)(key >> 31) & 0x7fffffffu));
 }
 
-template <int NC>
-__device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int topk, int32_t* out_idx,
+// TK > 0: topk is TK, known at compile time (the fast pass unrolls); 0: runtime
+template <int NC, int TK>
+__device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int topk_arg, int32_t* out_idx,
                                                    float* out_val, int lane) {
   int key[NC];
   int jj[NC];
@@ -151,15 +152,22 @@ __device__ __forceinline__ void wave_topk_row_regs(const float* row, int n, int 
   // the rounds' critical path.  A tie makes the pass wrong from that round
   // on, so then the rounds are redone from the sorted slots with the tie
   // rule (the lowest column among the tied heads wins).
+  const int topk = TK > 0 ? TK : topk_arg;
   uint32_t rounds_won = 0;
   uint64_t ties = 0;
-  for (int t = 0; t < topk; ++t) {
+  auto fast_round = [&](int t) __attribute__((always_inline)) {
     const int kmax = wave_max_i32(key[0]);  // the same in every lane
     const bool mine = key[0] == kmax;
     const uint64_t b = __builtin_amdgcn_ballot_w64(mine);
     ties |= b & (b - 1);  // non-zero when two or more lanes hold the maximum
     rounds_won |= (0u - (uint32_t)mine) & (1u << t);
     pop(mine);
+  };
+  if constexpr (TK > 0) {
+#pragma unroll
+    for (int t = 0; t < TK; ++t) fast_round(t);
+  } else {
+    for (int t = 0; t < topk; ++t) fast_round(t);
   }
   if (ties != 0) {  // uniform; equal logits among the leaders, rare
 #pragma unroll
@@ -234,7 +242,7 @@ __device__ void wave_topk_row_generic(const float* row, int n, int topk, int32_t
 
 // --- top-k launch: one wavefront per row, blockIdx.x = row -------------------
 // NC > 0: rows of at most 64 * NC columns held in registers; NC == 0: generic
-template <int NC>
+template <int NC, int TK>
 __global__ __launch_bounds__(64) void topk_rows_kernel(const float* __restrict__ logits, int64_t n,
                                                        int64_t ldl, int32_t* __restrict__ out_idx,
                                                        float* __restrict__ out_val, int topk) {
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(64) void topk_rows_kernel(const float* __restrict__
   int32_t* oi = out_idx + (int64_t)r * topk;
   float* ov = out_val + (int64_t)r * topk;
   if constexpr (NC > 0) {
-    wave_topk_row_regs<NC>(row, (int)n, topk, oi, ov, threadIdx.x);
+    wave_topk_row_regs<NC, TK>(row, (int)n, topk, oi, ov, threadIdx.x);
   } else {
     wave_topk_row_generic(row, (int)n, topk, oi, ov, threadIdx.x);
   }
@@ -366,12 +374,14 @@ hipError_t launch_topk(const float* logits, int m, int64_t n, int64_t ldl, int32
                        int topk, hipStream_t stream) {
   if (topk < 1 || topk > SKINNY_TOPK_MAX || topk > n) return hipErrorInvalidValue;  // the kernels' bounds
   typedef void (*topk_fn)(const float*, int64_t, int64_t, int32_t*, float*, int);
-  const topk_fn fn = n <= 64    ? topk_rows_kernel<1>
-                     : n <= 128 ? topk_rows_kernel<2>
-                     : n <= 256 ? topk_rows_kernel<4>
-                     : n <= 512 ? topk_rows_kernel<8>
-                     : n <= 1024 ? topk_rows_kernel<16>
-                                 : topk_rows_kernel<0>;
+  // top-10 (the router's) gets its own unrolled kernels
+  const bool ten = topk == 10;
+  const topk_fn fn = n <= 64    ? (ten ? topk_rows_kernel<1, 10> : topk_rows_kernel<1, 0>)
+                     : n <= 128 ? (ten ? topk_rows_kernel<2, 10> : topk_rows_kernel<2, 0>)
+                     : n <= 256 ? (ten ? topk_rows_kernel<4, 10> : topk_rows_kernel<4, 0>)
+                     : n <= 512 ? (ten ? topk_rows_kernel<8, 10> : topk_rows_kernel<8, 0>)
+                     : n <= 1024 ? (ten ? topk_rows_kernel<16, 10> : topk_rows_kernel<16, 0>)
+                                 : topk_rows_kernel<0, 0>;
   hipLaunchKernelGGL(fn, dim3((unsigned)m), dim3(64), 0, stream, logits, n, ldl, idx, val, topk);
   return hipGetLastError();
 }
