@@ -526,8 +526,14 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
         const int r = e - c * M;
         const int64_t j = rbase + c;
         if (e >= CPW * M || j >= g.n) break;  // past the last column
-        float acc = red[(w0 * CPW + c) * M + r];
-        for (int q = 1; q < g.S; ++q) acc += red[((w0 + q) * CPW + c) * M + r];
+        // every split's sum is read before the first add (slots past S read
+        // split 0 again and are not added); the adds keep the order q = 0..S-1
+        float part[kGemvBlockSplitMax];
+#pragma unroll
+        for (int q = 0; q < kGemvBlockSplitMax; ++q) part[q] = red[((w0 + (q < g.S ? q : 0)) * CPW + c) * M + r];
+        float acc = part[0];
+#pragma unroll
+        for (int q = 1; q < kGemvBlockSplitMax; ++q) acc = q < g.S ? acc + part[q] : acc;
         store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish<EPI>(acc));
       }
     }
