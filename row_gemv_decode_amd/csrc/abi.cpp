@@ -386,6 +386,14 @@ GemvArgs gemv_args(const skinny_plan* p, int64_t m_rows, const void* A, const vo
   const int64_t m = gemv_kernel_rows(p, m_rows);
   GemvArgs g;
   g.row_groups = (int32_t)gemv_row_groups(p, m_rows);
+  // wave w of an in-block split workgroup: range w / S, split w % S
+  g.wave_range = 0;
+  g.wave_split = 0;
+  if (p->gemv_S <= kGemvBlockSplitMax)
+    for (int w = 0; w < kGemvMaxWavesPerBlock; ++w) {
+      g.wave_range |= (uint32_t)(w / p->gemv_S) << (4 * w);
+      g.wave_split |= (uint32_t)(w % p->gemv_S) << (4 * w);
+    }
   g.A = A;
   g.a_kind = p->d.a_dtype == SKINNY_F32 ? kAF32 : kA16;
   g.lda = p->d.lda;

@@ -333,10 +333,10 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
     active = s < g.S;  // trailing waves of the last block have no columns
     wc = active ? gw - s * g.waves_per_split : 0;
   } else {
-    // in-block ranges (an unsplit k is the case S = 1)
-    const int S = SPLIT == kSplitNone ? 1 : g.S;
-    const int cg = wave / S;
-    s = wave - cg * S;
+    // in-block ranges (an unsplit k is the case S = 1): range wave / S, split
+    // wave % S, both from the host's 4-bit fields
+    const int cg = SPLIT == kSplitNone ? wave : (int)((g.wave_range >> (4 * wave)) & 15u);
+    s = SPLIT == kSplitNone ? 0 : (int)((g.wave_split >> (4 * wave)) & 15u);
     wc = blockIdx.x * g.cg_per_block + cg;
     active = cg < g.cg_per_block && wc < g.waves_per_split;
   }

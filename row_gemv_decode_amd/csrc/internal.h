@@ -46,6 +46,8 @@ struct GemvArgs {
                             // zero between calls
   int32_t epilogue;         // kEpiNone, or kEpiSigmoid: C = 1 / (1 + e^-sum)
   int32_t a_kind;           // kA16, or kAF32 (bf16 weights only)
+  uint32_t wave_range;      // S <= kGemvBlockSplitMax: 4 bits per wave w of a workgroup, w / S
+  uint32_t wave_split;      //   and w % S (no division in the kernel)
   int32_t row_groups;       // workgroup rows of the grid: row y of the grid takes rows y*m ..
                             // y*m + m - 1 of A and C (more than one only for S <= 8)
 };
