@@ -290,6 +290,10 @@ __device__ __forceinline__ u32x4 load_a8(const GemvArgs& g, int r, int c) {
 //     Each wave reduces its sums over its 64 lanes and parks them in LDS;
 //     after one barrier wave q adds the S splits of range q in the fixed
 //     order s = 0..S-1 and writes C.
+//   kSplitBlockFull: kSplitBlock where every chunk slot of every wave lies
+//     inside k (k = S * 512 * T elements, so no split ends inside a slot):
+//     the same sums, without the per-lane tail handling -- no clamped
+//     chunk index and no select after each slot's products.
 //   kSplitGlobal (S > kGemvBlockSplitMax): the waves of one range sit in
 //     different workgroups: each writes its sums to partial[s][r][j], makes
 //     them visible device-wide and counts itself in on its range; the wave
@@ -301,6 +305,7 @@ __device__ __forceinline__ u32x4 load_a8(const GemvArgs& g, int r, int c) {
 constexpr int kSplitNone = 0;
 constexpr int kSplitBlock = 1;
 constexpr int kSplitGlobal = 2;
+constexpr int kSplitBlockFull = 3;
 
 template <int M, int T, int WK, int CK, int CPW, int EPI, int AK, int SPLIT>
 __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(GemvArgs g) {
@@ -312,8 +317,12 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
   constexpr int LV = Shape::LV;
   static_assert(LV <= 6, "at most 64 values per lane");
 
+  // k split inside the workgroup; every chunk slot inside k
+  constexpr bool kInBlock = SPLIT == kSplitBlock || SPLIT == kSplitBlockFull;
+  constexpr bool kFull = SPLIT == kSplitBlockFull;
+
   // sums of one block's waves (in-block split): [wave][column of the wave][row]
-  __shared__ float red[SPLIT == kSplitBlock ? kGemvMaxWavesPerBlock * CPW * M : 1];
+  __shared__ float red[kInBlock ? kGemvMaxWavesPerBlock * CPW * M : 1];
 
   // row groups: workgroup row y of the grid (blockIdx.y) takes rows y M ..
   // y M + M - 1 of A and of C
@@ -377,8 +386,8 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
 #pragma unroll
   for (int t = 0; t < T; ++t) {
     chunk[t] = s * 64 * T + t * 64 + lane;
-    valid[t] = chunk[t] < g.nchunks;
-    lchunk[t] = valid[t] ? chunk[t] : 0;
+    valid[t] = kFull || chunk[t] < g.nchunks;
+    lchunk[t] = kFull ? chunk[t] : valid[t] ? chunk[t] : 0;
   }
 
   // every weight load of the wave, issued before anything else waits
@@ -413,18 +422,16 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
     // fp32 rows: every raw load first, then the rounding to bf16 -- a
     // conversion between the loads makes the compiler wait for each pair
     // before it issues the next
+    // (a wave without columns loads in-range chunks of its rows too and
+    // drops them: no branch and no zero fill ahead of the loads)
     u32x4 raw[T][M][2];
 #pragma unroll
     for (int t = 0; t < T; ++t)
 #pragma unroll
       for (int r = 0; r < M; ++r) {
-        if (active) {  // wave-uniform
-          const u32x4* p = (const u32x4*)((const float*)g.A + (int64_t)r * g.lda + (int64_t)lchunk[t] * 8);
-          raw[t][r][0] = p[0];
-          raw[t][r][1] = p[1];
-        } else {
-          raw[t][r][0] = raw[t][r][1] = u32x4{0u, 0u, 0u, 0u};
-        }
+        const u32x4* p = (const u32x4*)((const float*)g.A + (int64_t)r * g.lda + (int64_t)lchunk[t] * 8);
+        raw[t][r][0] = p[0];
+        raw[t][r][1] = p[1];
       }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -432,17 +439,12 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
 #pragma unroll
       for (int r = 0; r < M; ++r) a[t][r] = bf16x8_rne(raw[t][r][0], raw[t][r][1]);
   } else {
-    if (active) {  // wave-uniform
+    // (a wave without columns loads in-range chunks of its rows too and
+    // drops them: no branch and no zero fill ahead of the loads)
 #pragma unroll
-      for (int t = 0; t < T; ++t)
+    for (int t = 0; t < T; ++t)
 #pragma unroll
-        for (int r = 0; r < M; ++r) a[t][r] = load_a8<AK>(g, r, lchunk[t]);
-    } else {
-#pragma unroll
-      for (int t = 0; t < T; ++t)
-#pragma unroll
-        for (int r = 0; r < M; ++r) a[t][r] = u32x4{0u, 0u, 0u, 0u};
-    }
+      for (int r = 0; r < M; ++r) a[t][r] = load_a8<AK>(g, r, lchunk[t]);
   }
 
   // every load above is issued before the first product: without this fence
@@ -486,7 +488,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
         const int64_t j = j0 + c0 + gi;
         if constexpr (SPLIT == kSplitNone) {
           store_out<CK>(g.C, (int64_t)r * g.ldc + j, gemv_finish<EPI>(sum));
-        } else if constexpr (SPLIT == kSplitBlock) {
+        } else if constexpr (kInBlock) {
           red[(wave * CPW + c0 + gi) * M + r] = sum;
         } else {
           st_dev(g.partial + ((int64_t)s * M + r) * g.n + j, sum);
@@ -513,7 +515,7 @@ __global__ __launch_bounds__(64 * kGemvMaxWavesPerBlock) void gemv_rows_kernel(G
     }
   }
 
-  if constexpr (SPLIT == kSplitBlock) {
+  if constexpr (kInBlock) {
     __syncthreads();  // every wave's sums are in LDS
     // wave q adds the S splits of range q (its first split is wave q * S)
     if (wave < g.cg_per_block) {
@@ -597,6 +599,7 @@ gemv_fn gemv_pick_split(int split, bool gate, int m, int cpw_log2, int out_kind)
   switch (split) {
     case kSplitNone: return gemv_pick_any<T, WK, AK, kSplitNone>(gate, m, cpw_log2, out_kind);
     case kSplitBlock: return gemv_pick_any<T, WK, AK, kSplitBlock>(gate, m, cpw_log2, out_kind);
+    case kSplitBlockFull: return gemv_pick_any<T, WK, AK, kSplitBlockFull>(gate, m, cpw_log2, out_kind);
     default: return gemv_pick_any<T, WK, AK, kSplitGlobal>(gate, m, cpw_log2, out_kind);
   }
 }
@@ -612,7 +615,11 @@ hipError_t launch_gemv_kind(const GemvArgs& args, int m, int out_kind, int waves
     return hipErrorInvalidValue;  // (unsplit blocks stage A with at least 256 threads)
   const int cpw_log2 = args.cpw == 1 ? 0 : args.cpw == 2 ? 1 : args.cpw == 4 ? 2 : args.cpw == 8 ? 3 : -1;
   if (cpw_log2 < 0) return hipErrorInvalidValue;  // columns per wave: 1, 2, 4 or 8
-  const int split = args.S == 1 ? kSplitNone : args.S <= kGemvBlockSplitMax ? kSplitBlock : kSplitGlobal;
+  // an in-block split whose S * 64 T chunk slots cover k exactly needs no tail handling
+  const int split = args.S == 1                                        ? kSplitNone
+                    : args.S > kGemvBlockSplitMax                      ? kSplitGlobal
+                    : (int64_t)args.S * 64 * T == (int64_t)args.nchunks ? kSplitBlockFull
+                                                                       : kSplitBlock;
   if (args.epilogue != kEpiNone && args.epilogue != kEpiSigmoid) return hipErrorInvalidValue;
   // row groups: not with a k split across workgroups (its arrival counters
   // are per column range)
