@@ -66,8 +66,8 @@ def parse():
     p.add_argument("--oracle-seconds", type=float, default=0.25,
                    help="CPU-oracle budget per sweep row (a sample of rows, scaled to the call)")
     p.add_argument("--tiles", default=None, metavar="WORKLOAD",
-                   help="time every GEMM tile (and, for a plan that cuts k into chunks, both "
-                        "the split and the one-launch shape) at every m > 16 of WORKLOAD (cold "
+                   help="time every GEMM tile (and, for a plan that cuts k into chunks, each of "
+                        "the split, one-launch and fold shapes) at every m > 16 of WORKLOAD (cold "
                         "weights and A, HIP-graph replay, min of 5) and print one JSON line per "
                         "m; the measurements behind the tile selector's cost table")
     p.add_argument("--only", default=None, metavar="WORKLOAD:M[,M...][:TILE]",
@@ -90,7 +90,8 @@ def run_tiles(name):
     a, w, c = dtype_codes(sk, wl)
     cdt = torch.float32 if wl.c_kind == "f32" else torch.float16
     chunked = "chunks=1 " not in sk.Plan(wl.n, wl.k, max(wl.ms), a, w, c).info(max(wl.ms))
-    shapes = ((sk.GEMM_SPLIT_LAUNCH, "split"), (sk.GEMM_ONE_LAUNCH, "one")) if chunked else ((0, "plain"),)
+    shapes = (((sk.GEMM_SPLIT_LAUNCH, "split"), (sk.GEMM_ONE_LAUNCH, "one"), (sk.GEMM_FOLD_LAUNCH, "fold"))
+              if chunked else ((0, "plain"),))
     nA = len(inp.As)
     for m in [x for x in wl.ms if x > 16]:
         C = torch.empty((m, wl.n), dtype=cdt, device="cuda")
