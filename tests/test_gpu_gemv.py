@@ -229,9 +229,11 @@ def test_mm_run_equals_gemv_topk_logits():
 
 @pytest.mark.parametrize("n,k", [(300, 1032), (1001, 2048), (256, 16384), (37, 4096)])
 def test_split_shapes_parity_and_row_invariance(n, k):
-    """k splits summed inside a workgroup (k = 1032: 3 splits, 2048: 2, 4096:
-    4) and across workgroups (k = 16384: 16 splits), with ragged column
-    ranges; every row at m = 16 equals its m = 1 call bit for bit."""
+    """k splits summed inside a workgroup (k = 1032: 3 splits, the last ending
+    inside a chunk slot; 2048 and 4096: splits whose chunk slots cover k
+    exactly, the kernels without tail handling) and across workgroups
+    (k = 16384: 16 splits), with ragged column ranges; every row at m = 16
+    equals its m = 1 call bit for bit."""
     print(f"split shapes n={n} k={k}", flush=True)
     W = WL.gen_matrix((n, k), "f16", ("uniform", -0.05, 0.05), 401 + k)
     A = WL.gen_matrix((16, k), "f16", ("normal", 1.0), 402 + k)
