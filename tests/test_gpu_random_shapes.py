@@ -81,3 +81,48 @@ def test_random_shape_parity(i, kind, m, n, k, out_kind):
         row0 = C[:1].contiguous().view(torch.int16 if out_kind == "f16" else torch.int32)
         one = single.contiguous().view(torch.int16 if out_kind == "f16" else torch.int32)
         assert torch.equal(row0, one)
+
+
+def _strided_cases(count=20, seed=2027):
+    rng = random.Random(seed)
+    out = []
+    for i in range(count):
+        kind = ("f16", "bf16", "q8_0")[i % 3]
+        block = kind.startswith("q")
+        k = rng.randrange(64, 2049, 32) if block else rng.randrange(8, 2049, 8)
+        lda = k + 8 * rng.randrange(1, 9)          # rows stay 16-byte aligned
+        n = (rng.randrange(1, 40), rng.randrange(40, 600))[i % 2]
+        ldc = n + rng.randrange(1, 13)
+        m = rng.randrange(1, 17) if i % 2 == 0 else rng.randrange(17, 200)
+        out.append((i, kind, m, n, k, lda, ldc))
+    return out
+
+
+@pytest.mark.parametrize("i,kind,m,n,k,lda,ldc", _strided_cases())
+def test_random_strided_shape_parity(i, kind, m, n, k, lda, ldc):
+    """A rows at a stride lda > k and C rows at ldc > n (f32): the product
+    meets the oracle and the columns past n keep their sentinel."""
+    print(f"random strided {i}: {kind} m={m} n={n} k={k} lda={lda} ldc={ldc}", flush=True)
+    a_kind = "bf16" if kind == "bf16" else "f16"
+    Afull = WL.gen_matrix((m, lda), a_kind, ("normal", 1.0), 7500 + i)
+    A = np.ascontiguousarray(Afull[:, :k])
+    W, dW = _weight(kind, n, k, 7600 + 3 * i)
+    code = {"f16": sk.F16, "bf16": sk.BF16, "q8_0": sk.Q8_0}[kind]
+    plan = sk.Plan(n, k, max(m, 16), sk.BF16 if a_kind == "bf16" else sk.F16, code, sk.F32, lda=lda, ldc=ldc)
+    C = torch.full((m, ldc), -7.0, dtype=torch.float32, device="cuda")
+    if kind.startswith("q"):
+        plan.run(m, to_dev(Afull, a_kind), dW[0], C, scales=dW[1])
+    else:
+        plan.run(m, to_dev(Afull, a_kind), dW, C)
+    torch.cuda.synchronize()
+    out = C.cpu().numpy()
+    assert np.all(out[:, n:] == -7.0)
+    got = out[:, :n]
+    if kind.startswith("q"):
+        ref = oracle.mm(A, a_kind, W[0], kind, w_scales=W[1])
+        absum = oracle.mm(A, a_kind, W[0], kind, w_scales=W[1], absolute=True)
+    else:
+        ref = oracle.mm(A, a_kind, W, kind)
+        absum = oracle.mm(A, a_kind, W, kind, absolute=True)
+    assert rel_err(got, ref) <= REL_TOL
+    assert np.all(np.abs(got - ref) <= (k + 2) * 2.0 ** -24 * absum + 1e-30)
