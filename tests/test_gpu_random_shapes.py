@@ -4,7 +4,8 @@ CPU oracle: ragged n (1 .. 700), k anywhere the formats allow (a multiple of
 8, or of 32 for the block formats), f32 and f16 outputs.  Bars: 2e-3
 max-normalised, the fp32-accumulation bound per element (plus the output's
 own rounding), and in the GEMV regime row 0 equal to the m = 1 call, bit for
-bit."""
+bit; strided A and C rows; the router step's top-k at random n, topk and m
+with equal logits, bit for bit against the oracle's ranking."""
 import random
 
 import numpy as np
@@ -126,3 +127,37 @@ def test_random_strided_shape_parity(i, kind, m, n, k, lda, ldc):
         absum = oracle.mm(A, a_kind, W, kind, absolute=True)
     assert rel_err(got, ref) <= REL_TOL
     assert np.all(np.abs(got - ref) <= (k + 2) * 2.0 ** -24 * absum + 1e-30)
+
+
+def _topk_cases(count=30, seed=2028):
+    rng = random.Random(seed)
+    out = []
+    for i in range(count):
+        n = (rng.randrange(1, 65), rng.randrange(65, 1025), rng.randrange(1025, 1501))[i % 3]
+        topk = rng.randrange(1, min(32, n) + 1)
+        m = rng.randrange(1, 17)
+        k = rng.randrange(8, 6145, 8)
+        out.append((i, m, n, k, topk))
+    return out
+
+
+@pytest.mark.parametrize("i,m,n,k,topk", _topk_cases())
+def test_random_router_topk(i, m, n, k, topk):
+    """gemv_topk at random n (register and re-reading top-k paths), topk, m
+    and k, with duplicated weight rows (equal logits): the logits meet the
+    oracle, and the indices and values are the oracle's top-k of the GPU's
+    own logits (value descending, ties to the lower column), bit for bit."""
+    print(f"random top-k {i}: m={m} n={n} k={k} topk={topk}", flush=True)
+    rng = np.random.default_rng(7800 + i)
+    W = WL.gen_matrix((n, k), "bf16", ("normal", 0.02), 7900 + i)
+    for _ in range(n // 8):
+        src, dst = rng.integers(0, n, size=2)
+        W[dst] = W[src]
+    A = WL.gen_matrix((m, k), "bf16", ("normal", 1.0), 8000 + i)
+    logits, idx, val = sk.gemv_topk(to_dev(A, "bf16"), to_dev(W, "bf16"), topk=topk, max_m=16)
+    torch.cuda.synchronize()
+    lg = logits.cpu().numpy()
+    assert rel_err(lg, oracle.mm(A, "bf16", W, "bf16")) <= REL_TOL
+    oi, ov = oracle.topk(lg.astype(np.float64), topk)
+    assert np.array_equal(idx.cpu().numpy(), oi)
+    assert np.array_equal(val.cpu().numpy().view(np.uint32), ov.astype(np.float32).view(np.uint32))
