@@ -77,3 +77,20 @@ def test_combine_edge_shapes(m, topk, d):
     # than the grid's y dimension takes (the workgroups loop over tokens)
     print(f"combine edge m={m} topk={topk} d={d}", flush=True)
     _case(m, topk, d, 6300 + m + topk)
+
+
+def _random_combine_cases(count=24, seed=2029):
+    import random
+
+    rng = random.Random(seed)
+    kinds = (("f32", "f32"), ("bf16", "f32"), ("f32", "bf16"), ("bf16", "bf16"))
+    return [(i, rng.randrange(1, 65), rng.randrange(1, 33), rng.randrange(8, 12289, 8), *kinds[i % 4],
+             i % 3 != 2) for i in range(count)]
+
+
+@pytest.mark.parametrize("i,m,topk,d,kind,out,shared", _random_combine_cases())
+def test_combine_random_shapes(i, m, topk, d, kind, out, shared):
+    # seeded random tokens, topk, width, row and output types, with and
+    # without the shared expert
+    print(f"combine random {i}: m={m} topk={topk} d={d} rows={kind} out={out} shared={shared}", flush=True)
+    _case(m, topk, d, 6400 + i, kind, out, shared)
