@@ -213,3 +213,24 @@ def test_fp32_rows_strided():
         plain_plan.run(m, dA16[:m], W, b)
         torch.cuda.synchronize()
         assert np.array_equal(bits_of(a), bits_of(b)), m
+
+
+def _random_gate_cases(count=24, seed=2030):
+    import random
+
+    rng = random.Random(seed)
+    return [(i, rng.randrange(1, 17), (rng.randrange(1, 4), rng.randrange(4, 300))[i % 2],
+             rng.randrange(8, 12289, 8)) for i in range(count)]
+
+
+@pytest.mark.parametrize("i,m,n,k", _random_gate_cases())
+def test_gate_random_shapes(i, m, n, k):
+    # seeded random rows, columns and k (fused cast, cast launch, row groups,
+    # splits inside and across workgroups), each against the oracle; and row
+    # 0 equal to the one-row call
+    print(f"gate random {i}: m={m} n={n} k={k}", flush=True)
+    A, W, got = _gate_case(m, n, k, 6600 + 2 * i)
+    _check_gate(A, W, got)
+    one = sk.gate(torch.from_numpy(A[:1]).cuda(), to_dev(W, "bf16"), max_m=16)
+    torch.cuda.synchronize()
+    assert np.array_equal(got[:1].view(np.uint32), one.cpu().numpy().view(np.uint32))
