@@ -95,8 +95,11 @@ int gemv_cols_per_wave(int64_t n, int S, int num_cus, int waves_per_cu) {
 // also holds a k split, used at the m where the cost model prefers it: k is cut
 // until the column tiles (of 64) times the splits reach an eighth of the CU
 // count (32 on 256 CUs), keeping at least four 64-wide k-tiles per split and
-// at most 16 splits, with an even number of k-tiles per split.  Depends on n,
-// k and the CU count only.
+// at most four splits, with an even number of k-tiles per split.  Depends on
+// n, k and the CU count only.  Four was the best chunk count measured on
+// MI355X for N = 96, K = 2560 over M = 512 .. 2048 (best tile and launch shape
+// per M, summed: 10 chunks 59.9 us, 5 57.0, 4 55.4, 3 57.5): fewer, longer
+// chunks cost less fixed time per block and fewer partial sums to add.
 void gemm_split(int64_t n, int64_t k, int num_cus, int* splits, int* kps) {
   const int64_t nk = (k + 63) / 64;
   const int64_t col_tiles = (n + 63) / 64;
@@ -104,7 +107,7 @@ void gemm_split(int64_t n, int64_t k, int num_cus, int* splits, int* kps) {
   if (target < 8) target = 8;
   int64_t s = (target + col_tiles - 1) / col_tiles;
   if (s > nk / 4) s = nk / 4;
-  if (s > 16) s = 16;
+  if (s > 4) s = 4;
   if (s < 1) s = 1;
   int64_t per = (nk + s - 1) / s;
   if (per % 2 != 0 && per < nk) ++per;  // even chunks: a chunked launch folds between tile pairs
@@ -155,7 +158,7 @@ const TileCost& tile_cost(int id) {
       {0.4583, 1, 0.340, 1.000},  // 128x96_w4x1
       {0.5776, 2, 0.120, 1.225},  // 64x96_w2x1
       {0.3722, 1, 0.000, 1.000},  // 32x96_w1x1
-      {0.2406, 2, 0.600, 1.000},  // 32x64_w1x2
+      {0.2406, 2, 0.400, 1.000},  // 32x64_w1x2
       {0.8760, 1, 0.080, 1.000},  // 192x128_w2x2
       {1.4250, 1, 0.000, 1.000},  // 192x256_w2x4
       {1.1030, 1, 0.145, 1.000},  // 192x192_w3x2
@@ -191,11 +194,12 @@ double tile_estimate(const skinny_plan* p, int id, int64_t m, int64_t copies, in
 }
 
 // the split launch's extra cost, fitted to MI355X runs (N = 96 and 512,
-// K = 2560): about 6 us for the short blocks' fixed costs and the reduce
-// launch, plus the fp32 partials written and read back at about 2 TB/s
+// K = 2560, four chunks of ten k-tiles): about 4.5 us for the blocks' fixed
+// costs and the reduce launch, plus the fp32 partials written and read back
+// at about 2 TB/s
 double reduce_estimate(const skinny_plan* p, int64_t m) {
   const double bytes = (double)(p->gemm_splits + 1) * (double)m * (double)p->d.n * 4.0;
-  return 6.0 + bytes / 2.0e6;
+  return 4.5 + bytes / 2.0e6;
 }
 
 struct GemmChoice {

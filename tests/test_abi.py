@@ -180,14 +180,14 @@ def test_gemv_block_shape(k, S, shape, reduce):
     (7680, 2560, 700, "192x128_w2x2"),
     (7680, 2560, 1050, "192x192_w3x2"),  # 240 blocks (192 x 256: 180; 256 x 256: 150)
     (7680, 2560, 2048, "256x256_w2x4"),
-    (96, 2560, 1024, "64x64_w2x2"),      # narrow N: k chunks, one block per chunk
-    (96, 2560, 2048, "32x32_w1x1"),      # one launch folding the chunks
+    (96, 2560, 1024, "32x64_w1x2"),      # narrow N: four k chunks, one block per chunk
+    (96, 2560, 2048, "64x64_w2x2"),      # (the same launch shape, 64-row tiles)
 ])
 def test_tile_selector_picks(n, k, m, tile):
     assert f"name={tile} " in plan(n=n, k=k, max_m=2048).info(m)
 
 
-@pytest.mark.parametrize("n,k,splits", [(96, 2560, 10), (256, 2560, 7), (512, 2560, 4), (7680, 2560, 1),
+@pytest.mark.parametrize("n,k,splits", [(96, 2560, 4), (256, 2560, 4), (512, 2560, 4), (7680, 2560, 1),
                                         (200, 512, 2), (200, 64, 1), (4864, 896, 1)])
 def test_gemm_split_depends_on_n_k_only(n, k, splits):
     # narrow N splits k so that enough blocks exist at moderate M; the split
@@ -222,8 +222,8 @@ def test_gemm_split_workspace():
     # a tile without room for two accumulator sets always splits
     big = plan(n=512, k=2560, max_m=2048, flags=sk.GEMM_ONE_LAUNCH, tile_id=0)
     assert " launch=split " in big.info(300)
-    # narrow N: 10 chunks of 4 k-tiles
-    assert plan(n=96, k=2560, max_m=2048).workspace_bytes == 10 * 2048 * 96 * 4
+    # narrow N: 4 chunks of 10 k-tiles
+    assert plan(n=96, k=2560, max_m=2048).workspace_bytes == 4 * 2048 * 96 * 4
     assert plan_status(flags=sk.GEMM_SPLIT_LAUNCH | sk.GEMM_ONE_LAUNCH) == sk.ERR_INVALID_ARG
 
 
@@ -522,7 +522,8 @@ def test_fold_launch_plan_and_workspace():
         tiles = -(-m // tm) * -(-n // tn)
         ws = int(info.split("workspace=")[1].split()[0])
         # counters for the most tiles any foldable tile has at max_m (32 x 64: 64 x 2)
-        assert ws >= 64 * 2 * 4 + tiles * 10 * tm * tn * 4
+        chunks = int(info.split(" chunks=")[1].split()[0])
+        assert ws >= 64 * 2 * 4 + tiles * chunks * tm * tn * 4
         assert fold.workspace_bytes >= ws
     # a tile that cannot fold (two accumulator sets do not fit) takes the split launch
     big = plan(n=n, k=k, max_m=max_m, flags=sk.GEMM_FOLD_LAUNCH, tile_id=0)

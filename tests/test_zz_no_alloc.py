@@ -33,14 +33,14 @@ def _static_status(plan, m, A, W, S, C, stream=None):
 @pytest.mark.skipif(gpu_available(), reason="made-up pointers must never reach a GPU")
 def test_sizes_beyond_the_static_array_are_rejected_on_the_host():
     P, Pb, Pc = (ctypes.c_void_p(x << 20) for x in (1, 2, 3))
-    # narrow N with its k chunks run as separate blocks: 10 chunks x M x 96
-    # fp32 partials; M = 9000 needs 34.6 MB of the 31 MiB data region
-    p = sk.Plan(96, 2560, 9000, sk.F16, sk.F16, sk.F16, flags=sk.GEMM_SPLIT_LAUNCH, num_cus=256)
-    assert "launch=split" in p.info(9000)
-    assert _static_status(p, 9000, P, Pb, None, Pc) == sk.ERR_SCRATCH
+    # narrow N with its k chunks run as separate blocks: 4 chunks x M x 96
+    # fp32 partials; M = 30000 needs 46.1 MB of the 31 MiB data region
+    p = sk.Plan(96, 2560, 30000, sk.F16, sk.F16, sk.F16, flags=sk.GEMM_SPLIT_LAUNCH, num_cus=256)
+    assert "launch=split" in p.info(30000) and " chunks=4 " in p.info(30000)
+    assert _static_status(p, 30000, P, Pb, None, Pc) == sk.ERR_SCRATCH
     # argument errors come first, as in skinny_mm_run
     assert _static_status(p, 0, P, Pb, None, Pc) == sk.ERR_INVALID_ARG
-    assert _static_status(p, 9000, None, Pb, None, Pc) == sk.ERR_INVALID_ARG
+    assert _static_status(p, 30000, None, Pb, None, Pc) == sk.ERR_INVALID_ARG
     # a GEMV whose k splits are summed across workgroups: 16 splits x n fp32
     # partials (256 MiB at n = 2^22; its 2 MiB of arrival counters would not
     # fit their region either)
