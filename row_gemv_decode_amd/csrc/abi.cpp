@@ -141,7 +141,7 @@ struct TileCost {
   double sigma;
 };
 
-constexpr int kCostRows = 17;  // must equal gemm_tile_count(); the plan checks it
+constexpr int kCostRows = 18;  // must equal gemm_tile_count(); the plan checks it
 
 const TileCost& tile_cost(int id) {
   // indexed like the tile table in gemm.hip
@@ -163,6 +163,7 @@ const TileCost& tile_cost(int id) {
       {1.4250, 1, 0.000, 1.000},  // 192x256_w2x4
       {1.1030, 1, 0.145, 1.000},  // 192x192_w3x2
       {0.2700, 2, 0.000, 2.000},  // 32x32_w1x1
+      {0.8000, 1, 0.080, 1.000},  // 192x96_w6x1
   };
   static_assert(sizeof(kCost) / sizeof(kCost[0]) == kCostRows, "one cost row per tile");
   return kCost[id];

@@ -741,7 +741,8 @@ typedef void (*gemm_fn)(GemmArgs);
   X(192, 128, 2, 2, 3, false, "192x128_w2x2")     \
   X(192, 256, 2, 4, 2, false, "192x256_w2x4")     \
   X(192, 192, 3, 2, 3, false, "192x192_w3x2")     \
-  X(32, 32, 1, 1, 6, true, "32x32_w1x1")
+  X(32, 32, 1, 1, 6, true, "32x32_w1x1")          \
+  X(192, 96, 6, 1, 4, false, "192x96_w6x1")
 
 // the chunked one-launch variant keeps a second set of accumulators, so only
 // tiles with at most four 32 x 32 blocks per wave get it; the fold launch

@@ -58,13 +58,13 @@ def test_abi_version_and_status_strings():
 
 def test_tile_table():
     names = sk.gemm_tiles()
-    assert len(names) == L.skinny_gemm_tile_count() == 17
+    assert len(names) == L.skinny_gemm_tile_count() == 18
     for nm in names:
         tm, rest = nm.split("x", 1)
         tn, w = rest.split("_w")
         wm, wn = w.split("x")
         assert int(tm) % (32 * int(wm)) == 0 and int(tn) % (32 * int(wn)) == 0
-    assert L.skinny_gemm_tile_name(-1) is None and L.skinny_gemm_tile_name(17) is None
+    assert L.skinny_gemm_tile_name(-1) is None and L.skinny_gemm_tile_name(18) is None
 
 
 @pytest.mark.parametrize("fields,status", [
@@ -93,7 +93,7 @@ def test_tile_table():
     (dict(flags=sk.EPILOGUE_SIGMOID | sk.FORCE_GEMM, a_dtype=sk.BF16, w_dtype=sk.BF16), sk.ERR_UNSUPPORTED),
     (dict(flags=sk.FORCE_GEMV | sk.FORCE_GEMM), sk.ERR_INVALID_ARG),
     (dict(flags=sk.FORCE_GEMV, max_m=17), sk.ERR_INVALID_ARG),
-    (dict(tile_id=17), sk.ERR_INVALID_ARG),
+    (dict(tile_id=18), sk.ERR_INVALID_ARG),
     (dict(tile_id=-2), sk.ERR_INVALID_ARG),
     (dict(num_cus=-1), sk.ERR_INVALID_ARG),
     (dict(max_m=64, k=(1 << 20) + 8), sk.ERR_SHAPE),          # GEMM path: k <= 2^20
@@ -176,7 +176,7 @@ def test_gemv_block_shape(k, S, shape, reduce):
     (7680, 2560, 150, "128x64_w2x2"),
     (7680, 2560, 306, "128x96_w4x1"),
     (7680, 2560, 448, "128x128_w2x2"),
-    (7680, 2560, 520, "192x128_w2x2"),   # 3 row tiles, 8 padded rows (256 rows: 248)
+    (7680, 2560, 520, "192x96_w6x1"),    # 3 row tiles x 80 = 240 blocks (192 x 128: 180)
     (7680, 2560, 700, "192x128_w2x2"),
     (7680, 2560, 1050, "192x192_w3x2"),  # 240 blocks (192 x 256: 180; 256 x 256: 150)
     (7680, 2560, 2048, "256x256_w2x4"),
